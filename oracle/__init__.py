@@ -1,0 +1,227 @@
+"""CPU oracle for det_gemm -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, obviously correct implementation of what the RL-Kernel operator
+page "Batch-Invariant Deterministic GEMM (det_gemm)" specifies (sections
+"Guarantees" and "Ascend NPU backend"): 32-element fp32 leaves summed in
+ascending order and rounded once to bf16 (round-to-nearest-even), merged by the
+mid-split tree of bf16 adds, reduction length capped at 32768.  The arithmetic
+lives in ``det_gemm_oracle.c``; this module only marshals numpy arrays.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP library
+and never imports it.
+
+bf16 data are numpy ``uint16`` arrays holding the bit patterns.  2-D operands
+need a unit stride along their last axis; any row stride is accepted and is
+passed on as the leading dimension.
+
+Pins (see ``tests/test_oracle_*.py``): exhaustive fp32->bf16 rounding against
+torch's conversion; the bf16 add against exact rational arithmetic; hand-derived
+leaf-order and tree-shape cases in ``tests/golden/``; exact equality with int64
+matrix products in the integer regime, for all six operations; an independent
+exact-rational brute force on tiny shapes; the half-K identity; a forward error
+bound against float64.  Parity unpinned (fixed by reading, locked by tests):
+the odd-split direction, the fp32-output reading, the backward invariance
+reading.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+MAX_R = 32768
+LEAF = 32
+
+_ERRORS = {-1: "invalid argument", -2: "reduction length must be in [1, 32768]",
+           -4: "out of host memory"}
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code):
+        super().__init__(f"oracle error {code}: {_ERRORS.get(code, 'unknown')}")
+        self.code = code
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        p, i64 = ctypes.c_void_p, ctypes.c_int64
+        for name in ("oracle_det_gemm_fwd", "oracle_det_gemm_fwd_rhs_transposed",
+                     "oracle_det_gemm_fwd_fp32", "oracle_det_gemm_da", "oracle_det_gemm_db",
+                     "oracle_det_gemm_db_transposed"):
+            f = getattr(lib, name)
+            f.argtypes = [p, i64, p, i64, p, i64, i64, i64, i64]
+            f.restype = ctypes.c_int
+        lib.oracle_det_gemm_fwd_detail.argtypes = [p, i64, p, i64, p, i64, i64, i64, i64, p, p]
+        lib.oracle_det_gemm_fwd_detail.restype = ctypes.c_int
+        lib.oracle_tree_from_leaves.argtypes = [p, i64, i64, p, p]
+        lib.oracle_tree_from_leaves.restype = ctypes.c_int
+        lib.oracle_round_bf16_array.argtypes = [p, p, i64]
+        lib.oracle_round_bf16_array.restype = None
+        lib.oracle_add_bf16_array.argtypes = [p, p, p, i64]
+        lib.oracle_add_bf16_array.restype = None
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _mat(a, name):
+    a = np.asarray(a)
+    if a.dtype != np.uint16 or a.ndim != 2:
+        raise TypeError(f"{name} must be a 2-D uint16 (bf16 bit pattern) array")
+    if a.shape[1] > 1 and a.strides[1] != 2:
+        a = np.ascontiguousarray(a)
+    if a.shape[0] > 1 and (a.strides[0] <= 0 or a.strides[0] % 2):
+        a = np.ascontiguousarray(a)
+    ld = a.strides[0] // 2 if a.shape[0] > 1 else max(a.shape[1], 1)
+    return a, ld
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc):
+    if rc != 0:
+        raise OracleError(rc)
+
+
+def fwd(A, B):
+    """C[M,N] = A[M,K] @ B[K,N] under the leaf/tree contract (bf16 out)."""
+    A, lda = _mat(A, "A")
+    B, ldb = _mat(B, "B")
+    (M, K), (K2, N) = A.shape, B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    C = np.zeros((M, N), np.uint16)
+    _check(_load().oracle_det_gemm_fwd(_ptr(A), lda, _ptr(B), ldb, _ptr(C), max(N, 1), M, N, K))
+    return C
+
+
+def fwd_rhs_transposed(A, Bt):
+    """C[M,N] = A[M,K] @ Bt[N,K]^T (weight in [N,K] layout)."""
+    A, lda = _mat(A, "A")
+    Bt, ldbt = _mat(Bt, "Bt")
+    (M, K), (N, K2) = A.shape, Bt.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    C = np.zeros((M, N), np.uint16)
+    _check(_load().oracle_det_gemm_fwd_rhs_transposed(_ptr(A), lda, _ptr(Bt), ldbt, _ptr(C),
+                                                      max(N, 1), M, N, K))
+    return C
+
+
+def fwd_fp32(A, B):
+    """As :func:`fwd`, returning the bf16 root widened to float32."""
+    A, lda = _mat(A, "A")
+    B, ldb = _mat(B, "B")
+    (M, K), (K2, N) = A.shape, B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    C = np.zeros((M, N), np.float32)
+    _check(_load().oracle_det_gemm_fwd_fp32(_ptr(A), lda, _ptr(B), ldb, _ptr(C), max(N, 1),
+                                            M, N, K))
+    return C
+
+
+def da(dC, B):
+    """dA[M,K] = dC[M,N] @ B[K,N]^T (reduction over N)."""
+    dC, lddc = _mat(dC, "dC")
+    B, ldb = _mat(B, "B")
+    (M, N), (K, N2) = dC.shape, B.shape
+    if N != N2:
+        raise ValueError("dC and B disagree on N")
+    dA = np.zeros((M, K), np.uint16)
+    _check(_load().oracle_det_gemm_da(_ptr(dC), lddc, _ptr(B), ldb, _ptr(dA), max(K, 1),
+                                      M, N, K))
+    return dA
+
+
+def db(A, dC):
+    """dB[K,N] = A[M,K]^T @ dC[M,N] (reduction over M)."""
+    A, lda = _mat(A, "A")
+    dC, lddc = _mat(dC, "dC")
+    (M, K), (M2, N) = A.shape, dC.shape
+    if M != M2:
+        raise ValueError("A and dC disagree on M")
+    dB = np.zeros((K, N), np.uint16)
+    _check(_load().oracle_det_gemm_db(_ptr(A), lda, _ptr(dC), lddc, _ptr(dB), max(N, 1),
+                                      M, N, K))
+    return dB
+
+
+def db_transposed(A, dC):
+    """dBt[N,K] = (A[M,K]^T @ dC[M,N])^T, written in [N,K] layout."""
+    A, lda = _mat(A, "A")
+    dC, lddc = _mat(dC, "dC")
+    (M, K), (M2, N) = A.shape, dC.shape
+    if M != M2:
+        raise ValueError("A and dC disagree on M")
+    dBt = np.zeros((N, K), np.uint16)
+    _check(_load().oracle_det_gemm_db_transposed(_ptr(A), lda, _ptr(dC), lddc, _ptr(dBt),
+                                                 max(K, 1), M, N, K))
+    return dBt
+
+
+def fwd_detail(A, B):
+    """Forward product plus every element's leaves [M,N,L] and the largest node
+    magnitude of its tree [M,N] (float32)."""
+    A, lda = _mat(A, "A")
+    B, ldb = _mat(B, "B")
+    (M, K), (K2, N) = A.shape, B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    L = max((K + LEAF - 1) // LEAF, 1)
+    C = np.zeros((M, N), np.uint16)
+    leaves = np.zeros((M, N, L), np.uint16)
+    big = np.zeros((M, N), np.float32)
+    _check(_load().oracle_det_gemm_fwd_detail(_ptr(A), lda, _ptr(B), ldb, _ptr(C), max(N, 1),
+                                              M, N, K, _ptr(leaves), _ptr(big)))
+    return C, leaves, big
+
+
+def tree_from_leaves(leaves):
+    """Applies the mid-split bf16 tree to the last axis of ``leaves``; returns
+    (roots, largest node magnitude) with the leading shape of ``leaves``."""
+    lv = np.ascontiguousarray(np.asarray(leaves, dtype=np.uint16))
+    L = lv.shape[-1]
+    flat = lv.reshape(-1, L)
+    out = np.zeros(flat.shape[0], np.uint16)
+    big = np.zeros(flat.shape[0], np.float32)
+    _check(_load().oracle_tree_from_leaves(_ptr(flat), flat.shape[0], L, _ptr(out), _ptr(big)))
+    return out.reshape(lv.shape[:-1]), big.reshape(lv.shape[:-1])
+
+
+def round_bf16(x):
+    """fp32 -> bf16 bit patterns, round to nearest even (element-wise)."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    out = np.empty(x.shape, np.uint16)
+    _load().oracle_round_bf16_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def add_bf16(a, b):
+    """The tree's bf16 add, element-wise over bit-pattern arrays."""
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.uint16))
+    b = np.ascontiguousarray(np.asarray(b, dtype=np.uint16))
+    if a.shape != b.shape:
+        raise ValueError("shape mismatch")
+    out = np.empty(a.shape, np.uint16)
+    _load().oracle_add_bf16_array(_ptr(a), _ptr(b), _ptr(out), a.size)
+    return out
+
+
+def num_threads():
+    """Host threads the oracle's parallel loops use."""
+    return int(_load().oracle_num_threads())

@@ -1,0 +1,275 @@
+/*
+ * CPU oracle for the batch-invariant deterministic GEMM (det_gemm).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this file or the library built from it; only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg do.  It shares no code, header or
+ * table with the HIP library.
+ *
+ * What it computes (RL-Kernel operator page "Batch-Invariant Deterministic GEMM
+ * (det_gemm)"):
+ *   - section "Guarantees": forward C = A @ B, backward dA = dC * B^T and
+ *     dB = A^T * dC; bf16 inputs with fp32 accumulation; no split-K; a fixed
+ *     K-loop order.
+ *   - section "Ascend NPU backend", bullet "Reduction tree": the reduction is cut
+ *     into 32-element leaves; each leaf is accumulated in fp32 in ascending order
+ *     and rounded once to bf16 with round-to-nearest-even; the leaves are then
+ *     merged by the mid-split tree of bf16 additions in ascending leaf order, so
+ *     that a contiguous half-K product is one child of the tree.
+ *   - same section, "Dtypes" paragraph: bf16 out (the fp32-output entry point
+ *     returns fp32); the reduction length is capped at 32768.
+ *   - same section, first bullet: the six entry points and their operand roles;
+ *     db_transposed stores the weight gradient in [N,K].
+ *
+ * Readings where the page is silent (each one is also listed in the design
+ * notes of this repository):
+ *   - mid-split of an odd range: the left child takes floor(n/2) leaves;
+ *   - a leaf starts from +0.0f and adds products in ascending reduction index;
+ *     a product of two bf16 values is exact in fp32, so multiply-then-add and
+ *     fused multiply-add agree;
+ *   - a "bf16 add" is the fp32 sum of the two bf16 values rounded once to bf16
+ *     (this equals the correctly rounded bf16 sum);
+ *   - a partial last leaf (R % 32 != 0) holds only the remaining products;
+ *   - the fp32-output entry point returns the same bf16 root widened to fp32;
+ *   - R == 0 or R > 32768 is rejected; an empty output (I == 0 or J == 0) is a
+ *     successful no-op.
+ *
+ * Build: plain C99, -O2 -fno-fast-math -ffp-contract=off, OpenMP over output
+ * rows only (each output element is computed start to finish by one thread, in
+ * the order above, so the thread count never changes a bit).
+ *
+ * bf16 values travel as their uint16_t bit patterns.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL (-1)
+#define ORACLE_EKCAP (-2)
+#define ORACLE_ENOMEM (-4)
+
+#define ORACLE_LEAF 32
+#define ORACLE_MAX_R 32768
+
+/* bf16 bit pattern -> fp32 value (exact: bf16 is the top half of an fp32). */
+static float widen(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* fp32 -> bf16, round to nearest, ties to even (page: leaves "round once to
+ * BF16 (round-to-nearest-even)").  Written from the definition: keep the top 16
+ * bits (this truncates the magnitude), then step the magnitude up by one bf16
+ * ulp when the dropped 16 bits are more than half an ulp, or exactly half and
+ * the kept value is odd.  A step up from the largest finite bf16 carries into
+ * the exponent and gives infinity, as rounding requires.  NaN maps to the quiet
+ * NaN with the same sign. */
+static uint16_t round_bf16(float x) {
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    if (isnan(x))
+        return (uint16_t)(((u >> 16) & 0x8000u) | 0x7FC0u);
+    uint32_t kept = u >> 16;
+    uint32_t dropped = u & 0xFFFFu;
+    if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u)))
+        kept += 1u;
+    return (uint16_t)kept;
+}
+
+/* The bf16 add of the tree: both operands are exact in fp32, their fp32 sum is
+ * rounded once to bf16. */
+static uint16_t add_bf16(uint16_t a, uint16_t b) {
+    float s = widen(a) + widen(b);
+    return round_bf16(s);
+}
+
+/* One leaf: the products x[r]*y[r] for r in [r0, r1), added one by one in
+ * ascending r to an fp32 sum that starts at +0, then rounded once to bf16. */
+static uint16_t leaf(const uint16_t *x, int64_t sx, const uint16_t *y, int64_t sy,
+                     int64_t r0, int64_t r1) {
+    float s = 0.0f;
+    for (int64_t r = r0; r < r1; ++r) {
+        float p = widen(x[r * sx]) * widen(y[r * sy]);
+        s = s + p;
+    }
+    return round_bf16(s);
+}
+
+/* Mid-split tree over leaves [lo, hi): a single leaf is itself; otherwise the
+ * range splits at mid = lo + floor((hi - lo) / 2), both halves are reduced the
+ * same way and their roots are joined by one bf16 add.  Also records the
+ * largest magnitude of any node (leaf or inner) in *big. */
+static uint16_t tree(const uint16_t *leaves, int64_t lo, int64_t hi, float *big) {
+    uint16_t v;
+    if (hi - lo == 1) {
+        v = leaves[lo];
+    } else {
+        int64_t mid = lo + (hi - lo) / 2;
+        uint16_t left = tree(leaves, lo, mid, big);
+        uint16_t right = tree(leaves, mid, hi, big);
+        v = add_bf16(left, right);
+    }
+    float m = fabsf(widen(v));
+    if (!(m <= *big)) /* also takes NaN */
+        *big = m;
+    return v;
+}
+
+/*
+ * The whole contraction, for any operand layout.
+ *   output element (i, j), i < I, j < J, reduction index r < R;
+ *   x(i, r) = X[i*sxi + r*sxr],  y(j, r) = Y[j*syj + r*syr];
+ *   result written to C at element offset i*sci + j*scj, as bf16 (out_f32 == 0)
+ *   or as the bf16 root widened to fp32 (out_f32 == 1).
+ * Optional outputs (NULL to skip), indexed by i*J + j:
+ *   leaves_out[(i*J + j)*L + l]  the bf16 leaves of element (i, j);
+ *   big_out[i*J + j]             the largest node magnitude of its tree.
+ */
+static int contract(const uint16_t *X, int64_t sxi, int64_t sxr,
+                    const uint16_t *Y, int64_t syj, int64_t syr,
+                    void *C, int64_t sci, int64_t scj, int out_f32,
+                    int64_t I, int64_t J, int64_t R,
+                    uint16_t *leaves_out, float *big_out) {
+    if (I < 0 || J < 0 || R < 0)
+        return ORACLE_EINVAL;
+    if (I == 0 || J == 0)
+        return ORACLE_OK;
+    if (R == 0 || R > ORACLE_MAX_R)
+        return ORACLE_EKCAP;
+    if (!X || !Y || !C)
+        return ORACLE_EINVAL;
+    const int64_t L = (R + ORACLE_LEAF - 1) / ORACLE_LEAF;
+    int failed = 0;
+
+#pragma omp parallel
+    {
+        uint16_t *lv = (uint16_t *)malloc((size_t)L * sizeof(uint16_t));
+        if (!lv) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < I; ++i) {
+            if (!lv)
+                continue;
+            for (int64_t j = 0; j < J; ++j) {
+                const uint16_t *x = X + i * sxi;
+                const uint16_t *y = Y + j * syj;
+                for (int64_t l = 0; l < L; ++l) {
+                    int64_t r0 = l * ORACLE_LEAF;
+                    int64_t r1 = r0 + ORACLE_LEAF < R ? r0 + ORACLE_LEAF : R;
+                    lv[l] = leaf(x, sxr, y, syr, r0, r1);
+                }
+                float big = 0.0f;
+                uint16_t root = tree(lv, 0, L, &big);
+                int64_t off = i * sci + j * scj;
+                if (out_f32)
+                    ((float *)C)[off] = widen(root);
+                else
+                    ((uint16_t *)C)[off] = root;
+                if (leaves_out)
+                    memcpy(leaves_out + (i * J + j) * L, lv, (size_t)L * sizeof(uint16_t));
+                if (big_out)
+                    big_out[i * J + j] = big;
+            }
+        }
+        free(lv);
+    }
+    return failed ? ORACLE_ENOMEM : ORACLE_OK;
+}
+
+/* ---- the six operations (page section "Ascend NPU backend", first bullet) ----
+ * All matrices are row-major with the given leading dimension (elements). */
+
+/* C[M,N] = A[M,K] @ B[K,N]; reduction over K. */
+int oracle_det_gemm_fwd(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                        uint16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K) {
+    return contract(A, lda, 1, B, 1, ldb, C, ldc, 1, 0, M, N, K, NULL, NULL);
+}
+
+/* C[M,N] = A[M,K] @ Bt[N,K]^T; the weight is given as [N,K]. */
+int oracle_det_gemm_fwd_rhs_transposed(const uint16_t *A, int64_t lda, const uint16_t *Bt,
+                                       int64_t ldbt, uint16_t *C, int64_t ldc, int64_t M,
+                                       int64_t N, int64_t K) {
+    return contract(A, lda, 1, Bt, ldbt, 1, C, ldc, 1, 0, M, N, K, NULL, NULL);
+}
+
+/* As det_gemm_fwd, with the bf16 root written as fp32. */
+int oracle_det_gemm_fwd_fp32(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                             float *C, int64_t ldc, int64_t M, int64_t N, int64_t K) {
+    return contract(A, lda, 1, B, 1, ldb, C, ldc, 1, 1, M, N, K, NULL, NULL);
+}
+
+/* dA[M,K] = dC[M,N] @ B[K,N]^T; reduction over N. */
+int oracle_det_gemm_da(const uint16_t *dC, int64_t lddc, const uint16_t *B, int64_t ldb,
+                       uint16_t *dA, int64_t ldda, int64_t M, int64_t N, int64_t K) {
+    return contract(dC, lddc, 1, B, ldb, 1, dA, ldda, 1, 0, M, K, N, NULL, NULL);
+}
+
+/* dB[K,N] = A[M,K]^T @ dC[M,N]; reduction over M. */
+int oracle_det_gemm_db(const uint16_t *A, int64_t lda, const uint16_t *dC, int64_t lddc,
+                       uint16_t *dB, int64_t lddb, int64_t M, int64_t N, int64_t K) {
+    return contract(A, 1, lda, dC, 1, lddc, dB, lddb, 1, 0, K, N, M, NULL, NULL);
+}
+
+/* dBt[N,K] = (A[M,K]^T @ dC[M,N])^T, stored directly in the [N,K] layout. */
+int oracle_det_gemm_db_transposed(const uint16_t *A, int64_t lda, const uint16_t *dC,
+                                  int64_t lddc, uint16_t *dBt, int64_t lddbt, int64_t M,
+                                  int64_t N, int64_t K) {
+    return contract(A, 1, lda, dC, 1, lddc, dBt, 1, lddbt, 0, K, N, M, NULL, NULL);
+}
+
+/* ---- inspection helpers for the tests ---- */
+
+/* Forward product that also returns every element's leaves ([M][N][L]) and the
+ * largest node magnitude of its tree ([M][N]); either may be NULL. */
+int oracle_det_gemm_fwd_detail(const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                               uint16_t *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                               uint16_t *leaves, float *big) {
+    return contract(A, lda, 1, B, 1, ldb, C, ldc, 1, 0, M, N, K, leaves, big);
+}
+
+/* Applies the mid-split tree to count given leaf sequences of length L each
+ * (leaves[c*L + l]); writes each root to out[c] and its largest node magnitude
+ * to big[c] (big may be NULL). */
+int oracle_tree_from_leaves(const uint16_t *leaves, int64_t count, int64_t L, uint16_t *out,
+                            float *big) {
+    if (count < 0 || L < 1 || L * ORACLE_LEAF > ORACLE_MAX_R + ORACLE_LEAF - 1)
+        return ORACLE_EINVAL;
+    for (int64_t c = 0; c < count; ++c) {
+        float b = 0.0f;
+        out[c] = tree(leaves + c * L, 0, L, &b);
+        if (big)
+            big[c] = b;
+    }
+    return ORACLE_OK;
+}
+
+/* The two scalar primitives, element-wise, for exhaustive checks. */
+void oracle_round_bf16_array(const float *x, uint16_t *out, int64_t n) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = round_bf16(x[i]);
+}
+
+void oracle_add_bf16_array(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t n) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = add_bf16(a[i], b[i]);
+}
+
+/* Threads an OpenMP parallel region of this library uses. */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
