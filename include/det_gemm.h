@@ -1,0 +1,154 @@
+/*
+ * det_gemm -- batch-invariant deterministic bf16 GEMM for gfx950 (MI355X).
+ *
+ * Contract (RL-Kernel operator page "Batch-Invariant Deterministic GEMM
+ * (det_gemm)"; sections "Guarantees" and "Ascend NPU backend"):
+ *   - bf16 inputs, fp32 accumulation, no split-K, fixed reduction order;
+ *   - the reduction (length R) is cut into L = ceil(R/32) leaves of 32
+ *     consecutive indices; each leaf's products are summed in fp32 and the sum
+ *     is rounded once to bf16 (round to nearest, ties to even);
+ *   - the leaves are merged by the mid-split tree of bf16 adds: a range of n
+ *     leaves splits into floor(n/2) on the left and the rest on the right, and
+ *     the two subtree roots are added in fp32 and rounded to bf16;
+ *   - R is capped at 32768.
+ * Hence an output row's bits depend only on that row of the left operand and on
+ * the right operand: never on M, on padding rows, on leading dimensions or on
+ * how the rows are split across calls; and when L is even, a GEMM over the first
+ * (last) half of the reduction is exactly the left (right) child of the root.
+ *
+ * Conventions for every entry point below:
+ *   - det_bf16 is the bf16 bit pattern (uint16_t).  All pointers are DEVICE
+ *     pointers; all matrices are row-major with an explicit leading dimension
+ *     in elements (ld >= row width, any alignment of the element type).
+ *   - The caller owns every buffer; the library allocates no device memory.
+ *   - The call is asynchronous on `stream` (a hipStream_t; NULL is the default
+ *     stream).  Outputs must not overlap inputs.
+ *   - Return value: DET_GEMM_OK, or a negative status.  On any error the call
+ *     launches nothing and writes nothing.
+ *       DET_GEMM_EINVAL  null pointer with a non-empty shape, negative size,
+ *                        leading dimension smaller than the row width, or an
+ *                        output range overlapping an input range;
+ *       DET_GEMM_EKCAP   reduction length R == 0 or R > 32768 (with a
+ *                        non-empty output);
+ *       DET_GEMM_EHIP    the HIP runtime reported an error (launch failure or
+ *                        no gfx950 device).
+ *     An empty output (M == 0 or N == 0; K == 0 for da/db outputs) is a
+ *     successful no-op.  Unsupported inputs are rejected, never routed to a
+ *     different arithmetic.
+ *   - The reduction-internal order of a leaf is whatever the gfx950 bf16 MFMA
+ *     does (fixed, shape-independent); the CPU definition adds the 32 products
+ *     left to right.  The det_gemm_strict_* entry points add them left to right
+ *     as well and are bit-exact to that definition.
+ */
+#ifndef DET_GEMM_H
+#define DET_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t det_bf16;
+
+#define DET_GEMM_OK 0
+#define DET_GEMM_EINVAL (-1)
+#define DET_GEMM_EKCAP (-2)
+#define DET_GEMM_EHIP (-3)
+
+#define DET_GEMM_LEAF 32
+#define DET_GEMM_MAX_REDUCTION 32768
+
+/* Forward (page section "Guarantees": C = A @ B).
+ * A [M,K] (lda), B [K,N] (ldb), C [M,N] (ldc); reduction over K. */
+int det_gemm_fwd(const det_bf16 *A, int64_t lda, const det_bf16 *B, int64_t ldb,
+                 det_bf16 *C, int64_t ldc, int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Forward with the weight given transposed, as nn.Linear stores it (page
+ * section "Ascend NPU backend", entry point fwd_rhs_transposed):
+ * C [M,N] = A [M,K] @ Bt [N,K]^T. */
+int det_gemm_fwd_rhs_transposed(const det_bf16 *A, int64_t lda, const det_bf16 *Bt,
+                                int64_t ldbt, det_bf16 *C, int64_t ldc, int64_t M, int64_t N,
+                                int64_t K, void *stream);
+
+/* Forward with fp32 output (page section "Ascend NPU backend", Dtypes: the
+ * fp32 forward returns FP32).  Same leaves and tree as det_gemm_fwd; the bf16
+ * root is widened exactly to fp32, so the result equals det_gemm_fwd widened.
+ * C is float [M,N] (ldc in floats). */
+int det_gemm_fwd_fp32(const det_bf16 *A, int64_t lda, const det_bf16 *B, int64_t ldb,
+                      float *C, int64_t ldc, int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Input gradient (page section "Guarantees": dA = dC * B^T):
+ * dA [M,K] = dC [M,N] @ B [K,N]^T; reduction over N (cap applies to N). */
+int det_gemm_da(const det_bf16 *dC, int64_t lddc, const det_bf16 *B, int64_t ldb,
+                det_bf16 *dA, int64_t ldda, int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Weight gradient (page section "Guarantees": dB = A^T * dC):
+ * dB [K,N] = A [M,K]^T @ dC [M,N]; reduction over M (cap applies to M). */
+int det_gemm_db(const det_bf16 *A, int64_t lda, const det_bf16 *dC, int64_t lddc,
+                det_bf16 *dB, int64_t lddb, int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Weight gradient stored in the canonical [N,K] layout (page section "Ascend
+ * NPU backend": db_transposed stores the weight gradient born contiguous in
+ * [N,K]): dBt [N,K] with dBt[n][k] == dB[k][n] bit for bit. */
+int det_gemm_db_transposed(const det_bf16 *A, int64_t lda, const det_bf16 *dC, int64_t lddc,
+                           det_bf16 *dBt, int64_t lddbt, int64_t M, int64_t N, int64_t K,
+                           void *stream);
+
+/* Strict-order variants of the six operations: the same contract with every
+ * leaf summed by a scalar fp32 fused multiply-add chain in ascending index
+ * order (a bf16 product is exact in fp32, so this is the left-to-right sum of
+ * the page's leaf definition).  Bit-exact to the CPU definition; slow by design.
+ * Same arguments, ownership and errors as the entry points above. */
+int det_gemm_strict_fwd(const det_bf16 *A, int64_t lda, const det_bf16 *B, int64_t ldb,
+                        det_bf16 *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                        void *stream);
+int det_gemm_strict_fwd_rhs_transposed(const det_bf16 *A, int64_t lda, const det_bf16 *Bt,
+                                       int64_t ldbt, det_bf16 *C, int64_t ldc, int64_t M,
+                                       int64_t N, int64_t K, void *stream);
+int det_gemm_strict_fwd_fp32(const det_bf16 *A, int64_t lda, const det_bf16 *B, int64_t ldb,
+                             float *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                             void *stream);
+int det_gemm_strict_da(const det_bf16 *dC, int64_t lddc, const det_bf16 *B, int64_t ldb,
+                       det_bf16 *dA, int64_t ldda, int64_t M, int64_t N, int64_t K,
+                       void *stream);
+int det_gemm_strict_db(const det_bf16 *A, int64_t lda, const det_bf16 *dC, int64_t lddc,
+                       det_bf16 *dB, int64_t lddb, int64_t M, int64_t N, int64_t K,
+                       void *stream);
+int det_gemm_strict_db_transposed(const det_bf16 *A, int64_t lda, const det_bf16 *dC,
+                                  int64_t lddc, det_bf16 *dBt, int64_t lddbt, int64_t M,
+                                  int64_t N, int64_t K, void *stream);
+
+/* Inspection: the bf16 leaves of the MFMA forward kernel (same leaf code as
+ * det_gemm_fwd), for checking that the only difference from the CPU definition
+ * is the order of additions inside a leaf.  leaves is [M][N][L] bf16,
+ * L = ceil(K/32), fully packed (no leading dimension).  Same errors as
+ * det_gemm_fwd. */
+int det_gemm_debug_leaves(const det_bf16 *A, int64_t lda, const det_bf16 *B, int64_t ldb,
+                          det_bf16 *leaves, int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Inspection: element-wise device primitives exactly as the kernels use them.
+ *   det_gemm_debug_round:  out[i] = bf16 rounding of x[i] (fp32), as the MFMA
+ *                          kernel rounds leaves and tree nodes;
+ *   det_gemm_debug_add:    out[i] = bf16 add of a[i] and b[i], as the MFMA
+ *                          kernel merges two tree nodes.
+ * Device pointers, n elements; asynchronous on stream. */
+int det_gemm_debug_round(const float *x, det_bf16 *out, int64_t n, void *stream);
+int det_gemm_debug_add(const det_bf16 *a, const det_bf16 *b, det_bf16 *out, int64_t n,
+                       void *stream);
+
+/* Inspection: pins the MFMA kernel's tile configuration (0 .. count-1) for
+ * subsequent calls on this process, or restores automatic selection (-1).
+ * Every configuration computes the same leaves and tree, so the results must
+ * not change; tests use this to show it.  Returns the number of
+ * configurations, or DET_GEMM_EINVAL for an out-of-range value. */
+int det_gemm_debug_force_config(int config);
+
+/* Human-readable text for a status code (static storage). */
+const char *det_gemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DET_GEMM_H */

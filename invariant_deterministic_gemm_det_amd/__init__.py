@@ -1,0 +1,243 @@
+"""Python binding of the det_gemm C-ABI library (libdet_gemm.so, gfx950).
+
+Argument marshalling only: every function takes torch tensors on a gfx950
+device, checks dtype/shape/stride, allocates the output if none is given and
+calls the entry point of the same name in ``include/det_gemm.h`` on torch's
+current stream.  All arithmetic runs in the library's HIP kernels; there is no
+fallback of any kind -- if the library is missing or the device is not a
+gfx950, the call raises.
+
+The operation (RL-Kernel operator page "Batch-Invariant Deterministic GEMM
+(det_gemm)", sections "Guarantees" and "Ascend NPU backend"): bf16 inputs,
+32-element fp32 leaves rounded once to bf16, leaves merged by the mid-split
+tree of bf16 adds, reduction length capped at 32768.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdet_gemm.so")
+
+OK, EINVAL, EKCAP, EHIP = 0, -1, -2, -3
+MAX_REDUCTION = 32768
+LEAF = 32
+
+_SIX = ("det_gemm_fwd", "det_gemm_fwd_rhs_transposed", "det_gemm_fwd_fp32", "det_gemm_da",
+        "det_gemm_db", "det_gemm_db_transposed")
+EXPORTS = _SIX + tuple(n.replace("det_gemm_", "det_gemm_strict_") for n in _SIX) + (
+    "det_gemm_debug_leaves", "det_gemm_debug_round", "det_gemm_debug_add",
+    "det_gemm_debug_force_config", "det_gemm_status_string")
+
+
+class DetGemmError(RuntimeError):
+    def __init__(self, code, what=""):
+        msg = _status_string(code)
+        super().__init__(f"{what}: det_gemm status {code} ({msg})" if what else
+                         f"det_gemm status {code} ({msg})")
+        self.code = code
+
+
+_lib = None
+
+
+def library_loaded():
+    return _lib is not None
+
+
+def load_library(path=LIB_PATH):
+    """Load libdet_gemm.so (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() "
+                          "(or python -m invariant_deterministic_gemm_det_amd.build)")
+    lib = ctypes.CDLL(path)
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    for name in _SIX:
+        for n in (name, name.replace("det_gemm_", "det_gemm_strict_")):
+            f = getattr(lib, n)
+            f.argtypes = [p, i64, p, i64, p, i64, i64, i64, i64, p]
+            f.restype = ctypes.c_int
+    lib.det_gemm_debug_leaves.argtypes = [p, i64, p, i64, p, i64, i64, i64, p]
+    lib.det_gemm_debug_leaves.restype = ctypes.c_int
+    lib.det_gemm_debug_round.argtypes = [p, p, i64, p]
+    lib.det_gemm_debug_round.restype = ctypes.c_int
+    lib.det_gemm_debug_add.argtypes = [p, p, p, i64, p]
+    lib.det_gemm_debug_add.restype = ctypes.c_int
+    lib.det_gemm_debug_force_config.argtypes = [ctypes.c_int]
+    lib.det_gemm_debug_force_config.restype = ctypes.c_int
+    lib.det_gemm_status_string.argtypes = [ctypes.c_int]
+    lib.det_gemm_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _status_string(code):
+    try:
+        return load_library().det_gemm_status_string(code).decode()
+    except Exception:  # library unavailable: still report the number
+        return "unknown"
+
+
+def _check(rc, what):
+    if rc != OK:
+        raise DetGemmError(rc, what)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _mat(t, name, dtype=torch.bfloat16):
+    """(pointer, leading dimension) of a 2-D tensor with unit column stride."""
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D {dtype} tensor")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be on a GPU device")
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} needs unit stride along its last dimension")
+    ld = t.stride(0) if rows > 1 else max(cols, 1)
+    return ctypes.c_void_p(t.data_ptr()), ld
+
+
+def _out(out, shape, like, dtype):
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"output must have shape {tuple(shape)}")
+    return out
+
+
+def _call(name, P, Q, out, M, N, K, what):
+    pp, ldp = _mat(P, "first operand")
+    qp, ldq = _mat(Q, "second operand")
+    op, ldo = _mat(out, "output", out.dtype)
+    with torch.cuda.device(out.device):
+        rc = getattr(load_library(), name)(pp, ldp, qp, ldq, op, ldo, M, N, K, _stream(out))
+    _check(rc, what)
+    return out
+
+
+# ---------------------------------------------------------------- the six operations
+
+def det_gemm_fwd(A, B, out=None, strict=False):
+    """C[M,N] = A[M,K] @ B[K,N] (bf16 out)."""
+    M, K = A.shape
+    N = B.shape[1]
+    if B.shape[0] != K:
+        raise ValueError("A and B disagree on K")
+    out = _out(out, (M, N), A, torch.bfloat16)
+    return _call("det_gemm_strict_fwd" if strict else "det_gemm_fwd", A, B, out, M, N, K,
+                 "det_gemm_fwd")
+
+
+def det_gemm_fwd_rhs_transposed(A, Bt, out=None, strict=False):
+    """C[M,N] = A[M,K] @ Bt[N,K]^T (weight in nn.Linear layout)."""
+    M, K = A.shape
+    N = Bt.shape[0]
+    if Bt.shape[1] != K:
+        raise ValueError("A and Bt disagree on K")
+    out = _out(out, (M, N), A, torch.bfloat16)
+    return _call("det_gemm_strict_fwd_rhs_transposed" if strict else
+                 "det_gemm_fwd_rhs_transposed", A, Bt, out, M, N, K, "det_gemm_fwd_rhs_transposed")
+
+
+def det_gemm_fwd_fp32(A, B, out=None, strict=False):
+    """As det_gemm_fwd with the bf16 root widened to float32."""
+    M, K = A.shape
+    N = B.shape[1]
+    if B.shape[0] != K:
+        raise ValueError("A and B disagree on K")
+    out = _out(out, (M, N), A, torch.float32)
+    return _call("det_gemm_strict_fwd_fp32" if strict else "det_gemm_fwd_fp32", A, B, out,
+                 M, N, K, "det_gemm_fwd_fp32")
+
+
+def det_gemm_da(dC, B, out=None, strict=False):
+    """dA[M,K] = dC[M,N] @ B[K,N]^T."""
+    M, N = dC.shape
+    K = B.shape[0]
+    if B.shape[1] != N:
+        raise ValueError("dC and B disagree on N")
+    out = _out(out, (M, K), dC, torch.bfloat16)
+    return _call("det_gemm_strict_da" if strict else "det_gemm_da", dC, B, out, M, N, K,
+                 "det_gemm_da")
+
+
+def det_gemm_db(A, dC, out=None, strict=False):
+    """dB[K,N] = A[M,K]^T @ dC[M,N]."""
+    M, K = A.shape
+    N = dC.shape[1]
+    if dC.shape[0] != M:
+        raise ValueError("A and dC disagree on M")
+    out = _out(out, (K, N), A, torch.bfloat16)
+    return _call("det_gemm_strict_db" if strict else "det_gemm_db", A, dC, out, M, N, K,
+                 "det_gemm_db")
+
+
+def det_gemm_db_transposed(A, dC, out=None, strict=False):
+    """dBt[N,K] = (A[M,K]^T @ dC[M,N])^T, written directly in [N,K]."""
+    M, K = A.shape
+    N = dC.shape[1]
+    if dC.shape[0] != M:
+        raise ValueError("A and dC disagree on M")
+    out = _out(out, (N, K), A, torch.bfloat16)
+    return _call("det_gemm_strict_db_transposed" if strict else "det_gemm_db_transposed", A, dC,
+                 out, M, N, K, "det_gemm_db_transposed")
+
+
+# ---------------------------------------------------------------- inspection
+
+def det_gemm_debug_leaves(A, B):
+    """The MFMA forward kernel's bf16 leaves, [M, N, ceil(K/32)]."""
+    M, K = A.shape
+    N = B.shape[1]
+    L = (K + LEAF - 1) // LEAF
+    out = torch.empty((M, N, L), dtype=torch.bfloat16, device=A.device)
+    ap, lda = _mat(A, "A")
+    bp, ldb = _mat(B, "B")
+    with torch.cuda.device(A.device):
+        rc = load_library().det_gemm_debug_leaves(ap, lda, bp, ldb, ctypes.c_void_p(out.data_ptr()),
+                                                  M, N, K, _stream(A))
+    _check(rc, "det_gemm_debug_leaves")
+    return out
+
+
+def det_gemm_debug_round(x):
+    """Device bf16 rounding of a float32 tensor (as the MFMA kernel rounds)."""
+    x = x.contiguous()
+    out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    with torch.cuda.device(x.device):
+        rc = load_library().det_gemm_debug_round(ctypes.c_void_p(x.data_ptr()),
+                                                 ctypes.c_void_p(out.data_ptr()), x.numel(),
+                                                 _stream(x))
+    _check(rc, "det_gemm_debug_round")
+    return out
+
+
+def det_gemm_debug_add(a, b):
+    """Device bf16 add of two bf16 tensors (as the MFMA kernel merges nodes)."""
+    a, b = a.contiguous(), b.contiguous()
+    if a.shape != b.shape or a.dtype != torch.bfloat16 or b.dtype != torch.bfloat16:
+        raise TypeError("a and b must be bf16 tensors of one shape")
+    out = torch.empty_like(a)
+    with torch.cuda.device(a.device):
+        rc = load_library().det_gemm_debug_add(ctypes.c_void_p(a.data_ptr()),
+                                               ctypes.c_void_p(b.data_ptr()),
+                                               ctypes.c_void_p(out.data_ptr()), a.numel(),
+                                               _stream(a))
+    _check(rc, "det_gemm_debug_add")
+    return out
+
+
+def det_gemm_debug_force_config(config):
+    """Pin the MFMA tile configuration (-1 restores automatic selection).
+    Returns the number of configurations."""
+    rc = load_library().det_gemm_debug_force_config(int(config))
+    if rc < 0:
+        raise DetGemmError(rc, "det_gemm_debug_force_config")
+    return rc

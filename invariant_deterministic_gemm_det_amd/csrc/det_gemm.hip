@@ -1,0 +1,454 @@
+// C-ABI of the det_gemm library (declared in include/det_gemm.h): argument
+// validation, the mapping of the six operations onto one contraction
+// X(i, r) . Y(j, r), and kernel selection.
+//
+// Operation roles (RL-Kernel operator page "Batch-Invariant Deterministic GEMM
+// (det_gemm)", section "Ascend NPU backend", first bullet: backward reuses the
+// forward kernel on transposed operands; db_transposed writes [N,K]):
+//   op                  out[i][j]   X(i, r)        Y(j, r)        R
+//   fwd, fwd_fp32       C[m][n]     A[m][k]  (K)   B[k][n]  (MN)  K
+//   fwd_rhs_transposed  C[m][n]     A[m][k]  (K)   Bt[n][k] (K)   K
+//   da                  dA[m][k]    dC[m][n] (K)   B[k][n]  (K)   N
+//   db                  dB[k][n]    A[m][k]  (MN)  dC[m][n] (MN)  M
+//   db_transposed       dBt[n][k] = the db value at (k, n), stored transposed
+// (K) = the reduction index is contiguous in memory, (MN) = the row index is.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "det_gemm.h"
+#include "mfma_launch.h"
+#include "strict_kernel.h"
+
+using namespace detgemm;
+
+namespace {
+
+constexpr int64_t kMaxLd = int64_t(1) << 23;   // keeps buffer offsets of a tile below 2^31
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+enum Op { OP_FWD, OP_RHS_T, OP_FWD_F32, OP_DA, OP_DB, OP_DB_T, OP_LEAVES };
+
+struct Mat {
+    const void *p;
+    int64_t rows, cols, ld;
+    int elem;
+};
+
+struct Problem {
+    const uint16_t *x;
+    int64_t ldx;
+    bool xk;
+    const uint16_t *y;
+    int64_t ldy;
+    bool yk;
+    void *c;
+    int64_t ldc;
+    int out;
+    int64_t I, J, R;
+};
+
+bool mat_ok(const Mat &m) {
+    if (m.rows == 0 || m.cols == 0)
+        return true;
+    if (!m.p || m.ld < m.cols || m.ld < 1 || m.ld > kMaxLd)
+        return false;
+    return true;
+}
+
+void mat_range(const Mat &m, uintptr_t &lo, uintptr_t &hi) {
+    lo = reinterpret_cast<uintptr_t>(m.p);
+    hi = lo + (uintptr_t)(((m.rows - 1) * m.ld + m.cols) * m.elem);
+}
+
+bool overlaps(const Mat &a, const Mat &b) {
+    if (a.rows == 0 || a.cols == 0 || b.rows == 0 || b.cols == 0)
+        return false;
+    uintptr_t alo, ahi, blo, bhi;
+    mat_range(a, alo, ahi);
+    mat_range(b, blo, bhi);
+    return alo < bhi && blo < ahi;
+}
+
+// Once per device: the kernels are built for gfx950 only.
+std::atomic<int> g_device_ok[64];
+int g_force_config = -1;  // tile configuration pinned for inspection, -1 = automatic
+
+int check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return DET_GEMM_EHIP;
+    if (dev < 0 || dev >= 64)
+        return DET_GEMM_EHIP;
+    int state = g_device_ok[dev].load(std::memory_order_relaxed);
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return DET_GEMM_EHIP;
+        state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_device_ok[dev].store(state, std::memory_order_relaxed);
+    }
+    return state == 1 ? DET_GEMM_OK : DET_GEMM_EHIP;
+}
+
+// ---- tree selection.  L = b * 2^a with b odd.  For b in {1, 3} the tree is a
+// perfect binary tree of depth a - k over identical blocks of b * 2^k leaves,
+// reduced by the static block evaluator; otherwise the LDS-stack walk is used.
+TreeSel pick_tree(int L, int &levels) {
+    int a = 0;
+    while (((L >> a) & 1) == 0)
+        ++a;
+    const int b = L >> a;
+    if (b == 1 && a >= 3) {
+        levels = a - 3;
+        return {TREE_BLOCK, 1, 3};
+    }
+    if (b == 3 && a >= 2) {
+        levels = a - 2;
+        return {TREE_BLOCK, 3, 2};
+    }
+    // Deepest LDS stack of the streaming post-order walk over [0, L).
+    int top = 0, deepest = 0;
+    for (int t = 0; t < L; ++t) {
+        int lo = 0, hi = L, merges = 0;
+        while (hi - lo > 1) {
+            if (hi == t + 1)
+                ++merges;
+            const int mid = lo + (hi - lo) / 2;
+            if (t < mid)
+                hi = mid;
+            else
+                lo = mid;
+        }
+        top -= merges;
+        if (t + 1 < L)
+            ++top;
+        deepest = top > deepest ? top : deepest;
+    }
+    levels = deepest;
+    return {TREE_STACK, 1, 0};
+}
+
+int pick_config(const Problem &pr, const TreeSel &t, int levels) {
+    if (g_force_config >= 0)
+        return g_force_config;
+    if (pr.I <= 16)
+        return 1;
+    // 8-wave 128x64 tiles for blocks of 8 leaves; the 4-wave 64x64 tile (twice
+    // the registers per wave) for blocks of 12 and for the LDS stack.
+    if (t.mode == TREE_BLOCK && t.tb == 1 && kTileCfgs[0].lds_bytes(levels) <= kLdsMax)
+        return 0;
+    return 2;
+}
+
+bool aligned16(const void *p, int64_t ld) {
+    return (reinterpret_cast<uintptr_t>(p) & 15) == 0 && (ld % 8) == 0;
+}
+
+int run_mfma(const Problem &pr, hipStream_t st) {
+    MfmaParams p;
+    std::memset(&p, 0, sizeof p);
+    p.x = pr.x;
+    p.ldx = pr.ldx;
+    p.y = pr.y;
+    p.ldy = pr.ldy;
+    p.c = pr.c;
+    p.ldc = pr.ldc;
+    p.I = (int32_t)pr.I;
+    p.J = (int32_t)pr.J;
+    p.R = (int32_t)pr.R;
+    p.L = (int32_t)((pr.R + 31) / 32);
+    int levels = 0;
+    const TreeSel tree = pick_tree(p.L, levels);
+    p.levels = levels;
+    const int cfg = pick_config(pr, tree, levels);
+    const TileCfg &c = kTileCfgs[cfg];
+    if (pr.out != OUT_LEAVES && c.lds_bytes(levels) > kLdsMax)
+        return DET_GEMM_EINVAL;  // only reachable with a forced configuration
+    const int64_t tiles_i = (pr.I + c.bm() - 1) / c.bm();
+    const int64_t tiles_j = (pr.J + c.bn() - 1) / c.bn();
+    if (tiles_i * tiles_j > kMaxDim)
+        return DET_GEMM_EINVAL;
+    p.tiles_j = (int32_t)tiles_j;
+    p.xvec = aligned16(pr.x, pr.ldx);
+    p.yvec = aligned16(pr.y, pr.ldy);
+    const int64_t tiles = tiles_i * tiles_j;
+
+    hipError_t e;
+    if (pr.out == OUT_LEAVES) {
+        p.levels = 0;
+        e = launch_leaves(cfg, tree, p, tiles, st);
+    } else if (pr.xk && !pr.yk && pr.out == OUT_BF16)
+        e = launch_fwd_bf16(cfg, tree, p, tiles, st);
+    else if (pr.xk && !pr.yk && pr.out == OUT_F32)
+        e = launch_fwd_f32(cfg, tree, p, tiles, st);
+    else if (pr.xk && pr.yk && pr.out == OUT_BF16)
+        e = launch_kk_bf16(cfg, tree, p, tiles, st);
+    else if (!pr.xk && !pr.yk && pr.out == OUT_BF16)
+        e = launch_nn_bf16(cfg, tree, p, tiles, st);
+    else if (!pr.xk && !pr.yk && pr.out == OUT_BF16_T)
+        e = launch_nn_bf16t(cfg, tree, p, tiles, st);
+    else
+        return DET_GEMM_EINVAL;
+    return e == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
+}
+
+int run_strict(const Problem &pr, hipStream_t st) {
+    StrictParams p;
+    p.x = pr.x;
+    p.sxi = pr.xk ? pr.ldx : 1;
+    p.sxr = pr.xk ? 1 : pr.ldx;
+    p.y = pr.y;
+    p.syj = pr.yk ? pr.ldy : 1;
+    p.syr = pr.yk ? 1 : pr.ldy;
+    p.c = pr.c;
+    if (pr.out == OUT_BF16_T) {
+        p.sci = 1;
+        p.scj = pr.ldc;
+    } else {
+        p.sci = pr.ldc;
+        p.scj = 1;
+    }
+    p.I = pr.I;
+    p.J = pr.J;
+    p.R = pr.R;
+    p.L = (int32_t)((pr.R + 31) / 32);
+    const int64_t ti = (pr.I + kStrictTile - 1) / kStrictTile;
+    const int64_t tj = (pr.J + kStrictTile - 1) / kStrictTile;
+    if (ti * tj > kMaxDim || tj > kMaxDim)
+        return DET_GEMM_EINVAL;
+    p.tiles_j = (int32_t)tj;
+    const dim3 grid((unsigned)(ti * tj)), block(256);
+    if (pr.out == OUT_F32)
+        hipLaunchKernelGGL(strict_kernel<true>, grid, block, 0, st, p);
+    else
+        hipLaunchKernelGGL(strict_kernel<false>, grid, block, 0, st, p);
+    return hipGetLastError() == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
+}
+
+// Validates the operands of `op` and builds the contraction.  Returns
+// DET_GEMM_OK with *empty set when there is nothing to do.
+int build(Op op, const void *P, int64_t ldp, const void *Q, int64_t ldq, void *Out, int64_t ldo,
+          int64_t M, int64_t N, int64_t K, Problem &pr, bool &empty) {
+    empty = false;
+    if (M < 0 || N < 0 || K < 0)
+        return DET_GEMM_EINVAL;
+    Mat in1, in2, out;
+    const uint16_t *p16 = static_cast<const uint16_t *>(P);
+    const uint16_t *q16 = static_cast<const uint16_t *>(Q);
+    switch (op) {
+    case OP_FWD:
+    case OP_FWD_F32:
+    case OP_LEAVES:
+        in1 = {P, M, K, ldp, 2};
+        in2 = {Q, K, N, ldq, 2};
+        out = {Out, M, op == OP_LEAVES ? N * ((K + 31) / 32) : N,
+               op == OP_LEAVES ? N * ((K + 31) / 32) : ldo, op == OP_FWD_F32 ? 4 : 2};
+        pr = {p16, ldp, true, q16, ldq, false, Out, ldo,
+              op == OP_FWD ? OUT_BF16 : (op == OP_FWD_F32 ? OUT_F32 : OUT_LEAVES), M, N, K};
+        break;
+    case OP_RHS_T:
+        in1 = {P, M, K, ldp, 2};
+        in2 = {Q, N, K, ldq, 2};
+        out = {Out, M, N, ldo, 2};
+        pr = {p16, ldp, true, q16, ldq, true, Out, ldo, OUT_BF16, M, N, K};
+        break;
+    case OP_DA:  // P = dC [M,N], Q = B [K,N], Out = dA [M,K]
+        in1 = {P, M, N, ldp, 2};
+        in2 = {Q, K, N, ldq, 2};
+        out = {Out, M, K, ldo, 2};
+        pr = {p16, ldp, true, q16, ldq, true, Out, ldo, OUT_BF16, M, K, N};
+        break;
+    case OP_DB:    // P = A [M,K], Q = dC [M,N], Out = dB [K,N]
+    case OP_DB_T:  // Out = dBt [N,K]
+        in1 = {P, M, K, ldp, 2};
+        in2 = {Q, M, N, ldq, 2};
+        out = op == OP_DB ? Mat{Out, K, N, ldo, 2} : Mat{Out, N, K, ldo, 2};
+        pr = {p16, ldp, false, q16, ldq, false, Out, ldo, op == OP_DB ? OUT_BF16 : OUT_BF16_T,
+              K, N, M};
+        break;
+    }
+    if (pr.I == 0 || pr.J == 0) {
+        empty = true;
+        return DET_GEMM_OK;
+    }
+    if (pr.R == 0 || pr.R > DET_GEMM_MAX_REDUCTION)
+        return DET_GEMM_EKCAP;
+    if (pr.I > kMaxDim || pr.J > kMaxDim)
+        return DET_GEMM_EINVAL;
+    if (!mat_ok(in1) || !mat_ok(in2) || !mat_ok(out))
+        return DET_GEMM_EINVAL;
+    if (overlaps(out, in1) || overlaps(out, in2))
+        return DET_GEMM_EINVAL;
+    return DET_GEMM_OK;
+}
+
+int entry(Op op, bool strict, const void *P, int64_t ldp, const void *Q, int64_t ldq, void *Out,
+          int64_t ldo, int64_t M, int64_t N, int64_t K, void *stream) {
+    Problem pr;
+    bool empty;
+    const int rc = build(op, P, ldp, Q, ldq, Out, ldo, M, N, K, pr, empty);
+    if (rc != DET_GEMM_OK || empty)
+        return rc;
+    const int dev = check_device();
+    if (dev != DET_GEMM_OK)
+        return dev;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return strict ? run_strict(pr, st) : run_mfma(pr, st);
+}
+
+// ---- element-wise inspection kernels
+__global__ void debug_round_kernel(const float *x, uint16_t *out, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        out[i] = (uint16_t)pair_bits(round_pair(x[i], 0.0f));
+}
+
+__global__ void debug_add_kernel(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        const float l = __uint_as_float((uint32_t)a[i] << 16);
+        const float r = __uint_as_float((uint32_t)b[i] << 16);
+        out[i] = (uint16_t)pair_bits(round_pair(merge(l, r), 0.0f));
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int det_gemm_fwd(const det_bf16 *A, int64_t lda, const det_bf16 *B, int64_t ldb, det_bf16 *C,
+                 int64_t ldc, int64_t M, int64_t N, int64_t K, void *stream) {
+    return entry(OP_FWD, false, A, lda, B, ldb, C, ldc, M, N, K, stream);
+}
+
+int det_gemm_fwd_rhs_transposed(const det_bf16 *A, int64_t lda, const det_bf16 *Bt, int64_t ldbt,
+                                det_bf16 *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                void *stream) {
+    return entry(OP_RHS_T, false, A, lda, Bt, ldbt, C, ldc, M, N, K, stream);
+}
+
+int det_gemm_fwd_fp32(const det_bf16 *A, int64_t lda, const det_bf16 *B, int64_t ldb, float *C,
+                      int64_t ldc, int64_t M, int64_t N, int64_t K, void *stream) {
+    return entry(OP_FWD_F32, false, A, lda, B, ldb, C, ldc, M, N, K, stream);
+}
+
+int det_gemm_da(const det_bf16 *dC, int64_t lddc, const det_bf16 *B, int64_t ldb, det_bf16 *dA,
+                int64_t ldda, int64_t M, int64_t N, int64_t K, void *stream) {
+    return entry(OP_DA, false, dC, lddc, B, ldb, dA, ldda, M, N, K, stream);
+}
+
+int det_gemm_db(const det_bf16 *A, int64_t lda, const det_bf16 *dC, int64_t lddc, det_bf16 *dB,
+                int64_t lddb, int64_t M, int64_t N, int64_t K, void *stream) {
+    return entry(OP_DB, false, A, lda, dC, lddc, dB, lddb, M, N, K, stream);
+}
+
+int det_gemm_db_transposed(const det_bf16 *A, int64_t lda, const det_bf16 *dC, int64_t lddc,
+                           det_bf16 *dBt, int64_t lddbt, int64_t M, int64_t N, int64_t K,
+                           void *stream) {
+    return entry(OP_DB_T, false, A, lda, dC, lddc, dBt, lddbt, M, N, K, stream);
+}
+
+int det_gemm_strict_fwd(const det_bf16 *A, int64_t lda, const det_bf16 *B, int64_t ldb,
+                        det_bf16 *C, int64_t ldc, int64_t M, int64_t N, int64_t K, void *stream) {
+    return entry(OP_FWD, true, A, lda, B, ldb, C, ldc, M, N, K, stream);
+}
+
+int det_gemm_strict_fwd_rhs_transposed(const det_bf16 *A, int64_t lda, const det_bf16 *Bt,
+                                       int64_t ldbt, det_bf16 *C, int64_t ldc, int64_t M,
+                                       int64_t N, int64_t K, void *stream) {
+    return entry(OP_RHS_T, true, A, lda, Bt, ldbt, C, ldc, M, N, K, stream);
+}
+
+int det_gemm_strict_fwd_fp32(const det_bf16 *A, int64_t lda, const det_bf16 *B, int64_t ldb,
+                             float *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                             void *stream) {
+    return entry(OP_FWD_F32, true, A, lda, B, ldb, C, ldc, M, N, K, stream);
+}
+
+int det_gemm_strict_da(const det_bf16 *dC, int64_t lddc, const det_bf16 *B, int64_t ldb,
+                       det_bf16 *dA, int64_t ldda, int64_t M, int64_t N, int64_t K,
+                       void *stream) {
+    return entry(OP_DA, true, dC, lddc, B, ldb, dA, ldda, M, N, K, stream);
+}
+
+int det_gemm_strict_db(const det_bf16 *A, int64_t lda, const det_bf16 *dC, int64_t lddc,
+                       det_bf16 *dB, int64_t lddb, int64_t M, int64_t N, int64_t K,
+                       void *stream) {
+    return entry(OP_DB, true, A, lda, dC, lddc, dB, lddb, M, N, K, stream);
+}
+
+int det_gemm_strict_db_transposed(const det_bf16 *A, int64_t lda, const det_bf16 *dC,
+                                  int64_t lddc, det_bf16 *dBt, int64_t lddbt, int64_t M,
+                                  int64_t N, int64_t K, void *stream) {
+    return entry(OP_DB_T, true, A, lda, dC, lddc, dBt, lddbt, M, N, K, stream);
+}
+
+int det_gemm_debug_leaves(const det_bf16 *A, int64_t lda, const det_bf16 *B, int64_t ldb,
+                          det_bf16 *leaves, int64_t M, int64_t N, int64_t K, void *stream) {
+    return entry(OP_LEAVES, false, A, lda, B, ldb, leaves, 0, M, N, K, stream);
+}
+
+int det_gemm_debug_round(const float *x, det_bf16 *out, int64_t n, void *stream) {
+    if (n < 0)
+        return DET_GEMM_EINVAL;
+    if (n == 0)
+        return DET_GEMM_OK;
+    if (!x || !out)
+        return DET_GEMM_EINVAL;
+    const int dev = check_device();
+    if (dev != DET_GEMM_OK)
+        return dev;
+    const int64_t blocks = (n + 255) / 256;
+    if (blocks > kMaxDim)
+        return DET_GEMM_EINVAL;
+    hipLaunchKernelGGL(debug_round_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), x, out, n);
+    return hipGetLastError() == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
+}
+
+int det_gemm_debug_add(const det_bf16 *a, const det_bf16 *b, det_bf16 *out, int64_t n,
+                       void *stream) {
+    if (n < 0)
+        return DET_GEMM_EINVAL;
+    if (n == 0)
+        return DET_GEMM_OK;
+    if (!a || !b || !out)
+        return DET_GEMM_EINVAL;
+    const int dev = check_device();
+    if (dev != DET_GEMM_OK)
+        return dev;
+    const int64_t blocks = (n + 255) / 256;
+    if (blocks > kMaxDim)
+        return DET_GEMM_EINVAL;
+    hipLaunchKernelGGL(debug_add_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a, b, out, n);
+    return hipGetLastError() == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
+}
+
+int det_gemm_debug_force_config(int config) {
+    if (config < -1 || config >= kNumTileCfgs)
+        return DET_GEMM_EINVAL;
+    g_force_config = config;
+    return kNumTileCfgs;
+}
+
+const char *det_gemm_status_string(int status) {
+    switch (status) {
+    case DET_GEMM_OK:
+        return "success";
+    case DET_GEMM_EINVAL:
+        return "invalid argument (null pointer, negative size, leading dimension, overlap)";
+    case DET_GEMM_EKCAP:
+        return "reduction length must be in [1, 32768]";
+    case DET_GEMM_EHIP:
+        return "HIP runtime error or no gfx950 device";
+    default:
+        return "unknown status";
+    }
+}
+
+}  // extern "C"

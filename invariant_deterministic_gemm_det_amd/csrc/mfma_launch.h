@@ -1,0 +1,96 @@
+// Host-side launch helpers for the MFMA kernel: one function per operand layout
+// and output mode, each defined in its own translation unit (mfma_*.hip) so the
+// kernel instances compile in parallel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "mfma_kernel.h"
+
+namespace detgemm {
+
+constexpr int kLdsMax = 160 * 1024;  // LDS per workgroup on gfx950
+
+// Tile configurations.  Every one computes identical bits (same leaf
+// instruction, same lane assignment, same tree); they differ in tile shape only.
+//   0: 128 x 64 tile, 8 waves of 32 x 32
+//   1:  16 x 128 tile, 4 waves of 16 x 32   (few rows)
+//   2:  64 x 64 tile, 4 waves of 32 x 32    (deep LDS stacks)
+struct TileCfg {
+    int fm, fn, wm, wn;
+    int bm() const { return 16 * fm * wm; }
+    int bn() const { return 16 * fn * wn; }
+    int nw() const { return wm * wn; }
+    int lds_bytes(int levels) const {
+        return 2 * (bm() + bn()) * 128 + levels * fm * fn * nw() * 64 * 8;
+    }
+};
+constexpr TileCfg kTileCfgs[] = {{2, 2, 4, 2}, {1, 2, 1, 4}, {2, 2, 2, 2}};
+constexpr int kNumTileCfgs = 3;
+
+struct TreeSel {
+    int mode;  // TREE_BLOCK or TREE_STACK
+    int tb;    // block base size b (1 or 3)
+    int tk;    // block = b * 2^tk leaves: 8 for b = 1, 12 for b = 3
+};
+
+template <bool XK, bool YK, int OUT, int TREE, int TB, int TK, int FM, int FN, int WM, int WN>
+hipError_t launch_one(const MfmaParams &p, int64_t tiles, hipStream_t st) {
+    typedef Engine<XK, YK, FM, FN, WM, WN> E;
+    const int lds = E::lds_bytes(p.levels);
+    if (lds > kLdsMax)
+        return hipErrorInvalidConfiguration;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&mfma_kernel<XK, YK, OUT, TREE, TB, TK, FM, FN, WM, WN>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+        if (e != hipSuccess)
+            return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((mfma_kernel<XK, YK, OUT, TREE, TB, TK, FM, FN, WM, WN>), dim3((unsigned)tiles),
+                       dim3(64 * WM * WN), lds, st, p);
+    return hipGetLastError();
+}
+
+template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN>
+hipError_t launch_trees(const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st) {
+    if constexpr (OUT == OUT_LEAVES) {
+        return launch_one<XK, YK, OUT, TREE_STACK, 1, 0, FM, FN, WM, WN>(p, tiles, st);
+    } else {
+        if (t.mode == TREE_BLOCK) {
+            if (t.tb == 1 && t.tk == 3)
+                return launch_one<XK, YK, OUT, TREE_BLOCK, 1, 3, FM, FN, WM, WN>(p, tiles, st);
+            if (t.tb == 3 && t.tk == 2)
+                return launch_one<XK, YK, OUT, TREE_BLOCK, 3, 2, FM, FN, WM, WN>(p, tiles, st);
+            return hipErrorInvalidValue;
+        }
+        return launch_one<XK, YK, OUT, TREE_STACK, 1, 0, FM, FN, WM, WN>(p, tiles, st);
+    }
+}
+
+template <bool XK, bool YK, int OUT>
+hipError_t launch_layout(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles,
+                         hipStream_t st) {
+    switch (cfg) {
+    case 0:
+        return launch_trees<XK, YK, OUT, 2, 2, 4, 2>(t, p, tiles, st);
+    case 1:
+        return launch_trees<XK, YK, OUT, 1, 2, 1, 4>(t, p, tiles, st);
+    case 2:
+        return launch_trees<XK, YK, OUT, 2, 2, 2, 2>(t, p, tiles, st);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+// Defined in mfma_<layout>.hip.
+hipError_t launch_fwd_bf16(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st);
+hipError_t launch_fwd_f32(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st);
+hipError_t launch_kk_bf16(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st);
+hipError_t launch_nn_bf16(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st);
+hipError_t launch_nn_bf16t(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st);
+hipError_t launch_leaves(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st);
+
+}  // namespace detgemm
