@@ -1,0 +1,189 @@
+"""Benchmark of the det_gemm hot path on one MI355X.
+
+One step = one pass of the whole path at the QKV-projection shape
+(M=4096, K=4096, N=6144, bf16 inputs, synthetic): the forward product
+C = X W (det_gemm_fwd, W given as [K,N]) and the two backward products of that
+layer, dX = dC W^T (det_gemm_da, reduction over N) and dW = X^T dC (det_gemm_db,
+reduction over M).  Inputs are generated on the device from fixed seeds and are
+resident in HBM before timing starts.
+
+Prints one JSON line: throughput of the step in TFLOP/s (2*M*N*K per product),
+per-product timings from HIP events on the launch stream, the roofline record
+of the dominant kernel against MI355X's dense bf16 MFMA peak, and the CPU
+oracle timed on a bounded slice of the same products on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+M, K, N = 4096, 4096, 6144
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target host time of the oracle sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="run only the GPU steps (for rocprofv3 runs)")
+    return ap.parse_args()
+
+
+def cpu_baseline(X, W, dC, target_s):
+    """The oracle, untuned, on a row slice of each of the three products."""
+    import numpy as np
+    import oracle
+    import det_workloads as Wk
+
+    x, w, d = Wk.bits(X), Wk.bits(W), Wk.bits(dC)
+    threads = oracle.num_threads()
+    # calibrate: one slice of `threads` rows of the forward product
+    rows = max(1, threads)
+    t0 = time.perf_counter()
+    oracle.fwd(x[:rows], w)
+    t_cal = time.perf_counter() - t0
+    per_row = t_cal / rows  # seconds per forward row (all threads busy)
+    rows = max(threads, int(target_s / 3.0 / max(per_row, 1e-9)) // threads * threads)
+    rows = min(rows, 512)
+    t0 = time.perf_counter()
+    oracle.fwd(x[:rows], w)                                 # C[:rows]      2*rows*N*K
+    oracle.da(d[:rows], w)                                  # dX[:rows]     2*rows*K*N
+    oracle.db(np.ascontiguousarray(x[:, :rows]), d)         # dW[:rows]     2*rows*N*M
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * N * K + 2.0 * rows * K * N + 2.0 * rows * N * M
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"CPU oracle on {rows} output rows of each product: fwd C[:{rows}], "
+                      f"da dX[:{rows}], db dW[:{rows}] of the M=4096 K=4096 N=6144 step"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(det_gemm shards by rows/columns without communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import det_workloads as Wk
+    import invariant_deterministic_gemm_det_amd as dg
+
+    dev = torch.device("cuda:0")
+    dg.load_library()
+    X = Wk.randn_bf16((M, K), 1.0, 4001, dev)
+    W = Wk.randn_bf16((K, N), 0.02, 2001, dev)
+    dC = Wk.randn_bf16((M, N), 1e-3, 4003, dev)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty((K, N), dtype=torch.bfloat16, device=dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        dg.det_gemm_fwd(X, W, out=C)
+        if ev:
+            ev[1].record()
+        dg.det_gemm_da(dC, W, out=dX)
+        if ev:
+            ev[2].record()
+        dg.det_gemm_db(X, dC, out=dW)
+        if ev:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_op = {"fwd": [], "da": [], "db": []}
+    for ev in events:
+        per_op["fwd"].append(ev[0].elapsed_time(ev[1]))
+        per_op["da"].append(ev[1].elapsed_time(ev[2]))
+        per_op["db"].append(ev[2].elapsed_time(ev[3]))
+    flop = 2.0 * M * N * K
+    ms_step = wall * 1e3 / args.steps
+    value = 3 * flop / (ms_step * 1e-3) / 1e12
+    ops = {}
+    for name, ts in per_op.items():
+        avg = sum(ts) / len(ts)
+        ops[name] = {"ms": round(avg, 4), "tflops": round(flop / (avg * 1e-3) / 1e12, 2),
+                     "min_ms": round(min(ts), 4), "max_ms": round(max(ts), 4)}
+    dom = max(ops, key=lambda k: ops[k]["ms"])
+    achieved = ops[dom]["tflops"]
+    kernel_names = {"fwd": "mfma_kernel<K-major X, MN-major Y, bf16 out>",
+                    "da": "mfma_kernel<K-major X, K-major Y, bf16 out>",
+                    "db": "mfma_kernel<MN-major X, MN-major Y, bf16 out>"}
+
+    if args.profile_only:
+        print(json.dumps({"profile_only": True, "ops": ops}))
+        return
+
+    # context, not the metric: the nondeterministic library GEMM on the forward shape
+    ctx = {}
+    try:
+        for _ in range(3):
+            torch.matmul(X, W)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            torch.matmul(X, W)
+        e1.record()
+        torch.cuda.synchronize()
+        t_mm = e0.elapsed_time(e1) / 10
+        ctx = {"torch_matmul_fwd_tflops": round(flop / (t_mm * 1e-3) / 1e12, 1),
+               "determinism_tax_fwd_pct": round((ops["fwd"]["ms"] / t_mm - 1) * 100, 1)}
+    except Exception as e:  # context only
+        ctx = {"torch_matmul_error": str(e)[:120]}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(X, W, dC, args.cpu_seconds)
+
+    line = {
+        "metric": "det_gemm TFLOP/s and % of bf16 MFMA peak at M=4096,K=4096,N=6144 (1 GPU)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "det_gemm linear layer step: fwd C=XW, da dX=dC W^T, db dW=X^T dC",
+                   "M": M, "K": K, "N": N,
+                   "inputs": "X~N(0,1), W~N(0,0.02), dC~N(0,1e-3), bf16, seeded, resident in HBM"},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": ops["fwd"]["tflops"],
+        "ops": ops,
+        "roofline": {"bound": "mfma", "kernel": f"{dom}: {kernel_names[dom]}",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "context": ctx,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
