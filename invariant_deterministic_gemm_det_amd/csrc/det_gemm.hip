@@ -139,7 +139,7 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
         return 1;
     // 8-wave 128x64 tiles for blocks of 8 leaves; the 4-wave 64x64 tile (twice
     // the registers per wave) for blocks of 12 and for the LDS stack.
-    if (t.mode == TREE_BLOCK && t.tb == 1 && kTileCfgs[0].lds_bytes(levels) <= kLdsMax)
+    if (t.mode == TREE_BLOCK && t.tb == 1 && kTileCfgs[0].lds_bytes(levels) <= kLdsMax - 1024)
         return 0;
     return 2;
 }
@@ -166,8 +166,6 @@ int run_mfma(const Problem &pr, hipStream_t st) {
     p.levels = levels;
     const int cfg = pick_config(pr, tree, levels);
     const TileCfg &c = kTileCfgs[cfg];
-    if (pr.out != OUT_LEAVES && c.lds_bytes(levels) > kLdsMax)
-        return DET_GEMM_EINVAL;  // only reachable with a forced configuration
     const int64_t tiles_i = (pr.I + c.bm() - 1) / c.bm();
     const int64_t tiles_j = (pr.J + c.bn() - 1) / c.bn();
     if (tiles_i * tiles_j > kMaxDim)
@@ -193,6 +191,8 @@ int run_mfma(const Problem &pr, hipStream_t st) {
         e = launch_nn_bf16t(cfg, tree, p, tiles, st);
     else
         return DET_GEMM_EINVAL;
+    if (e == hipErrorInvalidConfiguration)
+        return DET_GEMM_EINVAL;  // a forced configuration without LDS room for this tree
     return e == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
 }
 

@@ -64,7 +64,10 @@ struct MfmaParams {
     int32_t levels;      // TREE_BLOCK: levels above the blocks; TREE_STACK: stack depth
 };
 
-__device__ __forceinline__ int lds_key(int row) { return (row ^ (row >> 3)) & 7; }
+// 16-byte chunk swizzle of the [row][64] stage tiles: measured on gfx950 at the
+// full ds_read_b128 rate for the MFMA fragment pattern (16 consecutive rows,
+// one chunk each).
+__device__ __forceinline__ int lds_key(int row) { return (row >> 1) & 7; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, -1, 0x00020000);
@@ -213,6 +216,97 @@ __device__ __forceinline__ Frag<FM, FN> merge_frag(const Frag<FM, FN> &l, const 
     return o;
 }
 
+// ---------------------------------------------------------------- tree arithmetic
+//
+// Two ways to perform the tree's bf16 adds on a fragment (FM x FN blocks of
+// 16x16 nodes, each node an unrounded fp32 value).  Both round the two children
+// with v_cvt_pk_bf16_f32 and add them in fp32; they give identical bits for
+// finite values.
+//
+// ValuAdd: v_dot2_f32_bf16 against (1.0, 1.0) per node.  Element positions
+// never move.
+//
+// MatrixAdd: the packed pairs of a 16x16 block form the A operand of one
+// v_mfma_f32_16x16x32_bf16 whose B operand is a constant 0/1 selector: output
+// column p of A-row i is A[i][2p] + A[i][2p+1].  Both products are exact and
+// every other product is zero, so the fp32 result equals the exact sum whenever
+// that sum fits in 24 bits, and otherwise differs from it by less than the
+// distance to the nearest bf16 rounding boundary; the bf16 rounding that follows
+// is therefore that of the correctly rounded sum (checked on the device over all
+// pairs of finite bf16 values).  An MFMA output row sums a whole A row, so one
+// non-finite node (Inf * 0 = NaN) would spoil the other 15 sums of its row: the
+// kernel detects non-finite roots and recomputes such a tile with ValuAdd.
+// The add also moves element positions: the value of block element (r, c)
+// ends up where (c, r) was, so a node's layout parity is the number of adds
+// applied to it, i.e. its height in the tree modulo 2; siblings of different
+// height parity are aligned by one "flip" (an add with a zero partner).
+struct ValuAdd {
+    static constexpr bool kTransposes = false;
+    template <int FM, int FN>
+    __device__ static __forceinline__ Frag<FM, FN> merge(const Frag<FM, FN> &l,
+                                                         const Frag<FM, FN> &r, bf16x8) {
+        return merge_frag(l, r);
+    }
+    template <int FM, int FN>
+    __device__ static __forceinline__ Frag<FM, FN> flip(const Frag<FM, FN> &x, bf16x8) {
+        return x;
+    }
+};
+
+struct MatrixAdd {
+    static constexpr bool kTransposes = true;
+    template <int FM, int FN>
+    __device__ static __forceinline__ Frag<FM, FN> merge(const Frag<FM, FN> &l,
+                                                         const Frag<FM, FN> &r, bf16x8 sel) {
+        const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        Frag<FM, FN> o;
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                u32x4 pk;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    pk[v] = pair_bits(round_pair(l.v[a][b][v], r.v[a][b][v]));
+                o.v[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, pk), sel, zero, 0, 0, 0);
+            }
+        return o;
+    }
+    template <int FM, int FN>
+    __device__ static __forceinline__ Frag<FM, FN> flip(const Frag<FM, FN> &x, bf16x8 sel) {
+        const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        Frag<FM, FN> o;
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                u32x4 pk;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    pk[v] = pair_bits(round_pair(x.v[a][b][v], 0.0f));
+                o.v[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, pk), sel, zero, 0, 0, 0);
+            }
+        return o;
+    }
+};
+
+// Selector B operand for MatrixAdd: lane 16g + j holds B[8g .. 8g+7][j]; the
+// entries B[2j][j] and B[2j+1][j] are 1.0 (they sit in lane 16*(j/4) + j, dword
+// j % 4), all others 0.
+__device__ __forceinline__ bf16x8 add_selector(int lane) {
+    const int j = lane & 15, g = lane >> 4;
+    u32x4 s = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        s[q] = ((j >> 2) == g && (j & 3) == q) ? 0x3F803F80u : 0u;
+    return __builtin_bit_cast(bf16x8, s);
+}
+
+// Height of the mid-split tree over n leaves: ceil(log2 n).
+constexpr int tree_height(int n) { return n <= 1 ? 0 : 1 + tree_height(n - n / 2); }
+
 // ---------------------------------------------------------------- engine
 //
 // The per-workgroup pipeline: operand staging, the two MFMA leaves of a stage,
@@ -351,11 +445,12 @@ struct Engine {
 
 // Evaluates the subtree over the BLK leaves of one aligned block, starting at
 // global stage `s0` (even), by compile-time recursion over the leaf range.
-template <class E, int BLK>
+template <class E, int BLK, class Arith>
 struct BlockEval {
     typedef typename E::F F;
     E &e;
     int s0;
+    bf16x8 sel;
     F odd;  // second leaf of the most recent stage
 
     template <int T>
@@ -375,9 +470,14 @@ struct BlockEval {
             return leaf<LO>();
         } else {
             constexpr int MID = LO + (HI - LO) / 2;
-            const F l = eval<LO, MID>();
+            F l = eval<LO, MID>();
             const F r = eval<MID, HI>();
-            return merge_frag(l, r);
+            // the left half is never taller; align layout parities of the two
+            // children when their heights differ by one
+            if constexpr (Arith::kTransposes &&
+                          (tree_height(MID - LO) % 2) != (tree_height(HI - MID) % 2))
+                l = Arith::flip(l, sel);
+            return Arith::merge(l, r, sel);
         }
     }
 };
@@ -406,6 +506,64 @@ __device__ __forceinline__ void quad_bits(const Frag<FM, FN> &x, int a, int b, u
     v4[1] = (uint16_t)(lo >> 16);
     v4[2] = (uint16_t)hi;
     v4[3] = (uint16_t)(hi >> 16);
+}
+
+// Height of the mid-split tree over L leaves at run time: ceil(log2 L).
+__device__ __forceinline__ int tree_height_rt(int L) { return L <= 1 ? 0 : 32 - __clz(L - 1); }
+
+// Blocks of BLK leaves, then the climb through the levels above them; the
+// pending left siblings of the upper levels wait in LDS.
+template <class E, int BLK, class Arith>
+__device__ __forceinline__ void run_blocks(E &e, const MfmaParams &p, bf16x8 sel,
+                                           typename E::F &root) {
+    const int nblk = p.L / BLK;
+    for (int blk = 0; blk < nblk; ++blk) {
+        BlockEval<E, BLK, Arith> ev{e, blk * (BLK / 2), sel};
+        typename E::F v = ev.template eval<0, BLK>();
+        int h = 0;
+        while (h < p.levels && ((blk >> h) & 1)) {
+            v = Arith::merge(e.unpark(h), v, sel);
+            ++h;
+        }
+        if (h < p.levels)
+            e.park(h, v);
+        else
+            root = v;
+    }
+}
+
+// Rounds the root to bf16 and stores it.  With odd layout parity, lane
+// 16g + c, register v holds block element (row c, column 4g + v); otherwise
+// element (row 4g + v, column c).  A zero root is stored as +0, the sign the
+// sequential definition gives every exact zero.
+template <int OUT, int FM, int FN>
+__device__ __forceinline__ void store_root(const MfmaParams &p, const Frag<FM, FN> &root,
+                                           bool odd, int i0, int j0, int wm, int wn, int lane) {
+    const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+            uint16_t v4[4];
+            quad_bits(root, a, b, v4);
+            const int ib = i0 + wm * FM * 16 + a * 16;
+            const int jb = j0 + wn * FN * 16 + b * 16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int i = ib + (odd ? c : 4 * g + v);
+                const int j = jb + (odd ? 4 * g + v : c);
+                const uint16_t h = (v4[v] & 0x7FFF) ? v4[v] : (uint16_t)0;
+                if (i < p.I && j < p.J) {
+                    if (OUT == OUT_BF16)
+                        static_cast<uint16_t *>(p.c)[(int64_t)i * p.ldc + j] = h;
+                    else if (OUT == OUT_F32)
+                        static_cast<float *>(p.c)[(int64_t)i * p.ldc + j] =
+                            __uint_as_float((uint32_t)h << 16);
+                    else
+                        static_cast<uint16_t *>(p.c)[(int64_t)j * p.ldc + i] = h;
+                }
+            }
+        }
 }
 
 // ---------------------------------------------------------------- the kernel
@@ -457,20 +615,24 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_kernel(MfmaParams p) {
         }
         return;
     } else if constexpr (TREE == TREE_BLOCK) {
-        constexpr int BLK = TB << TK;  // leaves per block (even)
-        const int nblk = p.L / BLK;
-        for (int blk = 0; blk < nblk; ++blk) {
-            BlockEval<E, BLK> ev{e, blk * (BLK / 2)};
-            F v = ev.template eval<0, BLK>();
-            int h = 0;
-            while (h < p.levels && ((blk >> h) & 1)) {
-                v = merge_frag(e.unpark(h), v);
-                ++h;
-            }
-            if (h < p.levels)
-                e.park(h, v);
-            else
-                root = v;
+        const bf16x8 sel = add_selector(lane);
+        run_blocks<E, TB << TK, MatrixAdd>(e, p, sel, root);
+        // A non-finite root may have spilled NaN into the other sums of its
+        // MatrixAdd rows: recompute such a tile with per-element VALU adds.
+        bool nonfinite = false;
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    nonfinite |= !(__builtin_fabsf(root.v[a][b][v]) <= 3.40282347e38f);
+        if (__syncthreads_or(nonfinite)) {
+            e.prologue();
+            run_blocks<E, TB << TK, ValuAdd>(e, p, sel, root);
+            store_root<OUT>(p, root, false, i0, j0, wm, wn, lane);
+        } else {
+            store_root<OUT>(p, root, (tree_height_rt(p.L) & 1) != 0, i0, j0, wm, wn, lane);
         }
     } else {
         int top = 0;
@@ -498,30 +660,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mfma_kernel(MfmaParams p) {
                 }
             }
         }
-    }
-
-    if constexpr (OUT != OUT_LEAVES) {
-#pragma unroll
-        for (int a = 0; a < FM; ++a)
-#pragma unroll
-            for (int b = 0; b < FN; ++b) {
-                uint16_t v4[4];
-                quad_bits(root, a, b, v4);
-                const int j = j0 + wn * FN * 16 + b * 16 + (lane & 15);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int i = i0 + wm * FM * 16 + a * 16 + 4 * (lane >> 4) + v;
-                    if (i < p.I && j < p.J) {
-                        if (OUT == OUT_BF16)
-                            static_cast<uint16_t *>(p.c)[(int64_t)i * p.ldc + j] = v4[v];
-                        else if (OUT == OUT_F32)
-                            static_cast<float *>(p.c)[(int64_t)i * p.ldc + j] =
-                                __uint_as_float((uint32_t)v4[v] << 16);
-                        else
-                            static_cast<uint16_t *>(p.c)[(int64_t)j * p.ldc + i] = v4[v];
-                    }
-                }
-            }
+        store_root<OUT>(p, root, false, i0, j0, wm, wn, lane);
     }
 }
 

@@ -34,21 +34,29 @@ struct TreeSel {
     int tk;    // block = b * 2^tk leaves: 8 for b = 1, 12 for b = 3
 };
 
+// Launches one kernel instance.  The dynamic LDS limit of each instance is
+// raised once to what its static LDS leaves of the 160 KB; a request beyond it
+// returns hipErrorInvalidConfiguration without launching.
 template <bool XK, bool YK, int OUT, int TREE, int TB, int TK, int FM, int FN, int WM, int WN>
 hipError_t launch_one(const MfmaParams &p, int64_t tiles, hipStream_t st) {
     typedef Engine<XK, YK, FM, FN, WM, WN> E;
-    const int lds = E::lds_bytes(p.levels);
-    if (lds > kLdsMax)
-        return hipErrorInvalidConfiguration;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&mfma_kernel<XK, YK, OUT, TREE, TB, TK, FM, FN, WM, WN>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+    const void *fn = reinterpret_cast<const void *>(
+        &mfma_kernel<XK, YK, OUT, TREE, TB, TK, FM, FN, WM, WN>);
+    static int max_dynamic = -1;
+    if (max_dynamic < 0) {
+        hipFuncAttributes attr;
+        hipError_t e = hipFuncGetAttributes(&attr, fn);
         if (e != hipSuccess)
             return e;
-        attr_set = true;
+        const int room = kLdsMax - (int)attr.sharedSizeBytes;
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, room);
+        if (e != hipSuccess)
+            return e;
+        max_dynamic = room;
     }
+    const int lds = E::lds_bytes(p.levels);
+    if (lds > max_dynamic)
+        return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((mfma_kernel<XK, YK, OUT, TREE, TB, TK, FM, FN, WM, WN>), dim3((unsigned)tiles),
                        dim3(64 * WM * WN), lds, st, p);
     return hipGetLastError();
