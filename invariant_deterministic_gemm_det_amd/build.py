@@ -27,7 +27,8 @@ OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["det_gemm.hip", "mfma_fwd_bf16.hip", "mfma_fwd_f32.hip", "mfma_kk_bf16.hip",
            "mfma_nn_bf16.hip", "mfma_nn_bf16t.hip", "mfma_leaves.hip"]
-HEADERS = ["bf16_device.h", "strict_kernel.h", "mfma_kernel.h", "mfma_launch.h"]
+HEADERS = ["bf16_device.h", "strict_kernel.h", "mfma_kernel.h", "mfma_fast.h",
+           "mfma_launch.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

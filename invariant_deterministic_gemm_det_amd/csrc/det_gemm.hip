@@ -132,6 +132,18 @@ TreeSel pick_tree(int L, int &levels) {
     return {TREE_STACK, 1, 0};
 }
 
+bool aligned16(const void *p, int64_t ld) {
+    return (reinterpret_cast<uintptr_t>(p) & 15) == 0 && (ld % 8) == 0;
+}
+
+// The direct-to-LDS kernels take whole 64-index stages, 16-byte aligned rows
+// and, for an operand whose row index is contiguous, whole 8-row chunks.
+bool fast_ok(const Problem &pr, const TreeSel &t) {
+    return pr.out != OUT_LEAVES && t.mode == TREE_BLOCK && pr.R % 64 == 0 &&
+           aligned16(pr.x, pr.ldx) && aligned16(pr.y, pr.ldy) && (pr.xk || pr.I % 8 == 0) &&
+           (pr.yk || pr.J % 8 == 0);
+}
+
 int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     if (g_force_config >= 0)
         return g_force_config;
@@ -139,13 +151,16 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
         return 1;
     // 8-wave 128x64 tiles for blocks of 8 leaves; the 4-wave 64x64 tile (twice
     // the registers per wave) for blocks of 12 and for the LDS stack.
-    if (t.mode == TREE_BLOCK && t.tb == 1 && kTileCfgs[0].lds_bytes(levels) <= kLdsMax - 1024)
+    const bool wide = t.mode == TREE_BLOCK && t.tb == 1;
+    if (fast_ok(pr, t)) {
+        if (wide && kTileCfgs[3].lds_bytes(levels) <= kLdsMax - 1024)
+            return 3;
+        if (kTileCfgs[4].lds_bytes(levels) <= kLdsMax - 1024)
+            return 4;
+    }
+    if (wide && kTileCfgs[0].lds_bytes(levels) <= kLdsMax - 1024)
         return 0;
     return 2;
-}
-
-bool aligned16(const void *p, int64_t ld) {
-    return (reinterpret_cast<uintptr_t>(p) & 15) == 0 && (ld % 8) == 0;
 }
 
 int run_mfma(const Problem &pr, hipStream_t st) {
@@ -166,6 +181,8 @@ int run_mfma(const Problem &pr, hipStream_t st) {
     p.levels = levels;
     const int cfg = pick_config(pr, tree, levels);
     const TileCfg &c = kTileCfgs[cfg];
+    if (c.fast && !fast_ok(pr, tree))
+        return DET_GEMM_EINVAL;  // a forced fast configuration this problem does not fit
     const int64_t tiles_i = (pr.I + c.bm() - 1) / c.bm();
     const int64_t tiles_j = (pr.J + c.bn() - 1) / c.bn();
     if (tiles_i * tiles_j > kMaxDim)

@@ -5,7 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "mfma_kernel.h"
+#include "mfma_fast.h"
 
 namespace detgemm {
 
@@ -16,17 +16,21 @@ constexpr int kLdsMax = 160 * 1024;  // LDS per workgroup on gfx950
 //   0: 128 x 64 tile, 8 waves of 32 x 32
 //   1:  16 x 128 tile, 4 waves of 16 x 32   (few rows)
 //   2:  64 x 64 tile, 4 waves of 32 x 32    (deep LDS stacks)
+//   3: configuration 0 on the direct-to-LDS fast path (mfma_fast.h)
+//   4: configuration 2 on the direct-to-LDS fast path
 struct TileCfg {
     int fm, fn, wm, wn;
+    bool fast;
     int bm() const { return 16 * fm * wm; }
     int bn() const { return 16 * fn * wn; }
     int nw() const { return wm * wn; }
     int lds_bytes(int levels) const {
-        return 2 * (bm() + bn()) * 128 + levels * fm * fn * nw() * 64 * 8;
+        return (fast ? 3 : 2) * (bm() + bn()) * 128 + levels * fm * fn * nw() * 64 * 8;
     }
 };
-constexpr TileCfg kTileCfgs[] = {{2, 2, 4, 2}, {1, 2, 1, 4}, {2, 2, 2, 2}};
-constexpr int kNumTileCfgs = 3;
+constexpr TileCfg kTileCfgs[] = {{2, 2, 4, 2, false}, {1, 2, 1, 4, false}, {2, 2, 2, 2, false},
+                                 {2, 2, 4, 2, true},  {2, 2, 2, 2, true}};
+constexpr int kNumTileCfgs = 5;
 
 struct TreeSel {
     int mode;  // TREE_BLOCK or TREE_STACK
@@ -37,11 +41,17 @@ struct TreeSel {
 // Launches one kernel instance.  The dynamic LDS limit of each instance is
 // raised once to what its static LDS leaves of the 160 KB; a request beyond it
 // returns hipErrorInvalidConfiguration without launching.
-template <bool XK, bool YK, int OUT, int TREE, int TB, int TK, int FM, int FN, int WM, int WN>
+template <bool FAST, bool XK, bool YK, int OUT, int TREE, int TB, int TK, int FM, int FN, int WM,
+          int WN>
 hipError_t launch_one(const MfmaParams &p, int64_t tiles, hipStream_t st) {
-    typedef Engine<XK, YK, FM, FN, WM, WN> E;
-    const void *fn = reinterpret_cast<const void *>(
-        &mfma_kernel<XK, YK, OUT, TREE, TB, TK, FM, FN, WM, WN>);
+    typedef typename std::conditional<FAST, FastEngine<XK, YK, FM, FN, WM, WN>,
+                                      Engine<XK, YK, FM, FN, WM, WN>>::type E;
+    void (*kernel)(MfmaParams);
+    if constexpr (FAST)
+        kernel = &mfma_fast_kernel<XK, YK, OUT, TB, TK, FM, FN, WM, WN>;
+    else
+        kernel = &mfma_kernel<XK, YK, OUT, TREE, TB, TK, FM, FN, WM, WN>;
+    const void *fn = reinterpret_cast<const void *>(kernel);
     static int max_dynamic = -1;
     if (max_dynamic < 0) {
         hipFuncAttributes attr;
@@ -57,24 +67,32 @@ hipError_t launch_one(const MfmaParams &p, int64_t tiles, hipStream_t st) {
     const int lds = E::lds_bytes(p.levels);
     if (lds > max_dynamic)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((mfma_kernel<XK, YK, OUT, TREE, TB, TK, FM, FN, WM, WN>), dim3((unsigned)tiles),
-                       dim3(64 * WM * WN), lds, st, p);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)tiles), dim3(64 * WM * WN), lds, st, p);
     return hipGetLastError();
 }
 
-template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN>
+template <bool FAST, bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN>
 hipError_t launch_trees(const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st) {
-    if constexpr (OUT == OUT_LEAVES) {
-        return launch_one<XK, YK, OUT, TREE_STACK, 1, 0, FM, FN, WM, WN>(p, tiles, st);
+    if constexpr (FAST) {
+        // block trees only, never the leaf dump (checked by the caller)
+        if constexpr (OUT != OUT_LEAVES) {
+            if (t.mode == TREE_BLOCK && t.tb == 1 && t.tk == 3)
+                return launch_one<true, XK, YK, OUT, TREE_BLOCK, 1, 3, FM, FN, WM, WN>(p, tiles, st);
+            if (t.mode == TREE_BLOCK && t.tb == 3 && t.tk == 2)
+                return launch_one<true, XK, YK, OUT, TREE_BLOCK, 3, 2, FM, FN, WM, WN>(p, tiles, st);
+        }
+        return hipErrorInvalidValue;
+    } else if constexpr (OUT == OUT_LEAVES) {
+        return launch_one<false, XK, YK, OUT, TREE_STACK, 1, 0, FM, FN, WM, WN>(p, tiles, st);
     } else {
         if (t.mode == TREE_BLOCK) {
             if (t.tb == 1 && t.tk == 3)
-                return launch_one<XK, YK, OUT, TREE_BLOCK, 1, 3, FM, FN, WM, WN>(p, tiles, st);
+                return launch_one<false, XK, YK, OUT, TREE_BLOCK, 1, 3, FM, FN, WM, WN>(p, tiles, st);
             if (t.tb == 3 && t.tk == 2)
-                return launch_one<XK, YK, OUT, TREE_BLOCK, 3, 2, FM, FN, WM, WN>(p, tiles, st);
+                return launch_one<false, XK, YK, OUT, TREE_BLOCK, 3, 2, FM, FN, WM, WN>(p, tiles, st);
             return hipErrorInvalidValue;
         }
-        return launch_one<XK, YK, OUT, TREE_STACK, 1, 0, FM, FN, WM, WN>(p, tiles, st);
+        return launch_one<false, XK, YK, OUT, TREE_STACK, 1, 0, FM, FN, WM, WN>(p, tiles, st);
     }
 }
 
@@ -83,11 +101,15 @@ hipError_t launch_layout(int cfg, const TreeSel &t, const MfmaParams &p, int64_t
                          hipStream_t st) {
     switch (cfg) {
     case 0:
-        return launch_trees<XK, YK, OUT, 2, 2, 4, 2>(t, p, tiles, st);
+        return launch_trees<false, XK, YK, OUT, 2, 2, 4, 2>(t, p, tiles, st);
     case 1:
-        return launch_trees<XK, YK, OUT, 1, 2, 1, 4>(t, p, tiles, st);
+        return launch_trees<false, XK, YK, OUT, 1, 2, 1, 4>(t, p, tiles, st);
     case 2:
-        return launch_trees<XK, YK, OUT, 2, 2, 2, 2>(t, p, tiles, st);
+        return launch_trees<false, XK, YK, OUT, 2, 2, 2, 2>(t, p, tiles, st);
+    case 3:
+        return launch_trees<true, XK, YK, OUT, 2, 2, 4, 2>(t, p, tiles, st);
+    case 4:
+        return launch_trees<true, XK, YK, OUT, 2, 2, 2, 2>(t, p, tiles, st);
     default:
         return hipErrorInvalidValue;
     }

@@ -329,6 +329,76 @@ def test_mfma_tile_configs_identical(dev, K):
         dg.det_gemm_debug_force_config(-1)
 
 
+# Tile configurations 3 and 4 are the direct-to-LDS kernels (whole 64-index
+# stages, 16-byte aligned rows, 8-row chunks of operands whose row index is
+# contiguous); 2 is the general kernel they must reproduce bit for bit.
+FAST_SHAPES = [(200, 192, 256), (256, 136, 768), (320, 256, 4096), (128, 64, 12288),
+               (72, 64, 32768)]
+GENERAL_CFG, FAST_CFGS = 2, (3, 4)
+
+
+def _six_forced(cfg, A, B, dC):
+    """The six ops with the tile configuration pinned; None where the pinned
+    kernel does not take the problem (EINVAL)."""
+    dg.det_gemm_debug_force_config(cfg)
+    out = {}
+    try:
+        Bt = B.t().contiguous()
+        calls = {
+            "fwd": lambda: dg.det_gemm_fwd(A, B),
+            "fwd_rhs_transposed": lambda: dg.det_gemm_fwd_rhs_transposed(A, Bt),
+            "fwd_fp32": lambda: dg.det_gemm_fwd_fp32(A, B),
+            "da": lambda: dg.det_gemm_da(dC, B),
+            "db": lambda: dg.det_gemm_db(A, dC),
+            "db_transposed": lambda: dg.det_gemm_db_transposed(A, dC),
+        }
+        for op, f in calls.items():
+            try:
+                out[op] = _as_bits(f())
+            except dg.DetGemmError as e:
+                assert e.code == dg.EINVAL, (op, e.code)
+                out[op] = None
+    finally:
+        dg.det_gemm_debug_force_config(-1)
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", FAST_SHAPES)
+def test_fast_path_matches_general_kernel(dev, M, N, K):
+    say("direct-to-LDS kernels vs general kernel, six ops", M, N, K)
+    A, B, dC = _inputs(M, N, K, 900 + K, sigma=0.02)
+    Ad, Bd, dCd = A.to(dev), B.to(dev), dC.to(dev)
+    ref = _six_forced(GENERAL_CFG, Ad, Bd, dCd)
+    assert all(v is not None for v in ref.values())
+    ran = 0
+    for cfg in FAST_CFGS:
+        got = _six_forced(cfg, Ad, Bd, dCd)
+        for op, g in got.items():
+            if g is None:
+                continue
+            ran += 1
+            assert np.array_equal(g, ref[op]), (cfg, op)
+    print("fast-path (config, op) runs compared:", ran)
+    assert ran >= 3
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 192, 256), (256, 136, 256), (256, 256, 256)])
+def test_fast_path_integer_regime_bit_exact(dev, M, N, K):
+    say("direct-to-LDS kernels, integer regime vs oracle", M, N, K)
+    A = W.int_bf16((M, K), 910 + K)
+    B = W.int_bf16((K, N), 920 + K)
+    dC = W.int_bf16((M, N), 930 + K)
+    want = _six_oracle(A, B, dC)
+    ran = 0
+    for cfg in FAST_CFGS:
+        got = _six_forced(cfg, A.to(dev), B.to(dev), dC.to(dev))
+        for op, g in got.items():
+            if g is not None:
+                ran += 1
+                assert np.array_equal(g, _oracle_bits(want[op])), (cfg, op)
+    assert ran >= 4
+
+
 @pytest.mark.parametrize("K", [4096, 12288, 32768, 192])
 def test_mfma_half_k_identity(dev, K):
     say("mfma half-K identity", K)
