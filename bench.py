@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 M, K, N = 4096, 4096, 6144
+COPY_BYTES = 256 << 20
 
 
 def parse():
@@ -35,6 +36,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--profile-only", action="store_true",
                     help="run only the GPU steps (for rocprofv3 runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="with --profile-only: also run a plain device copy of known size, "
+                         "the reference for the HBM byte counters")
     return ap.parse_args()
 
 
@@ -132,6 +136,13 @@ def main():
                     "db": "mfma_kernel<MN-major X, MN-major Y, bf16 out>"}
 
     if args.profile_only:
+        if args.copy_calibration:
+            # 256 MiB read + 256 MiB written per launch, far beyond the caches
+            src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
         print(json.dumps({"profile_only": True, "ops": ops}))
         return
 

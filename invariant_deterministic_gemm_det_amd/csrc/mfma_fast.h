@@ -5,8 +5,11 @@
 // Differences from the general kernel, all in the data movement:
 //   * operands go from global memory straight into LDS with
 //     buffer_load_dwordx4 ... lds (each lane writes 16 bytes at M0 + 16*lane),
-//     three stage buffers deep, so a stage's loads are issued two stages ahead
-//     and no vector registers or ds_write instructions carry them;
+//     three stage buffers deep, and no vector registers or ds_write
+//     instructions carry them;
+//   * software pipelining: the fragment reads of stage s + 1 are issued before
+//     the MFMAs of stage s, and a buffer is refilled (stage s + 3) as soon as
+//     its operands are in registers;
 //   * a K-major operand tile is stored [row][64 reduction indices] with its
 //     16-byte chunks XOR-swizzled by (row >> 1) & 7 and read with one
 //     ds_read_b128 per MFMA fragment, as in the general kernel;
@@ -183,57 +186,83 @@ struct FastEngine {
 
     static constexpr int LOADS = DirectStager<XK, BM, NW>::PER_WAVE + DirectStager<YK, BN, NW>::PER_WAVE;
 
+    // MFMA operands of two stages: set s & 1 holds stage s while stage s + 1
+    // is read into the other set.
+    bf16x8 fa[2][2][FM], fb[2][2][FN];  // [set][leaf][fragment]
+
     __device__ __forceinline__ void issue(int s) {
         char *buf = smem + (s % NBUF) * BUF;
         sx.issue(s, buf);
         sy.issue(s, buf + XB);
     }
 
+    template <int SET>
+    __device__ __forceinline__ void read_frags(int s) {
+        const char *buf = smem + (s % NBUF) * BUF;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int a = 0; a < FM; ++a)
+                fa[SET][h][a] = fx[a].read(buf, h);
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+                fb[SET][h][b] = fy[b].read(buf + XB, h);
+        }
+    }
+
+    // Joins the workgroup once this wave's loads are done up to `keep` stages
+    // of loads in flight; lgkmcnt(0) first retires this wave's LDS reads, so
+    // after the barrier no wave still reads a buffer it has consumed.
+    __device__ __forceinline__ void sync(int keep) {
+        if (keep >= 2)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LOADS) : "memory");
+        else if (keep == 1)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LOADS) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+
+    // Stages 0, 1, 2 in flight; stage 0 in LDS and read into set 0.
     __device__ __forceinline__ void prologue() {
         issue(0);
         if (S > 1)
             issue(1);
+        if (S > 2)
+            issue(2);
+        sync(S - 1);
+        read_frags<0>(0);
     }
 
-    // Both leaves of stage s.  Waits for this wave's loads of stage s, joins
-    // the workgroup (after which the whole stage is in LDS and no wave still
-    // reads the buffer of stage s - 1), issues the loads of stage s + 2 into
-    // that buffer and computes the two leaves.
-    template <int PAR_UNUSED>
+    // Both leaves of stage s (operands in set PAR = s & 1).  Before its MFMAs:
+    // waits for stage s + 1 to land (stage s + 2 may stay in flight), joins
+    // the workgroup, refills the buffer of stage s -- whose operands are
+    // already in registers -- with stage s + 3, and starts reading stage s + 1
+    // into the other set, so those LDS reads overlap this stage's MFMAs.
+    //
+    // The reads are issued even after the last stage (from a buffer no load
+    // targets any more; the values are never used): with them on every path,
+    // the compiler's wait before this stage's MFMAs only needs the older reads
+    // of set PAR, instead of draining the ones just issued.
+    template <int PAR>
     __device__ __forceinline__ void stage(int s, F &l0, F &l1) {
-        // This wave's loads of stage s are done once at most those of stage
-        // s + 1 are in flight; the barrier then makes the whole stage visible
-        // and, with every wave's LDS reads of stage s - 1 drained (lgkmcnt),
-        // frees that buffer for the loads of stage s + 2.
-        if (s + 1 < S)
-            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LOADS) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (s + 2 < S)
-            issue(s + 2);
-        const char *buf = smem + (s % NBUF) * BUF;
+        sync(s + 2 < S ? 1 : 0);
+        if (s + 3 < S)
+            issue(s + 3);
+        read_frags<PAR ^ 1>(s + 1);
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
         const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            bf16x8 fa[FM], fb[FN];
-#pragma unroll
-            for (int a = 0; a < FM; ++a)
-                fa[a] = fx[a].read(buf, h);
+        for (int a = 0; a < FM; ++a)
 #pragma unroll
             for (int b = 0; b < FN; ++b)
-                fb[b] = fy[b].read(buf + XB, h);
+                l0.v[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[PAR][0][a], fb[PAR][0][b],
+                                                                     zero, 0, 0, 0);
 #pragma unroll
-            for (int a = 0; a < FM; ++a)
+        for (int a = 0; a < FM; ++a)
 #pragma unroll
-                for (int b = 0; b < FN; ++b) {
-                    const f32x4 acc =
-                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[a], fb[b], zero, 0, 0, 0);
-                    if (h == 0)
-                        l0.v[a][b] = acc;
-                    else
-                        l1.v[a][b] = acc;
-                }
-        }
+            for (int b = 0; b < FN; ++b)
+                l1.v[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[PAR][1][a], fb[PAR][1][b],
+                                                                     zero, 0, 0, 0);
     }
 
     __device__ __forceinline__ void park(int slot, const F &v) {
