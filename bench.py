@@ -24,6 +24,38 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 M, K, N = 4096, 4096, 6144
 COPY_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "det_gemm_traffic_M4096_K4096_N6144.md")
+CSRC = os.path.join(ROOT, "invariant_deterministic_gemm_det_amd", "csrc")
+
+
+def kernel_source_hash():
+    """sha256 over the kernel sources, to tell whether recorded counters are current."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".h", ".hip")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(op):
+    """HBM bytes per launch of `op` from the rocprofv3 counter summary, or None when
+    the summary is missing or was taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    fields = {}
+    for ln in lines:
+        if ln.startswith("- ") and ": " in ln:
+            k, v = ln[2:].split(": ", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    v = fields.get(f"hbm_bytes_per_launch_{op}")
+    return int(v) if v else None
 
 
 def parse():
@@ -131,9 +163,9 @@ def main():
                      "min_ms": round(min(ts), 4), "max_ms": round(max(ts), 4)}
     dom = max(ops, key=lambda k: ops[k]["ms"])
     achieved = ops[dom]["tflops"]
-    kernel_names = {"fwd": "mfma_kernel<K-major X, MN-major Y, bf16 out>",
-                    "da": "mfma_kernel<K-major X, K-major Y, bf16 out>",
-                    "db": "mfma_kernel<MN-major X, MN-major Y, bf16 out>"}
+    kernel_names = {"fwd": "mfma_fast_kernel<K-major X, MN-major Y, bf16 out>",
+                    "da": "mfma_fast_kernel<K-major X, K-major Y, bf16 out>",
+                    "db": "mfma_fast_kernel<MN-major X, MN-major Y, bf16 out>"}
 
     if args.profile_only:
         if args.copy_calibration:
@@ -189,7 +221,8 @@ def main():
         "ops": ops,
         "roofline": {"bound": "mfma", "kernel": f"{dom}: {kernel_names[dom]}",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(dom)},
         "cpu_baseline": cpu,
         "context": ctx,
     }
