@@ -24,8 +24,11 @@ struct TileCfg {
     int bm() const { return 16 * fm * wm; }
     int bn() const { return 16 * fn * wn; }
     int nw() const { return wm * wn; }
+    // Must match Engine::lds_bytes / FastEngine::lds_bytes (the fast kernels keep
+    // the lowest parked level in registers).
     int lds_bytes(int levels) const {
-        return (fast ? 3 : 2) * (bm() + bn()) * 128 + levels * fm * fn * nw() * 64 * 8;
+        const int parked = fast ? (levels > 1 ? levels - 1 : 0) : levels;
+        return (fast ? 3 : 2) * (bm() + bn()) * 128 + parked * fm * fn * nw() * 64 * 8;
     }
 };
 constexpr TileCfg kTileCfgs[] = {{2, 2, 4, 2, false}, {1, 2, 1, 4, false}, {2, 2, 2, 2, false},
