@@ -27,7 +27,7 @@ OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["det_gemm.hip", "mfma_fwd_bf16.hip", "mfma_fwd_f32.hip", "mfma_kk_bf16.hip",
            "mfma_nn_bf16.hip", "mfma_nn_bf16t.hip", "mfma_leaves.hip"]
-HEADERS = ["bf16_device.h", "strict_kernel.h", "mfma_kernel.h", "mfma_fast.h",
+HEADERS = ["bf16_device.h", "strict_kernel.h", "mfma_kernel.h", "mfma_fast.h", "mfma_wide.h",
            "mfma_launch.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

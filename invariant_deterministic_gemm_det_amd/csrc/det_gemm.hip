@@ -144,11 +144,30 @@ bool fast_ok(const Problem &pr, const TreeSel &t) {
            (pr.yk || pr.J % 8 == 0);
 }
 
+// The wide kernel: the fast kernel's operand conditions and a power-of-two leaf
+// count with at least one group of 2^gl stages (with exactly one, the group
+// root is the root).  `up` receives the levels above the groups.
+bool wide_ok(const Problem &pr, const TreeSel &t, const TileCfg &c, int &up) {
+    const int64_t L = (pr.R + 31) / 32;
+    if (!fast_ok(pr, t) || (L & (L - 1)) != 0)
+        return false;
+    const int64_t S = L / 2, G = int64_t(1) << c.gl;
+    if (S < G)
+        return false;
+    up = 0;
+    while ((G << up) < S)
+        ++up;
+    return c.lds_bytes(up) <= kLdsMax - 1024;
+}
+
 int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     if (g_force_config >= 0)
         return g_force_config;
     if (pr.I <= 16)
         return 1;
+    int up = 0;
+    if (pr.I >= 128 && pr.J >= 128 && wide_ok(pr, t, kTileCfgs[5], up))
+        return 5;
     // 8-wave 128x64 tiles for blocks of 8 leaves; the 4-wave 64x64 tile (twice
     // the registers per wave) for blocks of 12 and for the LDS stack.
     const bool wide = t.mode == TREE_BLOCK && t.tb == 1;
@@ -181,8 +200,14 @@ int run_mfma(const Problem &pr, hipStream_t st) {
     p.levels = levels;
     const int cfg = pick_config(pr, tree, levels);
     const TileCfg &c = kTileCfgs[cfg];
-    if (c.fast && !fast_ok(pr, tree))
+    if (c.kind == KIND_WIDE) {
+        int up = 0;
+        if (!wide_ok(pr, tree, c, up))
+            return DET_GEMM_EINVAL;  // a forced wide configuration this problem does not fit
+        p.levels = up;
+    } else if (c.fast() && !fast_ok(pr, tree)) {
         return DET_GEMM_EINVAL;  // a forced fast configuration this problem does not fit
+    }
     const int64_t tiles_i = (pr.I + c.bm() - 1) / c.bm();
     const int64_t tiles_j = (pr.J + c.bn() - 1) / c.bn();
     if (tiles_i * tiles_j > kMaxDim)

@@ -5,35 +5,52 @@
 
 #include <hip/hip_runtime.h>
 
-#include "mfma_fast.h"
+#include "mfma_wide.h"
 
 namespace detgemm {
 
 constexpr int kLdsMax = 160 * 1024;  // LDS per workgroup on gfx950
 
+enum KernelKind { KIND_GENERAL = 0, KIND_FAST = 1, KIND_WIDE = 2 };
+
 // Tile configurations.  Every one computes identical bits (same leaf
-// instruction, same lane assignment, same tree); they differ in tile shape only.
-//   0: 128 x 64 tile, 8 waves of 32 x 32
+// instruction, same lane assignment, same tree); they differ in tile shape and
+// data movement only.
+//   0: 128 x 64 tile, 8 waves of 32 x 32, general kernel (mfma_kernel.h)
 //   1:  16 x 128 tile, 4 waves of 16 x 32   (few rows)
 //   2:  64 x 64 tile, 4 waves of 32 x 32    (deep LDS stacks)
-//   3: configuration 0 on the direct-to-LDS fast path (mfma_fast.h)
-//   4: configuration 2 on the direct-to-LDS fast path
+//   3: configuration 0 on the direct-to-LDS kernel (mfma_fast.h)
+//   4: configuration 2 on the direct-to-LDS kernel
+//   5: 128 x 128 tile, 8 waves of 64 x 32, wide kernel (mfma_wide.h), 2 stage
+//      buffers, groups of 16 stages, power-of-two leaf counts
+//   6: 128 x 64 tile, 4 waves of 64 x 32, wide kernel, 2 stage buffers (two
+//      workgroups per compute unit)
 struct TileCfg {
     int fm, fn, wm, wn;
-    bool fast;
+    int kind;
+    int nbuf, gl, ru;  // wide kernel: stage buffers, static group levels, register levels
     int bm() const { return 16 * fm * wm; }
     int bn() const { return 16 * fn * wn; }
     int nw() const { return wm * wn; }
-    // Must match Engine::lds_bytes / FastEngine::lds_bytes (the fast kernels keep
-    // the lowest parked level in registers).
+    bool fast() const { return kind != KIND_GENERAL; }
+    // Must match Engine::lds_bytes / FastEngine::lds_bytes / WideEngine::lds_bytes.
+    // `levels`: for the general and fast kernels the levels above the 8- or
+    // 12-leaf blocks; for the wide kernel the levels above the groups of 2^gl
+    // stages.
     int lds_bytes(int levels) const {
-        const int parked = fast ? (levels > 1 ? levels - 1 : 0) : levels;
-        return (fast ? 3 : 2) * (bm() + bn()) * 128 + parked * fm * fn * nw() * 64 * 8;
+        const int park = fm * fn * nw() * 64 * 8;
+        if (kind == KIND_WIDE)
+            return nbuf * (bm() + bn()) * 128 + (levels > ru ? levels - ru : 0) * park;
+        const int parked = kind == KIND_FAST ? (levels > 1 ? levels - 1 : 0) : levels;
+        return (kind == KIND_FAST ? 3 : 2) * (bm() + bn()) * 128 + parked * park;
     }
 };
-constexpr TileCfg kTileCfgs[] = {{2, 2, 4, 2, false}, {1, 2, 1, 4, false}, {2, 2, 2, 2, false},
-                                 {2, 2, 4, 2, true},  {2, 2, 2, 2, true}};
-constexpr int kNumTileCfgs = 5;
+constexpr TileCfg kTileCfgs[] = {
+    {2, 2, 4, 2, KIND_GENERAL, 0, 0, 0}, {1, 2, 1, 4, KIND_GENERAL, 0, 0, 0},
+    {2, 2, 2, 2, KIND_GENERAL, 0, 0, 0}, {2, 2, 4, 2, KIND_FAST, 0, 0, 0},
+    {2, 2, 2, 2, KIND_FAST, 0, 0, 0},    {4, 2, 2, 4, KIND_WIDE, 2, 4, 1},
+    {4, 2, 2, 2, KIND_WIDE, 2, 3, 1}};
+constexpr int kNumTileCfgs = 7;
 
 struct TreeSel {
     int mode;  // TREE_BLOCK or TREE_STACK
@@ -72,6 +89,37 @@ hipError_t launch_one(const MfmaParams &p, int64_t tiles, hipStream_t st) {
         return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(kernel, dim3((unsigned)tiles), dim3(64 * WM * WN), lds, st, p);
     return hipGetLastError();
+}
+
+// Wide kernel: power-of-two leaf counts only (checked by the caller), never the
+// leaf dump; p.levels holds the levels above the groups of 2^GL stages.
+template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU,
+          int OCC>
+hipError_t launch_wide(const MfmaParams &p, int64_t tiles, hipStream_t st) {
+    if constexpr (OUT == OUT_LEAVES) {
+        return hipErrorInvalidValue;
+    } else {
+        typedef WideEngine<XK, YK, OUT, FM, FN, WM, WN, NBUF> E;
+        void (*kernel)(MfmaParams) = &mfma_wide_kernel<XK, YK, OUT, FM, FN, WM, WN, NBUF, GL, RU, OCC>;
+        const void *fn = reinterpret_cast<const void *>(kernel);
+        static int max_dynamic = -1;
+        if (max_dynamic < 0) {
+            hipFuncAttributes attr;
+            hipError_t e = hipFuncGetAttributes(&attr, fn);
+            if (e != hipSuccess)
+                return e;
+            const int room = kLdsMax - (int)attr.sharedSizeBytes;
+            e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, room);
+            if (e != hipSuccess)
+                return e;
+            max_dynamic = room;
+        }
+        const int lds = E::lds_bytes(p.levels > RU ? p.levels - RU : 0);
+        if (lds > max_dynamic)
+            return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(kernel, dim3((unsigned)tiles), dim3(64 * WM * WN), lds, st, p);
+        return hipGetLastError();
+    }
 }
 
 template <bool FAST, bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN>
@@ -113,6 +161,10 @@ hipError_t launch_layout(int cfg, const TreeSel &t, const MfmaParams &p, int64_t
         return launch_trees<true, XK, YK, OUT, 2, 2, 4, 2>(t, p, tiles, st);
     case 4:
         return launch_trees<true, XK, YK, OUT, 2, 2, 2, 2>(t, p, tiles, st);
+    case 5:
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 2, 4, 1, 2>(p, tiles, st);
+    case 6:
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 2, 2, 3, 1, 2>(p, tiles, st);
     default:
         return hipErrorInvalidValue;
     }

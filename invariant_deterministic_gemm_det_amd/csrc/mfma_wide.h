@@ -1,0 +1,567 @@
+// Wide-wave MFMA det_gemm kernel for gfx950, for power-of-two leaf counts.
+//
+// Same leaves and same tree as mfma_kernel.h and mfma_fast.h, hence the same
+// bits (RL-Kernel operator page "Batch-Invariant Deterministic GEMM (det_gemm)",
+// sections "Guarantees" and "Ascend NPU backend": 32-element leaves rounded once
+// to bf16, mid-split tree of bf16 adds).  With L = 2^a the mid-split tree is the
+// perfect binary tree, and its lowest inner nodes are the pairs (2s, 2s + 1),
+// i.e. the two leaves of pipeline stage s.  What differs is the work layout:
+//   * each wave owns FM x FN blocks of 16x16 outputs (4 x 2: 64 x 32), so every
+//     step of the tree is FM * FN independent matrix-core instructions and a
+//     dependent step never waits on the latency of the previous one;
+//   * a stage's two leaf MFMAs per block are rounded at once into one packed
+//     pair (v_cvt_pk_bf16_f32), and the next stage begins with the tree add of
+//     that pair on the matrix core (selector MFMA, mfma_fast.h), followed by the
+//     climb of the resulting node; the leaf MFMAs of the stage come last, after
+//     their fragment reads have had the tree work to complete;
+//   * every node that waits for its right sibling is kept rounded and packed
+//     (two registers per block), never as fp32;
+//   * G = 2^GL stages are unrolled, so the pending nodes of the GL lowest levels
+//     of the pair tree sit in registers with static indices; the root of a group
+//     of stages climbs RU more levels held in registers (uniform branches on the
+//     group index), then levels parked in LDS;
+//   * operand staging is the direct global -> LDS copy of mfma_fast.h with
+//     NBUF stage buffers; fragment reads use one base register per operand and
+//     leaf half, the fragment index being an immediate offset.
+#pragma once
+
+#include "mfma_fast.h"
+
+namespace detgemm {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// A tree node rounded to bf16 and packed: per 16x16 block, the lane's four
+// values as the pairs (v0, v1), (v2, v3).  Vector-typed so that the compiler
+// keeps every node in registers.
+template <int FM, int FN>
+struct WPacked {
+    u32x2 w[FM][FN];
+};
+
+template <int FM, int FN>
+__device__ __forceinline__ WPacked<FM, FN> wpack(const Frag<FM, FN> &x) {
+    WPacked<FM, FN> o;
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+            o.w[a][b].x = pair_bits(round_pair(x.v[a][b][0], x.v[a][b][1]));
+            o.w[a][b].y = pair_bits(round_pair(x.v[a][b][2], x.v[a][b][3]));
+        }
+    return o;
+}
+
+// Tree adds of packed children on the matrix core: the A operand of a lane is
+// (left child's four values, right child's four values), the B operand the
+// split selector of mfma_fast.h; the parent's fp32 values land transposed.
+struct WideMatrixAdd {
+    template <int FM, int FN>
+    __device__ static __forceinline__ Frag<FM, FN> add(const WPacked<FM, FN> &l,
+                                                       const WPacked<FM, FN> &r, bf16x8 sel) {
+        const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        Frag<FM, FN> o;
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                const u32x4 A = __builtin_shufflevector(l.w[a][b], r.w[a][b], 0, 1, 2, 3);
+                o.v[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A),
+                                                                    sel, zero, 0, 0, 0);
+            }
+        return o;
+    }
+};
+
+// The same adds element by element on the VALU: exact IEEE behaviour for
+// non-finite values, and positions never move.
+struct WideValuAdd {
+    __device__ static __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+    __device__ static __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+    template <int FM, int FN>
+    __device__ static __forceinline__ Frag<FM, FN> add(const WPacked<FM, FN> &l,
+                                                       const WPacked<FM, FN> &r, bf16x8) {
+        Frag<FM, FN> o;
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                o.v[a][b][0] = lo(l.w[a][b].x) + lo(r.w[a][b].x);
+                o.v[a][b][1] = hi(l.w[a][b].x) + hi(r.w[a][b].x);
+                o.v[a][b][2] = lo(l.w[a][b].y) + lo(r.w[a][b].y);
+                o.v[a][b][3] = hi(l.w[a][b].y) + hi(r.w[a][b].y);
+            }
+        return o;
+    }
+};
+
+template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF>
+struct WideEngine {
+    static constexpr int kOUT = OUT, kWM = WM;
+    static constexpr int NW = WM * WN;
+    static constexpr int BM = 16 * FM * WM;
+    static constexpr int BN = 16 * FN * WN;
+    static constexpr int XB = BM * 128, YB = BN * 128;
+    static constexpr int BUF = XB + YB;
+    static constexpr int PARK_FRAG = NW * 64 * 8;
+    static constexpr int PARK_LEVEL = FM * FN * PARK_FRAG;
+    static constexpr int kFM = FM, kFN = FN;
+    static constexpr int lds_bytes(int parked) { return NBUF * BUF + parked * PARK_LEVEL; }
+    typedef Frag<FM, FN> F;
+    typedef WPacked<FM, FN> P;
+    typedef DirectStager<XK, BM, NW> SX;
+    typedef DirectStager<YK, BN, NW> SY;
+    static constexpr int LOADS = SX::PER_WAVE + SY::PER_WAVE;
+    static_assert(NBUF >= 2, "at least two stage buffers");
+
+    char *smem;
+    SX sx;
+    SY sy;
+    int xoff[XK ? 2 : FM];  // K-major: per leaf half h; MN-major: per fragment
+    int yoff[YK ? 2 : FN];
+    int park_off;
+    int S;
+    bf16x8 fa[2][FM], fb[2][FN];  // [leaf][fragment] of the current stage
+
+    // Fragment read offsets of a K-major operand: rows r0 + 16a + i (i = lane
+    // % 16), 16-byte chunk 4h + lane / 16 XOR-swizzled by (row >> 1) & 7, which
+    // does not depend on a (16a / 2 is a multiple of 8), so fragment a is at the
+    // fixed distance 16 * 128 * a.
+    __device__ __forceinline__ static void kmajor_offsets(int *off, int r0, int lane) {
+        const int row = r0 + (lane & 15);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            off[h] = row * 128 + (((4 * h + (lane >> 4)) ^ lds_key(row)) << 4);
+    }
+
+    // Fragment read offsets of an MN-major operand of NR rows per reduction
+    // index (natural [r][row] layout, chunk swizzle mn_key of the reduction
+    // index): lane 4m + q of group G reads reduction rows 32h + 8G + 4half + m,
+    // operand rows 4q .. 4q+3 of its fragment.  The swizzle key depends only on
+    // m and G, so the (h, half) variants are fixed distances from one base.
+    template <int NR>
+    __device__ __forceinline__ static int mnmajor_offset(int rbase, int lane) {
+        constexpr int NC = NR / 8;
+        const int i = lane & 15, G = lane >> 4;
+        const int m = i >> 2, q = i & 3;
+        const int r = 8 * G + m;
+        const int col = rbase + 4 * q;
+        const int lc = col >> 3;
+        return r * (NR * 2) + (((lc ^ mn_key<NC>(r)) << 4) | ((col & 7) * 2));
+    }
+
+    __device__ __forceinline__ WideEngine(const MfmaParams &p, char *smem_, int i0, int j0)
+        : smem(smem_) {
+        const int lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int wm = wave % WM, wn = wave / WM;
+        sx.init(p.x, p.ldx, i0, p.I, wave, lane);
+        sy.init(p.y, p.ldy, j0, p.J, wave, lane);
+        if constexpr (XK) {
+            kmajor_offsets(xoff, wm * FM * 16, lane);
+        } else {
+#pragma unroll
+            for (int a = 0; a < FM; ++a)
+                xoff[a] = mnmajor_offset<BM>(wm * FM * 16 + a * 16, lane);
+        }
+        if constexpr (YK) {
+            kmajor_offsets(yoff, wn * FN * 16, lane);
+            yoff[0] += XB;  // the Y tile follows the X tile in a stage buffer
+            yoff[1] += XB;
+        } else {
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+                yoff[b] = XB + mnmajor_offset<BN>(wn * FN * 16 + b * 16, lane);
+        }
+        S = p.R / 64;
+        park_off = NBUF * BUF + threadIdx.x * 8;
+    }
+
+    __device__ __forceinline__ void issue(int s) {
+        char *buf = smem + (s % NBUF) * BUF;
+        sx.issue(s, buf);
+        sy.issue(s, buf + XB);
+    }
+
+    // Stages 0 .. NBUF-2 in flight.
+    __device__ __forceinline__ void prologue() {
+#pragma unroll
+        for (int q = 0; q < NBUF - 1; ++q)
+            if (q < S)
+                issue(q);
+    }
+
+    // Start of stage s: this wave's copies of stage s are complete (those of
+    // later stages may stay in flight), then the workgroup joins -- after which
+    // all of stage s is in LDS and every wave has consumed stage s - 1, whose
+    // buffer is refilled with stage s + NBUF - 1 --, then the fragment reads of
+    // stage s are issued.
+    __device__ __forceinline__ void begin(int s) {
+        if (s + NBUF - 2 < S)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NBUF - 2) * LOADS)
+                         : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (s + NBUF - 1 < S)
+            issue(s + NBUF - 1);
+        const char *buf = smem + (s % NBUF) * BUF;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int a = 0; a < FM; ++a) {
+                if constexpr (XK) {
+                    fa[h][a] = *reinterpret_cast<const bf16x8 *>(buf + xoff[h] + a * 16 * 128);
+                } else {
+                    const char *q = buf + xoff[a] + h * 32 * BM * 2;
+                    fa[h][a] = tr_read(q, q + 4 * BM * 2);
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                if constexpr (YK) {
+                    fb[h][b] = *reinterpret_cast<const bf16x8 *>(buf + yoff[h] + b * 16 * 128);
+                } else {
+                    const char *q = buf + yoff[b] + h * 32 * BN * 2;
+                    fb[h][b] = tr_read(q, q + 4 * BN * 2);
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ static bf16x8 tr_read(const char *p0, const char *p1) {
+        const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
+        const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        const s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        return __builtin_bit_cast(bf16x8, v);
+    }
+
+    // The two leaves of the current stage: the first rounded and packed per
+    // block, the second as fp32.
+    __device__ __forceinline__ void leaves(P &x0, F &l1) {
+        const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        F l0;
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+                l0.v[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[0][a], fb[0][b], zero, 0, 0, 0);
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+                l1.v[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[1][a], fb[1][b], zero, 0, 0, 0);
+        x0 = wpack(l0);
+    }
+
+    __device__ __forceinline__ void park(int slot, const P &v) {
+        char *base = smem + park_off + slot * PARK_LEVEL;
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+                *reinterpret_cast<u32x2 *>(base + (a * FN + b) * PARK_FRAG) = v.w[a][b];
+    }
+
+    __device__ __forceinline__ P unpark(int slot) const {
+        const char *base = smem + park_off + slot * PARK_LEVEL;
+        P v;
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+                v.w[a][b] = *reinterpret_cast<const u32x2 *>(base + (a * FN + b) * PARK_FRAG);
+        return v;
+    }
+};
+
+// The perfect tree over the S = L / 2 stage pairs.  Level 1 holds the pair
+// nodes; a node at level j waits, packed, until its right sibling arrives.
+// Levels 1 .. GL belong to a group of G = 2^GL consecutive stages (static
+// register slots); the group roots (level GL + 1) climb the `nup` levels above,
+// the first RU of them in registers, the rest parked in LDS.
+//
+// Stage s: fragment reads; the climb of the pair node of stage s - 1; the leaf
+// MFMAs of stage s, their rounding and their pair add, whose result is rounded
+// and carried (packed) into stage s + 1.  Each phase is kept to itself by a
+// scheduling barrier, which bounds the registers a wave holds at any time; the
+// other wave of the SIMD overlaps its phases with this one's.
+template <class E, class Arith, int GL, int RU>
+struct WideTree {
+    static constexpr int G = 1 << GL;
+    static_assert(GL >= 1, "groups of at least two stages");
+    // RU >= 1: the zero-leaf step of group 0 writes the first upper slot,
+    // which must then be a register (with no upper levels, no LDS slot exists).
+    static_assert(RU >= 1, "the first upper level is held in registers");
+    typedef typename E::F F;
+    typedef typename E::P P;
+    E &e;
+    const MfmaParams &p;
+    const bf16x8 sel;
+    const int nup;
+    const int i0, j0;
+    const bool odd;  // layout parity of the root (matrix-core adds transpose)
+    // Pending nodes in registers: levels 1 .. GL of a group (static slots
+    // l0 .. l3), then the RU upper levels (u0 .. u3).  Plain members rather than
+    // arrays, so that nothing keeps them from living in registers.
+    P l0, l1, l2, l3, u0, u1, u2, u3;
+    static_assert(GL <= 4 && RU <= 4, "at most four register levels of each kind");
+
+    template <int J>
+    __device__ __forceinline__ P &low() {
+        if constexpr (J == 0)
+            return l0;
+        else if constexpr (J == 1)
+            return l1;
+        else if constexpr (J == 2)
+            return l2;
+        else
+            return l3;
+    }
+    template <int Q>
+    __device__ __forceinline__ P &upreg() {
+        if constexpr (Q == 0)
+            return u0;
+        else if constexpr (Q == 1)
+            return u1;
+        else if constexpr (Q == 2)
+            return u2;
+        else
+            return u3;
+    }
+
+    __device__ __forceinline__ WideTree(E &e_, const MfmaParams &p_, bf16x8 sel_, int i0_, int j0_,
+                                        bool odd_)
+        : e(e_), p(p_), sel(sel_), nup(p_.levels), i0(i0_), j0(j0_), odd(odd_) {}
+
+    __device__ __forceinline__ void store(const F &root) {
+        const int wave = threadIdx.x >> 6;
+        store_root<E::kOUT>(p, root, odd, i0, j0, wave % E::kWM, wave / E::kWM, threadIdx.x & 63);
+    }
+
+    // An empty statement that takes a value and may change it: the value must
+    // be complete at this point, and nothing computing it can move below it.
+    __device__ __forceinline__ static void pin_p(P &x) {
+#pragma unroll
+        for (int a = 0; a < E::kFM; ++a)
+#pragma unroll
+            for (int b = 0; b < E::kFN; ++b)
+                asm volatile("" : "+v"(x.w[a][b]));
+    }
+    __device__ __forceinline__ static void pin_f(F &x) {
+#pragma unroll
+        for (int a = 0; a < E::kFM; ++a)
+#pragma unroll
+            for (int b = 0; b < E::kFN; ++b)
+                asm volatile("" : "+v"(x.v[a][b]));
+    }
+
+    __device__ __forceinline__ F add(const P &l, const P &r) { return Arith::add(l, r, sel); }
+
+    // The pending node of upper level Q (static slot).
+    template <int Q>
+    __device__ __forceinline__ P upper(void) {
+        if constexpr (Q < RU)
+            return upreg<Q>();
+        else
+            return e.unpark(Q - RU);
+    }
+    template <int Q>
+    __device__ __forceinline__ void set_upper(const P &x) {
+        if constexpr (Q < RU) {
+            upreg<Q>() = x;
+            pin_p(upreg<Q>());
+        } else {
+            e.park(Q - RU, x);
+        }
+    }
+
+    // Group root x (packed, level GL + 1) of a group t < T - 1 climbs from
+    // upper level Q while it is a right child; t has a clear bit below nup,
+    // where the climb stops.  Unrolled by recursion (at most 9 - GL upper levels:
+    // L <= 1024), so every slot index is static; the branches are uniform.
+    static constexpr int kMaxUp = 9 - GL;
+    template <int Q>
+    __device__ __forceinline__ void climb_up(const P &x, int t) {
+        if constexpr (Q < kMaxUp) {
+            if (!((t >> Q) & 1))
+                set_upper<Q>(x);
+            else
+                climb_up<Q + 1>(wpack(add(upper<Q>(), x)), t);
+        }
+    }
+
+    // Pair node x (packed, level J + 1) of stage U of group t climbs within the
+    // group while it is a right child; a group root continues above.
+    template <int U, int J>
+    __device__ __forceinline__ void climb_low(const P &x, int t) {
+        if constexpr (J == GL)
+            climb_up<0>(x, t);
+        else if constexpr ((U >> J) & 1)
+            climb_low<U, J + 1>(wpack(add(low<J>(), x)), t);
+        else {
+            low<J>() = x;
+            pin_p(low<J>());
+        }
+    }
+
+    // The last stage's pair node: every step is a right child up to the root.
+    template <int J>
+    __device__ __forceinline__ F final_low(const P &x) {
+        const F y = add(low<J>(), x);
+        if constexpr (J + 1 < GL)
+            return final_low<J + 1>(wpack(y));
+        else
+            return nup > 0 ? final_up<0>(wpack(y), y) : y;
+    }
+    __device__ __forceinline__ F final_chain(const P &x1) { return final_low<0>(x1); }
+    template <int Q>
+    __device__ __forceinline__ F final_up(const P &x, const F &y) {
+        if constexpr (Q < kMaxUp) {
+            if (Q == nup)
+                return y;
+            const F z = add(upper<Q>(), x);
+            return final_up<Q + 1>(wpack(z), z);
+        } else {
+            return y;
+        }
+    }
+
+    // Tree work of stage U of group t, whose leaves are x0 (rounded, packed)
+    // and l1 (fp32): their pair add, rounded, climbs while it is a right child.
+    template <int U>
+    __device__ __forceinline__ void step(const P &x0, const F &l1, int t) {
+        climb_low<U, 0>(wpack(add(x0, wpack(l1))), t);
+    }
+
+    // Tree work of the last stage, then the root is rounded and stored.
+    // Returns whether the root has a non-finite value.
+    __device__ __forceinline__ bool finish(const P &x0, const F &l1) {
+        const F root = final_chain(wpack(add(x0, wpack(l1))));
+        bool nonfinite = false;
+#pragma unroll
+        for (int a = 0; a < E::kFM; ++a)
+#pragma unroll
+            for (int b = 0; b < E::kFN; ++b)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    nonfinite |= !(__builtin_fabsf(root.v[a][b][v]) <= 3.40282347e38f);
+        store(root);
+        return nonfinite;
+    }
+
+    // Stage U of group t: the fragment reads of the stage, the tree work of
+    // the previous stage (which covers the latency of the reads), then the
+    // stage's leaves, which wait across the barrier (l0 packed, l1 as fp32).
+    // `pin` keeps the leaves where they are computed: without it the compiler
+    // sinks their MFMAs into the next stage, behind its barrier.
+    //
+    // The first stage of group t > 0 finishes group t - 1.  Group 0 runs the
+    // same code on zero leaves, as group index 0: its only effect is a write
+    // of the first upper slot, which group 0's own root overwrites before any
+    // read (group 1 reads it); a branch here would split the stage's code.
+    template <int U>
+    __device__ __forceinline__ void stage(int t, P &x0, F &l1) {
+        e.begin(t * G + U);
+        if constexpr (U == 0)
+            step<G - 1>(x0, l1, t > 0 ? t - 1 : 0);
+        else
+            step<U - 1>(x0, l1, t);
+        e.leaves(x0, l1);
+        pin_p(x0);
+        pin_f(l1);
+        if constexpr (U + 1 < G)
+            stage<U + 1>(t, x0, l1);
+    }
+
+    // Requires S = e.S = G * 2^nup.  Computes and stores the tile; returns
+    // whether a root was non-finite.
+    __device__ __forceinline__ bool run() {
+        const int T = e.S >> GL;
+        e.prologue();
+        P x0;
+        F l1;
+#pragma unroll
+        for (int a = 0; a < E::kFM; ++a)
+#pragma unroll
+            for (int b = 0; b < E::kFN; ++b) {
+                x0.w[a][b] = u32x2{0u, 0u};
+                l1.v[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        for (int t = 0; t < T; ++t)
+            stage<0>(t, x0, l1);
+        return finish(x0, l1);
+    }
+};
+
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+template <class T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+    return reinterpret_cast<T *>(uniform64(reinterpret_cast<int64_t>(p)));
+}
+
+// Recomputes a tile with element-wise adds (exact IEEE behaviour for non-finite
+// values; positions never move) and stores it.  Kept out of line so that its
+// registers do not weigh on the main kernel's allocation: it runs only for
+// tiles whose matrix-core tree produced a non-finite root.  Arguments of a
+// called function arrive in vector registers, so the workgroup-uniform values
+// are made scalar again for the staging code.
+template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU>
+__device__ __attribute__((noinline)) void wide_valu_tile(MfmaParams q) {
+    typedef WideEngine<XK, YK, OUT, FM, FN, WM, WN, NBUF> E;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    MfmaParams p = q;
+    p.x = uniform_ptr(q.x);
+    p.y = uniform_ptr(q.y);
+    p.c = uniform_ptr(q.c);
+    p.ldx = uniform64(q.ldx);
+    p.ldy = uniform64(q.ldy);
+    p.ldc = uniform64(q.ldc);
+    p.I = __builtin_amdgcn_readfirstlane(q.I);
+    p.J = __builtin_amdgcn_readfirstlane(q.J);
+    p.R = __builtin_amdgcn_readfirstlane(q.R);
+    p.L = __builtin_amdgcn_readfirstlane(q.L);
+    p.tiles_j = __builtin_amdgcn_readfirstlane(q.tiles_j);
+    p.levels = __builtin_amdgcn_readfirstlane(q.levels);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int tile = blockIdx.x;
+    const int i0 = (tile / p.tiles_j) * E::BM;
+    const int j0 = (tile % p.tiles_j) * E::BN;
+    E e(p, smem, i0, j0);
+    WideTree<E, WideValuAdd, GL, RU> valu(e, p, split_selector(threadIdx.x & 63), i0, j0, false);
+    valu.run();
+}
+
+// OCC: waves per SIMD the register allocation must allow (a 4-wave workgroup
+// asks for 2 so that two workgroups share a compute unit).
+template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU,
+          int OCC>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void mfma_wide_kernel(MfmaParams p) {
+    typedef WideEngine<XK, YK, OUT, FM, FN, WM, WN, NBUF> E;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int lane = threadIdx.x & 63;
+    const int tile = blockIdx.x;
+    const int i0 = (tile / p.tiles_j) * E::BM;
+    const int j0 = (tile % p.tiles_j) * E::BN;
+
+    E e(p, smem, i0, j0);
+    WideTree<E, WideMatrixAdd, GL, RU> tree(e, p, split_selector(lane), i0, j0,
+                                            (tree_height_rt(p.L) & 1) != 0);
+    const bool nonfinite = tree.run();
+    __threadfence_block();  // this tile's stores are done before a recomputation overwrites them
+    // A non-finite root may have spilled NaN into the other sums of its
+    // matrix-core add rows: recompute such a tile with element-wise adds, which
+    // overwrite what was stored.
+    if (__syncthreads_or(nonfinite))
+        wide_valu_tile<XK, YK, OUT, FM, FN, WM, WN, NBUF, GL, RU>(p);
+}
+
+}  // namespace detgemm

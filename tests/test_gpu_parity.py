@@ -331,10 +331,11 @@ def test_mfma_tile_configs_identical(dev, K):
 
 # Tile configurations 3 and 4 are the direct-to-LDS kernels (whole 64-index
 # stages, 16-byte aligned rows, 8-row chunks of operands whose row index is
-# contiguous); 2 is the general kernel they must reproduce bit for bit.
+# contiguous), 5 and 6 the wide kernels (the same, and power-of-two leaf
+# counts); 2 is the general kernel they must reproduce bit for bit.
 FAST_SHAPES = [(200, 192, 256), (256, 136, 768), (320, 256, 4096), (128, 64, 12288),
-               (72, 64, 32768)]
-GENERAL_CFG, FAST_CFGS = 2, (3, 4)
+               (72, 64, 32768), (512, 512, 1024), (264, 392, 8192)]
+GENERAL_CFG, FAST_CFGS = 2, (3, 4, 5, 6)
 
 
 def _six_forced(cfg, A, B, dC):
@@ -382,7 +383,7 @@ def test_fast_path_matches_general_kernel(dev, M, N, K):
     assert ran >= 3
 
 
-@pytest.mark.parametrize("M,N,K", [(200, 192, 256), (256, 136, 256), (256, 256, 256)])
+@pytest.mark.parametrize("M,N,K", [(200, 192, 256), (256, 136, 256), (256, 256, 256), (512, 256, 1024)])
 def test_fast_path_integer_regime_bit_exact(dev, M, N, K):
     say("direct-to-LDS kernels, integer regime vs oracle", M, N, K)
     A = W.int_bf16((M, K), 910 + K)
@@ -453,3 +454,28 @@ def test_errors_leave_output_untouched(dev):
     _sync()
     roots, _ = oracle.tree_from_leaves(bits(leaves))
     assert np.array_equal(roots, bits(got))
+
+
+# The wide kernels' tree adds run on the matrix core, where one non-finite node
+# spoils the other sums of its row; such tiles are recomputed with element-wise
+# adds.  Inf and NaN inputs must give the general kernel's bits.
+@pytest.mark.parametrize("K", [1024, 2048])
+def test_wide_kernel_nonfinite_inputs(dev, K):
+    say("wide kernels, non-finite inputs vs general kernel", K)
+    M, N = 1024, 384
+    A, B, dC = _inputs(M, N, K, 950 + K, sigma=0.02)
+    A[3, 100] = float("inf")
+    A[130, 7] = float("nan")
+    B[K - 12, 77] = float("-inf")
+    dC[517, 5] = float("inf")
+    Ad, Bd, dCd = A.to(dev), B.to(dev), dC.to(dev)
+    ref = _six_forced(GENERAL_CFG, Ad, Bd, dCd)
+    ran = 0
+    for cfg in (5, 6):
+        got = _six_forced(cfg, Ad, Bd, dCd)
+        for op, g in got.items():
+            if g is None:
+                continue
+            ran += 1
+            assert np.array_equal(g, ref[op]), (cfg, op)
+    assert ran >= 6
