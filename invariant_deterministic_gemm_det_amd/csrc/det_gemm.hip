@@ -144,15 +144,16 @@ bool fast_ok(const Problem &pr, const TreeSel &t) {
            (pr.yk || pr.J % 8 == 0);
 }
 
-// The wide kernel: the fast kernel's operand conditions and a power-of-two leaf
-// count with at least one group of 2^gl stages (with exactly one, the group
-// root is the root).  `up` receives the levels above the groups.
+// The wide kernel: the fast kernel's operand conditions and a leaf count
+// L = 2 * tb * 2^k with at least one group of 2^gl nodes of 2 * tb leaves
+// (with exactly one group, the group root is the root).  `up` receives the
+// levels above the groups.
 bool wide_ok(const Problem &pr, const TreeSel &t, const TileCfg &c, int &up) {
     const int64_t L = (pr.R + 31) / 32;
-    if (!fast_ok(pr, t) || (L & (L - 1)) != 0)
+    if (!fast_ok(pr, t) || L % (2 * c.tb) != 0)
         return false;
-    const int64_t S = L / 2, G = int64_t(1) << c.gl;
-    if (S < G)
+    const int64_t S = L / (2 * c.tb), G = int64_t(1) << c.gl;  // nodes of 2 * tb leaves
+    if ((S & (S - 1)) != 0 || S < G)
         return false;
     up = 0;
     while ((G << up) < S)
@@ -168,6 +169,8 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     int up = 0;
     if (pr.I >= 128 && pr.J >= 128 && wide_ok(pr, t, kTileCfgs[5], up))
         return 5;
+    if (pr.I >= 128 && pr.J >= 128 && wide_ok(pr, t, kTileCfgs[7], up))
+        return 7;
     // 8-wave 128x64 tiles for blocks of 8 leaves; the 4-wave 64x64 tile (twice
     // the registers per wave) for blocks of 12 and for the LDS stack.
     const bool wide = t.mode == TREE_BLOCK && t.tb == 1;

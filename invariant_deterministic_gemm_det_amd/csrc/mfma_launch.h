@@ -25,10 +25,13 @@ enum KernelKind { KIND_GENERAL = 0, KIND_FAST = 1, KIND_WIDE = 2 };
 //      buffers, groups of 16 stages, power-of-two leaf counts
 //   6: 128 x 64 tile, 4 waves of 64 x 32, wide kernel, 2 stage buffers (two
 //      workgroups per compute unit)
+//   7: configuration 5 for leaf counts 3 * 2^a (units of three leaves), groups
+//      of 4 six-leaf nodes
 struct TileCfg {
     int fm, fn, wm, wn;
     int kind;
     int nbuf, gl, ru;  // wide kernel: stage buffers, static group levels, register levels
+    int tb;            // wide kernel: leaves per unit (1 or 3)
     int bm() const { return 16 * fm * wm; }
     int bn() const { return 16 * fn * wn; }
     int nw() const { return wm * wn; }
@@ -46,11 +49,11 @@ struct TileCfg {
     }
 };
 constexpr TileCfg kTileCfgs[] = {
-    {2, 2, 4, 2, KIND_GENERAL, 0, 0, 0}, {1, 2, 1, 4, KIND_GENERAL, 0, 0, 0},
-    {2, 2, 2, 2, KIND_GENERAL, 0, 0, 0}, {2, 2, 4, 2, KIND_FAST, 0, 0, 0},
-    {2, 2, 2, 2, KIND_FAST, 0, 0, 0},    {4, 2, 2, 4, KIND_WIDE, 2, 4, 1},
-    {4, 2, 2, 2, KIND_WIDE, 2, 3, 1}};
-constexpr int kNumTileCfgs = 7;
+    {2, 2, 4, 2, KIND_GENERAL, 0, 0, 0, 1}, {1, 2, 1, 4, KIND_GENERAL, 0, 0, 0, 1},
+    {2, 2, 2, 2, KIND_GENERAL, 0, 0, 0, 1}, {2, 2, 4, 2, KIND_FAST, 0, 0, 0, 1},
+    {2, 2, 2, 2, KIND_FAST, 0, 0, 0, 1},    {4, 2, 2, 4, KIND_WIDE, 2, 4, 1, 1},
+    {4, 2, 2, 2, KIND_WIDE, 2, 3, 1, 1},    {4, 2, 2, 4, KIND_WIDE, 2, 2, 1, 3}};
+constexpr int kNumTileCfgs = 8;
 
 struct TreeSel {
     int mode;  // TREE_BLOCK or TREE_STACK
@@ -93,14 +96,14 @@ hipError_t launch_one(const MfmaParams &p, int64_t tiles, hipStream_t st) {
 
 // Wide kernel: power-of-two leaf counts only (checked by the caller), never the
 // leaf dump; p.levels holds the levels above the groups of 2^GL stages.
-template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU,
-          int OCC>
+template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int TB, int GL,
+          int RU, int OCC>
 hipError_t launch_wide(const MfmaParams &p, int64_t tiles, hipStream_t st) {
     if constexpr (OUT == OUT_LEAVES) {
         return hipErrorInvalidValue;
     } else {
         typedef WideEngine<XK, YK, OUT, FM, FN, WM, WN, NBUF> E;
-        void (*kernel)(MfmaParams) = &mfma_wide_kernel<XK, YK, OUT, FM, FN, WM, WN, NBUF, GL, RU, OCC>;
+        void (*kernel)(MfmaParams) = &mfma_wide_kernel<XK, YK, OUT, FM, FN, WM, WN, NBUF, TB, GL, RU, OCC>;
         const void *fn = reinterpret_cast<const void *>(kernel);
         static int max_dynamic = -1;
         if (max_dynamic < 0) {
@@ -162,9 +165,11 @@ hipError_t launch_layout(int cfg, const TreeSel &t, const MfmaParams &p, int64_t
     case 4:
         return launch_trees<true, XK, YK, OUT, 2, 2, 2, 2>(t, p, tiles, st);
     case 5:
-        return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 2, 4, 1, 2>(p, tiles, st);
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 2, 1, 4, 1, 2>(p, tiles, st);
     case 6:
-        return launch_wide<XK, YK, OUT, 4, 2, 2, 2, 2, 3, 1, 2>(p, tiles, st);
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 2, 2, 1, 3, 1, 2>(p, tiles, st);
+    case 7:
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 2, 3, 2, 1, 2>(p, tiles, st);
     default:
         return hipErrorInvalidValue;
     }

@@ -56,6 +56,7 @@ __device__ __forceinline__ WPacked<FM, FN> wpack(const Frag<FM, FN> &x) {
 // (left child's four values, right child's four values), the B operand the
 // split selector of mfma_fast.h; the parent's fp32 values land transposed.
 struct WideMatrixAdd {
+    static constexpr bool kTransposes = true;
     template <int FM, int FN>
     __device__ static __forceinline__ Frag<FM, FN> add(const WPacked<FM, FN> &l,
                                                        const WPacked<FM, FN> &r, bf16x8 sel) {
@@ -76,6 +77,7 @@ struct WideMatrixAdd {
 // The same adds element by element on the VALU: exact IEEE behaviour for
 // non-finite values, and positions never move.
 struct WideValuAdd {
+    static constexpr bool kTransposes = false;
     __device__ static __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
     __device__ static __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
     template <int FM, int FN>
@@ -119,7 +121,8 @@ struct WideEngine {
     SY sy;
     int xoff[XK ? 2 : FM];  // K-major: per leaf half h; MN-major: per fragment
     int yoff[YK ? 2 : FN];
-    int park_off;
+    char *park_lane;  // this lane's first parking slot
+    const char *cur;  // stage buffer of the current stage
     int S;
     bf16x8 fa[2][FM], fb[2][FN];  // [leaf][fragment] of the current stage
 
@@ -150,8 +153,11 @@ struct WideEngine {
         return r * (NR * 2) + (((lc ^ mn_key<NC>(r)) << 4) | ((col & 7) * 2));
     }
 
-    __device__ __forceinline__ WideEngine(const MfmaParams &p, char *smem_, int i0, int j0)
-        : smem(smem_) {
+    // LDS: the parked tree levels first (`parked` of them), so that a lane's
+    // slots are within the immediate offset of one address register, then the
+    // NBUF stage buffers.
+    __device__ __forceinline__ WideEngine(const MfmaParams &p, char *lds, int parked, int i0, int j0)
+        : smem(lds + parked * PARK_LEVEL) {
         const int lane = threadIdx.x & 63;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const int wm = wave % WM, wn = wave / WM;
@@ -174,7 +180,7 @@ struct WideEngine {
                 yoff[b] = XB + mnmajor_offset<BN>(wn * FN * 16 + b * 16, lane);
         }
         S = p.R / 64;
-        park_off = NBUF * BUF + threadIdx.x * 8;
+        park_lane = lds + threadIdx.x * 8;
     }
 
     __device__ __forceinline__ void issue(int s) {
@@ -204,26 +210,33 @@ struct WideEngine {
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if (s + NBUF - 1 < S)
             issue(s + NBUF - 1);
-        const char *buf = smem + (s % NBUF) * BUF;
+        cur = smem + (s % NBUF) * BUF;
+        read<0>();
+    }
+
+    // Fragment reads of leaf half H of the current stage (the first half is
+    // read by begin(), the second just before the first half's MFMAs, which
+    // cover its latency; holding only one half through the tree work saves
+    // registers).
+    template <int H>
+    __device__ __forceinline__ void read() {
+        const char *buf = cur;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int a = 0; a < FM; ++a) {
-                if constexpr (XK) {
-                    fa[h][a] = *reinterpret_cast<const bf16x8 *>(buf + xoff[h] + a * 16 * 128);
-                } else {
-                    const char *q = buf + xoff[a] + h * 32 * BM * 2;
-                    fa[h][a] = tr_read(q, q + 4 * BM * 2);
-                }
+        for (int a = 0; a < FM; ++a) {
+            if constexpr (XK) {
+                fa[H][a] = *reinterpret_cast<const bf16x8 *>(buf + xoff[H] + a * 16 * 128);
+            } else {
+                const char *q = buf + xoff[a] + H * 32 * BM * 2;
+                fa[H][a] = tr_read(q, q + 4 * BM * 2);
             }
+        }
 #pragma unroll
-            for (int b = 0; b < FN; ++b) {
-                if constexpr (YK) {
-                    fb[h][b] = *reinterpret_cast<const bf16x8 *>(buf + yoff[h] + b * 16 * 128);
-                } else {
-                    const char *q = buf + yoff[b] + h * 32 * BN * 2;
-                    fb[h][b] = tr_read(q, q + 4 * BN * 2);
-                }
+        for (int b = 0; b < FN; ++b) {
+            if constexpr (YK) {
+                fb[H][b] = *reinterpret_cast<const bf16x8 *>(buf + yoff[H] + b * 16 * 128);
+            } else {
+                const char *q = buf + yoff[b] + H * 32 * BN * 2;
+                fb[H][b] = tr_read(q, q + 4 * BN * 2);
             }
         }
     }
@@ -240,6 +253,7 @@ struct WideEngine {
     // block, the second as fp32.
     __device__ __forceinline__ void leaves(P &x0, F &l1) {
         const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        read<1>();
         F l0;
 #pragma unroll
         for (int a = 0; a < FM; ++a)
@@ -254,8 +268,25 @@ struct WideEngine {
         x0 = wpack(l0);
     }
 
+    // Leaf h of the current stage, rounded and packed.  SWAP exchanges the
+    // operands of the MFMA: the same products, summed by the same instruction
+    // for each output, land transposed -- the layout a matrix-core add
+    // produces, so the leaf can meet a sibling one level taller.
+    template <int H, bool SWAP>
+    __device__ __forceinline__ P leaf() const {
+        const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        F l;
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+                l.v[a][b] = SWAP ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[H][b], fa[H][a], zero, 0, 0, 0)
+                                 : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[H][a], fb[H][b], zero, 0, 0, 0);
+        return wpack(l);
+    }
+
     __device__ __forceinline__ void park(int slot, const P &v) {
-        char *base = smem + park_off + slot * PARK_LEVEL;
+        char *base = park_lane + slot * PARK_LEVEL;
 #pragma unroll
         for (int a = 0; a < FM; ++a)
 #pragma unroll
@@ -264,7 +295,7 @@ struct WideEngine {
     }
 
     __device__ __forceinline__ P unpark(int slot) const {
-        const char *base = smem + park_off + slot * PARK_LEVEL;
+        const char *base = park_lane + slot * PARK_LEVEL;
         P v;
 #pragma unroll
         for (int a = 0; a < FM; ++a)
@@ -286,9 +317,10 @@ struct WideEngine {
 // and carried (packed) into stage s + 1.  Each phase is kept to itself by a
 // scheduling barrier, which bounds the registers a wave holds at any time; the
 // other wave of the SIMD overlaps its phases with this one's.
-template <class E, class Arith, int GL, int RU>
+template <class E, class Arith, int TB, int GL, int RU>
 struct WideTree {
     static constexpr int G = 1 << GL;
+    static_assert(TB == 1 || TB == 3, "units of one or three leaves");
     static_assert(GL >= 1, "groups of at least two stages");
     // RU >= 1: the zero-leaf step of group 0 writes the first upper slot,
     // which must then be a register (with no upper levels, no LDS slot exists).
@@ -437,7 +469,10 @@ struct WideTree {
     // Tree work of the last stage, then the root is rounded and stored.
     // Returns whether the root has a non-finite value.
     __device__ __forceinline__ bool finish(const P &x0, const F &l1) {
-        const F root = final_chain(wpack(add(x0, wpack(l1))));
+        return finish_root(final_chain(wpack(add(x0, wpack(l1)))));
+    }
+
+    __device__ __forceinline__ bool finish_root(const F &root) {
         bool nonfinite = false;
 #pragma unroll
         for (int a = 0; a < E::kFM; ++a)
@@ -474,9 +509,82 @@ struct WideTree {
             stage<U + 1>(t, x0, l1);
     }
 
-    // Requires S = e.S = G * 2^nup.  Computes and stores the tile; returns
-    // whether a root was non-finite.
+    // ---- L = 3 * 2^a.  The mid-split tree is the perfect tree over units of
+    // three leaves, u = x0 (+) (x1 (+) x2).  Three stages (leaves a0 a1 | b0 b1
+    // | c0 c1) hold two units, a0 (+) (a1 (+) b0) and b1 (+) (c0 (+) c1), whose
+    // add is the six-leaf node that climbs (levels counted from it).  With
+    // matrix-core adds the single leaves a0 and b1 are computed with swapped
+    // operands, so they are laid out like the two-leaf nodes they meet.
+    struct Carry {
+        P a0, a1, b0, b1, u0, c0, c1;
+    };
+
+    // Tree work that finishes super-stage U of group t: the second unit and
+    // the six-leaf node.
+    template <int U>
+    __device__ __forceinline__ void step3(const Carry &c, int t) {
+        const P u1 = wpack(add(c.b1, wpack(add(c.c0, c.c1))));
+        climb_low<U, 0>(wpack(add(c.u0, u1)), t);
+    }
+
+    // Super-stage U of group t: stages A, B, C.
+    //   A: finish super-stage U - 1 (group t - 1's last one for U = 0, with the
+    //      zero-leaf convention of the one-leaf schedule), then leaves a0, a1;
+    //   B: leaves b0, b1;
+    //   C: the first unit, then leaves c0, c1.
+    template <int U>
+    __device__ __forceinline__ void stage3(int t, Carry &c) {
+        const int s = 3 * (t * G + U);
+        e.begin(s);
+        if constexpr (U == 0)
+            step3<G - 1>(c, t > 0 ? t - 1 : 0);
+        else
+            step3<U - 1>(c, t);
+        e.template read<1>();
+        c.a0 = e.template leaf<0, Arith::kTransposes>();
+        c.a1 = e.template leaf<1, false>();
+        pin_p(c.a0);
+        pin_p(c.a1);
+        e.begin(s + 1);
+        e.template read<1>();
+        c.b0 = e.template leaf<0, false>();
+        c.b1 = e.template leaf<1, Arith::kTransposes>();
+        pin_p(c.b0);
+        pin_p(c.b1);
+        e.begin(s + 2);
+        c.u0 = wpack(add(c.a0, wpack(add(c.a1, c.b0))));
+        e.template read<1>();
+        c.c0 = e.template leaf<0, false>();
+        c.c1 = e.template leaf<1, false>();
+        pin_p(c.u0);
+        pin_p(c.c0);
+        pin_p(c.c1);
+        if constexpr (U + 1 < G)
+            stage3<U + 1>(t, c);
+    }
+
+    __device__ __forceinline__ bool run3() {
+        const int T = e.S / (3 * G);
+        e.prologue();
+        Carry c;
+#pragma unroll
+        for (int a = 0; a < E::kFM; ++a)
+#pragma unroll
+            for (int b = 0; b < E::kFN; ++b) {
+                c.a0.w[a][b] = c.a1.w[a][b] = c.b0.w[a][b] = c.b1.w[a][b] = u32x2{0u, 0u};
+                c.u0.w[a][b] = c.c0.w[a][b] = c.c1.w[a][b] = u32x2{0u, 0u};
+            }
+        for (int t = 0; t < T; ++t)
+            stage3<0>(t, c);
+        const P u1 = wpack(add(c.b1, wpack(add(c.c0, c.c1))));
+        return finish_root(final_chain(wpack(add(c.u0, u1))));
+    }
+
+    // Requires S = e.S = TB * G * 2^nup.  Computes and stores the tile;
+    // returns whether a root was non-finite.
     __device__ __forceinline__ bool run() {
+        if constexpr (TB == 3)
+            return run3();
         const int T = e.S >> GL;
         e.prologue();
         P x0;
@@ -511,7 +619,8 @@ __device__ __forceinline__ T *uniform_ptr(T *p) {
 // tiles whose matrix-core tree produced a non-finite root.  Arguments of a
 // called function arrive in vector registers, so the workgroup-uniform values
 // are made scalar again for the staging code.
-template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU>
+template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int TB, int GL,
+          int RU>
 __device__ __attribute__((noinline)) void wide_valu_tile(MfmaParams q) {
     typedef WideEngine<XK, YK, OUT, FM, FN, WM, WN, NBUF> E;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -533,15 +642,15 @@ __device__ __attribute__((noinline)) void wide_valu_tile(MfmaParams q) {
     const int tile = blockIdx.x;
     const int i0 = (tile / p.tiles_j) * E::BM;
     const int j0 = (tile % p.tiles_j) * E::BN;
-    E e(p, smem, i0, j0);
-    WideTree<E, WideValuAdd, GL, RU> valu(e, p, split_selector(threadIdx.x & 63), i0, j0, false);
+    E e(p, smem, p.levels > RU ? p.levels - RU : 0, i0, j0);
+    WideTree<E, WideValuAdd, TB, GL, RU> valu(e, p, split_selector(threadIdx.x & 63), i0, j0, false);
     valu.run();
 }
 
 // OCC: waves per SIMD the register allocation must allow (a 4-wave workgroup
 // asks for 2 so that two workgroups share a compute unit).
-template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU,
-          int OCC>
+template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int TB, int GL,
+          int RU, int OCC>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void mfma_wide_kernel(MfmaParams p) {
     typedef WideEngine<XK, YK, OUT, FM, FN, WM, WN, NBUF> E;
@@ -552,8 +661,8 @@ void mfma_wide_kernel(MfmaParams p) {
     const int i0 = (tile / p.tiles_j) * E::BM;
     const int j0 = (tile % p.tiles_j) * E::BN;
 
-    E e(p, smem, i0, j0);
-    WideTree<E, WideMatrixAdd, GL, RU> tree(e, p, split_selector(lane), i0, j0,
+    E e(p, smem, p.levels > RU ? p.levels - RU : 0, i0, j0);
+    WideTree<E, WideMatrixAdd, TB, GL, RU> tree(e, p, split_selector(lane), i0, j0,
                                             (tree_height_rt(p.L) & 1) != 0);
     const bool nonfinite = tree.run();
     __threadfence_block();  // this tile's stores are done before a recomputation overwrites them
@@ -561,7 +670,7 @@ void mfma_wide_kernel(MfmaParams p) {
     // matrix-core add rows: recompute such a tile with element-wise adds, which
     // overwrite what was stored.
     if (__syncthreads_or(nonfinite))
-        wide_valu_tile<XK, YK, OUT, FM, FN, WM, WN, NBUF, GL, RU>(p);
+        wide_valu_tile<XK, YK, OUT, FM, FN, WM, WN, NBUF, TB, GL, RU>(p);
 }
 
 }  // namespace detgemm

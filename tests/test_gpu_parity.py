@@ -331,11 +331,12 @@ def test_mfma_tile_configs_identical(dev, K):
 
 # Tile configurations 3 and 4 are the direct-to-LDS kernels (whole 64-index
 # stages, 16-byte aligned rows, 8-row chunks of operands whose row index is
-# contiguous), 5 and 6 the wide kernels (the same, and power-of-two leaf
-# counts); 2 is the general kernel they must reproduce bit for bit.
+# contiguous), 5 to 7 the wide kernels (the same, and leaf counts 2^a or
+# 3 * 2^a); 2 is the general kernel they must reproduce bit for bit.
 FAST_SHAPES = [(200, 192, 256), (256, 136, 768), (320, 256, 4096), (128, 64, 12288),
-               (72, 64, 32768), (512, 512, 1024), (264, 392, 8192)]
-GENERAL_CFG, FAST_CFGS = 2, (3, 4, 5, 6)
+               (72, 64, 32768), (512, 512, 1024), (264, 392, 8192), (768, 384, 1536),
+               (384, 768, 6144)]
+GENERAL_CFG, FAST_CFGS = 2, (3, 4, 5, 6, 7)
 
 
 def _six_forced(cfg, A, B, dC):
@@ -383,7 +384,8 @@ def test_fast_path_matches_general_kernel(dev, M, N, K):
     assert ran >= 3
 
 
-@pytest.mark.parametrize("M,N,K", [(200, 192, 256), (256, 136, 256), (256, 256, 256), (512, 256, 1024)])
+@pytest.mark.parametrize("M,N,K", [(200, 192, 256), (256, 136, 256), (256, 256, 256), (512, 256, 1024),
+                                   (768, 192, 1536)])
 def test_fast_path_integer_regime_bit_exact(dev, M, N, K):
     say("direct-to-LDS kernels, integer regime vs oracle", M, N, K)
     A = W.int_bf16((M, K), 910 + K)
@@ -459,10 +461,10 @@ def test_errors_leave_output_untouched(dev):
 # The wide kernels' tree adds run on the matrix core, where one non-finite node
 # spoils the other sums of its row; such tiles are recomputed with element-wise
 # adds.  Inf and NaN inputs must give the general kernel's bits.
-@pytest.mark.parametrize("K", [1024, 2048])
+@pytest.mark.parametrize("K", [1024, 1536])
 def test_wide_kernel_nonfinite_inputs(dev, K):
     say("wide kernels, non-finite inputs vs general kernel", K)
-    M, N = 1024, 384
+    M, N = 1024, 768
     A, B, dC = _inputs(M, N, K, 950 + K, sigma=0.02)
     A[3, 100] = float("inf")
     A[130, 7] = float("nan")
@@ -471,7 +473,7 @@ def test_wide_kernel_nonfinite_inputs(dev, K):
     Ad, Bd, dCd = A.to(dev), B.to(dev), dC.to(dev)
     ref = _six_forced(GENERAL_CFG, Ad, Bd, dCd)
     ran = 0
-    for cfg in (5, 6):
+    for cfg in (5, 6, 7):
         got = _six_forced(cfg, Ad, Bd, dCd)
         for op, g in got.items():
             if g is None:
