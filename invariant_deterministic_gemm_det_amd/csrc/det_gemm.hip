@@ -218,6 +218,7 @@ int run_mfma(const Problem &pr, hipStream_t st) {
     p.tiles_j = (int32_t)tiles_j;
     p.xvec = aligned16(pr.x, pr.ldx);
     p.yvec = aligned16(pr.y, pr.ldy);
+    p.cvec = pr.out != OUT_F32 && aligned16(pr.c, pr.ldc);
     const int64_t tiles = tiles_i * tiles_j;
 
     hipError_t e;

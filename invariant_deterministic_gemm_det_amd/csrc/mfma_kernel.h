@@ -61,6 +61,7 @@ struct MfmaParams {
     int32_t I, J, R, L;
     int32_t tiles_j;
     int32_t xvec, yvec;  // 16-byte aligned rows/columns: vector loads allowed
+    int32_t cvec;        // 16-byte aligned output rows: vector stores allowed
     int32_t levels;      // TREE_BLOCK: levels above the blocks; TREE_STACK: stack depth
 };
 

@@ -97,6 +97,71 @@ struct WideValuAdd {
     }
 };
 
+// Stores a tile's roots (bf16, as [row][column] of the output, i.e. transposed
+// for OUT_BF16_T) through LDS, so that global memory sees whole 16-byte chunks
+// of output rows instead of 2-byte writes scattered over 16 rows.  The LDS rows
+// are padded by 16 bytes, which spreads the lanes of a write over the banks.
+// Needs every wave past a barrier that ends its use of `lds`.  A zero root is
+// stored as +0, the sign the sequential definition gives every exact zero.
+template <int OUT, int FM, int FN, int BM, int BN, int NW>
+__device__ __forceinline__ void store_staged(const MfmaParams &p, const Frag<FM, FN> &root, bool odd,
+                                             int i0, int j0, int wm, int wn, int lane, char *lds) {
+    constexpr bool T = OUT == OUT_BF16_T;
+    constexpr int ROWS = T ? BN : BM, COLS = T ? BM : BN;  // of the staged block
+    constexpr int RS = COLS * 2 + 16;                      // LDS row stride, bytes
+    const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+            uint16_t v4[4];
+            quad_bits(root, a, b, v4);
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                v4[v] = (v4[v] & 0x7FFF) ? v4[v] : (uint16_t)0;
+            const int rb = wm * FM * 16 + a * 16, cb = wn * FN * 16 + b * 16;  // block origin (i, j)
+            // the lane's four values: odd parity (rb + c, cb + 4g + v), even (rb + 4g + v, cb + c);
+            // they are contiguous in a staged row when that row is i (odd, not T) or j (even, T)
+            if (odd != T) {
+                const int r = T ? cb + c : rb + c;
+                const int col = T ? rb + 4 * g : cb + 4 * g;
+                const uint2 w = make_uint2(v4[0] | ((uint32_t)v4[1] << 16), v4[2] | ((uint32_t)v4[3] << 16));
+                *reinterpret_cast<uint2 *>(lds + r * RS + col * 2) = w;
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = T ? cb + 4 * g + v : rb + 4 * g + v;
+                    const int col = T ? rb + c : cb + c;
+                    *reinterpret_cast<uint16_t *>(lds + r * RS + col * 2) = v4[v];
+                }
+            }
+        }
+    __syncthreads();
+    // read out: 16-byte chunks of staged rows
+    const int row0 = T ? j0 : i0, col0 = T ? i0 : j0;
+    const int rows_ok = (T ? p.J : p.I) - row0, cols_ok = (T ? p.I : p.J) - col0;
+    uint16_t *out = static_cast<uint16_t *>(p.c);
+    constexpr int CH = COLS / 8;  // chunks per row
+#pragma unroll
+    for (int k = 0; k < ROWS * CH / (64 * NW); ++k) {
+        const int q = threadIdx.x + k * 64 * NW;
+        const int r = q / CH, ch = q % CH;
+        if (r >= rows_ok)
+            continue;
+        const uint4 w = *reinterpret_cast<const uint4 *>(lds + r * RS + ch * 16);
+        uint16_t *dst = out + (int64_t)(row0 + r) * p.ldc + col0 + ch * 8;
+        if (p.cvec && ch * 8 + 8 <= cols_ok) {
+            *reinterpret_cast<uint4 *>(dst) = w;
+        } else {
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (ch * 8 + e < cols_ok)
+                    dst[e] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+}
+
 template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF>
 struct WideEngine {
     static constexpr int kOUT = OUT, kWM = WM;
@@ -116,7 +181,8 @@ struct WideEngine {
     static constexpr int LOADS = SX::PER_WAVE + SY::PER_WAVE;
     static_assert(NBUF >= 2, "at least two stage buffers");
 
-    char *smem;
+    char *lds;   // the workgroup's LDS allocation
+    char *smem;  // the stage buffers
     SX sx;
     SY sy;
     int xoff[XK ? 2 : FM];  // K-major: per leaf half h; MN-major: per fragment
@@ -156,8 +222,8 @@ struct WideEngine {
     // LDS: the parked tree levels first (`parked` of them), so that a lane's
     // slots are within the immediate offset of one address register, then the
     // NBUF stage buffers.
-    __device__ __forceinline__ WideEngine(const MfmaParams &p, char *lds, int parked, int i0, int j0)
-        : smem(lds + parked * PARK_LEVEL) {
+    __device__ __forceinline__ WideEngine(const MfmaParams &p, char *lds_, int parked, int i0, int j0)
+        : lds(lds_), smem(lds_ + parked * PARK_LEVEL) {
         const int lane = threadIdx.x & 63;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const int wm = wave % WM, wn = wave / WM;
@@ -180,7 +246,7 @@ struct WideEngine {
                 yoff[b] = XB + mnmajor_offset<BN>(wn * FN * 16 + b * 16, lane);
         }
         S = p.R / 64;
-        park_lane = lds + threadIdx.x * 8;
+        park_lane = lds_ + threadIdx.x * 8;
     }
 
     __device__ __forceinline__ void issue(int s) {
@@ -472,17 +538,30 @@ struct WideTree {
         return finish_root(final_chain(wpack(add(x0, wpack(l1)))));
     }
 
+    // With matrix-core adds, a tile whose root has a non-finite value is not
+    // stored (true is returned, the caller recomputes it); element-wise adds
+    // always store.  The barrier of the check also frees the LDS for staging.
     __device__ __forceinline__ bool finish_root(const F &root) {
         bool nonfinite = false;
+        if constexpr (Arith::kTransposes) {
 #pragma unroll
-        for (int a = 0; a < E::kFM; ++a)
+            for (int a = 0; a < E::kFM; ++a)
 #pragma unroll
-            for (int b = 0; b < E::kFN; ++b)
+                for (int b = 0; b < E::kFN; ++b)
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    nonfinite |= !(__builtin_fabsf(root.v[a][b][v]) <= 3.40282347e38f);
-        store(root);
-        return nonfinite;
+                    for (int v = 0; v < 4; ++v)
+                        nonfinite |= !(__builtin_fabsf(root.v[a][b][v]) <= 3.40282347e38f);
+        }
+        if (__syncthreads_or(nonfinite))
+            return true;
+        if constexpr (E::kOUT == OUT_F32) {
+            store(root);
+        } else {
+            const int wave = threadIdx.x >> 6;
+            store_staged<E::kOUT, E::kFM, E::kFN, E::BM, E::BN, E::NW>(
+                p, root, odd, i0, j0, wave % E::kWM, wave / E::kWM, threadIdx.x & 63, e.lds);
+        }
+        return false;
     }
 
     // Stage U of group t: the fragment reads of the stage, the tree work of
@@ -664,12 +743,10 @@ void mfma_wide_kernel(MfmaParams p) {
     E e(p, smem, p.levels > RU ? p.levels - RU : 0, i0, j0);
     WideTree<E, WideMatrixAdd, TB, GL, RU> tree(e, p, split_selector(lane), i0, j0,
                                             (tree_height_rt(p.L) & 1) != 0);
-    const bool nonfinite = tree.run();
-    __threadfence_block();  // this tile's stores are done before a recomputation overwrites them
     // A non-finite root may have spilled NaN into the other sums of its
-    // matrix-core add rows: recompute such a tile with element-wise adds, which
-    // overwrite what was stored.
-    if (__syncthreads_or(nonfinite))
+    // matrix-core add rows: such a tile is not stored but recomputed with
+    // element-wise adds.
+    if (tree.run())
         wide_valu_tile<XK, YK, OUT, FM, FN, WM, WN, NBUF, TB, GL, RU>(p);
 }
 
