@@ -163,9 +163,11 @@ def main():
                      "min_ms": round(min(ts), 4), "max_ms": round(max(ts), 4)}
     dom = max(ops, key=lambda k: ops[k]["ms"])
     achieved = ops[dom]["tflops"]
-    kernel_names = {"fwd": "mfma_fast_kernel<K-major X, MN-major Y, bf16 out>",
-                    "da": "mfma_fast_kernel<K-major X, K-major Y, bf16 out>",
-                    "db": "mfma_fast_kernel<MN-major X, MN-major Y, bf16 out>"}
+    # the kernels the library selects for these shapes (wide kernel, 128x128 tiles):
+    # L = 128 for fwd (R = K) and db (R = M), L = 192 = 3 * 64 for da (R = N)
+    kernel_names = {"fwd": "mfma_wide_kernel<K-major X, MN-major Y, bf16 out, 2-leaf units>",
+                    "da": "mfma_wide_kernel<K-major X, K-major Y, bf16 out, 3-leaf units>",
+                    "db": "mfma_wide_kernel<MN-major X, MN-major Y, bf16 out, 2-leaf units>"}
 
     if args.profile_only:
         if args.copy_calibration:
