@@ -158,7 +158,7 @@ bool wide_ok(const Problem &pr, const TreeSel &t, const TileCfg &c, int &up) {
     up = 0;
     while ((G << up) < S)
         ++up;
-    return c.lds_bytes(up) <= kLdsMax - 1024;
+    return c.lds_bytes(up) <= kLdsMax;  // the wide kernels use no static LDS
 }
 
 int pick_config(const Problem &pr, const TreeSel &t, int levels) {

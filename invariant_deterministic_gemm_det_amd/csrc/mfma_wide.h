@@ -255,10 +255,10 @@ struct WideEngine {
         sy.issue(s, buf + XB);
     }
 
-    // Stages 0 .. NBUF-2 in flight.
+    // Stages 0 .. NBUF-2 in flight (0 and 1 with four buffers).
     __device__ __forceinline__ void prologue() {
 #pragma unroll
-        for (int q = 0; q < NBUF - 1; ++q)
+        for (int q = 0; q < (kPairs ? 2 : NBUF - 1); ++q)
             if (q < S)
                 issue(q);
     }
@@ -268,14 +268,31 @@ struct WideEngine {
     // all of stage s is in LDS and every wave has consumed stage s - 1, whose
     // buffer is refilled with stage s + NBUF - 1 --, then the fragment reads of
     // stage s are issued.
+    //
+    // With four stage buffers the workgroup joins every other stage instead:
+    // at an even stage s, stages s and s + 1 are complete and the copies of
+    // s + 2 and s + 3 start (PAR: the parity of s, when the caller knows it).
+    static constexpr bool kPairs = NBUF == 4;
+    template <int PAR = -1>
     __device__ __forceinline__ void begin(int s) {
-        if (s + NBUF - 2 < S)
-            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NBUF - 2) * LOADS)
-                         : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (s + NBUF - 1 < S)
-            issue(s + NBUF - 1);
+        if constexpr (kPairs) {
+            static_assert(PAR == 0 || PAR == 1, "stage parity must be static");
+            if constexpr (PAR == 0) {
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                if (s + 2 < S) {
+                    issue(s + 2);
+                    issue(s + 3);
+                }
+            }
+        } else {
+            if (s + NBUF - 2 < S)
+                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NBUF - 2) * LOADS)
+                             : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (s + NBUF - 1 < S)
+                issue(s + NBUF - 1);
+        }
         cur = smem + (s % NBUF) * BUF;
         read<0>();
     }
@@ -332,6 +349,26 @@ struct WideEngine {
             for (int b = 0; b < FN; ++b)
                 l1.v[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[1][a], fb[1][b], zero, 0, 0, 0);
         x0 = wpack(l0);
+    }
+
+    // Workgroup-wide OR of a flag, through one dword per wave at the end of
+    // the stage buffers (the output staging stays below it).  Two barriers:
+    // the first also retires every wave's use of the LDS.  (Not the runtime's
+    // block reduction, which reserves static LDS and so would shrink the
+    // dynamic allocation below the full 160 KB.)
+    __device__ __forceinline__ bool any_in_workgroup(bool flag) {
+        int *slot = reinterpret_cast<int *>(smem + NBUF * BUF) - NW;
+        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const bool any = __builtin_amdgcn_ballot_w64(flag) != 0;
+        __syncthreads();
+        if ((threadIdx.x & 63) == 0)
+            slot[w] = any ? 1 : 0;
+        __syncthreads();
+        int r = 0;
+#pragma unroll
+        for (int q = 0; q < NW; ++q)
+            r |= slot[q];
+        return r != 0;
     }
 
     // Leaf h of the current stage, rounded and packed.  SWAP exchanges the
@@ -552,7 +589,7 @@ struct WideTree {
                     for (int v = 0; v < 4; ++v)
                         nonfinite |= !(__builtin_fabsf(root.v[a][b][v]) <= 3.40282347e38f);
         }
-        if (__syncthreads_or(nonfinite))
+        if (e.any_in_workgroup(nonfinite))
             return true;
         if constexpr (E::kOUT == OUT_F32) {
             store(root);
@@ -576,7 +613,7 @@ struct WideTree {
     // read (group 1 reads it); a branch here would split the stage's code.
     template <int U>
     __device__ __forceinline__ void stage(int t, P &x0, F &l1) {
-        e.begin(t * G + U);
+        e.template begin<U & 1>(t * G + U);
         if constexpr (U == 0)
             step<G - 1>(x0, l1, t > 0 ? t - 1 : 0);
         else
@@ -614,7 +651,7 @@ struct WideTree {
     template <int U>
     __device__ __forceinline__ void stage3(int t, Carry &c) {
         const int s = 3 * (t * G + U);
-        e.begin(s);
+        e.template begin<U & 1>(s);
         if constexpr (U == 0)
             step3<G - 1>(c, t > 0 ? t - 1 : 0);
         else
@@ -624,13 +661,13 @@ struct WideTree {
         c.a1 = e.template leaf<1, false>();
         pin_p(c.a0);
         pin_p(c.a1);
-        e.begin(s + 1);
+        e.template begin<(U + 1) & 1>(s + 1);
         e.template read<1>();
         c.b0 = e.template leaf<0, false>();
         c.b1 = e.template leaf<1, Arith::kTransposes>();
         pin_p(c.b0);
         pin_p(c.b1);
-        e.begin(s + 2);
+        e.template begin<U & 1>(s + 2);
         c.u0 = wpack(add(c.a0, wpack(add(c.a1, c.b0))));
         e.template read<1>();
         c.c0 = e.template leaf<0, false>();
