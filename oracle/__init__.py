@@ -23,6 +23,14 @@ exact-rational brute force on tiny shapes; the half-K identity; a forward error
 bound against float64.  Parity unpinned (fixed by reading, locked by tests):
 the odd-split direction, the fp32-output reading, the backward invariance
 reading.
+
+The MoE grouped GEMM's per-token epilogue (reading notes on bitwise-
+deterministic pretraining in Megatron Core, section "Kernel redesign: the
+grouped-GEMM epilogue") is pinned in ``tests/test_oracle_moe.py``: exact
+integer dot products and expert routing, hand-derived tree-shape and
+signed-zero cases in ``tests/golden/moe_cases.txt``, and the float64 sum within
+the pairwise-summation error bound.  Parity unpinned (fixed by reading): the
+slot width of 128 columns, fp32 adds, the two tree shapes.
 """
 import ctypes
 import os
@@ -70,6 +78,11 @@ def _load():
         lib.oracle_round_bf16_array.restype = None
         lib.oracle_add_bf16_array.argtypes = [p, p, p, i64]
         lib.oracle_add_bf16_array.restype = None
+        lib.oracle_moe_dprob.argtypes = [p, i64, p, i64, i64, i64, p, i64, p]
+        lib.oracle_moe_dprob.restype = ctypes.c_int
+        lib.oracle_moe_fwd_dprob.argtypes = [p, i64, p, i64, i64, p, i64, p, i64, p, i64, p, i64,
+                                             p, i64, i64, i64]
+        lib.oracle_moe_fwd_dprob.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -220,6 +233,52 @@ def add_bf16(a, b):
     out = np.empty(a.shape, np.uint16)
     _load().oracle_add_bf16_array(_ptr(a), _ptr(b), _ptr(out), a.size)
     return out
+
+
+SLOT = 128
+
+
+def moe_dprob(Y, G):
+    """Per-token reduction epilogue of the MoE grouped GEMM: for Y, G [T,N]
+    (bf16 bit patterns) returns (slots [J,T] float32, dprob [T] float32) with
+    J = ceil(N/128): slot j of row r is the mid-split fp32 tree over the 128
+    column positions of columns [128j, 128j+128) of Y[r]*G[r] (+0 past N), and
+    dprob[r] the mid-split fp32 tree over the J slots of row r."""
+    Y, ldy = _mat(Y, "Y")
+    G, ldg = _mat(G, "G")
+    if Y.shape != G.shape:
+        raise ValueError("Y and G differ in shape")
+    T, N = Y.shape
+    J = (N + SLOT - 1) // SLOT
+    slots = np.zeros((J, T), np.float32)
+    dprob = np.zeros(T, np.float32)
+    _check(_load().oracle_moe_dprob(_ptr(Y), ldy, _ptr(G), ldg, T, N, _ptr(slots), max(T, 1),
+                                    _ptr(dprob)))
+    return slots, dprob
+
+
+def moe_fwd_dprob(X, W, offsets, G):
+    """The MoE grouped GEMM with its per-token epilogue: X [T,K] with rows grouped
+    by expert (expert e owns rows offsets[e]..offsets[e+1]), W [E,K,N], G [T,N].
+    Returns (Y [T,N] bf16 bits, slots [J,T], dprob [T])."""
+    X, ldx = _mat(X, "X")
+    G, ldg = _mat(G, "G")
+    W = np.ascontiguousarray(np.asarray(W))
+    if W.dtype != np.uint16 or W.ndim != 3:
+        raise TypeError("W must be a 3-D uint16 array [E,K,N]")
+    E, K, N = W.shape
+    T = X.shape[0]
+    off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+    if off.shape != (E + 1,) or X.shape[1] != K or G.shape != (T, N):
+        raise ValueError("shape mismatch")
+    J = (N + SLOT - 1) // SLOT
+    Y = np.zeros((T, N), np.uint16)
+    slots = np.zeros((J, T), np.float32)
+    dprob = np.zeros(T, np.float32)
+    _check(_load().oracle_moe_fwd_dprob(_ptr(X), ldx, _ptr(W), max(N, 1), K * N, _ptr(off), E,
+                                        _ptr(G), ldg, _ptr(Y), max(N, 1), _ptr(slots), max(T, 1),
+                                        _ptr(dprob), T, N, K))
+    return Y, slots, dprob
 
 
 def num_threads():

@@ -273,3 +273,98 @@ int oracle_num_threads(void) {
     return 1;
 #endif
 }
+
+/* ==== MoE grouped GEMM with a per-token reduction epilogue ====
+ *
+ * Reading notes "Bitwise-Deterministic Pretraining at Scale: How Megatron Core
+ * Finds and Removes Every Flipped Bit", section "Kernel redesign: the
+ * grouped-GEMM epilogue": in the epilogue of the MoE grouped GEMM several
+ * N-tiles contribute to the same per-token value dprob[token]; instead of
+ * atomic adds (whose order varies from run to run), every N-tile writes a
+ * private slot and, once all writers are done, the slots are combined by a
+ * fixed reduction tree.
+ *
+ * What is computed here:
+ *   - rows of X are grouped by expert: expert e owns rows [off[e], off[e+1]);
+ *     Y[r, :] = det_gemm forward of X[r, :] with that expert's weight W_e [K,N]
+ *     (the operation defined above, per segment);
+ *   - dprob[r] is the reduction over n of p(r, n) = Y[r, n] * G[r, n]
+ *     (G: the gradient of the expert output for that row);
+ *   - slot j of row r holds the reduction of the products of columns
+ *     [128 j, 128 j + 128); dprob[r] combines the slots of row r.
+ *
+ * Readings where the page is silent (each one is also listed in the design
+ * notes of this repository):
+ *   - the slot width is 128 columns (the output tile width of the kernels);
+ *   - products are fp32 products of the two bf16 values (exact in fp32);
+ *   - every add is an fp32 add, round to nearest even;
+ *   - inside a slot the products are combined by the mid-split tree over the
+ *     128 column positions of the slot, positions at or past N holding +0
+ *     (for 128 positions the mid-split tree is the perfect pairwise tree);
+ *   - the slots of a row are combined by the mid-split tree over the J slots
+ *     (the same split rule as the leaves of det_gemm: left child floor(n/2));
+ *   - N == 0 gives dprob = +0 and no slot.
+ */
+#define ORACLE_SLOT 128
+
+/* Mid-split tree of fp32 adds over v[lo, hi) (hi > lo). */
+static float tree_f32(const float *v, int64_t lo, int64_t hi) {
+    if (hi - lo == 1)
+        return v[lo];
+    int64_t mid = lo + (hi - lo) / 2;
+    float left = tree_f32(v, lo, mid);
+    float right = tree_f32(v, mid, hi);
+    return left + right;
+}
+
+/* slots[j*slot_ld + r] (J = ceil(N/128) slots per row) and dprob[r] for the
+ * T rows of Y [T,N] and G [T,N].  slots may be NULL. */
+int oracle_moe_dprob(const uint16_t *Y, int64_t ldy, const uint16_t *G, int64_t ldg,
+                     int64_t T, int64_t N, float *slots, int64_t slot_ld, float *dprob) {
+    if (T < 0 || N < 0 || (T > 0 && N > 0 && (ldy < N || ldg < N)) || (slots && slot_ld < T))
+        return ORACLE_EINVAL;
+    const int64_t J = (N + ORACLE_SLOT - 1) / ORACLE_SLOT;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < T; ++r) {
+        float prod[ORACLE_SLOT];
+        float *s = J > 0 ? malloc((size_t)J * sizeof *s) : NULL;
+        if (J > 0 && !s) {
+            failed = 1;
+            continue;
+        }
+        for (int64_t j = 0; j < J; ++j) {
+            for (int64_t c = 0; c < ORACLE_SLOT; ++c) {
+                int64_t n = j * ORACLE_SLOT + c;
+                prod[c] = n < N ? widen(Y[r * ldy + n]) * widen(G[r * ldg + n]) : 0.0f;
+            }
+            s[j] = tree_f32(prod, 0, ORACLE_SLOT);
+            if (slots)
+                slots[j * slot_ld + r] = s[j];
+        }
+        dprob[r] = J > 0 ? tree_f32(s, 0, J) : 0.0f;
+        free(s);
+    }
+    return failed ? ORACLE_ENOMEM : ORACLE_OK;
+}
+
+/* The whole operation: Y per expert segment (det_gemm forward), then the
+ * slots and dprob.  off holds E + 1 row offsets, off[0] = 0, nondecreasing,
+ * off[E] = T; W_e starts at W + e * w_stride. */
+int oracle_moe_fwd_dprob(const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw,
+                         int64_t w_stride, const int64_t *off, int64_t E, const uint16_t *G,
+                         int64_t ldg, uint16_t *Y, int64_t ldy, float *slots, int64_t slot_ld,
+                         float *dprob, int64_t T, int64_t N, int64_t K) {
+    if (E < 1 || off[0] != 0 || off[E] != T)
+        return ORACLE_EINVAL;
+    for (int64_t e = 0; e < E; ++e)
+        if (off[e + 1] < off[e])
+            return ORACLE_EINVAL;
+    for (int64_t e = 0; e < E; ++e) {
+        int rc = oracle_det_gemm_fwd(X + off[e] * ldx, ldx, W + e * w_stride, ldw,
+                                     Y + off[e] * ldy, ldy, off[e + 1] - off[e], N, K);
+        if (rc)
+            return rc;
+    }
+    return oracle_moe_dprob(Y, ldy, G, ldg, T, N, slots, slot_ld, dprob);
+}
