@@ -136,3 +136,51 @@ def deep_inputs(device="cpu"):
     """(A[2048,32768] ~N(0,1), B[32768,4096] ~N(0,0.02)): the 32768 depth cap."""
     return (randn_bf16((DEEP_M, DEEP_K), 1.0, 5003, device),
             randn_bf16((DEEP_K, DEEP_N), 0.02, 5004, device))
+
+
+# ---------------------------------------------------------------- MoE grouped GEMM
+# Expert down projection of a top-2 MoE layer: 4096 tokens routed to 2 of 8
+# experts give 8192 rows grouped by expert; expert width 2048 -> model width
+# 4096.  The routing is skewed (expert e drawn with weight (e+1)^-1/2), as a
+# learned router's load is uneven.
+MOE_TOKENS, MOE_TOPK, MOE_E = 4096, 2, 8
+MOE_K, MOE_N = 2048, 4096
+
+
+@dataclass
+class MoEInputs:
+    x: torch.Tensor       # [T, K] expert inputs, rows grouped by expert
+    w: torch.Tensor       # [E, K, N] expert weights
+    g: torch.Tensor       # [T, N] gradient of each row's expert output (its token's)
+    offsets: list         # E + 1 row offsets
+    token: torch.Tensor   # token of each grouped row (int64, CPU)
+
+
+def moe_routing(tokens, topk, E, seed, skew=0.5):
+    """Seeded top-k routing: each token draws topk distinct experts with weights
+    (e+1)^-skew.  Returns (offsets [E+1], token of each row, expert of each row)
+    with rows sorted by expert (stable: ascending token within an expert)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(seed))
+    w = torch.arange(1, E + 1, dtype=torch.float64).pow(-skew)
+    picks = torch.multinomial(w.expand(tokens, E).contiguous(), topk, replacement=False,
+                              generator=gen)
+    expert = picks.reshape(-1)
+    token = torch.arange(tokens).repeat_interleave(topk)
+    order = torch.sort(expert, stable=True).indices
+    counts = torch.bincount(expert, minlength=E)
+    offsets = [0] + torch.cumsum(counts, 0).tolist()
+    return offsets, token[order], expert[order]
+
+
+def moe_inputs(device="cpu", tokens=MOE_TOKENS, topk=MOE_TOPK, E=MOE_E, K=MOE_K, N=MOE_N,
+               seed=6000):
+    """X ~N(0,1) [T,K], W ~N(0,0.02) [E,K,N], G = dO[token of the row] with
+    dO ~N(0,1e-3) [tokens,N]."""
+    offsets, token, _ = moe_routing(tokens, topk, E, seed)
+    T = offsets[-1]
+    x = randn_bf16((T, K), 1.0, seed + 1, device)
+    w = randn_bf16((E, K, N), 0.02, seed + 2, device)
+    dO = randn_bf16((tokens, N), 1e-3, seed + 3, device)
+    g = dO[token.to(dO.device)].contiguous()
+    return MoEInputs(x, w, g, offsets, token)

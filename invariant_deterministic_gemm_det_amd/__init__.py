@@ -28,7 +28,10 @@ _SIX = ("det_gemm_fwd", "det_gemm_fwd_rhs_transposed", "det_gemm_fwd_fp32", "det
         "det_gemm_db", "det_gemm_db_transposed")
 EXPORTS = _SIX + tuple(n.replace("det_gemm_", "det_gemm_strict_") for n in _SIX) + (
     "det_gemm_debug_leaves", "det_gemm_debug_round", "det_gemm_debug_add",
-    "det_gemm_debug_force_config", "det_gemm_status_string")
+    "det_gemm_debug_force_config", "det_gemm_status_string", "det_moe_fwd_dprob",
+    "det_moe_debug_slots")
+MOE_SLOT = 128
+MOE_MAX_EXPERTS = 128
 
 
 class DetGemmError(RuntimeError):
@@ -69,6 +72,11 @@ def load_library(path=LIB_PATH):
     lib.det_gemm_debug_add.restype = ctypes.c_int
     lib.det_gemm_debug_force_config.argtypes = [ctypes.c_int]
     lib.det_gemm_debug_force_config.restype = ctypes.c_int
+    lib.det_moe_fwd_dprob.argtypes = [p, i64, p, i64, i64, p, i64, p, i64, p, i64, p, i64, p,
+                                      i64, i64, i64, p]
+    lib.det_moe_fwd_dprob.restype = ctypes.c_int
+    lib.det_moe_debug_slots.argtypes = [p, i64, p, i64, p, i64, i64, i64, p]
+    lib.det_moe_debug_slots.restype = ctypes.c_int
     lib.det_gemm_status_string.argtypes = [ctypes.c_int]
     lib.det_gemm_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -188,6 +196,69 @@ def det_gemm_db_transposed(A, dC, out=None, strict=False):
     out = _out(out, (N, K), A, torch.bfloat16)
     return _call("det_gemm_strict_db_transposed" if strict else "det_gemm_db_transposed", A, dC,
                  out, M, N, K, "det_gemm_db_transposed")
+
+
+# ---------------------------------------------------------------- MoE grouped GEMM
+
+def det_moe_fwd_dprob(X, W, offsets, G, Y=None, slots=None, dprob=None):
+    """MoE grouped GEMM with the per-token slot epilogue (include/det_moe.h).
+
+    X [T,K] bf16, rows grouped by expert (expert e owns rows offsets[e] ..
+    offsets[e+1]-1); W [E,K,N] bf16 (unit stride along N); G [T,N] bf16;
+    offsets: E + 1 host integers.  Returns (Y [T,N] bf16, dprob [T] float32,
+    slots [ceil(N/128), T] float32): Y row r = det_gemm_fwd(X[r], W[e(r)]);
+    slot j of row r and dprob[r] are fixed fp32 trees over Y[r]*G[r]."""
+    T, K = X.shape
+    if W.dim() != 3 or W.dtype != torch.bfloat16 or not W.is_cuda:
+        raise TypeError("W must be a 3-D bfloat16 GPU tensor [E,K,N]")
+    E, K2, N = W.shape
+    if K2 != K or tuple(G.shape) != (T, N):
+        raise ValueError("X, W and G disagree in shape")
+    if N > 1 and W.stride(2) != 1:
+        raise ValueError("W needs unit stride along N")
+    off = [int(v) for v in offsets]
+    if len(off) != E + 1:
+        raise ValueError("offsets must hold E + 1 entries")
+    J = (N + MOE_SLOT - 1) // MOE_SLOT
+    Y = _out(Y, (T, N), X, torch.bfloat16)
+    dprob = _out(dprob, (T,), X, torch.float32)
+    if slots is None:
+        slots = torch.empty((J, T), dtype=torch.float32, device=X.device)
+    if slots.dtype != torch.float32 or slots.dim() != 2 or slots.shape[0] != J or \
+            slots.shape[1] < T or (J > 0 and T > 1 and slots.stride(1) != 1):
+        raise ValueError("slots must be float32 [ceil(N/128), >= T] with unit column stride")
+    xp, ldx = _mat(X, "X")
+    gp, ldg = _mat(G, "G")
+    yp, ldy = _mat(Y, "Y")
+    ldw = W.stride(1) if K > 1 else max(N, 1)
+    slot_ld = slots.stride(0) if J > 1 else max(T, 1)
+    if not dprob.is_contiguous():
+        raise ValueError("dprob must be contiguous")
+    off_arr = (ctypes.c_int64 * (E + 1))(*off)
+    with torch.cuda.device(X.device):
+        rc = load_library().det_moe_fwd_dprob(
+            xp, ldx, ctypes.c_void_p(W.data_ptr()), ldw, W.stride(0) if E > 1 else K * ldw,
+            off_arr, E, gp, ldg, yp, ldy, ctypes.c_void_p(slots.data_ptr()), slot_ld,
+            ctypes.c_void_p(dprob.data_ptr()), T, N, K, _stream(X))
+    _check(rc, "det_moe_fwd_dprob")
+    return Y, dprob, slots
+
+
+def det_moe_debug_slots(Y, G, slots=None):
+    """The slot writer as a kernel of its own over given Y and G: [ceil(N/128), T]."""
+    T, N = Y.shape
+    J = (N + MOE_SLOT - 1) // MOE_SLOT
+    if slots is None:
+        slots = torch.empty((J, T), dtype=torch.float32, device=Y.device)
+    yp, ldy = _mat(Y, "Y")
+    gp, ldg = _mat(G, "G")
+    slot_ld = slots.stride(0) if J > 1 else max(T, 1)
+    with torch.cuda.device(Y.device):
+        rc = load_library().det_moe_debug_slots(yp, ldy, gp, ldg,
+                                                ctypes.c_void_p(slots.data_ptr()), slot_ld, T, N,
+                                                _stream(Y))
+    _check(rc, "det_moe_debug_slots")
+    return slots
 
 
 # ---------------------------------------------------------------- inspection

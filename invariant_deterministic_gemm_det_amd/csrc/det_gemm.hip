@@ -20,6 +20,7 @@
 #include <vector>
 
 #include "det_gemm.h"
+#include "det_moe.h"
 #include "mfma_launch.h"
 #include "strict_kernel.h"
 
@@ -495,6 +496,239 @@ const char *det_gemm_status_string(int status) {
     default:
         return "unknown status";
     }
+}
+
+}  // extern "C"
+
+// ==== MoE grouped GEMM with the per-token slot epilogue (det_moe.h) ====
+namespace {
+
+constexpr int kCombineDepth = 24;  // pending left subtrees of a slot tree, J < 2^23
+
+// Slots as a kernel of their own (when the grouped GEMM does not write them):
+// block (rows 16*bx .. 16*bx+15, slot by), one wave per row.
+__global__ __launch_bounds__(256) void moe_slot_kernel(const uint16_t *y, int64_t ldy,
+                                                       const uint16_t *g, int64_t ldg,
+                                                       float *slots, int64_t slot_ld, int T,
+                                                       int N) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = blockIdx.y;
+    const int c = j * kSlot + 2 * lane;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int r = blockIdx.x * 16 + wave * 4 + q;
+        if (r >= T)
+            break;
+        const uint16_t *yr = y + (int64_t)r * ldy, *gr = g + (int64_t)r * ldg;
+        float p0 = 0.0f, p1 = 0.0f;
+        if (c < N)
+            p0 = bf16_value(yr[c]) * bf16_value(gr[c]);
+        if (c + 1 < N)
+            p1 = bf16_value(yr[c + 1]) * bf16_value(gr[c + 1]);
+        const float v = slot_tree(p0, p1);
+        if (lane == 0)
+            slots[(int64_t)j * slot_ld + r] = v;
+    }
+}
+
+// dprob[r]: the mid-split tree of fp32 adds over the J slots of row r, one
+// thread per row, as a post-order walk over the slots in ascending order with
+// a stack of pending left subtrees (in LDS, one column per thread): after slot
+// t, every inner node whose range ends at t is closed by adding its left
+// subtree (popped) to the running node.
+__global__ __launch_bounds__(256) void moe_combine_kernel(const float *slots, int64_t slot_ld,
+                                                          float *dprob, int T, int J) {
+    __shared__ float stack[kCombineDepth][256];
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= T)
+        return;
+    if (J == 0) {
+        dprob[r] = 0.0f;
+        return;
+    }
+    int sp = 0;
+    for (int t = 0; t < J; ++t) {
+        float v = slots[(int64_t)t * slot_ld + r];
+        for (int m = merges_after(t, J); m > 0; --m)
+            v = stack[--sp][threadIdx.x] + v;
+        stack[sp++][threadIdx.x] = v;
+    }
+    dprob[r] = stack[0][threadIdx.x];
+}
+
+bool aligned4(const void *p, int64_t ld) {
+    return (reinterpret_cast<uintptr_t>(p) & 3) == 0 && (ld % 2) == 0;
+}
+
+int launch_slots(const uint16_t *Y, int64_t ldy, const uint16_t *G, int64_t ldg, float *slots,
+                 int64_t slot_ld, int64_t T, int64_t J, int64_t N, hipStream_t st) {
+    if (J == 0)
+        return DET_GEMM_OK;
+    hipLaunchKernelGGL(moe_slot_kernel, dim3((unsigned)((T + 15) / 16), (unsigned)J), dim3(256),
+                       0, st, Y, ldy, G, ldg, slots, slot_ld, (int)T, (int)N);
+    return hipGetLastError() == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
+}
+
+int moe_entry(const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw, int64_t w_stride,
+              const int64_t *off, int64_t E, const uint16_t *G, int64_t ldg, uint16_t *Y,
+              int64_t ldy, float *slots, int64_t slot_ld, float *dprob, int64_t T, int64_t N,
+              int64_t K, hipStream_t st) {
+    if (T < 0 || N < 0 || K < 0 || E < 1 || E > DET_MOE_MAX_EXPERTS || !off)
+        return DET_GEMM_EINVAL;
+    if (off[0] != 0 || off[E] != T)
+        return DET_GEMM_EINVAL;
+    for (int64_t e = 0; e < E; ++e)
+        if (off[e + 1] < off[e])
+            return DET_GEMM_EINVAL;
+    if (T == 0)
+        return DET_GEMM_OK;
+    if (K == 0 || K > DET_GEMM_MAX_REDUCTION)
+        return DET_GEMM_EKCAP;
+    const int64_t J = (N + kSlot - 1) / kSlot;
+    if (T > kMaxDim || N > kMaxDim || J > 65535 || !dprob || slot_ld < T || slot_ld > kMaxDim ||
+        (J > 0 && !slots) || w_stride < 0)
+        return DET_GEMM_EINVAL;
+    const Mat x{X, T, K, ldx, 2}, gm{G, T, N, ldg, 2}, ym{Y, T, N, ldy, 2};
+    const Mat sm{slots, J, T, slot_ld, 4}, dm{dprob, 1, T, T, 4};
+    // the weights as one range: E matrices [K,N] w_stride apart
+    const Mat wm{W, K, N, ldw, 2};
+    if (!mat_ok(x) || !mat_ok(gm) || !mat_ok(ym) || !mat_ok(wm) || !mat_ok(sm) || !mat_ok(dm))
+        return DET_GEMM_EINVAL;
+    if (N > 0 && (w_stride > (kMaxDim << 8) / E))
+        return DET_GEMM_EINVAL;
+    const Mat wall{W, 1, N > 0 ? (E - 1) * w_stride + (K - 1) * ldw + N : 0, 1, 2};
+    const Mat *outs[3] = {&ym, &sm, &dm};
+    const Mat *ins[3] = {&x, &gm, &wall};
+    for (int a = 0; a < 3; ++a) {
+        for (int b = 0; b < 3; ++b)
+            if (overlaps(*outs[a], *ins[b]))
+                return DET_GEMM_EINVAL;
+        for (int b = a + 1; b < 3; ++b)
+            if (overlaps(*outs[a], *outs[b]))
+                return DET_GEMM_EINVAL;
+    }
+    const int dev = check_device();
+    if (dev != DET_GEMM_OK)
+        return dev;
+    const int64_t blocks = (T + 255) / 256;
+    if (N > 0) {
+        // the grouped wide kernel when the shape allows it, else one product per expert
+        Problem base{X, ldx, true, W, ldw, false, Y, ldy, OUT_BF16, T, N, K};
+        const int L = (int)((K + 31) / 32);
+        int levels = 0;
+        const TreeSel tree = pick_tree(L, levels);
+        int cfg = -1, up = 0;
+        if (g_force_config >= 0) {
+            if (kTileCfgs[g_force_config].kind == KIND_WIDE) {
+                if (g_force_config == 6 || !wide_ok(base, tree, kTileCfgs[g_force_config], up))
+                    return DET_GEMM_EINVAL;
+                cfg = g_force_config;
+            }
+        } else if (wide_ok(base, tree, kTileCfgs[5], up)) {
+            cfg = 5;
+        } else if (wide_ok(base, tree, kTileCfgs[7], up)) {
+            cfg = 7;
+        }
+        bool fused = false;
+        if (cfg >= 0) {
+            GroupTable g;
+            std::memset(&g, 0, sizeof g);
+            const int64_t tiles_j = (N + kTileCfgs[cfg].bn() - 1) / kTileCfgs[cfg].bn();
+            int64_t tiles = 0;
+            g.groups = (int32_t)E;
+            for (int64_t e = 0; e < E; ++e) {
+                const int64_t rows = off[e + 1] - off[e];
+                g.tile_start[e] = (int32_t)tiles;
+                g.row_start[e] = (int32_t)off[e];
+                g.rows[e] = (int32_t)rows;
+                tiles += (rows + kTileCfgs[cfg].bm() - 1) / kTileCfgs[cfg].bm() * tiles_j;
+                if (tiles > kMaxDim)
+                    return DET_GEMM_EINVAL;
+            }
+            g.tile_start[E] = (int32_t)tiles;
+            g.y_stride = w_stride;
+            MfmaParams p;
+            std::memset(&p, 0, sizeof p);
+            p.x = X;
+            p.ldx = ldx;
+            p.y = W;
+            p.ldy = ldw;
+            p.c = Y;
+            p.ldc = ldy;
+            p.I = 0;  // per group
+            p.J = (int32_t)N;
+            p.R = (int32_t)K;
+            p.L = L;
+            p.tiles_j = (int32_t)tiles_j;
+            p.levels = up;
+            p.xvec = aligned16(X, ldx);
+            p.yvec = aligned16(W, ldw) && (w_stride % 8) == 0;
+            p.cvec = aligned16(Y, ldy);
+            fused = aligned4(G, ldg);
+            if (fused) {
+                p.g = G;
+                p.ldg = ldg;
+                p.slots = slots;
+                p.slot_ld = slot_ld;
+            }
+            const hipError_t e = launch_moe_grouped(cfg, p, g, tiles, st);
+            if (e == hipErrorInvalidConfiguration)
+                return DET_GEMM_EINVAL;
+            if (e != hipSuccess)
+                return DET_GEMM_EHIP;
+        } else {
+            for (int64_t e = 0; e < E; ++e) {
+                if (off[e + 1] == off[e])
+                    continue;
+                Problem pr = base;
+                pr.x = X + off[e] * ldx;
+                pr.y = W + e * w_stride;
+                pr.c = Y + off[e] * ldy;
+                pr.I = off[e + 1] - off[e];
+                const int rc = run_mfma(pr, st);
+                if (rc != DET_GEMM_OK)
+                    return rc;
+            }
+        }
+        if (!fused) {
+            const int rc = launch_slots(Y, ldy, G, ldg, slots, slot_ld, T, J, N, st);
+            if (rc != DET_GEMM_OK)
+                return rc;
+        }
+    }
+    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, st, slots,
+                       slot_ld, dprob, (int)T, (int)J);
+    return hipGetLastError() == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int det_moe_fwd_dprob(const det_bf16 *X, int64_t ldx, const det_bf16 *W, int64_t ldw,
+                      int64_t w_stride, const int64_t *offsets, int64_t E, const det_bf16 *G,
+                      int64_t ldg, det_bf16 *Y, int64_t ldy, float *slots, int64_t slot_ld,
+                      float *dprob, int64_t T, int64_t N, int64_t K, void *stream) {
+    return moe_entry(X, ldx, W, ldw, w_stride, offsets, E, G, ldg, Y, ldy, slots, slot_ld, dprob,
+                     T, N, K, static_cast<hipStream_t>(stream));
+}
+
+int det_moe_debug_slots(const det_bf16 *Y, int64_t ldy, const det_bf16 *G, int64_t ldg,
+                        float *slots, int64_t slot_ld, int64_t T, int64_t N, void *stream) {
+    if (T < 0 || N < 0)
+        return DET_GEMM_EINVAL;
+    const int64_t J = (N + kSlot - 1) / kSlot;
+    if (T == 0 || J == 0)
+        return DET_GEMM_OK;
+    if (T > kMaxDim || J > 65535 || slot_ld < T || !slots)
+        return DET_GEMM_EINVAL;
+    const Mat ym{Y, T, N, ldy, 2}, gm{G, T, N, ldg, 2}, sm{slots, J, T, slot_ld, 4};
+    if (!mat_ok(ym) || !mat_ok(gm) || !mat_ok(sm) || overlaps(sm, ym) || overlaps(sm, gm))
+        return DET_GEMM_EINVAL;
+    const int dev = check_device();
+    if (dev != DET_GEMM_OK)
+        return dev;
+    return launch_slots(Y, ldy, G, ldg, slots, slot_ld, T, J, N, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

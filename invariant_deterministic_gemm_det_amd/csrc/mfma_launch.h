@@ -125,6 +125,34 @@ hipError_t launch_wide(const MfmaParams &p, int64_t tiles, hipStream_t st) {
     }
 }
 
+// Grouped wide kernel (forward layout, bf16 out): one launch over the tiles of
+// every row group of `g`.
+template <int FM, int FN, int WM, int WN, int NBUF, int TB, int GL, int RU, int OCC>
+hipError_t launch_wide_grouped(const MfmaParams &p, const GroupTable &g, int64_t tiles,
+                               hipStream_t st) {
+    typedef WideEngine<true, false, OUT_BF16, FM, FN, WM, WN, NBUF> E;
+    void (*kernel)(MfmaParams, GroupTable) =
+        &mfma_wide_grouped_kernel<FM, FN, WM, WN, NBUF, TB, GL, RU, OCC>;
+    const void *fn = reinterpret_cast<const void *>(kernel);
+    static int max_dynamic = -1;
+    if (max_dynamic < 0) {
+        hipFuncAttributes attr;
+        hipError_t e = hipFuncGetAttributes(&attr, fn);
+        if (e != hipSuccess)
+            return e;
+        const int room = kLdsMax - (int)attr.sharedSizeBytes;
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, room);
+        if (e != hipSuccess)
+            return e;
+        max_dynamic = room;
+    }
+    const int lds = E::lds_bytes(p.levels > RU ? p.levels - RU : 0);
+    if (lds > max_dynamic)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)tiles), dim3(64 * WM * WN), lds, st, p, g);
+    return hipGetLastError();
+}
+
 template <bool FAST, bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN>
 hipError_t launch_trees(const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st) {
     if constexpr (FAST) {
@@ -182,5 +210,8 @@ hipError_t launch_kk_bf16(int cfg, const TreeSel &t, const MfmaParams &p, int64_
 hipError_t launch_nn_bf16(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st);
 hipError_t launch_nn_bf16t(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st);
 hipError_t launch_leaves(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st);
+// Grouped forward (configurations 5 and 7 only); defined in mfma_moe.hip.
+hipError_t launch_moe_grouped(int cfg, const MfmaParams &p, const GroupTable &g, int64_t tiles,
+                              hipStream_t st);
 
 }  // namespace detgemm

@@ -103,7 +103,29 @@ struct WideValuAdd {
 // are padded by 16 bytes, which spreads the lanes of a write over the banks.
 // Needs every wave past a barrier that ends its use of `lds`.  A zero root is
 // stored as +0, the sign the sequential definition gives every exact zero.
-template <int OUT, int FM, int FN, int BM, int BN, int NW>
+// ---- per-token epilogue of the MoE grouped GEMM (reading notes on
+// bitwise-deterministic pretraining in Megatron Core, section "Kernel
+// redesign: the grouped-GEMM epilogue": private per-N-tile slots and a fixed
+// tree instead of atomic adds).  A slot is the mid-split tree of fp32 adds over
+// the 128 column positions of one output tile row, positions past the last
+// column holding +0; for 128 positions that is the perfect pairwise tree.
+constexpr int kSlot = 128;
+
+// The slot of one row whose 128 products are held two per lane (columns
+// 2*lane and 2*lane + 1): level 1 is the lane's own pair, level k joins lanes
+// 2^(k-2) apart.  IEEE addition is commutative, so the two lanes of a join hold
+// the same node; every lane ends with the slot.
+__device__ __forceinline__ float slot_tree(float p0, float p1) {
+    float v = p0 + p1;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1)
+        v = v + __shfl_xor(v, m, 64);
+    return v;
+}
+
+__device__ __forceinline__ float bf16_value(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+template <int OUT, int FM, int FN, int BM, int BN, int NW, bool EPI = false>
 __device__ __forceinline__ void store_staged(const MfmaParams &p, const Frag<FM, FN> &root, bool odd,
                                              int i0, int j0, int wm, int wn, int lane, char *lds) {
     constexpr bool T = OUT == OUT_BF16_T;
@@ -158,6 +180,30 @@ __device__ __forceinline__ void store_staged(const MfmaParams &p, const Frag<FM,
             for (int e = 0; e < 8; ++e)
                 if (ch * 8 + e < cols_ok)
                     dst[e] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+    // Slots of the per-token epilogue, from the staged rows (the values just
+    // stored): one wave per row, products of the row's 128 columns two per lane.
+    // G rows are 4-byte aligned here (checked by the host).
+    if constexpr (EPI && !T && COLS == kSlot) {
+        if (p.slots != nullptr) {
+            const int wave = threadIdx.x >> 6, c = 2 * lane;
+            float *slot = p.slots + (int64_t)(col0 / kSlot) * p.slot_ld + row0;
+            for (int r = wave; r < ROWS && r < rows_ok; r += NW) {
+                const uint32_t yy = *reinterpret_cast<const uint32_t *>(lds + r * RS + c * 2);
+                const uint16_t *gr = p.g + (int64_t)(row0 + r) * p.ldg + col0 + c;
+                float p0 = 0.0f, p1 = 0.0f;
+                if (c + 1 < cols_ok) {
+                    const uint32_t gg = *reinterpret_cast<const uint32_t *>(gr);
+                    p0 = bf16_value(yy & 0xFFFFu) * bf16_value(gg & 0xFFFFu);
+                    p1 = bf16_value(yy >> 16) * bf16_value(gg >> 16);
+                } else if (c < cols_ok) {
+                    p0 = bf16_value(yy & 0xFFFFu) * bf16_value(*gr);
+                }
+                const float v = slot_tree(p0, p1);
+                if (lane == 0)
+                    slot[r] = v;
+            }
         }
     }
 }
@@ -420,7 +466,8 @@ struct WideEngine {
 // and carried (packed) into stage s + 1.  Each phase is kept to itself by a
 // scheduling barrier, which bounds the registers a wave holds at any time; the
 // other wave of the SIMD overlaps its phases with this one's.
-template <class E, class Arith, int TB, int GL, int RU>
+// EPI: the tile also writes the per-token slots of p (grouped launches).
+template <class E, class Arith, int TB, int GL, int RU, bool EPI = false>
 struct WideTree {
     static constexpr int G = 1 << GL;
     static_assert(TB == 1 || TB == 3, "units of one or three leaves");
@@ -595,7 +642,7 @@ struct WideTree {
             store(root);
         } else {
             const int wave = threadIdx.x >> 6;
-            store_staged<E::kOUT, E::kFM, E::kFN, E::BM, E::BN, E::NW>(
+            store_staged<E::kOUT, E::kFM, E::kFN, E::BM, E::BN, E::NW, EPI>(
                 p, root, odd, i0, j0, wave % E::kWM, wave / E::kWM, threadIdx.x & 63, e.lds);
         }
         return false;
@@ -736,8 +783,8 @@ __device__ __forceinline__ T *uniform_ptr(T *p) {
 // called function arrive in vector registers, so the workgroup-uniform values
 // are made scalar again for the staging code.
 template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int TB, int GL,
-          int RU>
-__device__ __attribute__((noinline)) void wide_valu_tile(MfmaParams q) {
+          int RU, bool EPI>
+__device__ __attribute__((noinline)) void wide_valu_tile(MfmaParams q, int tile_arg) {
     typedef WideEngine<XK, YK, OUT, FM, FN, WM, WN, NBUF> E;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     MfmaParams p = q;
@@ -753,38 +800,88 @@ __device__ __attribute__((noinline)) void wide_valu_tile(MfmaParams q) {
     p.L = __builtin_amdgcn_readfirstlane(q.L);
     p.tiles_j = __builtin_amdgcn_readfirstlane(q.tiles_j);
     p.levels = __builtin_amdgcn_readfirstlane(q.levels);
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int tile = blockIdx.x;
+    if constexpr (EPI) {
+        p.g = uniform_ptr(q.g);
+        p.ldg = uniform64(q.ldg);
+        p.slots = uniform_ptr(q.slots);
+        p.slot_ld = uniform64(q.slot_ld);
+    }
+    const int tile = __builtin_amdgcn_readfirstlane(tile_arg);
     const int i0 = (tile / p.tiles_j) * E::BM;
     const int j0 = (tile % p.tiles_j) * E::BN;
     E e(p, smem, p.levels > RU ? p.levels - RU : 0, i0, j0);
-    WideTree<E, WideValuAdd, TB, GL, RU> valu(e, p, split_selector(threadIdx.x & 63), i0, j0, false);
+    WideTree<E, WideValuAdd, TB, GL, RU, EPI> valu(e, p, split_selector(threadIdx.x & 63), i0, j0, false);
     valu.run();
 }
 
 // OCC: waves per SIMD the register allocation must allow (a 4-wave workgroup
 // asks for 2 so that two workgroups share a compute unit).
+// One output tile (tile index `tile` of the row-major tile grid of p).
 template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int TB, int GL,
-          int RU, int OCC>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
-void mfma_wide_kernel(MfmaParams p) {
+          int RU, bool EPI>
+__device__ __forceinline__ void wide_tile(const MfmaParams &p, int tile) {
     typedef WideEngine<XK, YK, OUT, FM, FN, WM, WN, NBUF> E;
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int lane = threadIdx.x & 63;
-    const int tile = blockIdx.x;
     const int i0 = (tile / p.tiles_j) * E::BM;
     const int j0 = (tile % p.tiles_j) * E::BN;
 
     E e(p, smem, p.levels > RU ? p.levels - RU : 0, i0, j0);
-    WideTree<E, WideMatrixAdd, TB, GL, RU> tree(e, p, split_selector(lane), i0, j0,
+    WideTree<E, WideMatrixAdd, TB, GL, RU, EPI> tree(e, p, split_selector(lane), i0, j0,
                                             (tree_height_rt(p.L) & 1) != 0);
     // A non-finite root may have spilled NaN into the other sums of its
     // matrix-core add rows: such a tile is not stored but recomputed with
     // element-wise adds.
     if (tree.run())
-        wide_valu_tile<XK, YK, OUT, FM, FN, WM, WN, NBUF, TB, GL, RU>(p);
+        wide_valu_tile<XK, YK, OUT, FM, FN, WM, WN, NBUF, TB, GL, RU, EPI>(p, tile);
+}
+
+template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int TB, int GL,
+          int RU, int OCC>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void mfma_wide_kernel(MfmaParams p) {
+    wide_tile<XK, YK, OUT, FM, FN, WM, WN, NBUF, TB, GL, RU, false>(p, blockIdx.x);
+}
+
+// ---- grouped launch (MoE grouped GEMM): the row-major X is cut into
+// consecutive row groups, group e multiplied by its own Y operand
+// y + e * y_stride; one launch covers the tiles of every group, group e owning
+// tiles tile_start[e] .. tile_start[e+1]-1.  The same tile code runs on the
+// group's rows, so each row gets the bits of an ungrouped product.
+constexpr int kMaxGroups = 128;
+
+struct GroupTable {
+    int32_t groups;
+    int32_t tile_start[kMaxGroups + 1];
+    int32_t row_start[kMaxGroups];
+    int32_t rows[kMaxGroups];
+    int64_t y_stride;
+};
+
+template <int FM, int FN, int WM, int WN, int NBUF, int TB, int GL, int RU, int OCC>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void mfma_wide_grouped_kernel(MfmaParams p, GroupTable g) {
+    const int t = blockIdx.x;
+    int lo = 0, hi = g.groups;  // the last group whose first tile is <= t
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (g.tile_start[mid] <= t)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    MfmaParams q = p;
+    const int64_t r0 = g.row_start[lo];
+    q.x = p.x + r0 * p.ldx;
+    q.y = p.y + (int64_t)lo * g.y_stride;
+    q.c = static_cast<uint16_t *>(p.c) + r0 * p.ldc;
+    q.I = g.rows[lo];
+    if (p.slots != nullptr) {
+        q.g = p.g + r0 * p.ldg;
+        q.slots = p.slots + r0;
+    }
+    wide_tile<true, false, OUT_BF16, FM, FN, WM, WN, NBUF, TB, GL, RU, true>(q, t - g.tile_start[lo]);
 }
 
 }  // namespace detgemm

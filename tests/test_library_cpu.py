@@ -12,6 +12,8 @@ import invariant_deterministic_gemm_det_amd as dg
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "det_gemm.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation
 NULL = ctypes.c_void_p(0)
@@ -25,8 +27,11 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(det_gemm_\w+)\s*\(", text, re.M)))
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        names |= set(re.findall(r"^\s*(?:int|const char \*)\s*(det_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_six_operations():
@@ -90,3 +95,42 @@ def test_force_config_bounds(lib):
     assert lib.det_gemm_debug_force_config(-2) == dg.EINVAL
     assert lib.det_gemm_debug_force_config(0) == n
     assert lib.det_gemm_debug_force_config(-1) == n
+
+
+# ---------------------------------------------------------------- det_moe.h
+
+def _moe(lib, T, N, K, offsets, E=None, slot_ld=None, X=FAKE, W=FAKE, G=FAKE, Y=FAKE,
+         slots=ctypes.c_void_p(0x900000000), dprob=ctypes.c_void_p(0xA00000000), w_stride=None):
+    E = len(offsets) - 1 if E is None else E
+    off = (ctypes.c_int64 * max(len(offsets), 1))(*offsets)
+    return lib.det_moe_fwd_dprob(X, K, W, N, K * N if w_stride is None else w_stride, off, E,
+                                 G, N, Y, N, slots, T if slot_ld is None else slot_ld, dprob,
+                                 T, N, K, NULL)
+
+
+def test_moe_argument_errors_without_device(lib):
+    """Section "Kernel redesign: the grouped-GEMM epilogue" of the Megatron Core
+    reading notes; every error is reported before any device work."""
+    assert _moe(lib, 0, 128, 64, [0, 0]) == dg.OK                 # no rows: no-op
+    assert _moe(lib, 4, 128, 0, [0, 4]) == dg.EKCAP
+    assert _moe(lib, 4, 128, 32769, [0, 4]) == dg.EKCAP
+    assert _moe(lib, 4, 128, 64, [0, 3, 2, 4]) == dg.EINVAL       # decreasing offsets
+    assert _moe(lib, 4, 128, 64, [1, 4]) == dg.EINVAL             # offsets[0] != 0
+    assert _moe(lib, 4, 128, 64, [0, 5]) == dg.EINVAL             # offsets[E] != T
+    assert _moe(lib, 4, 128, 64, [0, 4], E=0) == dg.EINVAL
+    assert _moe(lib, 4, 128, 64, [0] * 129 + [4]) == dg.EINVAL    # more than 128 experts
+    assert _moe(lib, 4, 128, 64, [0, 4], slot_ld=3) == dg.EINVAL  # slot rows shorter than T
+    assert _moe(lib, -1, 128, 64, [0, -1]) == dg.EINVAL
+    assert _moe(lib, 4, 128, 64, [0, 4], w_stride=-1) == dg.EINVAL
+    # the output Y over the input X
+    assert _moe(lib, 4, 128, 64, [0, 4], Y=FAKE, X=FAKE) == dg.EINVAL
+    # dprob over the slots
+    assert _moe(lib, 4, 128, 64, [0, 4], Y=ctypes.c_void_p(0x700000000),
+                dprob=ctypes.c_void_p(0x900000000)) == dg.EINVAL
+
+
+def test_moe_debug_slots_argument_errors(lib):
+    s = ctypes.c_void_p(0x900000000)
+    assert lib.det_moe_debug_slots(FAKE, 128, FAKE, 128, s, 3, 4, 128, NULL) == dg.EINVAL
+    assert lib.det_moe_debug_slots(FAKE, 128, FAKE, 128, s, 4, -1, 128, NULL) == dg.EINVAL
+    assert lib.det_moe_debug_slots(FAKE, 128, FAKE, 128, s, 4, 0, 128, NULL) == dg.OK
