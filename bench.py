@@ -66,6 +66,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target host time of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-moe", action="store_true", help="skip the MoE grouped GEMM leg")
     ap.add_argument("--profile-only", action="store_true",
                     help="run only the GPU steps (for rocprofv3 runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -100,6 +101,82 @@ def cpu_baseline(X, W, dC, target_s):
             "seconds": round(dt, 3),
             "sample": f"CPU oracle on {rows} output rows of each product: fwd C[:{rows}], "
                       f"da dX[:{rows}], db dW[:{rows}] of the M=4096 K=4096 N=6144 step"}
+
+
+def moe_leg(dev, steps, warmup, with_cpu, context=True):
+    """The MoE grouped GEMM with its per-token slot epilogue (det_moe_fwd_dprob) on
+    the expert down projection of a top-2-of-8 MoE layer: 4096 tokens -> 8192
+    rows grouped by expert, K = 2048, N = 4096.  Also times the same products
+    as one det_gemm_fwd launch per expert (no epilogue), as context."""
+    import torch
+    import det_workloads as Wk
+    import invariant_deterministic_gemm_det_amd as dg
+
+    inp = Wk.moe_inputs(dev)
+    T, K, N, E = inp.x.shape[0], Wk.MOE_K, Wk.MOE_N, Wk.MOE_E
+    off = inp.offsets
+    Y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    dprob = torch.empty((T,), dtype=torch.float32, device=dev)
+    slots = torch.empty(((N + 127) // 128, T), dtype=torch.float32, device=dev)
+
+    def call():
+        dg.det_moe_fwd_dprob(inp.x, inp.w, off, inp.g, Y=Y, slots=slots, dprob=dprob)
+
+    def per_expert():
+        for e in range(E):
+            dg.det_gemm_fwd(inp.x[off[e]:off[e + 1]], inp.w[e], out=Y[off[e]:off[e + 1]])
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ts]
+
+    flop = 2.0 * T * K * N
+    t = timed(call)
+    avg = sum(t) / len(t)
+    out = {"workload": "MoE expert down projection: 4096 tokens, top-2 of 8 experts "
+                       "(skewed routing), rows grouped by expert, K=2048, N=4096, "
+                       "epilogue dprob[r] = fixed trees over 128-column slots of Y*G",
+           "rows": T, "segments": [off[e + 1] - off[e] for e in range(E)],
+           "ms": round(avg, 4), "min_ms": round(min(t), 4), "max_ms": round(max(t), 4),
+           "tflops": round(flop / (avg * 1e-3) / 1e12, 2),
+           "roofline": {"bound": "mfma",
+                        "kernel": "mfma_wide_grouped_kernel<2-leaf units> + slot tree combine",
+                        "achieved": round(flop / (avg * 1e-3) / 1e12, 2),
+                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(flop / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                        "traffic": None}}
+    out["roofline"]["traffic"] = recorded_traffic("moe")
+    if context:
+        tp = timed(per_expert)
+        out["per_expert_det_gemm_fwd_ms"] = round(sum(tp) / len(tp), 4)
+    if with_cpu:
+        import numpy as np
+        import oracle
+        rows = [np.arange(off[e], min(off[e + 1], off[e] + 32)) for e in range(E)]
+        idx = np.concatenate(rows)
+        sub_off = [0] + list(np.cumsum([len(r) for r in rows]))
+        x = Wk.bits(inp.x[torch.as_tensor(idx, device=dev)])
+        g = Wk.bits(inp.g[torch.as_tensor(idx, device=dev)])
+        w = Wk.bits(inp.w)
+        t0 = time.perf_counter()
+        oracle.moe_fwd_dprob(x, w, sub_off, g)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": 2.0 * len(idx) * K * N / dt / 1e12, "unit": "TFLOP/s",
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "seconds": round(dt, 3),
+                               "sample": f"CPU oracle on the first 32 rows of each expert "
+                                         f"({len(idx)} rows) of the same workload"}
+    return out
 
 
 def main():
@@ -170,6 +247,8 @@ def main():
                     "db": "mfma_wide_kernel<MN-major X, MN-major Y, bf16 out, 2-leaf units>"}
 
     if args.profile_only:
+        if not args.no_moe:
+            moe_leg(dev, args.steps, args.warmup, False, context=False)
         if args.copy_calibration:
             # 256 MiB read + 256 MiB written per launch, far beyond the caches
             src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
@@ -201,6 +280,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(X, W, dC, args.cpu_seconds)
+    moe = None if args.no_moe else moe_leg(dev, args.steps, args.warmup, not args.no_cpu)
 
     line = {
         "metric": "det_gemm TFLOP/s and % of bf16 MFMA peak at M=4096,K=4096,N=6144 (1 GPU)",
@@ -227,6 +307,7 @@ def main():
                      "traffic": recorded_traffic(dom)},
         "cpu_baseline": cpu,
         "context": ctx,
+        "moe_grouped_gemm": moe,
     }
     print(json.dumps(line))
 

@@ -536,10 +536,14 @@ __global__ __launch_bounds__(256) void moe_slot_kernel(const uint16_t *y, int64_
 // a stack of pending left subtrees (in LDS, one column per thread): after slot
 // t, every inner node whose range ends at t is closed by adding its left
 // subtree (popped) to the running node.
-__global__ __launch_bounds__(256) void moe_combine_kernel(const float *slots, int64_t slot_ld,
-                                                          float *dprob, int T, int J) {
-    __shared__ float stack[kCombineDepth][256];
-    const int r = blockIdx.x * 256 + threadIdx.x;
+// The slots are loaded 32 at a time ahead of their tree steps.
+constexpr int kCombineThreads = 64, kCombineChunk = 32;
+
+__global__ __launch_bounds__(kCombineThreads) void moe_combine_kernel(const float *slots,
+                                                                      int64_t slot_ld,
+                                                                      float *dprob, int T, int J) {
+    __shared__ float stack[kCombineDepth][kCombineThreads];
+    const int r = blockIdx.x * kCombineThreads + threadIdx.x;
     if (r >= T)
         return;
     if (J == 0) {
@@ -547,17 +551,22 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float *slots, in
         return;
     }
     int sp = 0;
-    for (int t = 0; t < J; ++t) {
-        float v = slots[(int64_t)t * slot_ld + r];
-        for (int m = merges_after(t, J); m > 0; --m)
-            v = stack[--sp][threadIdx.x] + v;
-        stack[sp++][threadIdx.x] = v;
+    for (int t0 = 0; t0 < J; t0 += kCombineChunk) {
+        float v[kCombineChunk];
+#pragma unroll
+        for (int q = 0; q < kCombineChunk; ++q)
+            v[q] = t0 + q < J ? slots[(int64_t)(t0 + q) * slot_ld + r] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < kCombineChunk; ++q) {
+            if (t0 + q >= J)
+                break;
+            float x = v[q];
+            for (int m = merges_after(t0 + q, J); m > 0; --m)
+                x = stack[--sp][threadIdx.x] + x;
+            stack[sp++][threadIdx.x] = x;
+        }
     }
     dprob[r] = stack[0][threadIdx.x];
-}
-
-bool aligned4(const void *p, int64_t ld) {
-    return (reinterpret_cast<uintptr_t>(p) & 3) == 0 && (ld % 2) == 0;
 }
 
 int launch_slots(const uint16_t *Y, int64_t ldy, const uint16_t *G, int64_t ldg, float *slots,
@@ -610,7 +619,7 @@ int moe_entry(const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw, in
     const int dev = check_device();
     if (dev != DET_GEMM_OK)
         return dev;
-    const int64_t blocks = (T + 255) / 256;
+    const int64_t blocks = (T + kCombineThreads - 1) / kCombineThreads;
     if (N > 0) {
         // the grouped wide kernel when the shape allows it, else one product per expert
         Problem base{X, ldx, true, W, ldw, false, Y, ldy, OUT_BF16, T, N, K};
@@ -628,6 +637,12 @@ int moe_entry(const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw, in
             cfg = 5;
         } else if (wide_ok(base, tree, kTileCfgs[7], up)) {
             cfg = 7;
+        }
+        // the grouped kernel's LDS also holds the epilogue header
+        if (cfg >= 0 && kTileCfgs[cfg].lds_bytes(up) + kEpiLds > kLdsMax) {
+            if (g_force_config >= 0)
+                return DET_GEMM_EINVAL;
+            cfg = -1;
         }
         bool fused = false;
         if (cfg >= 0) {
@@ -664,12 +679,12 @@ int moe_entry(const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw, in
             p.xvec = aligned16(X, ldx);
             p.yvec = aligned16(W, ldw) && (w_stride % 8) == 0;
             p.cvec = aligned16(Y, ldy);
-            fused = aligned4(G, ldg);
+            fused = aligned16(G, ldg);
             if (fused) {
-                p.g = G;
-                p.ldg = ldg;
-                p.slots = slots;
-                p.slot_ld = slot_ld;
+                g.g = G;
+                g.ldg = ldg;
+                g.slots = slots;
+                g.slot_ld = slot_ld;
             }
             const hipError_t e = launch_moe_grouped(cfg, p, g, tiles, st);
             if (e == hipErrorInvalidConfiguration)
@@ -696,7 +711,7 @@ int moe_entry(const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw, in
                 return rc;
         }
     }
-    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, st, slots,
+    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)blocks), dim3(kCombineThreads), 0, st, slots,
                        slot_ld, dprob, (int)T, (int)J);
     return hipGetLastError() == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
 }

@@ -63,14 +63,6 @@ struct MfmaParams {
     int32_t xvec, yvec;  // 16-byte aligned rows/columns: vector loads allowed
     int32_t cvec;        // 16-byte aligned output rows: vector stores allowed
     int32_t levels;      // TREE_BLOCK: levels above the blocks; TREE_STACK: stack depth
-    // Per-token epilogue of the MoE grouped GEMM (wide kernel, bf16 out only):
-    // g(i, j) = g[i*ldg + j]; the tile at columns j0 .. j0+127 writes, for each
-    // of its rows i, the reduction of c(i, j) * g(i, j) over its columns to
-    // slots[(j0/128)*slot_ld + i].  slots == nullptr: no epilogue.
-    const uint16_t *g;
-    int64_t ldg;
-    float *slots;
-    int64_t slot_ld;
 };
 
 // 16-byte chunk swizzle of the [row][64] stage tiles: measured on gfx950 at the

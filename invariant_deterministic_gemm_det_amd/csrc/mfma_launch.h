@@ -126,7 +126,7 @@ hipError_t launch_wide(const MfmaParams &p, int64_t tiles, hipStream_t st) {
 }
 
 // Grouped wide kernel (forward layout, bf16 out): one launch over the tiles of
-// every row group of `g`.
+// every row group of `g`; its LDS starts with the epilogue header (kEpiLds).
 template <int FM, int FN, int WM, int WN, int NBUF, int TB, int GL, int RU, int OCC>
 hipError_t launch_wide_grouped(const MfmaParams &p, const GroupTable &g, int64_t tiles,
                                hipStream_t st) {
@@ -146,7 +146,7 @@ hipError_t launch_wide_grouped(const MfmaParams &p, const GroupTable &g, int64_t
             return e;
         max_dynamic = room;
     }
-    const int lds = E::lds_bytes(p.levels > RU ? p.levels - RU : 0);
+    const int lds = kEpiLds + E::lds_bytes(p.levels > RU ? p.levels - RU : 0);
     if (lds > max_dynamic)
         return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(kernel, dim3((unsigned)tiles), dim3(64 * WM * WN), lds, st, p, g);

@@ -111,6 +111,48 @@ struct WideValuAdd {
 // column holding +0; for 128 positions that is the perfect pairwise tree.
 constexpr int kSlot = 128;
 
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+template <class T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+    return reinterpret_cast<T *>(uniform64(reinterpret_cast<int64_t>(p)));
+}
+
+// Row groups of a grouped launch (see mfma_wide_grouped_kernel) and the
+// operands of the epilogue: g(i, j) = g[i*ldg + j] for the rows i of the
+// whole launch; the tile at columns j0 .. j0+127 writes, for each of its rows
+// i, the slot of c(i, j) * g(i, j) to slots[(j0/128)*slot_ld + i].
+// slots == nullptr: no epilogue.
+constexpr int kMaxGroups = 128;
+
+struct GroupTable {
+    int32_t groups;
+    int32_t tile_start[kMaxGroups + 1];
+    int32_t row_start[kMaxGroups];
+    int32_t rows[kMaxGroups];
+    int64_t y_stride;
+    const uint16_t *g;
+    int64_t ldg;
+    float *slots;
+    int64_t slot_ld;
+};
+
+// What the epilogue of a grouped tile needs, written by the workgroup at the
+// start of the dynamic LDS (its engine's buffers start kEpiLds bytes later):
+// read back at the end of the tile rather than held in registers through the
+// main loop.  r0: the first row of the tile's group.
+struct EpiInfo {
+    const uint16_t *g;
+    float *slots;
+    int64_t ldg, slot_ld;
+    int32_t r0;
+};
+constexpr int kEpiLds = 64;
+
 // The slot of one row whose 128 products are held two per lane (columns
 // 2*lane and 2*lane + 1): level 1 is the lane's own pair, level k joins lanes
 // 2^(k-2) apart.  IEEE addition is commutative, so the two lanes of a join hold
@@ -125,12 +167,69 @@ __device__ __forceinline__ float slot_tree(float p0, float p1) {
 
 __device__ __forceinline__ float bf16_value(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
+// The same tree with 8 consecutive columns per lane and 16 lanes per row
+// (lanes 16q .. 16q+15 hold one row): levels 1-3 inside the lane, levels 4-7
+// join lanes 1, 2, 4, 8 apart; every lane of the 16 ends with the slot.
+__device__ __forceinline__ float slot_tree8(const float (&pr)[8]) {
+    float v = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1)
+        v = v + __shfl_xor(v, m, 16);
+    return v;
+}
+
+// EPI: also the slots of the epilogue (operands in the EpiInfo at the start of
+// the dynamic LDS; this tile's rows start at its row r0).
 template <int OUT, int FM, int FN, int BM, int BN, int NW, bool EPI = false>
 __device__ __forceinline__ void store_staged(const MfmaParams &p, const Frag<FM, FN> &root, bool odd,
                                              int i0, int j0, int wm, int wn, int lane, char *lds) {
     constexpr bool T = OUT == OUT_BF16_T;
     constexpr int ROWS = T ? BN : BM, COLS = T ? BM : BN;  // of the staged block
     constexpr int RS = COLS * 2 + 16;                      // LDS row stride, bytes
+    // Per-token epilogue: a row's slot is reduced by 16 lanes holding 8
+    // columns each; a wave takes 4 rows per pass.  The G chunks are loaded
+    // first, so that their latency overlaps the staging.
+    constexpr bool kEpi = EPI && !T && COLS == kSlot;
+    constexpr int EP = kEpi ? ROWS / (NW * 4) : 1;  // passes
+    static_assert(!kEpi || EP * NW * 4 == ROWS, "the epilogue passes cover the tile rows");
+    extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
+    const EpiInfo *info = reinterpret_cast<const EpiInfo *>(dyn_lds);
+    const uint16_t *eg = nullptr;
+    float *eslots = nullptr;
+    int64_t eldg = 0, eslot_ld = 0;
+    int r0 = 0;
+    if constexpr (kEpi) {
+        eg = uniform_ptr(info->g);
+        eslots = uniform_ptr(info->slots);
+        eldg = uniform64(info->ldg);
+        eslot_ld = uniform64(info->slot_ld);
+        r0 = __builtin_amdgcn_readfirstlane(info->r0);
+    }
+    const bool epi = kEpi && eslots != nullptr;
+    const int c8 = (lane & 15) * 8;
+    const int erow = ((threadIdx.x >> 6) * 4 + (lane >> 4));  // + 4 * NW per pass
+    uint4 gq[EP];
+    if constexpr (kEpi) {
+        if (epi) {
+            const int rows_in = p.I - i0, cols_in = p.J - j0;
+#pragma unroll
+            for (int k = 0; k < EP; ++k) {
+                const int r = erow + k * 4 * NW;
+                gq[k] = make_uint4(0u, 0u, 0u, 0u);
+                if (r < rows_in) {
+                    const uint16_t *gr = eg + (int64_t)(r0 + i0 + r) * eldg + j0 + c8;
+                    if (c8 + 8 <= cols_in) {
+                        gq[k] = *reinterpret_cast<const uint4 *>(gr);
+                    } else {
+                        uint32_t w[4] = {0u, 0u, 0u, 0u};
+                        for (int e = 0; e < 8 && c8 + e < cols_in; ++e)
+                            w[e >> 1] |= (uint32_t)gr[e] << (16 * (e & 1));
+                        gq[k] = make_uint4(w[0], w[1], w[2], w[3]);
+                    }
+                }
+            }
+        }
+    }
     const int g = lane >> 4, c = lane & 15;
 #pragma unroll
     for (int a = 0; a < FM; ++a)
@@ -182,26 +281,27 @@ __device__ __forceinline__ void store_staged(const MfmaParams &p, const Frag<FM,
                     dst[e] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
         }
     }
-    // Slots of the per-token epilogue, from the staged rows (the values just
-    // stored): one wave per row, products of the row's 128 columns two per lane.
-    // G rows are 4-byte aligned here (checked by the host).
-    if constexpr (EPI && !T && COLS == kSlot) {
-        if (p.slots != nullptr) {
-            const int wave = threadIdx.x >> 6, c = 2 * lane;
-            float *slot = p.slots + (int64_t)(col0 / kSlot) * p.slot_ld + row0;
-            for (int r = wave; r < ROWS && r < rows_ok; r += NW) {
-                const uint32_t yy = *reinterpret_cast<const uint32_t *>(lds + r * RS + c * 2);
-                const uint16_t *gr = p.g + (int64_t)(row0 + r) * p.ldg + col0 + c;
-                float p0 = 0.0f, p1 = 0.0f;
-                if (c + 1 < cols_ok) {
-                    const uint32_t gg = *reinterpret_cast<const uint32_t *>(gr);
-                    p0 = bf16_value(yy & 0xFFFFu) * bf16_value(gg & 0xFFFFu);
-                    p1 = bf16_value(yy >> 16) * bf16_value(gg >> 16);
-                } else if (c < cols_ok) {
-                    p0 = bf16_value(yy & 0xFFFFu) * bf16_value(*gr);
-                }
-                const float v = slot_tree(p0, p1);
-                if (lane == 0)
+    // Slots from the staged rows (the values just stored).  Columns past the
+    // last one hold the product +0, as the slot definition requires (not y * 0,
+    // which is -0 for negative y).
+    if constexpr (kEpi) {
+        if (epi) {
+            float *slot = eslots + (int64_t)(col0 / kSlot) * eslot_ld + r0 + row0;
+#pragma unroll
+            for (int k = 0; k < EP; ++k) {
+                const int r = erow + k * 4 * NW;
+                const uint4 yq = *reinterpret_cast<const uint4 *>(lds + r * RS + c8 * 2);
+                const uint32_t yw[4] = {yq.x, yq.y, yq.z, yq.w};
+                const uint32_t gw[4] = {gq[k].x, gq[k].y, gq[k].z, gq[k].w};
+                float pr[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pr[e] = c8 + e < cols_ok
+                                ? bf16_value((yw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) *
+                                      bf16_value((gw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu)
+                                : 0.0f;
+                const float v = slot_tree8(pr);
+                if ((lane & 15) == 0 && r < rows_ok)
                     slot[r] = v;
             }
         }
@@ -765,16 +865,6 @@ struct WideTree {
     }
 };
 
-__device__ __forceinline__ int64_t uniform64(int64_t v) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
-template <class T>
-__device__ __forceinline__ T *uniform_ptr(T *p) {
-    return reinterpret_cast<T *>(uniform64(reinterpret_cast<int64_t>(p)));
-}
 
 // Recomputes a tile with element-wise adds (exact IEEE behaviour for non-finite
 // values; positions never move) and stores it.  Kept out of line so that its
@@ -800,17 +890,12 @@ __device__ __attribute__((noinline)) void wide_valu_tile(MfmaParams q, int tile_
     p.L = __builtin_amdgcn_readfirstlane(q.L);
     p.tiles_j = __builtin_amdgcn_readfirstlane(q.tiles_j);
     p.levels = __builtin_amdgcn_readfirstlane(q.levels);
-    if constexpr (EPI) {
-        p.g = uniform_ptr(q.g);
-        p.ldg = uniform64(q.ldg);
-        p.slots = uniform_ptr(q.slots);
-        p.slot_ld = uniform64(q.slot_ld);
-    }
     const int tile = __builtin_amdgcn_readfirstlane(tile_arg);
     const int i0 = (tile / p.tiles_j) * E::BM;
     const int j0 = (tile % p.tiles_j) * E::BN;
-    E e(p, smem, p.levels > RU ? p.levels - RU : 0, i0, j0);
-    WideTree<E, WideValuAdd, TB, GL, RU, EPI> valu(e, p, split_selector(threadIdx.x & 63), i0, j0, false);
+    E e(p, EPI ? smem + kEpiLds : smem, p.levels > RU ? p.levels - RU : 0, i0, j0);
+    WideTree<E, WideValuAdd, TB, GL, RU, EPI> valu(e, p, split_selector(threadIdx.x & 63), i0, j0,
+                                                   false);
     valu.run();
 }
 
@@ -827,9 +912,9 @@ __device__ __forceinline__ void wide_tile(const MfmaParams &p, int tile) {
     const int i0 = (tile / p.tiles_j) * E::BM;
     const int j0 = (tile % p.tiles_j) * E::BN;
 
-    E e(p, smem, p.levels > RU ? p.levels - RU : 0, i0, j0);
+    E e(p, EPI ? smem + kEpiLds : smem, p.levels > RU ? p.levels - RU : 0, i0, j0);
     WideTree<E, WideMatrixAdd, TB, GL, RU, EPI> tree(e, p, split_selector(lane), i0, j0,
-                                            (tree_height_rt(p.L) & 1) != 0);
+                                                 (tree_height_rt(p.L) & 1) != 0);
     // A non-finite root may have spilled NaN into the other sums of its
     // matrix-core add rows: such a tile is not stored but recomputed with
     // element-wise adds.
@@ -849,16 +934,6 @@ void mfma_wide_kernel(MfmaParams p) {
 // y + e * y_stride; one launch covers the tiles of every group, group e owning
 // tiles tile_start[e] .. tile_start[e+1]-1.  The same tile code runs on the
 // group's rows, so each row gets the bits of an ungrouped product.
-constexpr int kMaxGroups = 128;
-
-struct GroupTable {
-    int32_t groups;
-    int32_t tile_start[kMaxGroups + 1];
-    int32_t row_start[kMaxGroups];
-    int32_t rows[kMaxGroups];
-    int64_t y_stride;
-};
-
 template <int FM, int FN, int WM, int WN, int NBUF, int TB, int GL, int RU, int OCC>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void mfma_wide_grouped_kernel(MfmaParams p, GroupTable g) {
@@ -872,14 +947,19 @@ void mfma_wide_grouped_kernel(MfmaParams p, GroupTable g) {
             hi = mid;
     }
     MfmaParams q = p;
-    const int64_t r0 = g.row_start[lo];
-    q.x = p.x + r0 * p.ldx;
+    const int r0 = g.row_start[lo];
+    q.x = p.x + (int64_t)r0 * p.ldx;
     q.y = p.y + (int64_t)lo * g.y_stride;
-    q.c = static_cast<uint16_t *>(p.c) + r0 * p.ldc;
+    q.c = static_cast<uint16_t *>(p.c) + (int64_t)r0 * p.ldc;
     q.I = g.rows[lo];
-    if (p.slots != nullptr) {
-        q.g = p.g + r0 * p.ldg;
-        q.slots = p.slots + r0;
+    if (threadIdx.x == 0) {  // visible to all waves after the first stage barrier
+        extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
+        EpiInfo *info = reinterpret_cast<EpiInfo *>(dyn_lds);
+        info->g = g.g;
+        info->slots = g.slots;
+        info->ldg = g.ldg;
+        info->slot_ld = g.slot_ld;
+        info->r0 = r0;
     }
     wide_tile<true, false, OUT_BF16, FM, FN, WM, WN, NBUF, TB, GL, RU, true>(q, t - g.tile_start[lo]);
 }

@@ -146,7 +146,7 @@ def test_fused_epilogue_equals_slot_kernel(dev):
     assert torch.equal(Y3.view(torch.int16), Y.view(torch.int16))
     assert torch.equal(s3.view(torch.int32), slots.view(torch.int32))
     assert torch.equal(d3.view(torch.int32), dprob.view(torch.int32))
-    # G rows not 4-byte aligned: the grouped kernel leaves the slots to the slot kernel
+    # G rows not 16-byte aligned: the grouped kernel leaves the slots to the slot kernel
     Gpad = torch.zeros((G.shape[0], G.shape[1] + 1), dtype=G.dtype, device=dev)
     Gpad[:, 1:] = G
     Yu, du, su = dg.det_moe_fwd_dprob(X, W, off, Gpad[:, 1:])
