@@ -83,6 +83,15 @@ def _load():
         lib.oracle_moe_fwd_dprob.argtypes = [p, i64, p, i64, i64, p, i64, p, i64, p, i64, p, i64,
                                              p, i64, i64, i64]
         lib.oracle_moe_fwd_dprob.restype = ctypes.c_int
+        u64 = ctypes.c_uint64
+        lib.oracle_mix64.argtypes = [u64]
+        lib.oracle_mix64.restype = u64
+        lib.oracle_fingerprint.argtypes = [p, i64, p]
+        lib.oracle_fingerprint.restype = ctypes.c_int
+        lib.oracle_fingerprint_rows.argtypes = [p, i64, i64, i64, p]
+        lib.oracle_fingerprint_rows.restype = ctypes.c_int
+        lib.oracle_first_mismatch.argtypes = [p, p, i64]
+        lib.oracle_first_mismatch.restype = i64
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -279,6 +288,44 @@ def moe_fwd_dprob(X, W, offsets, G):
                                         _ptr(G), ldg, _ptr(Y), max(N, 1), _ptr(slots), max(T, 1),
                                         _ptr(dprob), T, N, K))
     return Y, slots, dprob
+
+
+def _bytes(a):
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint8).reshape(-1)
+
+
+def mix64(z):
+    """SplitMix64's 64-bit finalizer (the digest's mixer)."""
+    return int(_load().oracle_mix64(ctypes.c_uint64(int(z) & (2**64 - 1))))
+
+
+def fingerprint(a):
+    """64-bit digest of the bytes of array ``a`` (C order): mix(S + n) with
+    S = sum of mix(w_i + GAMMA*(i+1)) over its little-endian 64-bit words."""
+    b = _bytes(a)
+    out = np.zeros(1, np.uint64)
+    _check(_load().oracle_fingerprint(_ptr(b), b.size, _ptr(out)))
+    return int(out[0])
+
+
+def fingerprint_rows(a):
+    """One digest per row of a 2-D array (the bytes of each row)."""
+    a = np.ascontiguousarray(a)
+    if a.ndim != 2:
+        raise ValueError("2-D array expected")
+    rows, row_bytes = a.shape[0], a.shape[1] * a.itemsize
+    out = np.zeros(rows, np.uint64)
+    _check(_load().oracle_fingerprint_rows(_ptr(a), rows, row_bytes, max(row_bytes, 1), _ptr(out)))
+    return out
+
+
+def first_mismatch(a, b):
+    """Smallest byte index where the bytes of a and b differ, or -1."""
+    x, y = _bytes(a), _bytes(b)
+    if x.size != y.size:
+        raise ValueError("byte lengths differ")
+    return int(_load().oracle_first_mismatch(_ptr(x), _ptr(y), x.size))
 
 
 def num_threads():

@@ -368,3 +368,86 @@ int oracle_moe_fwd_dprob(const uint16_t *X, int64_t ldx, const uint16_t *W, int6
     }
     return oracle_moe_dprob(Y, ldy, G, ldg, T, N, slots, slot_ld, dprob);
 }
+
+/* ==== Tensor fingerprints and the first-mismatch comparator ====
+ *
+ * Reading notes "Bitwise-Deterministic Pretraining at Scale", section
+ * "5. Fingerprinting Tensors on the GPU": digests are computed in GPU memory
+ * from the bit patterns; a whole-tensor hash that ignores positions cannot see
+ * a permutation, so order-sensitive data is hashed per row or chunk; the final
+ * confirmation is a byte-level comparison.  Section "Reading the first
+ * mismatch": the origin is the first traced event whose input digests agree
+ * and whose output digests differ.
+ *
+ * The digest of a byte string of n bytes (a reading: the pages name no hash):
+ *   words      w_i, i < ceil(n/8): little-endian 64-bit words of the bytes,
+ *              bytes past n read as 0;
+ *   mix(z)     the 64-bit finalizer of SplitMix64 (Steele, Lea and Flood,
+ *              "Fast splittable pseudorandom number generators", 2014):
+ *              z ^= z >> 30; z *= 0xBF58476D1CE4E5B9; z ^= z >> 27;
+ *              z *= 0x94D049BB133111EB; z ^= z >> 31   (all mod 2^64);
+ *   S          sum over i of mix(w_i + GAMMA * (i + 1)) mod 2^64, with
+ *              GAMMA = 0x9E3779B97F4A7C15 (SplitMix64's increment);
+ *   digest     mix(S + n).
+ * The position enters every term, so moving a word changes the digest; the
+ * terms are combined by addition mod 2^64, which is associative, so a
+ * parallel evaluation may add them in any grouping and get the same bits.
+ * A row digest is the digest of the row's bytes alone (positions counted from
+ * the row start).  The first mismatch is the smallest byte index where two
+ * byte strings differ, or -1.
+ */
+#define ORACLE_GAMMA 0x9E3779B97F4A7C15ull
+
+static uint64_t mix64(uint64_t z) {
+    z ^= z >> 30;
+    z *= 0xBF58476D1CE4E5B9ull;
+    z ^= z >> 27;
+    z *= 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return z;
+}
+
+static uint64_t word_at(const uint8_t *p, int64_t n, int64_t i) {
+    uint64_t w = 0;
+    for (int b = 0; b < 8; ++b) {
+        int64_t k = 8 * i + b;
+        if (k < n)
+            w |= (uint64_t)p[k] << (8 * b);
+    }
+    return w;
+}
+
+static uint64_t digest_bytes(const uint8_t *p, int64_t n) {
+    uint64_t s = 0;
+    int64_t W = (n + 7) / 8;
+    for (int64_t i = 0; i < W; ++i)
+        s += mix64(word_at(p, n, i) + ORACLE_GAMMA * (uint64_t)(i + 1));
+    return mix64(s + (uint64_t)n);
+}
+
+uint64_t oracle_mix64(uint64_t z) { return mix64(z); }
+
+int oracle_fingerprint(const void *data, int64_t nbytes, uint64_t *digest) {
+    if (nbytes < 0 || (nbytes > 0 && !data))
+        return ORACLE_EINVAL;
+    *digest = digest_bytes((const uint8_t *)data, nbytes);
+    return ORACLE_OK;
+}
+
+int oracle_fingerprint_rows(const void *data, int64_t rows, int64_t row_bytes, int64_t ld_bytes,
+                            uint64_t *digests) {
+    if (rows < 0 || row_bytes < 0 || (rows > 1 && ld_bytes < row_bytes))
+        return ORACLE_EINVAL;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        digests[r] = digest_bytes((const uint8_t *)data + r * ld_bytes, row_bytes);
+    return ORACLE_OK;
+}
+
+int64_t oracle_first_mismatch(const void *a, const void *b, int64_t nbytes) {
+    const uint8_t *x = (const uint8_t *)a, *y = (const uint8_t *)b;
+    for (int64_t k = 0; k < nbytes; ++k)
+        if (x[k] != y[k])
+            return k;
+    return -1;
+}
