@@ -67,6 +67,7 @@ def parse():
                     help="target host time of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-moe", action="store_true", help="skip the MoE grouped GEMM leg")
+    ap.add_argument("--no-fingerprint", action="store_true", help="skip the fingerprint leg")
     ap.add_argument("--profile-only", action="store_true",
                     help="run only the GPU steps (for rocprofv3 runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -179,6 +180,71 @@ def moe_leg(dev, steps, warmup, with_cpu, context=True):
     return out
 
 
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+FP_BYTES = 1 << 30
+FP_ROWS, FP_ROW_BYTES = 16384, 32768
+
+
+def fingerprint_leg(dev, steps, warmup, with_cpu):
+    """Tensor fingerprints and the byte comparator (det_fingerprint.h) on
+    seeded random bytes resident in HBM: the digest of a 1 GiB buffer, per-row
+    digests of a [16384, 32 KiB] layout (512 MiB), and the first mismatch of two
+    equal 1 GiB buffers (the whole of both is read)."""
+    import torch
+    import invariant_deterministic_gemm_det_amd as dg
+
+    def draw():  # the same bytes each time (no copy kernel: the counter runs
+        g = torch.Generator(device=dev)  # calibrate on the only device copy)
+        g.manual_seed(7001)
+        return torch.randint(0, 256, (FP_BYTES,), generator=g, dtype=torch.uint8, device=dev)
+
+    a, b = draw(), draw()
+    rows = a[:FP_ROWS * FP_ROW_BYTES].view(FP_ROWS, FP_ROW_BYTES)
+    d = torch.empty(1, dtype=torch.int64, device=dev)
+    dr = torch.empty(FP_ROWS, dtype=torch.int64, device=dev)
+    mm = torch.empty(1, dtype=torch.int64, device=dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        t = [x.elapsed_time(y) for x, y in ts]
+        return sum(t) / len(t)
+
+    t_d = timed(lambda: dg.det_fingerprint(a, out=d))
+    t_r = timed(lambda: dg.det_fingerprint_rows(rows, out=dr))
+    t_m = timed(lambda: dg.det_first_mismatch(a, b, out=mm))
+    gbs = lambda nbytes, ms: round(nbytes / (ms * 1e-3) / 1e9, 1)
+    out = {"workload": "digest of 1 GiB, row digests of 16384 x 32 KiB, first mismatch of two "
+                       "equal 1 GiB buffers; seeded random bytes in HBM",
+           "digest": {"ms": round(t_d, 4), "GB/s": gbs(FP_BYTES, t_d)},
+           "rows": {"ms": round(t_r, 4), "GB/s": gbs(FP_ROWS * FP_ROW_BYTES, t_r)},
+           "first_mismatch": {"ms": round(t_m, 4), "GB/s": gbs(2 * FP_BYTES, t_m)},
+           "roofline": {"bound": "hbm", "kernel": "digest_sum_kernel (1 GiB digest)",
+                        "achieved": gbs(FP_BYTES, t_d), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs(FP_BYTES, t_d) / PEAK_HBM_GBS, 4),
+                        "traffic": recorded_traffic("fp")}}
+    if with_cpu:
+        import oracle
+        n = 64 << 20
+        host = a[:n].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.fingerprint(host)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(n / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "seconds": round(dt, 3),
+                               "sample": "CPU oracle digest of the first 64 MiB of the buffer"}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -249,6 +315,8 @@ def main():
     if args.profile_only:
         if not args.no_moe:
             moe_leg(dev, args.steps, args.warmup, False, context=False)
+        if not args.no_fingerprint:
+            fingerprint_leg(dev, args.steps, args.warmup, False)
         if args.copy_calibration:
             # 256 MiB read + 256 MiB written per launch, far beyond the caches
             src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
@@ -281,6 +349,8 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(X, W, dC, args.cpu_seconds)
     moe = None if args.no_moe else moe_leg(dev, args.steps, args.warmup, not args.no_cpu)
+    fp = None if args.no_fingerprint else fingerprint_leg(dev, args.steps, args.warmup,
+                                                          not args.no_cpu)
 
     line = {
         "metric": "det_gemm TFLOP/s and % of bf16 MFMA peak at M=4096,K=4096,N=6144 (1 GPU)",
@@ -308,6 +378,7 @@ def main():
         "cpu_baseline": cpu,
         "context": ctx,
         "moe_grouped_gemm": moe,
+        "fingerprint": fp,
     }
     print(json.dumps(line))
 

@@ -29,7 +29,7 @@ _SIX = ("det_gemm_fwd", "det_gemm_fwd_rhs_transposed", "det_gemm_fwd_fp32", "det
 EXPORTS = _SIX + tuple(n.replace("det_gemm_", "det_gemm_strict_") for n in _SIX) + (
     "det_gemm_debug_leaves", "det_gemm_debug_round", "det_gemm_debug_add",
     "det_gemm_debug_force_config", "det_gemm_status_string", "det_moe_fwd_dprob",
-    "det_moe_debug_slots")
+    "det_moe_debug_slots", "det_fingerprint", "det_fingerprint_rows", "det_first_mismatch")
 MOE_SLOT = 128
 MOE_MAX_EXPERTS = 128
 
@@ -77,6 +77,12 @@ def load_library(path=LIB_PATH):
     lib.det_moe_fwd_dprob.restype = ctypes.c_int
     lib.det_moe_debug_slots.argtypes = [p, i64, p, i64, p, i64, i64, i64, p]
     lib.det_moe_debug_slots.restype = ctypes.c_int
+    lib.det_fingerprint.argtypes = [p, i64, p, p]
+    lib.det_fingerprint.restype = ctypes.c_int
+    lib.det_fingerprint_rows.argtypes = [p, i64, i64, i64, p, p]
+    lib.det_fingerprint_rows.restype = ctypes.c_int
+    lib.det_first_mismatch.argtypes = [p, p, i64, p, p]
+    lib.det_first_mismatch.restype = ctypes.c_int
     lib.det_gemm_status_string.argtypes = [ctypes.c_int]
     lib.det_gemm_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -259,6 +265,66 @@ def det_moe_debug_slots(Y, G, slots=None):
                                                 _stream(Y))
     _check(rc, "det_moe_debug_slots")
     return slots
+
+
+# ---------------------------------------------------------------- fingerprints
+
+def _bytes_of(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (its bytes are hashed in order)")
+    return ctypes.c_void_p(t.data_ptr() if t.numel() else 0), t.numel() * t.element_size()
+
+
+def det_fingerprint(t, out=None):
+    """64-bit digest of the bytes of a contiguous GPU tensor (include/
+    det_fingerprint.h); returned in an int64 device tensor [1] holding its bits."""
+    p, n = _bytes_of(t, "t")
+    out = _out(out, (1,), t, torch.int64)
+    with torch.cuda.device(t.device):
+        rc = load_library().det_fingerprint(p, n, ctypes.c_void_p(out.data_ptr()), _stream(t))
+    _check(rc, "det_fingerprint")
+    return out
+
+
+def det_fingerprint_rows(t, out=None):
+    """One digest per row of a 2-D GPU tensor with unit column stride (row r =
+    the bytes of t[r]); int64 device tensor [rows] holding the digest bits."""
+    if not isinstance(t, torch.Tensor) or t.dim() != 2 or not t.is_cuda:
+        raise TypeError("t must be a 2-D GPU tensor")
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError("t needs unit stride along its last dimension")
+    es = t.element_size()
+    ld = t.stride(0) * es if rows > 1 else cols * es
+    out = _out(out, (rows,), t, torch.int64)
+    with torch.cuda.device(t.device):
+        rc = load_library().det_fingerprint_rows(
+            ctypes.c_void_p(t.data_ptr() if t.numel() else 0), rows, cols * es, ld,
+            ctypes.c_void_p(out.data_ptr() if rows else 0), _stream(t))
+    _check(rc, "det_fingerprint_rows")
+    return out
+
+
+def det_first_mismatch(a, b, out=None):
+    """Smallest byte index where the bytes of two contiguous GPU tensors differ,
+    or -1; int64 device tensor [1]."""
+    pa, na = _bytes_of(a, "a")
+    pb, nb = _bytes_of(b, "b")
+    if na != nb:
+        raise ValueError("a and b differ in byte length")
+    out = _out(out, (1,), a, torch.int64)
+    with torch.cuda.device(a.device):
+        rc = load_library().det_first_mismatch(pa, pb, na, ctypes.c_void_p(out.data_ptr()),
+                                               _stream(a))
+    _check(rc, "det_first_mismatch")
+    return out
+
+
+def digest_value(d):
+    """The unsigned 64-bit digest held in an int64 tensor element."""
+    return int(d.reshape(-1)[0].item()) & (2**64 - 1)
 
 
 # ---------------------------------------------------------------- inspection

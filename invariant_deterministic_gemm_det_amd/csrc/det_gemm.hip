@@ -23,6 +23,7 @@
 #include "det_moe.h"
 #include "mfma_launch.h"
 #include "strict_kernel.h"
+#include "device_check.h"
 
 using namespace detgemm;
 
@@ -74,9 +75,14 @@ bool overlaps(const Mat &a, const Mat &b) {
     return alo < bhi && blo < ahi;
 }
 
+int g_force_config = -1;  // tile configuration pinned for inspection, -1 = automatic
+
+}  // namespace
+
+namespace detgemm {
+
 // Once per device: the kernels are built for gfx950 only.
 std::atomic<int> g_device_ok[64];
-int g_force_config = -1;  // tile configuration pinned for inspection, -1 = automatic
 
 int check_device() {
     int dev = 0;
@@ -94,6 +100,10 @@ int check_device() {
     }
     return state == 1 ? DET_GEMM_OK : DET_GEMM_EHIP;
 }
+
+}  // namespace detgemm
+
+namespace {
 
 // ---- tree selection.  L = b * 2^a with b odd.  For b in {1, 3} the tree is a
 // perfect binary tree of depth a - k over identical blocks of b * 2^k leaves,

@@ -134,3 +134,23 @@ def test_moe_debug_slots_argument_errors(lib):
     assert lib.det_moe_debug_slots(FAKE, 128, FAKE, 128, s, 3, 4, 128, NULL) == dg.EINVAL
     assert lib.det_moe_debug_slots(FAKE, 128, FAKE, 128, s, 4, -1, 128, NULL) == dg.EINVAL
     assert lib.det_moe_debug_slots(FAKE, 128, FAKE, 128, s, 4, 0, 128, NULL) == dg.OK
+
+
+# ---------------------------------------------------------------- det_fingerprint.h
+
+def test_fingerprint_argument_errors_without_device(lib):
+    """Reading notes on bitwise-deterministic pretraining, section "5.
+    Fingerprinting Tensors on the GPU"; errors are reported before any device
+    work."""
+    out = ctypes.c_void_p(0x900000000)
+    assert lib.det_fingerprint(FAKE, -1, out, NULL) == dg.EINVAL
+    assert lib.det_fingerprint(NULL, 16, out, NULL) == dg.EINVAL
+    assert lib.det_fingerprint(FAKE, 16, NULL, NULL) == dg.EINVAL
+    assert lib.det_fingerprint(FAKE, 64, ctypes.c_void_p(0x10008), NULL) == dg.EINVAL  # overlap
+    assert lib.det_fingerprint_rows(FAKE, 4, 32, 16, out, NULL) == dg.EINVAL          # ld < row
+    assert lib.det_fingerprint_rows(FAKE, -1, 32, 32, out, NULL) == dg.EINVAL
+    assert lib.det_fingerprint_rows(FAKE, 0, 32, 32, out, NULL) == dg.OK               # no rows
+    assert lib.det_fingerprint_rows(FAKE, 4, 32, 32, ctypes.c_void_p(0x10040), NULL) == dg.EINVAL
+    assert lib.det_first_mismatch(FAKE, FAKE, -1, out, NULL) == dg.EINVAL
+    assert lib.det_first_mismatch(FAKE, NULL, 8, out, NULL) == dg.EINVAL
+    assert lib.det_first_mismatch(FAKE, FAKE, 8, NULL, NULL) == dg.EINVAL
