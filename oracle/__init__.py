@@ -92,6 +92,8 @@ def _load():
         lib.oracle_fingerprint_rows.restype = ctypes.c_int
         lib.oracle_first_mismatch.argtypes = [p, p, i64]
         lib.oracle_first_mismatch.restype = i64
+        lib.oracle_rmsnorm.argtypes = [p, i64, p, ctypes.c_float, p, i64, p, p, i64, i64]
+        lib.oracle_rmsnorm.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -326,6 +328,25 @@ def first_mismatch(a, b):
     if x.size != y.size:
         raise ValueError("byte lengths differ")
     return int(_load().oracle_first_mismatch(_ptr(x), _ptr(y), x.size))
+
+
+def rmsnorm(x, w, eps):
+    """Batch-invariant RMSNorm of the rows of x [R,H] (bf16 bits) with weight w
+    [H]: returns (y [R,H] bf16 bits, rstd [R] float32, sum of squares [R]
+    float32).  Lane t of 256 sums the squares of its 8-element chunks (chunk c
+    belongs to lane c mod 256) in ascending order; the lanes are joined by the
+    pairwise tree; rstd = 1/sqrt(ss/H + eps); y = bf16((x*rstd)*w)."""
+    x, ldx = _mat(x, "x")
+    w = np.ascontiguousarray(np.asarray(w, dtype=np.uint16)).reshape(-1)
+    R, H = x.shape
+    if w.size != H:
+        raise ValueError("w must have H entries")
+    y = np.zeros((R, H), np.uint16)
+    rstd = np.zeros(R, np.float32)
+    ss = np.zeros(R, np.float32)
+    _check(_load().oracle_rmsnorm(_ptr(x), ldx, _ptr(w), ctypes.c_float(eps), _ptr(y), max(H, 1),
+                                  _ptr(rstd), _ptr(ss), R, H))
+    return y, rstd, ss
 
 
 def num_threads():
