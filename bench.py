@@ -24,7 +24,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 M, K, N = 4096, 4096, 6144
 COPY_BYTES = 256 << 20
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "det_gemm_traffic_M4096_K4096_N6144.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles",
+                            "hbm_traffic_det_gemm_M4096_K4096_N6144_moe_fingerprint_rmsnorm.md")
 CSRC = os.path.join(ROOT, "invariant_deterministic_gemm_det_amd", "csrc")
 
 
@@ -68,6 +69,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-moe", action="store_true", help="skip the MoE grouped GEMM leg")
     ap.add_argument("--no-fingerprint", action="store_true", help="skip the fingerprint leg")
+    ap.add_argument("--no-rmsnorm", action="store_true", help="skip the RMSNorm leg")
     ap.add_argument("--profile-only", action="store_true",
                     help="run only the GPU steps (for rocprofv3 runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -245,6 +247,60 @@ def fingerprint_leg(dev, steps, warmup, with_cpu):
     return out
 
 
+NORM_R, NORM_H = 8192, 4096
+
+
+def rmsnorm_leg(dev, steps, warmup, with_cpu, decode=True):
+    """Batch-invariant RMSNorm (det_norm.h) over 8192 token rows of width 4096
+    (the MLP input of the workloads), and a 64-row decode batch."""
+    import torch
+    import det_workloads as Wk
+    import invariant_deterministic_gemm_det_amd as dg
+
+    x = Wk.randn_bf16((NORM_R, NORM_H), 1.0, 9500, dev)
+    w = Wk.randn_bf16((NORM_H,), 1.0, 9501, dev)
+    y = torch.empty_like(x)
+    r = torch.empty(NORM_R, dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        t = [a.elapsed_time(b) for a, b in ts]
+        return sum(t) / len(t)
+
+    t_full = timed(lambda: dg.det_rmsnorm(x, w, out=y, rstd=r))
+    t_dec = timed(lambda: dg.det_rmsnorm(x[:64], w, out=y[:64], rstd=r[:64])) if decode else 0.0
+    nbytes = NORM_R * NORM_H * 4 + NORM_H * 2 + NORM_R * 4
+    gbs = nbytes / (t_full * 1e-3) / 1e9
+    out = {"workload": "RMSNorm of 8192 x 4096 bf16 rows (read x, write y and rstd); "
+                       "decode: 64 rows",
+           "ms": round(t_full, 4), "GB/s": round(gbs, 1), "decode_64_rows_us": round(t_dec * 1e3, 2),
+           "roofline": {"bound": "hbm", "kernel": "rmsnorm_kernel (8192 x 4096)",
+                        "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": recorded_traffic("norm")}}
+    if with_cpu:
+        import oracle
+        rows = 1024
+        xb, wb = Wk.bits(x[:rows]), Wk.bits(w)
+        t0 = time.perf_counter()
+        oracle.rmsnorm(xb, wb, 1e-6)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(rows * NORM_H * 4 / dt / 1e9, 3), "unit": "GB/s",
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "seconds": round(dt, 3),
+                               "sample": f"CPU oracle on the first {rows} rows"}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -317,6 +373,8 @@ def main():
             moe_leg(dev, args.steps, args.warmup, False, context=False)
         if not args.no_fingerprint:
             fingerprint_leg(dev, args.steps, args.warmup, False)
+        if not args.no_rmsnorm:
+            rmsnorm_leg(dev, args.steps, args.warmup, False, decode=False)
         if args.copy_calibration:
             # 256 MiB read + 256 MiB written per launch, far beyond the caches
             src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
@@ -351,6 +409,7 @@ def main():
     moe = None if args.no_moe else moe_leg(dev, args.steps, args.warmup, not args.no_cpu)
     fp = None if args.no_fingerprint else fingerprint_leg(dev, args.steps, args.warmup,
                                                           not args.no_cpu)
+    norm = None if args.no_rmsnorm else rmsnorm_leg(dev, args.steps, args.warmup, not args.no_cpu)
 
     line = {
         "metric": "det_gemm TFLOP/s and % of bf16 MFMA peak at M=4096,K=4096,N=6144 (1 GPU)",
@@ -379,6 +438,7 @@ def main():
         "context": ctx,
         "moe_grouped_gemm": moe,
         "fingerprint": fp,
+        "rmsnorm": norm,
     }
     print(json.dumps(line))
 

@@ -29,7 +29,8 @@ _SIX = ("det_gemm_fwd", "det_gemm_fwd_rhs_transposed", "det_gemm_fwd_fp32", "det
 EXPORTS = _SIX + tuple(n.replace("det_gemm_", "det_gemm_strict_") for n in _SIX) + (
     "det_gemm_debug_leaves", "det_gemm_debug_round", "det_gemm_debug_add",
     "det_gemm_debug_force_config", "det_gemm_status_string", "det_moe_fwd_dprob",
-    "det_moe_debug_slots", "det_fingerprint", "det_fingerprint_rows", "det_first_mismatch")
+    "det_moe_debug_slots", "det_fingerprint", "det_fingerprint_rows", "det_first_mismatch",
+    "det_rmsnorm")
 MOE_SLOT = 128
 MOE_MAX_EXPERTS = 128
 
@@ -83,6 +84,8 @@ def load_library(path=LIB_PATH):
     lib.det_fingerprint_rows.restype = ctypes.c_int
     lib.det_first_mismatch.argtypes = [p, p, i64, p, p]
     lib.det_first_mismatch.restype = ctypes.c_int
+    lib.det_rmsnorm.argtypes = [p, i64, p, ctypes.c_float, p, i64, p, i64, i64, p]
+    lib.det_rmsnorm.restype = ctypes.c_int
     lib.det_gemm_status_string.argtypes = [ctypes.c_int]
     lib.det_gemm_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -265,6 +268,26 @@ def det_moe_debug_slots(Y, G, slots=None):
                                                 _stream(Y))
     _check(rc, "det_moe_debug_slots")
     return slots
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def det_rmsnorm(x, w, eps=1e-6, out=None, rstd=None):
+    """Batch-invariant RMSNorm (include/det_norm.h): x [R,H] bf16, w [H] bf16.
+    Returns (y [R,H] bf16, rstd [R] float32)."""
+    R, H = x.shape
+    if w.dim() != 1 or w.shape[0] != H or w.dtype != torch.bfloat16 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous bf16 vector of H entries")
+    out = _out(out, (R, H), x, torch.bfloat16)
+    rstd = _out(rstd, (R,), x, torch.float32)
+    xp, ldx = _mat(x, "x")
+    yp, ldy = _mat(out, "y")
+    with torch.cuda.device(x.device):
+        rc = load_library().det_rmsnorm(xp, ldx, ctypes.c_void_p(w.data_ptr()), ctypes.c_float(eps),
+                                        yp, ldy, ctypes.c_void_p(rstd.data_ptr() if R else 0), R,
+                                        H, _stream(x))
+    _check(rc, "det_rmsnorm")
+    return out, rstd
 
 
 # ---------------------------------------------------------------- fingerprints

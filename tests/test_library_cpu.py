@@ -154,3 +154,20 @@ def test_fingerprint_argument_errors_without_device(lib):
     assert lib.det_first_mismatch(FAKE, FAKE, -1, out, NULL) == dg.EINVAL
     assert lib.det_first_mismatch(FAKE, NULL, 8, out, NULL) == dg.EINVAL
     assert lib.det_first_mismatch(FAKE, FAKE, 8, NULL, NULL) == dg.EINVAL
+
+
+# ---------------------------------------------------------------- det_norm.h
+
+def test_rmsnorm_argument_errors_without_device(lib):
+    """Summary of "Defeating Nondeterminism in LLM Inference", batch-invariant
+    RMSNorm; errors before any device work."""
+    y, r = ctypes.c_void_p(0x900000000), ctypes.c_void_p(0xA00000000)
+    eps = ctypes.c_float(1e-6)
+    assert lib.det_rmsnorm(FAKE, 64, FAKE, eps, y, 64, r, -1, 64, NULL) == dg.EINVAL
+    assert lib.det_rmsnorm(FAKE, 64, FAKE, eps, y, 64, r, 4, 0, NULL) == dg.EINVAL
+    assert lib.det_rmsnorm(FAKE, 64, FAKE, eps, y, 64, r, 4, (1 << 20) + 1, NULL) == dg.EINVAL
+    assert lib.det_rmsnorm(FAKE, 32, FAKE, eps, y, 64, r, 4, 64, NULL) == dg.EINVAL   # ldx < H
+    assert lib.det_rmsnorm(NULL, 64, FAKE, eps, y, 64, r, 4, 64, NULL) == dg.EINVAL
+    assert lib.det_rmsnorm(FAKE, 64, FAKE, eps, FAKE, 64, r, 4, 64, NULL) == dg.EINVAL  # y over x
+    assert lib.det_rmsnorm(FAKE, 64, FAKE, eps, y, 64, y, 4, 64, NULL) == dg.EINVAL    # rstd over y
+    assert lib.det_rmsnorm(FAKE, 64, FAKE, eps, y, 64, r, 0, 64, NULL) == dg.OK        # no rows
