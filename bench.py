@@ -25,7 +25,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 M, K, N = 4096, 4096, 6144
 COPY_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles",
-                            "hbm_traffic_det_gemm_M4096_K4096_N6144_moe_fingerprint_rmsnorm.md")
+                            "hbm_traffic_per_launch_det_gemm_moe_fingerprint_rmsnorm_attention.md")
 CSRC = os.path.join(ROOT, "invariant_deterministic_gemm_det_amd", "csrc")
 
 
@@ -70,6 +70,7 @@ def parse():
     ap.add_argument("--no-moe", action="store_true", help="skip the MoE grouped GEMM leg")
     ap.add_argument("--no-fingerprint", action="store_true", help="skip the fingerprint leg")
     ap.add_argument("--no-rmsnorm", action="store_true", help="skip the RMSNorm leg")
+    ap.add_argument("--no-attention", action="store_true", help="skip the decode attention leg")
     ap.add_argument("--profile-only", action="store_true",
                     help="run only the GPU steps (for rocprofv3 runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -301,6 +302,62 @@ def rmsnorm_leg(dev, steps, warmup, with_cpu, decode=True):
     return out
 
 
+ATT_B, ATT_HQ, ATT_HKV, ATT_S, ATT_D = 64, 32, 8, 4096, 128
+
+
+def attention_leg(dev, steps, warmup, with_cpu):
+    """Decode attention with fixed 256-position splits (det_attention.h): 64
+    sequences with seeded lengths in [1024, 4096], 32 query heads on 8
+    key/value heads, head dimension 128 (the shape of an 8B-class GQA model)."""
+    import numpy as np
+    import torch
+    import det_workloads as Wk
+    import invariant_deterministic_gemm_det_amd as dg
+
+    lens = (1024 + Wk.randperm(3073, 2100)[:ATT_B]).tolist()
+    q = Wk.randn_bf16((ATT_B, ATT_HQ, ATT_D), 1.0, 2200, dev)
+    k = Wk.randn_bf16((ATT_B, ATT_HKV, ATT_S, ATT_D), 1.0, 2201, dev)
+    v = Wk.randn_bf16((ATT_B, ATT_HKV, ATT_S, ATT_D), 1.0, 2202, dev)
+    L = torch.tensor(lens, dtype=torch.int32, device=dev)
+    o = torch.empty((ATT_B, ATT_HQ, ATT_D), dtype=torch.bfloat16, device=dev)
+    ns = (ATT_S + 255) // 256
+    work = torch.empty(ATT_B * ATT_HQ * ns * (ATT_D + 2), dtype=torch.float32, device=dev)
+    scale = 1.0 / np.sqrt(ATT_D)
+    fn = lambda: dg.det_attention_decode(q, k, v, L, scale, out=o, work=work)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    t = sum(a.elapsed_time(b) for a, b in ts) / len(ts)
+    kv_bytes = sum(lens) * ATT_HKV * ATT_D * 2 * 2
+    gbs = kv_bytes / (t * 1e-3) / 1e9
+    out = {"workload": "decode attention: 64 sequences, lengths 1024..4096 (seeded), 32 query "
+                       "heads on 8 key/value heads, head dim 128, fixed 256-position splits",
+           "ms": round(t, 4), "kv_bytes": kv_bytes, "GB/s": round(gbs, 1),
+           "roofline": {"bound": "hbm", "kernel": "attn_split_kernel + attn_combine_kernel",
+                        "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": recorded_traffic("attn")}}
+    if with_cpu:
+        from oracle.attention import attention_decode
+        sel = [0, 1]
+        t0 = time.perf_counter()
+        attention_decode(Wk.bits(q[sel]), Wk.bits(k[sel]), Wk.bits(v[sel]),
+                         np.array([lens[i] for i in sel]), scale)
+        dt = time.perf_counter() - t0
+        nb = sum(lens[i] for i in sel) * ATT_HKV * ATT_D * 4
+        out["cpu_baseline"] = {"value": round(nb / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "seconds": round(dt, 3),
+                               "sample": "float64 oracle on 2 of the 64 sequences"}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -375,6 +432,8 @@ def main():
             fingerprint_leg(dev, args.steps, args.warmup, False)
         if not args.no_rmsnorm:
             rmsnorm_leg(dev, args.steps, args.warmup, False, decode=False)
+        if not args.no_attention:
+            attention_leg(dev, args.steps, args.warmup, False)
         if args.copy_calibration:
             # 256 MiB read + 256 MiB written per launch, far beyond the caches
             src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
@@ -410,6 +469,8 @@ def main():
     fp = None if args.no_fingerprint else fingerprint_leg(dev, args.steps, args.warmup,
                                                           not args.no_cpu)
     norm = None if args.no_rmsnorm else rmsnorm_leg(dev, args.steps, args.warmup, not args.no_cpu)
+    attn = None if args.no_attention else attention_leg(dev, args.steps, args.warmup,
+                                                        not args.no_cpu)
 
     line = {
         "metric": "det_gemm TFLOP/s and % of bf16 MFMA peak at M=4096,K=4096,N=6144 (1 GPU)",
@@ -439,6 +500,7 @@ def main():
         "moe_grouped_gemm": moe,
         "fingerprint": fp,
         "rmsnorm": norm,
+        "attention_decode": attn,
     }
     print(json.dumps(line))
 

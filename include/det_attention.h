@@ -1,0 +1,65 @@
+/*
+ * det_attention -- batch-invariant decode attention with a fixed split-KV
+ * size, for gfx950 (MI355X).
+ *
+ * Source: the summary page of "Defeating Nondeterminism in LLM Inference",
+ * section on batch-invariant kernel design, attention: a split-KV
+ * (FlashDecoding) reduction keeps batch invariance only with a fixed split
+ * size, so that the order of the reduction never depends on the batch or on
+ * how a sequence is cut; the cached keys and values keep one layout.
+ *
+ * What is computed, for sequence b with len[b] cached positions and query
+ * head h (key/value head h / G, G = Hq / Hkv):
+ *   o[b, h] = softmax(scale * K[b, h/G, :len] q[b, h]) V[b, h/G, :len]
+ * as follows (fp32 throughout, bf16 output):
+ *   splits     the positions are cut into splits of DET_ATTN_SPLIT = 256
+ *              from position 0, whatever the batch, the lengths of the other
+ *              sequences or Smax;
+ *   per split  scores s_j = (sum over d of q_d k_jd) * scale * log2(e), the
+ *              dot product in four 32-wide parts, each a chain of 16 bf16-pair
+ *              dot instructions in ascending d, the parts joined as
+ *              (0 + 1) + (2 + 3); m = max s_j;
+ *              p_j = 2^(s_j - m); l = pairwise sum of p_j over the split's
+ *              256 slots (empty slots 0); acc_d = sum of p_j v_jd in
+ *              ascending j;
+ *   combine    M = max of the splits' m; L and o_d are the sums over splits
+ *              in ascending order of l and acc_d times 2^(m - M);
+ *              o_d = bf16(o_d / L).  len 0 gives o = 0.
+ * The bits of o[b, h] therefore depend only on q[b, h], the first len[b]
+ * keys and values of its head and len[b].
+ *
+ * Layouts (row-major, DEVICE pointers): Q [B, Hq, D], K and V [B, Hkv, Smax,
+ * D], lens [B] int32 (values outside [0, Smax] are clamped into it), O [B,
+ * Hq, D] bf16, work: a caller-owned fp32 buffer of
+ * B * Hq * ceil(Smax / 256) * (D + 2) floats (the per-split partial results;
+ * the library allocates nothing).  D must be 128; G = Hq / Hkv must divide
+ * evenly and be at most 8.  Asynchronous on `stream`.  Returns DET_GEMM_OK,
+ * DET_GEMM_EINVAL (negative or unsupported sizes, null pointer, overlapping
+ * output) or DET_GEMM_EHIP; nothing is launched on error.  B == 0 is a no-op.
+ */
+#ifndef DET_ATTENTION_H
+#define DET_ATTENTION_H
+
+#include <stdint.h>
+
+#include "det_gemm.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DET_ATTN_SPLIT 256
+#define DET_ATTN_HEAD_DIM 128
+#define DET_ATTN_MAX_GROUP 8
+
+/* Decode attention with fixed 256-position splits (section on batch-invariant
+ * kernel design, attention). */
+int det_attention_decode(const det_bf16 *Q, const det_bf16 *K, const det_bf16 *V,
+                         const int32_t *lens, int64_t B, int64_t Hq, int64_t Hkv, int64_t Smax,
+                         int64_t D, float scale, float *work, det_bf16 *O, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DET_ATTENTION_H */

@@ -30,7 +30,8 @@ EXPORTS = _SIX + tuple(n.replace("det_gemm_", "det_gemm_strict_") for n in _SIX)
     "det_gemm_debug_leaves", "det_gemm_debug_round", "det_gemm_debug_add",
     "det_gemm_debug_force_config", "det_gemm_status_string", "det_moe_fwd_dprob",
     "det_moe_debug_slots", "det_fingerprint", "det_fingerprint_rows", "det_first_mismatch",
-    "det_rmsnorm")
+    "det_rmsnorm", "det_attention_decode")
+ATTN_SPLIT = 256
 MOE_SLOT = 128
 MOE_MAX_EXPERTS = 128
 
@@ -86,6 +87,9 @@ def load_library(path=LIB_PATH):
     lib.det_first_mismatch.restype = ctypes.c_int
     lib.det_rmsnorm.argtypes = [p, i64, p, ctypes.c_float, p, i64, p, i64, i64, p]
     lib.det_rmsnorm.restype = ctypes.c_int
+    lib.det_attention_decode.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, ctypes.c_float, p,
+                                         p, p]
+    lib.det_attention_decode.restype = ctypes.c_int
     lib.det_gemm_status_string.argtypes = [ctypes.c_int]
     lib.det_gemm_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -288,6 +292,34 @@ def det_rmsnorm(x, w, eps=1e-6, out=None, rstd=None):
                                         H, _stream(x))
     _check(rc, "det_rmsnorm")
     return out, rstd
+
+
+# ---------------------------------------------------------------- decode attention
+
+def det_attention_decode(q, k, v, lens, scale, out=None, work=None):
+    """Decode attention with fixed 256-position splits (include/det_attention.h):
+    q [B,Hq,128], k and v [B,Hkv,Smax,128] bf16 (contiguous), lens [B] int32 on
+    the device.  Returns o [B,Hq,128] bf16."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous bf16 GPU tensor")
+    B, Hq, D = q.shape
+    _, Hkv, Smax, D2 = k.shape
+    if tuple(v.shape) != tuple(k.shape) or D2 != D or k.shape[0] != B:
+        raise ValueError("q, k, v disagree in shape")
+    if lens.dtype != torch.int32 or not lens.is_cuda or tuple(lens.shape) != (B,):
+        raise TypeError("lens must be an int32 GPU tensor [B]")
+    NS = (Smax + ATTN_SPLIT - 1) // ATTN_SPLIT
+    out = _out(out, (B, Hq, D), q, torch.bfloat16)
+    if work is None:
+        work = torch.empty((max(B * Hq * NS * (D + 2), 1),), dtype=torch.float32, device=q.device)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t.numel() else 0)
+    with torch.cuda.device(q.device):
+        rc = load_library().det_attention_decode(ptr(q), ptr(k), ptr(v), ptr(lens), B, Hq, Hkv,
+                                                 Smax, D, ctypes.c_float(scale), ptr(work),
+                                                 ptr(out), _stream(q))
+    _check(rc, "det_attention_decode")
+    return out
 
 
 # ---------------------------------------------------------------- fingerprints

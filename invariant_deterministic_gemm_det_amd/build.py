@@ -25,7 +25,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdet_gemm.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["det_gemm.hip", "mfma_fwd_bf16.hip", "mfma_fwd_f32.hip", "mfma_kk_bf16.hip", "mfma_moe.hip", "fingerprint.hip", "rmsnorm.hip",
+SOURCES = ["det_gemm.hip", "mfma_fwd_bf16.hip", "mfma_fwd_f32.hip", "mfma_kk_bf16.hip", "mfma_moe.hip", "fingerprint.hip", "rmsnorm.hip", "attention.hip",
            "mfma_nn_bf16.hip", "mfma_nn_bf16t.hip", "mfma_leaves.hip"]
 HEADERS = ["bf16_device.h", "device_check.h", "strict_kernel.h", "mfma_kernel.h", "mfma_fast.h", "mfma_wide.h",
            "mfma_launch.h"]
@@ -40,7 +40,8 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 
 def _inputs():
     return [os.path.join(CSRC, f) for f in SOURCES + HEADERS] + \
-        [os.path.join(ROOT, "include", h) for h in ("det_gemm.h", "det_moe.h", "det_fingerprint.h", "det_norm.h")]
+        [os.path.join(ROOT, "include", h) for h in ("det_gemm.h", "det_moe.h", "det_fingerprint.h", "det_norm.h",
+                                                       "det_attention.h")]
 
 
 def _compile(src, extra):

@@ -1,0 +1,291 @@
+// Decode attention with a fixed split-KV size (declared in
+// include/det_attention.h).
+//
+// Summary page of "Defeating Nondeterminism in LLM Inference", section on
+// batch-invariant kernel design, attention: split-KV stays batch-invariant
+// when the split size is fixed.
+//
+// Two kernels.  attn_split_kernel: one workgroup (256 threads) per (split,
+// key/value head, sequence) computes the split's scores for the G query heads
+// of the key/value head, its max, its sum of weights and its weighted value
+// sum, and writes them to the caller's work buffer.  attn_combine_kernel: one
+// workgroup per (query head, sequence) merges the sequence's splits in
+// ascending order.  Keys and values pass through LDS in 64-row tiles (rows
+// padded to 272 bytes so that the 16-byte reads of different rows fall in
+// different banks).  Every reduction has a fixed shape, so a sequence's bits
+// depend only on its own data and length.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "bf16_device.h"
+#include "det_attention.h"
+#include "device_check.h"
+
+using namespace detgemm;
+
+namespace {
+
+constexpr int kSplit = DET_ATTN_SPLIT;
+constexpr int kD = DET_ATTN_HEAD_DIM;
+constexpr int kGMax = DET_ATTN_MAX_GROUP;
+constexpr int kThreads = 256;
+constexpr int kTile = 64;            // positions per LDS tile
+constexpr int kRowBytes = kD * 2 + 16;  // padded LDS row of one key or value
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bfv(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+
+// Positions [p0, p0 + 64) of one head's key or value rows into the LDS tile;
+// rows at or past n are zero.  16-byte chunks, 16 per row, 4 per thread.
+__device__ __forceinline__ void load_tile(char *tile, const uint16_t *rows, int p0, int n) {
+#pragma unroll
+    for (int i = 0; i < kTile * 16 / kThreads; ++i) {
+        const int c = threadIdx.x + i * kThreads;
+        const int r = c >> 4, col = c & 15;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (p0 + r < n)
+            v = *reinterpret_cast<const uint4 *>(rows + (int64_t)(p0 + r) * kD + col * 8);
+        *reinterpret_cast<uint4 *>(tile + r * kRowBytes + col * 16) = v;
+    }
+}
+
+__device__ __forceinline__ bf16x2 as_pair(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+// GM: a power of two >= G (the register arrays are sized by it).
+template <int GM>
+__global__ __launch_bounds__(kThreads) void attn_split_kernel(
+    const uint16_t *Q, const uint16_t *K, const uint16_t *V, const int32_t *lens, int Hq, int Hkv,
+    int Smax, int G, int NS, float scale_log2, float *work) {
+    __shared__ __attribute__((aligned(16))) float sc[GM][kSplit];
+    __shared__ __attribute__((aligned(16))) char tile[kTile * kRowBytes];
+    __shared__ float red[GM][kThreads / 64];
+
+    const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    int len = lens[b];
+    len = len < 0 ? 0 : (len > Smax ? Smax : len);
+    const int j0 = s * kSplit;
+    if (j0 >= len)
+        return;  // the whole workgroup: no barrier is reached
+    const int n = len - j0 < kSplit ? len - j0 : kSplit;
+    const int64_t head = ((int64_t)b * Hkv + kvh) * Smax;
+    const uint16_t *Kh = K + (head + j0) * kD, *Vh = V + (head + j0) * kD;
+
+    // ---- scores: thread t takes position r = t / 4 of a tile and the 32-wide
+    // part pp = t % 4 of the dot products (its q part in registers as bf16
+    // pairs, v_dot2 over the 16 pairs in ascending order); the four parts
+    // meet as (0 + 1) + (2 + 3)
+    const int r = t >> 2, pp = t & 3;
+    uint32_t qp[GM][16];
+#pragma unroll
+    for (int g = 0; g < GM; ++g)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (g < G)
+                v = *reinterpret_cast<const uint4 *>(
+                    Q + ((int64_t)b * Hq + kvh * G + g) * kD + pp * 32 + c * 8);
+            qp[g][4 * c] = v.x;
+            qp[g][4 * c + 1] = v.y;
+            qp[g][4 * c + 2] = v.z;
+            qp[g][4 * c + 3] = v.w;
+        }
+    for (int sub = 0; sub < kSplit / kTile; ++sub) {
+        if (sub * kTile >= n)
+            break;  // uniform: n is the workgroup's
+        __syncthreads();  // the previous tile consumed
+        load_tile(tile, Kh, sub * kTile, n);
+        __syncthreads();
+        uint32_t kw[16];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(tile + r * kRowBytes + pp * 64 + c * 16);
+            kw[4 * c] = v.x;
+            kw[4 * c + 1] = v.y;
+            kw[4 * c + 2] = v.z;
+            kw[4 * c + 3] = v.w;
+        }
+        const int j = sub * kTile + r;
+#pragma unroll
+        for (int g = 0; g < GM; ++g) {
+            if (g < G) {
+                float part = 0.0f;
+#pragma unroll
+                for (int c = 0; c < 16; ++c)
+                    part = __builtin_amdgcn_fdot2_f32_bf16(as_pair(qp[g][c]), as_pair(kw[c]), part,
+                                                           false);
+                float v = part + __shfl_xor(part, 1, 64);
+                v = v + __shfl_xor(v, 2, 64);
+                if (pp == 0)
+                    sc[g][j] = j < n ? v * scale_log2 : -__builtin_inff();
+            }
+        }
+    }
+    // slots past the last tile read are empty
+    for (int i = t; i < G * kSplit; i += kThreads)
+        if (i % kSplit >= ((n + kTile - 1) / kTile) * kTile)
+            sc[i / kSplit][i % kSplit] = -__builtin_inff();
+    __syncthreads();
+    // ---- per head: max, weights, pairwise sum of the 256 weight slots
+    float m[GM], l[GM];
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+        if (g >= G)
+            break;
+        float x = sc[g][t];
+#pragma unroll
+        for (int k = 1; k < 64; k <<= 1)
+            x = fmaxf(x, __shfl_xor(x, k, 64));
+        if (lane == 0)
+            red[g][wave] = x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+        if (g >= G)
+            break;
+        m[g] = fmaxf(fmaxf(red[g][0], red[g][1]), fmaxf(red[g][2], red[g][3]));
+        const float p = t < n ? exp2f(sc[g][t] - m[g]) : 0.0f;
+        sc[g][t] = p;
+        float x = p;
+#pragma unroll
+        for (int k = 1; k < 64; k <<= 1)
+            x = x + __shfl_xor(x, k, 64);
+        l[g] = x;
+    }
+    __syncthreads();  // every max read from red before it is reused
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+        if (g >= G)
+            break;
+        if (lane == 0)
+            red[g][wave] = l[g];
+    }
+    // ---- weighted values: output pair o = t, t + 256 (head o / 64, columns
+    // 2 (o % 64) and 2 (o % 64) + 1); positions in ascending order, four
+    // weights read at a time
+    float acc[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+    const int npairs = G * (kD / 2);
+    for (int sub = 0; sub < kSplit / kTile; ++sub) {
+        if (sub * kTile >= n)
+            break;
+        __syncthreads();
+        load_tile(tile, Vh, sub * kTile, n);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int o = t + i * kThreads;
+            if (o < npairs) {
+                const int g = o >> 6, dp = o & 63;
+                const float *pw = &sc[g][sub * kTile];
+                for (int rr = 0; rr < kTile; rr += 4) {
+                    const float4 w4 = *reinterpret_cast<const float4 *>(pw + rr);
+                    const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint32_t vv =
+                            *reinterpret_cast<const uint32_t *>(tile + (rr + u) * kRowBytes + dp * 4);
+                        acc[i][0] = fmaf(wv[u], bfv(vv & 0xFFFFu), acc[i][0]);
+                        acc[i][1] = fmaf(wv[u], bfv(vv >> 16), acc[i][1]);
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();  // the l values in red
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int o = t + i * kThreads;
+        if (o < npairs) {
+            const int g = o >> 6, dp = o & 63;
+            float *w = work + (((int64_t)b * Hq + kvh * G + g) * NS + s) * (kD + 2);
+            w[2 * dp] = acc[i][0];
+            w[2 * dp + 1] = acc[i][1];
+            if (dp == 0) {
+                w[kD] = m[g];
+                w[kD + 1] = (red[g][0] + red[g][1]) + (red[g][2] + red[g][3]);
+            }
+        }
+    }
+}
+
+// One workgroup of 128 threads (one per column) per (query head, sequence).
+__global__ __launch_bounds__(kD) void attn_combine_kernel(const int32_t *lens, int Hq, int Smax,
+                                                          int NS, const float *work, uint16_t *O) {
+    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    int len = lens[b];
+    len = len < 0 ? 0 : (len > Smax ? Smax : len);
+    const int ns = (len + kSplit - 1) / kSplit;
+    uint16_t *o = O + ((int64_t)b * Hq + h) * kD;
+    if (ns == 0) {
+        o[d] = 0;
+        return;
+    }
+    const float *w = work + ((int64_t)b * Hq + h) * NS * (kD + 2);
+    float M = w[kD];
+    for (int s = 1; s < ns; ++s)
+        M = fmaxf(M, w[s * (kD + 2) + kD]);
+    float L = 0.0f, acc = 0.0f;
+    for (int s = 0; s < ns; ++s) {
+        const float f = exp2f(w[s * (kD + 2) + kD] - M);
+        L = fmaf(w[s * (kD + 2) + kD + 1], f, L);
+        acc = fmaf(w[s * (kD + 2) + d], f, acc);
+    }
+    o[d] = (uint16_t)pair_bits(round_pair(acc / L, 0.0f));
+}
+
+bool disjoint(const void *a, int64_t na, const void *b, int64_t nb) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return na <= 0 || nb <= 0 || a0 + (uintptr_t)na <= b0 || b0 + (uintptr_t)nb <= a0;
+}
+
+}  // namespace
+
+extern "C" int det_attention_decode(const det_bf16 *Q, const det_bf16 *K, const det_bf16 *V,
+                                    const int32_t *lens, int64_t B, int64_t Hq, int64_t Hkv,
+                                    int64_t Smax, int64_t D, float scale, float *work,
+                                    det_bf16 *O, void *stream) {
+    if (B < 0 || Hq < 1 || Hkv < 1 || Smax < 0 || D != kD || Hq % Hkv != 0 ||
+        Hq / Hkv > kGMax || B > 65535 || Hkv > 65535 || Hq > 65535 || Smax > (1 << 24))
+        return DET_GEMM_EINVAL;
+    if (B == 0)
+        return DET_GEMM_OK;
+    const int64_t NS = (Smax + kSplit - 1) / kSplit;
+    if (!Q || !lens || !O || (NS > 0 && (!K || !V || !work)))
+        return DET_GEMM_EINVAL;
+    const int64_t qb = B * Hq * kD * 2, kvb = B * Hkv * Smax * kD * 2;
+    const int64_t wb = B * Hq * NS * (kD + 2) * 4;
+    if (!disjoint(O, qb, Q, qb) || !disjoint(O, qb, K, kvb) || !disjoint(O, qb, V, kvb) ||
+        !disjoint(O, qb, lens, B * 4) || !disjoint(O, qb, work, wb) ||
+        !disjoint(work, wb, Q, qb) || !disjoint(work, wb, K, kvb) || !disjoint(work, wb, V, kvb) ||
+        !disjoint(work, wb, lens, B * 4))
+        return DET_GEMM_EINVAL;
+    if (((reinterpret_cast<uintptr_t>(K) | reinterpret_cast<uintptr_t>(V)) & 15) != 0)
+        return DET_GEMM_EINVAL;  // 16-byte rows
+    const int dev = check_device();
+    if (dev != DET_GEMM_OK)
+        return dev;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int G = (int)(Hq / Hkv);
+    if (NS > 0) {
+        const dim3 grid((unsigned)NS, (unsigned)Hkv, (unsigned)B);
+        const float sl = scale * kLog2e;
+        if (G == 1)
+            hipLaunchKernelGGL(attn_split_kernel<1>, grid, dim3(kThreads), 0, st, Q, K, V, lens,
+                               (int)Hq, (int)Hkv, (int)Smax, G, (int)NS, sl, work);
+        else if (G == 2)
+            hipLaunchKernelGGL(attn_split_kernel<2>, grid, dim3(kThreads), 0, st, Q, K, V, lens,
+                               (int)Hq, (int)Hkv, (int)Smax, G, (int)NS, sl, work);
+        else if (G <= 4)
+            hipLaunchKernelGGL(attn_split_kernel<4>, grid, dim3(kThreads), 0, st, Q, K, V, lens,
+                               (int)Hq, (int)Hkv, (int)Smax, G, (int)NS, sl, work);
+        else
+            hipLaunchKernelGGL(attn_split_kernel<8>, grid, dim3(kThreads), 0, st, Q, K, V, lens,
+                               (int)Hq, (int)Hkv, (int)Smax, G, (int)NS, sl, work);
+    }
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)Hq, (unsigned)B), dim3(kD), 0, st, lens,
+                       (int)Hq, (int)Smax, (int)NS, work, O);
+    return hipGetLastError() == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
+}

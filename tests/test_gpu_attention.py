@@ -1,0 +1,108 @@
+"""GPU parity of decode attention with fixed split-KV size through the C-ABI
+(include/det_attention.h).
+
+Summary page of "Defeating Nondeterminism in LLM Inference", section on
+batch-invariant kernel design, attention: with a fixed split size a
+sequence's result does not depend on the batch.
+
+Checks: against the float64 oracle within a bound derived from the
+arithmetic (bf16 output rounding, 2^-9 relative, plus fp32 score, exp2 and
+accumulation errors, far below 2e-5 of the largest |v| at these sizes), and
+bitwise: a sequence alone, in another batch, at another position, with another
+Smax (padding) or with other data past its length gives the same bits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import det_workloads as Wk
+from oracle.attention import attention_decode
+import invariant_deterministic_gemm_det_amd as dg
+from gpu_util import device, say, bits
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+SCALE = 1.0 / np.sqrt(D)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    d = device()
+    dg.load_library()
+    return d
+
+
+def _case(B, Hq, Hkv, Smax, lens, seed, dev):
+    q = Wk.randn_bf16((B, Hq, D), 1.0, seed, dev)
+    k = Wk.randn_bf16((B, Hkv, Smax, D), 1.0, seed + 1, dev)
+    v = Wk.randn_bf16((B, Hkv, Smax, D), 1.0, seed + 2, dev)
+    return q, k, v, torch.tensor(lens, dtype=torch.int32, device=dev)
+
+
+def _within(o, q, k, v, lens):
+    want = attention_decode(bits(q), bits(k), bits(v), lens.cpu().numpy(), SCALE)
+    got = (bits(o).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    vmax = np.abs((bits(v).astype(np.uint32) << 16).view(np.float32)).max()
+    lim = 2.0 ** -8 * np.abs(want) + 2e-5 * vmax
+    ratio = float((np.abs(got - want) / lim).max())
+    print("  worst |o - o64| / bound:", round(ratio, 3))
+    assert ratio <= 1.0
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Smax,lens", [
+    (3, 4, 4, 300, [300, 1, 257]),            # G = 1, a one-position sequence, a split edge
+    (4, 32, 8, 1100, [1100, 0, 256, 513]),    # G = 4, an empty sequence, a whole split
+    (2, 16, 2, 777, [700, 777]),              # G = 8
+])
+def test_attention_matches_oracle(dev, B, Hq, Hkv, Smax, lens):
+    say("attention decode", B, Hq, Hkv, Smax, lens)
+    q, k, v, L = _case(B, Hq, Hkv, Smax, lens, 1000 + Smax, dev)
+    o = dg.det_attention_decode(q, k, v, L, SCALE)
+    _within(o, q, k, v, L)
+    if 0 in lens:
+        assert torch.all(o[lens.index(0)].float() == 0)
+
+
+def test_sequence_bits_independent_of_batch_padding_and_tail(dev):
+    say("attention batch invariance")
+    B, Hq, Hkv, Smax = 6, 32, 8, 1300
+    lens = [1300, 17, 600, 256, 1024, 999]
+    q, k, v, L = _case(B, Hq, Hkv, Smax, lens, 2000, dev)
+    o = dg.det_attention_decode(q, k, v, L, SCALE)
+    assert torch.equal(dg.det_attention_decode(q, k, v, L, SCALE).view(torch.int16),
+                       o.view(torch.int16))
+    for b in (0, 2, 5):
+        n = lens[b]
+        # alone, with Smax = its own length (other padding)
+        ob = dg.det_attention_decode(q[b:b + 1].contiguous(), k[b:b + 1, :, :n].contiguous(),
+                                     v[b:b + 1, :, :n].contiguous(),
+                                     torch.tensor([n], dtype=torch.int32, device=dev), SCALE)
+        assert torch.equal(ob[0].view(torch.int16), o[b].view(torch.int16))
+    # another batch order, other data past each length
+    perm = [5, 3, 0, 4, 1, 2]
+    k2, v2 = k[perm].clone(), v[perm].clone()
+    for i, b in enumerate(perm):
+        k2[i, :, lens[b]:] = 7.0
+        v2[i, :, lens[b]:] = -3.0
+    o2 = dg.det_attention_decode(q[perm].contiguous(), k2, v2,
+                                 torch.tensor([lens[b] for b in perm], dtype=torch.int32,
+                                              device=dev), SCALE)
+    assert torch.equal(o2.view(torch.int16), o[perm].view(torch.int16))
+
+
+def test_decode_workload_full_size(dev):
+    """64 sequences, 32 query heads on 8 key/value heads, up to 4096 cached
+    positions: a few sequences alone and against the oracle."""
+    lens = (1024 + Wk.randperm(3073, 2100)[:64]).tolist()
+    say("attention decode full size, lens", min(lens), "..", max(lens))
+    q, k, v, L = _case(64, 32, 8, 4096, lens, 2200, dev)
+    o = dg.det_attention_decode(q, k, v, L, SCALE)
+    for b in (0, 31, 63):
+        n = lens[b]
+        ob = dg.det_attention_decode(q[b:b + 1].contiguous(), k[b:b + 1, :, :n].contiguous(),
+                                     v[b:b + 1, :, :n].contiguous(),
+                                     torch.tensor([n], dtype=torch.int32, device=dev), SCALE)
+        assert torch.equal(ob[0].view(torch.int16), o[b].view(torch.int16))
+    sel = [0, 63]
+    _within(o[sel], q[sel], k[sel], v[sel], L[sel])

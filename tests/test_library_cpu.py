@@ -171,3 +171,21 @@ def test_rmsnorm_argument_errors_without_device(lib):
     assert lib.det_rmsnorm(FAKE, 64, FAKE, eps, FAKE, 64, r, 4, 64, NULL) == dg.EINVAL  # y over x
     assert lib.det_rmsnorm(FAKE, 64, FAKE, eps, y, 64, y, 4, 64, NULL) == dg.EINVAL    # rstd over y
     assert lib.det_rmsnorm(FAKE, 64, FAKE, eps, y, 64, r, 0, 64, NULL) == dg.OK        # no rows
+
+
+# ---------------------------------------------------------------- det_attention.h
+
+def test_attention_argument_errors_without_device(lib):
+    """Summary of "Defeating Nondeterminism in LLM Inference", attention with a
+    fixed split-KV size; errors before any device work."""
+    f = lib.det_attention_decode
+    o, w = ctypes.c_void_p(0x900000000), ctypes.c_void_p(0xA00000000)
+    s = ctypes.c_float(0.1)
+    A = ctypes.c_void_p(0x100000000)
+    assert f(FAKE, A, A, FAKE, 2, 8, 2, 64, 64, s, w, o, NULL) == dg.EINVAL    # D != 128
+    assert f(FAKE, A, A, FAKE, 2, 8, 3, 64, 128, s, w, o, NULL) == dg.EINVAL   # Hq % Hkv
+    assert f(FAKE, A, A, FAKE, 2, 32, 2, 64, 128, s, w, o, NULL) == dg.EINVAL  # G > 8
+    assert f(FAKE, A, A, FAKE, -1, 8, 2, 64, 128, s, w, o, NULL) == dg.EINVAL
+    assert f(FAKE, A, A, NULL, 2, 8, 2, 64, 128, s, w, o, NULL) == dg.EINVAL   # no lens
+    assert f(FAKE, A, A, FAKE, 2, 8, 2, 64, 128, s, w, A, NULL) == dg.EINVAL   # O over K
+    assert f(FAKE, A, A, FAKE, 0, 8, 2, 64, 128, s, w, o, NULL) == dg.OK       # no sequences
