@@ -37,17 +37,26 @@ constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float bfv(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
 
-// Positions [p0, p0 + 64) of one head's key or value rows into the LDS tile;
-// rows at or past n are zero.  16-byte chunks, 16 per row, 4 per thread.
-__device__ __forceinline__ void load_tile(char *tile, const uint16_t *rows, int p0, int n) {
+// Positions [p0, p0 + 64) of one head's key or value rows, as this thread's
+// four 16-byte chunks (16 per row; rows at or past n are zero): fetched into
+// registers one tile ahead of their use, then written to the LDS tile.
+constexpr int kPer = kTile * 16 / kThreads;
+
+__device__ __forceinline__ void fetch_tile(uint4 (&v)[kPer], const uint16_t *rows, int p0, int n) {
 #pragma unroll
-    for (int i = 0; i < kTile * 16 / kThreads; ++i) {
+    for (int i = 0; i < kPer; ++i) {
         const int c = threadIdx.x + i * kThreads;
         const int r = c >> 4, col = c & 15;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (p0 + r < n)
-            v = *reinterpret_cast<const uint4 *>(rows + (int64_t)(p0 + r) * kD + col * 8);
-        *reinterpret_cast<uint4 *>(tile + r * kRowBytes + col * 16) = v;
+        v[i] = p0 + r < n ? *reinterpret_cast<const uint4 *>(rows + (int64_t)(p0 + r) * kD + col * 8)
+                          : make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+__device__ __forceinline__ void put_tile(char *tile, const uint4 (&v)[kPer]) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int c = threadIdx.x + i * kThreads;
+        *reinterpret_cast<uint4 *>(tile + (c >> 4) * kRowBytes + (c & 15) * 16) = v[i];
     }
 }
 
@@ -92,11 +101,16 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
             qp[g][4 * c + 2] = v.z;
             qp[g][4 * c + 3] = v.w;
         }
-    for (int sub = 0; sub < kSplit / kTile; ++sub) {
-        if (sub * kTile >= n)
-            break;  // uniform: n is the workgroup's
+    const int ntiles = (n + kTile - 1) / kTile;
+    uint4 nxt[kPer];
+    fetch_tile(nxt, Kh, 0, n);
+    for (int sub = 0; sub < ntiles; ++sub) {
         __syncthreads();  // the previous tile consumed
-        load_tile(tile, Kh, sub * kTile, n);
+        put_tile(tile, nxt);
+        if (sub + 1 < ntiles)
+            fetch_tile(nxt, Kh, (sub + 1) * kTile, n);
+        else
+            fetch_tile(nxt, Vh, 0, n);  // the first value tile, in flight through the softmax
         __syncthreads();
         uint32_t kw[16];
 #pragma unroll
@@ -125,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     }
     // slots past the last tile read are empty
     for (int i = t; i < G * kSplit; i += kThreads)
-        if (i % kSplit >= ((n + kTile - 1) / kTile) * kTile)
+        if (i % kSplit >= ntiles * kTile)
             sc[i / kSplit][i % kSplit] = -__builtin_inff();
     __syncthreads();
     // ---- per head: max, weights, pairwise sum of the 256 weight slots
@@ -168,11 +182,11 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     // weights read at a time
     float acc[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
     const int npairs = G * (kD / 2);
-    for (int sub = 0; sub < kSplit / kTile; ++sub) {
-        if (sub * kTile >= n)
-            break;
+    for (int sub = 0; sub < ntiles; ++sub) {
         __syncthreads();
-        load_tile(tile, Vh, sub * kTile, n);
+        put_tile(tile, nxt);
+        if (sub + 1 < ntiles)
+            fetch_tile(nxt, Vh, (sub + 1) * kTile, n);
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
