@@ -178,10 +178,12 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     if (pr.I <= 16)
         return 1;
     int up = 0;
-    if (pr.I >= 128 && pr.J >= 128 && wide_ok(pr, t, kTileCfgs[5], up))
-        return 5;
-    if (pr.I >= 128 && pr.J >= 128 && wide_ok(pr, t, kTileCfgs[7], up))
-        return 7;
+    if (pr.I >= 128 && pr.J >= 128) {
+        // three stage buffers with early copies where the LDS holds them
+        for (int c : {8, 5, 9, 7})
+            if (wide_ok(pr, t, kTileCfgs[c], up))
+                return c;
+    }
     // 8-wave 128x64 tiles for blocks of 8 leaves; the 4-wave 64x64 tile (twice
     // the registers per wave) for blocks of 12 and for the LDS stack.
     const bool wide = t.mode == TREE_BLOCK && t.tb == 1;
@@ -643,10 +645,13 @@ int moe_entry(const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw, in
                     return DET_GEMM_EINVAL;
                 cfg = g_force_config;
             }
-        } else if (wide_ok(base, tree, kTileCfgs[5], up)) {
-            cfg = 5;
-        } else if (wide_ok(base, tree, kTileCfgs[7], up)) {
-            cfg = 7;
+        } else {
+            for (int c : {8, 5, 9, 7})
+                if (wide_ok(base, tree, kTileCfgs[c], up) &&
+                    kTileCfgs[c].lds_bytes(up) + kEpiLds <= kLdsMax) {
+                    cfg = c;
+                    break;
+                }
         }
         // the grouped kernel's LDS also holds the epilogue header
         if (cfg >= 0 && kTileCfgs[cfg].lds_bytes(up) + kEpiLds > kLdsMax) {

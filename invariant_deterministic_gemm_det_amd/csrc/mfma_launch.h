@@ -52,8 +52,9 @@ constexpr TileCfg kTileCfgs[] = {
     {2, 2, 4, 2, KIND_GENERAL, 0, 0, 0, 1}, {1, 2, 1, 4, KIND_GENERAL, 0, 0, 0, 1},
     {2, 2, 2, 2, KIND_GENERAL, 0, 0, 0, 1}, {2, 2, 4, 2, KIND_FAST, 0, 0, 0, 1},
     {2, 2, 2, 2, KIND_FAST, 0, 0, 0, 1},    {4, 2, 2, 4, KIND_WIDE, 2, 4, 1, 1},
-    {4, 2, 2, 2, KIND_WIDE, 2, 3, 1, 1},    {4, 2, 2, 4, KIND_WIDE, 2, 2, 1, 3}};
-constexpr int kNumTileCfgs = 8;
+    {4, 2, 2, 2, KIND_WIDE, 2, 3, 1, 1},    {4, 2, 2, 4, KIND_WIDE, 2, 2, 1, 3},
+    {4, 2, 2, 4, KIND_WIDE, 3, 4, 1, 1},    {4, 2, 2, 4, KIND_WIDE, 3, 2, 1, 3}};
+constexpr int kNumTileCfgs = 10;
 
 struct TreeSel {
     int mode;  // TREE_BLOCK or TREE_STACK
@@ -198,6 +199,10 @@ hipError_t launch_layout(int cfg, const TreeSel &t, const MfmaParams &p, int64_t
         return launch_wide<XK, YK, OUT, 4, 2, 2, 2, 2, 1, 3, 1, 2>(p, tiles, st);
     case 7:
         return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 2, 3, 2, 1, 2>(p, tiles, st);
+    case 8:
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 1, 4, 1, 2>(p, tiles, st);
+    case 9:
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 3, 2, 1, 2>(p, tiles, st);
     default:
         return hipErrorInvalidValue;
     }
@@ -210,7 +215,7 @@ hipError_t launch_kk_bf16(int cfg, const TreeSel &t, const MfmaParams &p, int64_
 hipError_t launch_nn_bf16(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st);
 hipError_t launch_nn_bf16t(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st);
 hipError_t launch_leaves(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st);
-// Grouped forward (configurations 5 and 7 only); defined in mfma_moe.hip.
+// Grouped forward (wide configurations 5, 7, 8, 9 only); defined in mfma_moe.hip.
 hipError_t launch_moe_grouped(int cfg, const MfmaParams &p, const GroupTable &g, int64_t tiles,
                               hipStream_t st);
 

@@ -12,6 +12,10 @@ hipError_t launch_moe_grouped(int cfg, const MfmaParams &p, const GroupTable &g,
         return launch_wide_grouped<4, 2, 2, 4, 2, 1, 4, 1, 2>(p, g, tiles, st);
     case 7:
         return launch_wide_grouped<4, 2, 2, 4, 2, 3, 2, 1, 2>(p, g, tiles, st);
+    case 8:
+        return launch_wide_grouped<4, 2, 2, 4, 3, 1, 4, 1, 2>(p, g, tiles, st);
+    case 9:
+        return launch_wide_grouped<4, 2, 2, 4, 3, 3, 2, 1, 2>(p, g, tiles, st);
     default:
         return hipErrorInvalidValue;
     }

@@ -308,6 +308,12 @@ __device__ __forceinline__ void store_staged(const MfmaParams &p, const Frag<FM,
     }
 }
 
+// With NBUF >= 3 the copies are issued early: before the barrier that opens
+// stage s, the first NP waves (the ones the issue arbiter favours, which reach
+// the barrier first) issue the copies of stage s + NBUF - 2, so the copy issue
+// happens in time those waves would spend waiting, and the waves that finish
+// last issue no copies.  With NBUF == 2 every wave issues its share right
+// after the barrier (the copies need a stage of lead time either way).
 template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF>
 struct WideEngine {
     static constexpr int kOUT = OUT, kWM = WM;
@@ -322,8 +328,10 @@ struct WideEngine {
     static constexpr int lds_bytes(int parked) { return NBUF * BUF + parked * PARK_LEVEL; }
     typedef Frag<FM, FN> F;
     typedef WPacked<FM, FN> P;
-    typedef DirectStager<XK, BM, NW> SX;
-    typedef DirectStager<YK, BN, NW> SY;
+    static constexpr bool kEarly = NBUF >= 3;
+    static constexpr int NP = kEarly ? NW / 2 : NW;  // waves issuing copies
+    typedef DirectStager<XK, BM, NP> SX;
+    typedef DirectStager<YK, BN, NP> SY;
     static constexpr int LOADS = SX::PER_WAVE + SY::PER_WAVE;
     static_assert(NBUF >= 2, "at least two stage buffers");
 
@@ -331,6 +339,7 @@ struct WideEngine {
     char *smem;  // the stage buffers
     SX sx;
     SY sy;
+    bool producer;  // this wave issues copies
     int xoff[XK ? 2 : FM];  // K-major: per leaf half h; MN-major: per fragment
     int yoff[YK ? 2 : FN];
     char *park_lane;  // this lane's first parking slot
@@ -373,8 +382,9 @@ struct WideEngine {
         const int lane = threadIdx.x & 63;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const int wm = wave % WM, wn = wave / WM;
-        sx.init(p.x, p.ldx, i0, p.I, wave, lane);
-        sy.init(p.y, p.ldy, j0, p.J, wave, lane);
+        producer = wave < NP;
+        sx.init(p.x, p.ldx, i0, p.I, producer ? wave : 0, lane);
+        sy.init(p.y, p.ldy, j0, p.J, producer ? wave : 0, lane);
         if constexpr (XK) {
             kmajor_offsets(xoff, wm * FM * 16, lane);
         } else {
@@ -396,15 +406,18 @@ struct WideEngine {
     }
 
     __device__ __forceinline__ void issue(int s) {
-        char *buf = smem + (s % NBUF) * BUF;
-        sx.issue(s, buf);
-        sy.issue(s, buf + XB);
+        if (NP == NW || producer) {
+            char *buf = smem + (s % NBUF) * BUF;
+            sx.issue(s, buf);
+            sy.issue(s, buf + XB);
+        }
     }
 
-    // Stages 0 .. NBUF-2 in flight (0 and 1 with four buffers).
+    // Stages 0 .. NBUF-2 in flight (early issue: 0 .. NBUF-3; begin(0)
+    // issues NBUF-2).
     __device__ __forceinline__ void prologue() {
 #pragma unroll
-        for (int q = 0; q < (kPairs ? 2 : NBUF - 1); ++q)
+        for (int q = 0; q < (kEarly ? NBUF - 2 : NBUF - 1); ++q)
             if (q < S)
                 issue(q);
     }
@@ -415,20 +428,18 @@ struct WideEngine {
     // buffer is refilled with stage s + NBUF - 1 --, then the fragment reads of
     // stage s are issued.
     //
-    // With four stage buffers the workgroup joins every other stage instead:
-    // at an even stage s, stages s and s + 1 are complete and the copies of
-    // s + 2 and s + 3 start (PAR: the parity of s, when the caller knows it).
-    static constexpr bool kPairs = NBUF == 4;
+    // Early issue (NBUF >= 3): the copies of stage s + NBUF - 2 go out before
+    // the barrier; their buffer held stage s - 2, which every wave finished
+    // reading before the barrier of stage s - 1.
     template <int PAR = -1>
     __device__ __forceinline__ void begin(int s) {
-        if constexpr (kPairs) {
-            static_assert(PAR == 0 || PAR == 1, "stage parity must be static");
-            if constexpr (PAR == 0) {
+        if constexpr (kEarly) {
+            if (s + NBUF - 2 < S) {
+                issue(s + NBUF - 2);
+                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NBUF - 2) * LOADS)
+                             : "memory");
+            } else {
                 asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-                if (s + 2 < S) {
-                    issue(s + 2);
-                    issue(s + 3);
-                }
             }
         } else {
             if (s + NBUF - 2 < S)

@@ -336,7 +336,7 @@ def test_mfma_tile_configs_identical(dev, K):
 FAST_SHAPES = [(200, 192, 256), (256, 136, 768), (320, 256, 4096), (128, 64, 12288),
                (72, 64, 32768), (512, 512, 1024), (264, 392, 8192), (768, 384, 1536),
                (384, 768, 6144)]
-GENERAL_CFG, FAST_CFGS = 2, (3, 4, 5, 6, 7)
+GENERAL_CFG, FAST_CFGS = 2, (3, 4, 5, 6, 7, 8, 9)
 
 
 def _six_forced(cfg, A, B, dC):
@@ -473,7 +473,7 @@ def test_wide_kernel_nonfinite_inputs(dev, K):
     Ad, Bd, dCd = A.to(dev), B.to(dev), dC.to(dev)
     ref = _six_forced(GENERAL_CFG, Ad, Bd, dCd)
     ran = 0
-    for cfg in (5, 6, 7):
+    for cfg in (5, 6, 7, 8, 9):
         got = _six_forced(cfg, Ad, Bd, dCd)
         for op, g in got.items():
             if g is None:
