@@ -25,7 +25,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 M, K, N = 4096, 4096, 6144
 COPY_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles",
-                            "hbm_traffic_per_launch_det_gemm_moe_fingerprint_rmsnorm_attention.md")
+                            "hbm_traffic_per_launch.md")
 CSRC = os.path.join(ROOT, "invariant_deterministic_gemm_det_amd", "csrc")
 
 
@@ -71,6 +71,7 @@ def parse():
     ap.add_argument("--no-fingerprint", action="store_true", help="skip the fingerprint leg")
     ap.add_argument("--no-rmsnorm", action="store_true", help="skip the RMSNorm leg")
     ap.add_argument("--no-attention", action="store_true", help="skip the decode attention leg")
+    ap.add_argument("--no-shard", action="store_true", help="skip the K-shard combination leg")
     ap.add_argument("--profile-only", action="store_true",
                     help="run only the GPU steps (for rocprofv3 runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -358,6 +359,38 @@ def attention_leg(dev, steps, warmup, with_cpu):
     return out
 
 
+def shard_leg(dev, steps, warmup):
+    """Combination of TP = 8 K-shard partial products of the step shape's
+    forward ([4096, 6144] bf16 each) by the fixed rank-order tree."""
+    import torch
+    import det_workloads as Wk
+    import invariant_deterministic_gemm_det_amd as dg
+
+    parts = [Wk.randn_bf16((M, N), 1.0, 9600 + k, dev) for k in range(8)]
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    fn = lambda: dg.det_gemm_shard_reduce(parts, out=out)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    t = sum(a.elapsed_time(b) for a, b in ts) / len(ts)
+    nbytes = 9 * M * N * 2
+    gbs = nbytes / (t * 1e-3) / 1e9
+    return {"workload": "TP = 8 partial products [4096, 6144] bf16 -> fixed rank-order tree of "
+                        "bf16 adds (the local step of a deterministic reduce-scatter)",
+            "ms": round(t, 4), "GB/s": round(gbs, 1),
+            "roofline": {"bound": "hbm", "kernel": "shard_reduce_kernel<8>", "achieved": round(gbs, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": recorded_traffic("shard")}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -434,6 +467,8 @@ def main():
             rmsnorm_leg(dev, args.steps, args.warmup, False, decode=False)
         if not args.no_attention:
             attention_leg(dev, args.steps, args.warmup, False)
+        if not args.no_shard:
+            shard_leg(dev, args.steps, args.warmup)
         if args.copy_calibration:
             # 256 MiB read + 256 MiB written per launch, far beyond the caches
             src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
@@ -471,6 +506,7 @@ def main():
     norm = None if args.no_rmsnorm else rmsnorm_leg(dev, args.steps, args.warmup, not args.no_cpu)
     attn = None if args.no_attention else attention_leg(dev, args.steps, args.warmup,
                                                         not args.no_cpu)
+    shard = None if args.no_shard else shard_leg(dev, args.steps, args.warmup)
 
     line = {
         "metric": "det_gemm TFLOP/s and % of bf16 MFMA peak at M=4096,K=4096,N=6144 (1 GPU)",
@@ -501,6 +537,7 @@ def main():
         "fingerprint": fp,
         "rmsnorm": norm,
         "attention_decode": attn,
+        "shard_reduce": shard,
     }
     print(json.dumps(line))
 

@@ -119,6 +119,23 @@ int det_gemm_strict_db_transposed(const det_bf16 *A, int64_t lda, const det_bf16
                                   int64_t lddc, det_bf16 *dBt, int64_t lddbt, int64_t M,
                                   int64_t N, int64_t K, void *stream);
 
+/* Combination of K-shard partial products (page section "Ascend NPU backend",
+ * bullet "Reduction tree": a contiguous half of the reduction is one child of
+ * the tree, which is what makes TP = 2 equal TP = 1).  parts is a HOST array
+ * of nparts device pointers, each an [M,N] bf16 matrix with leading dimension
+ * ldp, in rank (reduction) order; out [M,N] (ldo) receives, element by
+ * element, the mid-split tree of bf16 adds over the nparts values (a range of
+ * n parts splits into floor(n/2) on the left; each add is the fp32 sum
+ * rounded to bf16).  When the parts are det_gemm products over TP = 2^j
+ * contiguous equal shards of a reduction whose leaf count L is a multiple of
+ * TP, each part is a subtree of the full product's tree and out equals the
+ * unsharded product bit for bit: this is the local step of a deterministic
+ * reduce-scatter across GPUs.  1 <= nparts <= DET_GEMM_MAX_PARTS; out must
+ * not overlap a part.  Same errors as above. */
+#define DET_GEMM_MAX_PARTS 16
+int det_gemm_shard_reduce(const det_bf16 *const *parts, int64_t nparts, int64_t ldp,
+                          det_bf16 *out, int64_t ldo, int64_t M, int64_t N, void *stream);
+
 /* Inspection: the bf16 leaves of the MFMA forward kernel (same leaf code as
  * det_gemm_fwd), for checking that the only difference from the CPU definition
  * is the order of additions inside a leaf.  leaves is [M][N][L] bf16,

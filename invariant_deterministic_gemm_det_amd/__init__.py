@@ -30,7 +30,8 @@ EXPORTS = _SIX + tuple(n.replace("det_gemm_", "det_gemm_strict_") for n in _SIX)
     "det_gemm_debug_leaves", "det_gemm_debug_round", "det_gemm_debug_add",
     "det_gemm_debug_force_config", "det_gemm_status_string", "det_moe_fwd_dprob",
     "det_moe_debug_slots", "det_fingerprint", "det_fingerprint_rows", "det_first_mismatch",
-    "det_rmsnorm", "det_attention_decode")
+    "det_rmsnorm", "det_attention_decode", "det_gemm_shard_reduce")
+MAX_PARTS = 16
 ATTN_SPLIT = 256
 MOE_SLOT = 128
 MOE_MAX_EXPERTS = 128
@@ -90,6 +91,8 @@ def load_library(path=LIB_PATH):
     lib.det_attention_decode.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, ctypes.c_float, p,
                                          p, p]
     lib.det_attention_decode.restype = ctypes.c_int
+    lib.det_gemm_shard_reduce.argtypes = [p, i64, i64, p, i64, i64, i64, p]
+    lib.det_gemm_shard_reduce.restype = ctypes.c_int
     lib.det_gemm_status_string.argtypes = [ctypes.c_int]
     lib.det_gemm_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -209,6 +212,35 @@ def det_gemm_db_transposed(A, dC, out=None, strict=False):
     out = _out(out, (N, K), A, torch.bfloat16)
     return _call("det_gemm_strict_db_transposed" if strict else "det_gemm_db_transposed", A, dC,
                  out, M, N, K, "det_gemm_db_transposed")
+
+
+# ---------------------------------------------------------------- K-shard combination
+
+def det_gemm_shard_reduce(parts, out=None):
+    """The mid-split tree of bf16 adds over K-shard partial products in rank
+    order (include/det_gemm.h): parts is a list of [M,N] bf16 GPU tensors with
+    one common leading dimension."""
+    if not 1 <= len(parts) <= MAX_PARTS:
+        raise ValueError(f"between 1 and {MAX_PARTS} parts")
+    M, N = parts[0].shape
+    lds = set()
+    ptrs = []
+    for t in parts:
+        if tuple(t.shape) != (M, N):
+            raise ValueError("parts differ in shape")
+        pp, ld = _mat(t, "part")
+        lds.add(ld)
+        ptrs.append(pp.value or 0)
+    if len(lds) != 1:
+        raise ValueError("parts must share one leading dimension")
+    out = _out(out, (M, N), parts[0], torch.bfloat16)
+    op, ldo = _mat(out, "out")
+    arr = (ctypes.c_void_p * len(parts))(*ptrs)
+    with torch.cuda.device(out.device):
+        rc = load_library().det_gemm_shard_reduce(arr, len(parts), lds.pop(), op, ldo, M, N,
+                                                  _stream(out))
+    _check(rc, "det_gemm_shard_reduce")
+    return out
 
 
 # ---------------------------------------------------------------- MoE grouped GEMM

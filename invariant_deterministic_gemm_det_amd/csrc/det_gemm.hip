@@ -375,9 +375,123 @@ __global__ void debug_add_kernel(const uint16_t *a, const uint16_t *b, uint16_t 
     }
 }
 
+// ---- combination of K-shard partials: each thread takes 8 consecutive
+// columns of one row (16-byte loads when aligned) and evaluates the mid-split
+// tree over the parts, unrolled at compile time for each part count.
+struct Parts {
+    const uint16_t *p[DET_GEMM_MAX_PARTS];
+};
+
+template <int LO, int HI>
+__device__ __forceinline__ float tree_of_parts(const float (&v)[DET_GEMM_MAX_PARTS]) {
+    if constexpr (HI - LO == 1) {
+        return v[LO];
+    } else {
+        constexpr int MID = LO + (HI - LO) / 2;
+        const float l = tree_of_parts<LO, MID>(v), r = tree_of_parts<MID, HI>(v);
+        // the bf16 add: fp32 sum of the two bf16 values, rounded to bf16 (kept in fp32)
+        const uint32_t b = pair_bits(round_pair(merge(l, r), 0.0f)) & 0xFFFFu;
+        return __uint_as_float(b << 16);
+    }
+}
+
+template <int NP>
+__global__ __launch_bounds__(256) void shard_reduce_kernel(Parts parts, int64_t ldp, uint16_t *out,
+                                                           int64_t ldo, int64_t M, int64_t N,
+                                                           int64_t chunks_per_row, bool vec) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= M * chunks_per_row)
+        return;
+    const int64_t r = q / chunks_per_row, c0 = (q % chunks_per_row) * 8;
+    const int n = N - c0 < 8 ? (int)(N - c0) : 8;
+    uint16_t vals[NP][8];
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+        const uint16_t *src = parts.p[k] + r * ldp + c0;
+        if (vec && n == 8) {
+            const uint4 w = *reinterpret_cast<const uint4 *>(src);
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                vals[k][e] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
+        } else {
+            for (int e = 0; e < 8; ++e)
+                vals[k][e] = e < n ? src[e] : (uint16_t)0;
+        }
+    }
+    uint16_t res[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float v[DET_GEMM_MAX_PARTS];
+#pragma unroll
+        for (int k = 0; k < DET_GEMM_MAX_PARTS; ++k)
+            v[k] = k < NP ? __uint_as_float((uint32_t)vals[k < NP ? k : 0][e] << 16) : 0.0f;
+        res[e] = (uint16_t)(__float_as_uint(tree_of_parts<0, NP>(v)) >> 16);
+    }
+    uint16_t *dst = out + r * ldo + c0;
+    if (vec && n == 8) {
+        *reinterpret_cast<uint4 *>(dst) =
+            make_uint4(res[0] | ((uint32_t)res[1] << 16), res[2] | ((uint32_t)res[3] << 16),
+                       res[4] | ((uint32_t)res[5] << 16), res[6] | ((uint32_t)res[7] << 16));
+    } else {
+        for (int e = 0; e < n; ++e)
+            dst[e] = res[e];
+    }
+}
+
+template <int NP>
+hipError_t launch_shard_reduce(const Parts &parts, int64_t ldp, uint16_t *out, int64_t ldo,
+                               int64_t M, int64_t N, bool vec, hipStream_t st) {
+    const int64_t cpr = (N + 7) / 8, blocks = (M * cpr + 255) / 256;
+    hipLaunchKernelGGL(shard_reduce_kernel<NP>, dim3((unsigned)blocks), dim3(256), 0, st, parts,
+                       ldp, out, ldo, M, N, cpr, vec);
+    return hipGetLastError();
+}
+
+template <int NP>
+hipError_t dispatch_shard_reduce(int n, const Parts &parts, int64_t ldp, uint16_t *out,
+                                 int64_t ldo, int64_t M, int64_t N, bool vec, hipStream_t st) {
+    if constexpr (NP > DET_GEMM_MAX_PARTS) {
+        return hipErrorInvalidValue;
+    } else {
+        if (n == NP)
+            return launch_shard_reduce<NP>(parts, ldp, out, ldo, M, N, vec, st);
+        return dispatch_shard_reduce<NP + 1>(n, parts, ldp, out, ldo, M, N, vec, st);
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+int det_gemm_shard_reduce(const det_bf16 *const *parts, int64_t nparts, int64_t ldp,
+                          det_bf16 *out, int64_t ldo, int64_t M, int64_t N, void *stream) {
+    if (M < 0 || N < 0 || nparts < 1 || nparts > DET_GEMM_MAX_PARTS || !parts)
+        return DET_GEMM_EINVAL;
+    if (M == 0 || N == 0)
+        return DET_GEMM_OK;
+    if (M > kMaxDim || N > kMaxDim || (M * ((N + 7) / 8) + 255) / 256 > kMaxDim)
+        return DET_GEMM_EINVAL;
+    const Mat om{out, M, N, ldo, 2};
+    if (!mat_ok(om))
+        return DET_GEMM_EINVAL;
+    Parts ps;
+    std::memset(&ps, 0, sizeof ps);
+    bool vec = aligned16(out, ldo);
+    for (int64_t k = 0; k < nparts; ++k) {
+        const Mat pm{parts[k], M, N, ldp, 2};
+        if (!mat_ok(pm) || overlaps(om, pm))
+            return DET_GEMM_EINVAL;
+        ps.p[k] = parts[k];
+        vec = vec && aligned16(parts[k], ldp);
+    }
+    const int dev = check_device();
+    if (dev != DET_GEMM_OK)
+        return dev;
+    const hipError_t e = dispatch_shard_reduce<1>((int)nparts, ps, ldp, out, ldo, M, N, vec,
+                                                  static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
+}
 
 int det_gemm_fwd(const det_bf16 *A, int64_t lda, const det_bf16 *B, int64_t ldb, det_bf16 *C,
                  int64_t ldc, int64_t M, int64_t N, int64_t K, void *stream) {

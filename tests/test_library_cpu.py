@@ -189,3 +189,16 @@ def test_attention_argument_errors_without_device(lib):
     assert f(FAKE, A, A, NULL, 2, 8, 2, 64, 128, s, w, o, NULL) == dg.EINVAL   # no lens
     assert f(FAKE, A, A, FAKE, 2, 8, 2, 64, 128, s, w, A, NULL) == dg.EINVAL   # O over K
     assert f(FAKE, A, A, FAKE, 0, 8, 2, 64, 128, s, w, o, NULL) == dg.OK       # no sequences
+
+
+def test_shard_reduce_argument_errors_without_device(lib):
+    """det_gemm.h, combination of K-shard partials: errors before any device work."""
+    parts = (ctypes.c_void_p * 3)(0x100000000, 0x200000000, 0x300000000)
+    f = lib.det_gemm_shard_reduce
+    out = ctypes.c_void_p(0x900000000)
+    assert f(parts, 0, 64, out, 64, 4, 64, NULL) == dg.EINVAL           # no parts
+    assert f(parts, 17, 64, out, 64, 4, 64, NULL) == dg.EINVAL          # too many
+    assert f(parts, 3, 32, out, 64, 4, 64, NULL) == dg.EINVAL           # ld < N
+    assert f(parts, 3, 64, ctypes.c_void_p(0x200000000), 64, 4, 64, NULL) == dg.EINVAL  # overlap
+    assert f(parts, 3, 64, out, 64, 0, 64, NULL) == dg.OK               # empty
+    assert f(None, 3, 64, out, 64, 4, 64, NULL) == dg.EINVAL
