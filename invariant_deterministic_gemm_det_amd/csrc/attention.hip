@@ -10,9 +10,10 @@
 // of the key/value head, its max, its sum of weights and its weighted value
 // sum, and writes them to the caller's work buffer.  attn_combine_kernel: one
 // workgroup per (query head, sequence) merges the sequence's splits in
-// ascending order.  Keys and values pass through LDS in 64-row tiles (rows
-// padded to 272 bytes so that the 16-byte reads of different rows fall in
-// different banks).  Every reduction has a fixed shape, so a sequence's bits
+// ascending order.  Keys go from global memory straight to the registers of
+// the threads that use them; values pass through LDS in 64-row tiles (rows
+// padded to 272 bytes so that reads of different rows fall in different
+// banks), each tile fetched into registers while the previous one is used.  Every reduction has a fixed shape, so a sequence's bits
 // depend only on its own data and length.
 #include <hip/hip_runtime.h>
 
@@ -101,25 +102,32 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
             qp[g][4 * c + 2] = v.z;
             qp[g][4 * c + 3] = v.w;
         }
+    // The key slice of thread (r, pp) -- 64 contiguous bytes of row r -- is read
+    // straight from global memory (a wave reads 16 whole rows, 4 KB
+    // contiguous) one tile ahead; keys need no LDS.
     const int ntiles = (n + kTile - 1) / kTile;
-    uint4 nxt[kPer];
-    fetch_tile(nxt, Kh, 0, n);
+    auto key_slice = [&](uint4 (&kv)[4], int sub) {
+        const int row = sub * kTile + r;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            kv[c] = row < n ? *reinterpret_cast<const uint4 *>(Kh + (int64_t)row * kD + pp * 32 + c * 8)
+                            : make_uint4(0u, 0u, 0u, 0u);
+    };
+    uint4 kcur[4], knext[4];
+    key_slice(knext, 0);
     for (int sub = 0; sub < ntiles; ++sub) {
-        __syncthreads();  // the previous tile consumed
-        put_tile(tile, nxt);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            kcur[c] = knext[c];
         if (sub + 1 < ntiles)
-            fetch_tile(nxt, Kh, (sub + 1) * kTile, n);
-        else
-            fetch_tile(nxt, Vh, 0, n);  // the first value tile, in flight through the softmax
-        __syncthreads();
+            key_slice(knext, sub + 1);
         uint32_t kw[16];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(tile + r * kRowBytes + pp * 64 + c * 16);
-            kw[4 * c] = v.x;
-            kw[4 * c + 1] = v.y;
-            kw[4 * c + 2] = v.z;
-            kw[4 * c + 3] = v.w;
+            kw[4 * c] = kcur[c].x;
+            kw[4 * c + 1] = kcur[c].y;
+            kw[4 * c + 2] = kcur[c].z;
+            kw[4 * c + 3] = kcur[c].w;
         }
         const int j = sub * kTile + r;
 #pragma unroll
@@ -137,6 +145,8 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
             }
         }
     }
+    uint4 nxt[kPer];
+    fetch_tile(nxt, Vh, 0, n);  // the first value tile, in flight through the softmax
     // slots past the last tile read are empty
     for (int i = t; i < G * kSplit; i += kThreads)
         if (i % kSplit >= ntiles * kTile)
