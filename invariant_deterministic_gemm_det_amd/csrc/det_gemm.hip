@@ -172,18 +172,28 @@ bool wide_ok(const Problem &pr, const TreeSel &t, const TileCfg &c, int &up) {
     return c.lds_bytes(up) <= kLdsMax;  // the wide kernels use no static LDS
 }
 
+// Selection (measured on MI355X; every configuration gives the same bits).
+// 128x128 wide tiles when they make at least four waves of workgroups over the
+// 256 compute units; otherwise the 128x64 wide kernel, two workgroups per
+// compute unit, which keeps more units busy on small and mid-size products
+// (M <= 16 at K = 4096, N = 6144: 41 us instead of 104 us with the 16x128
+// general kernel; M = 1024: 94 us instead of 111 us).
 int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     if (g_force_config >= 0)
         return g_force_config;
-    if (pr.I <= 16)
-        return 1;
     int up = 0;
-    if (pr.I >= 128 && pr.J >= 128) {
-        // three stage buffers with early copies where the LDS holds them
-        for (int c : {8, 5, 9, 7})
+    const int64_t t128 = ((pr.I + 127) / 128) * ((pr.J + 127) / 128);
+    if (t128 >= 4 * 256)
+        for (int c : {8, 5, 9, 7})  // three stage buffers with early copies if the LDS holds them
             if (wide_ok(pr, t, kTileCfgs[c], up))
                 return c;
-    }
+    if (wide_ok(pr, t, kTileCfgs[6], up))
+        return 6;
+    for (int c : {8, 5, 9, 7})
+        if (wide_ok(pr, t, kTileCfgs[c], up))
+            return c;
+    if (pr.I <= 16)
+        return 1;
     // 8-wave 128x64 tiles for blocks of 8 leaves; the 4-wave 64x64 tile (twice
     // the registers per wave) for blocks of 12 and for the LDS stack.
     const bool wide = t.mode == TREE_BLOCK && t.tb == 1;
