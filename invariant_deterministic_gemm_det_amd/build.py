@@ -26,7 +26,7 @@ LIB = os.path.join(HERE, "libdet_gemm.so")
 OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["det_gemm.hip", "mfma_fwd_bf16.hip", "mfma_fwd_f32.hip", "mfma_kk_bf16.hip", "mfma_moe.hip", "fingerprint.hip", "rmsnorm.hip", "attention.hip",
-           "mfma_nn_bf16.hip", "mfma_nn_bf16t.hip", "mfma_leaves.hip"]
+           "mfma_nn_bf16.hip", "mfma_nn_bf16t.hip", "mfma_leaves.hip", "mfma_decode.hip"]
 HEADERS = ["bf16_device.h", "device_check.h", "strict_kernel.h", "mfma_kernel.h", "mfma_fast.h", "mfma_wide.h",
            "mfma_launch.h"]
 

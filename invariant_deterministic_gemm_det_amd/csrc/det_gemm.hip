@@ -172,15 +172,32 @@ bool wide_ok(const Problem &pr, const TreeSel &t, const TileCfg &c, int &up) {
     return c.lds_bytes(up) <= kLdsMax;  // the wide kernels use no static LDS
 }
 
+// The decode kernel (configuration 10): X K-major with at most 16 rows, bf16
+// or fp32 output, whole leaves, at least 8 and at most 1024 of them (one leaf
+// or more per wave, at most 8 pending left siblings per wave), 16-byte aligned
+// rows and, for a [K][N] operand Y, whole 8-column chunks.
+bool decode_ok(const Problem &pr) {
+    const int64_t L = pr.R / 32;
+    return pr.xk && (pr.out == OUT_BF16 || pr.out == OUT_F32) && pr.I >= 1 && pr.I <= 16 &&
+           pr.R % 32 == 0 && L >= 8 && L <= 1024 && aligned16(pr.x, pr.ldx) &&
+           aligned16(pr.y, pr.ldy) && (pr.yk || pr.J % 8 == 0);
+}
+
 // Selection (measured on MI355X; every configuration gives the same bits).
-// 128x128 wide tiles when they make at least four waves of workgroups over the
-// 256 compute units; otherwise the 128x64 wide kernel, two workgroups per
-// compute unit, which keeps more units busy on small and mid-size products
-// (M <= 16 at K = 4096, N = 6144: 41 us instead of 104 us with the 16x128
-// general kernel; M = 1024: 94 us instead of 111 us).
+// At most 16 rows: the decode kernel, whose workgroups split the reduction
+// along the tree; 16 columns per workgroup (N / 16 workgroups, two per
+// compute unit) until 64-column tiles, whose copies read whole 128-byte rows,
+// make one round over the 256 compute units (M = 1, K = 4096: N = 6144 24 us
+// instead of 28 us, N = 151936 293 us instead of 366 us).  Otherwise 128x128
+// wide tiles when they make at least four waves of workgroups over the 256
+// compute units, else the 128x64 wide kernel, two workgroups per compute
+// unit, which keeps more units busy on small and mid-size products (M = 1024
+// at K = 4096, N = 6144: 94 us instead of 111 us).
 int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     if (g_force_config >= 0)
         return g_force_config;
+    if (decode_ok(pr))
+        return (pr.J + 63) / 64 >= 256 ? 11 : 10;
     int up = 0;
     const int64_t t128 = ((pr.I + 127) / 128) * ((pr.J + 127) / 128);
     if (t128 >= 4 * 256)
@@ -226,6 +243,14 @@ int run_mfma(const Problem &pr, hipStream_t st) {
     p.levels = levels;
     const int cfg = pick_config(pr, tree, levels);
     const TileCfg &c = kTileCfgs[cfg];
+    if (c.kind == KIND_DECODE) {
+        if (!decode_ok(pr))
+            return DET_GEMM_EINVAL;  // a forced decode configuration this problem does not fit
+        if ((pr.J + 15) / 16 > kMaxDim)
+            return DET_GEMM_EINVAL;
+        const hipError_t e = launch_decode(p, pr.yk, pr.out, c.fn, st);
+        return e == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
+    }
     if (c.kind == KIND_WIDE) {
         int up = 0;
         if (!wide_ok(pr, tree, c, up))

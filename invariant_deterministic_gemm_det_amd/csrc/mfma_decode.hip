@@ -1,0 +1,357 @@
+// Decode-shaped forward products: at most 16 rows of X (one token, or a small
+// batch of them, against a weight matrix).  Same leaves, same tree, same bits
+// as every other det_gemm kernel; only the work split differs.
+//
+// The contract (RL-Kernel operator page "Batch-Invariant Deterministic GEMM
+// (det_gemm)", sections on the leaf product-sum and the mid-split reduction
+// tree) forbids splitting the reduction across workgroups, and a 16-row
+// product has only N / 16 output blocks: 384 at N = 6144, too few to keep 256
+// compute units streaming the weights if each block walks the whole reduction
+// alone.  Here the tree itself supplies the parallelism inside a workgroup:
+//   * a workgroup owns one 16 x 16 output block (all rows, 16 columns) and
+//     has 8 waves; wave w evaluates the subtree rooted at node w of depth 3 of
+//     the mid-split tree over the L leaves (L >= 8, so every such node holds at
+//     least one leaf), i.e. a contiguous leaf range of about L / 8 leaves;
+//   * a wave walks its leaves in ascending order with the streaming post-order
+//     (after leaf t, as many adds as there are inner nodes whose range ends at
+//     t + 1), pending left siblings in registers;
+//   * the 8 subtree roots meet in LDS and the first wave adds them in the
+//     order of the three top levels: ((0+1)+(2+3))+((4+5)+(6+7)).
+// A leaf is the same v_mfma_f32_16x16x32_bf16 with the same lane assignment as
+// in the other kernels (lane l: X row l % 16 and Y column l % 16 at reduction
+// indices 8(l / 16) .. +7); a tree add is the same round-both-then-add-in-fp32
+// VALU add.  So the bits are those of every other configuration.
+//
+// Data movement, per wave and without workgroup barriers: a private ring of
+// NB leaf slots in LDS, filled by buffer_load_dwordx4 ... lds (16 bytes per
+// lane at M0 + 16 * lane) NB - 1 leaves ahead, drained with s_waitcnt vmcnt.
+//   * Y, reduction index contiguous (the weight stored [N][K]): the slot holds
+//     16 columns x 32 indices, 64-byte rows, 16-byte chunk c of row r at chunk
+//     c ^ ((r >> 2) & 3): the 16 rows of one quarter-wave's ds_read_b128 land
+//     on all 64 banks.
+//   * Y, column index contiguous (the weight stored [K][N]): the slot holds
+//     32 indices x 16 columns, 32-byte rows; rows with bit 3 set swap 128-byte
+//     halves, so the two 16-lane groups of each half-wave ds_read_b64_tr_b16
+//     (indices r0 .. r0+3 and r0+8 .. r0+11) use disjoint banks.
+//   * X: the MP rows the product needs (MP = 1 for a single row, else 16, rows
+//     past the last clamped to it) in the K-major layout above.
+// Workgroup b runs on XCD b mod 8; consecutive column blocks go to the same
+// XCD, so the workgroups that share a 128-byte line of a [K][N] weight share
+// that XCD's L2.
+#include "mfma_launch.h"
+
+namespace detgemm {
+
+namespace {
+
+constexpr int kDecWaves = 8;   // subtrees of depth 3
+
+// CB column blocks of 16 per workgroup (a tile of 16 * CB columns), MP staged
+// rows of X.
+template <int MP, int CB>
+struct DecodeShape {
+    static constexpr int Y_BYTES = CB * 1024;
+    static constexpr int SLOT = Y_BYTES + MP * 64;        // Y tile, then X tile
+    static constexpr int NB = (MP == 1 && CB == 1) ? 8 : 4;  // ring slots per wave
+    static constexpr int AHEAD = NB - 1;                  // leaves in flight per wave
+    static constexpr int OPS = CB + 1;                    // copies per leaf
+    static constexpr int WAVE_BYTES = NB * SLOT;
+    static constexpr int LDS = kDecWaves * WAVE_BYTES;
+};
+
+__device__ __forceinline__ int kt_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+__device__ __forceinline__ int nt_row(int r) { return (r * 32) ^ (((r >> 3) & 1) << 7); }
+// 128-byte rows (64 columns): chunk c of row r at c ^ key8(r); one half-wave's
+// transposed read (rows r0 .. r0+3 and r0+8 .. r0+11, one aligned chunk pair
+// each) then covers disjoint banks.
+__device__ __forceinline__ int key8(int r) { return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)); }
+
+__device__ __forceinline__ u32x4 rsrc_at(const void *base) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const u32x4 rs = {(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, 0xFFFFFFFFu, 0x00020000u};
+    return rs;
+}
+
+// One 1 KB (or, with fewer active lanes, smaller) LDS DMA.  Waits for the
+// wave's outstanding LDS reads first: the slot being refilled was read by the
+// previous leaf.  One wait state separates the M0 write from the load.
+__device__ __forceinline__ void dma16(uint32_t lds, int voff, u32x4 rs) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rs)
+                 : "memory", "m0");
+}
+
+// The pending left siblings of one 16 x 16 block of a wave, indexed by the
+// wave-uniform depth: eight named registers behind a switch, so that no
+// per-lane scratch array arises.
+struct NodeStack {
+    f32x4 s0, s1, s2, s3, s4, s5, s6, s7;
+    __device__ __forceinline__ f32x4 get(int d) const {
+        switch (d) {
+        case 0: return s0;
+        case 1: return s1;
+        case 2: return s2;
+        case 3: return s3;
+        case 4: return s4;
+        case 5: return s5;
+        case 6: return s6;
+        default: return s7;
+        }
+    }
+    __device__ __forceinline__ void put(int d, f32x4 v) {
+        switch (d) {
+        case 0: s0 = v; break;
+        case 1: s1 = v; break;
+        case 2: s2 = v; break;
+        case 3: s3 = v; break;
+        case 4: s4 = v; break;
+        case 5: s5 = v; break;
+        case 6: s6 = v; break;
+        default: s7 = v; break;
+        }
+    }
+};
+
+template <bool YK, int OUT, int MP, int CB>
+__global__ __launch_bounds__(64 * kDecWaves, 2) void mfma_decode_kernel(MfmaParams p) {
+    typedef DecodeShape<MP, CB> S;
+    typedef Frag<1, CB> F;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    // Tile of this workgroup: XCD x = b mod 8 owns a contiguous run of tiles.
+    const int nb = p.tiles_j, b = blockIdx.x;
+    const int x = b & 7, q8 = nb >> 3, rem = nb & 7;
+    const int tile = x * q8 + (x < rem ? x : rem) + (b >> 3);
+    const int j0 = tile * 16 * CB;
+
+    // Leaf range of this wave: node `wave` at depth 3 of the mid-split tree.
+    int lo = 0, hi = p.L;
+#pragma unroll
+    for (int bit = 2; bit >= 0; --bit) {
+        const int mid = lo + (hi - lo) / 2;
+        if ((wave >> bit) & 1)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    const int n = hi - lo;
+
+    // Per-lane source offsets (bytes) of the copies of a leaf; the leaf's base
+    // address moves in the scalar resource.
+    int yoff[CB];
+    const uint16_t *ybase;
+    if (YK) {
+        // copy q: columns 16q .. 16q+15 of the tile, K-major slot layout
+        const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+            const int col = j0 + 16 * q + r < p.J ? j0 + 16 * q + r : p.J - 1;
+            yoff[q] = (int)(((int64_t)(col - j0) * p.ldy + 8 * c) * 2);
+        }
+        ybase = p.y + (int64_t)j0 * p.ldy;
+    } else if (CB == 1) {
+        const int P = 16 * lane;
+        const int qq = P ^ (((P >> 8) & 1) << 7);
+        const int r = qq >> 5, c = (qq >> 4) & 1;
+        int col = j0 + 8 * c;
+        if (col >= p.J)
+            col = p.J - 8;  // J is a multiple of 8 on this path
+        yoff[0] = (int)(((int64_t)r * p.ldy + (col - j0)) * 2);
+        ybase = p.y + j0;
+    } else {
+        // copy q: reduction rows 8q .. 8q+7, 128 bytes each
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+            const int r = 8 * q + (lane >> 3), c = (lane & 7) ^ key8(r);
+            int col = j0 + 8 * c;
+            if (col >= p.J)
+                col = p.J - 8;
+            yoff[q] = (int)(((int64_t)r * p.ldy + (col - j0)) * 2);
+        }
+        ybase = p.y + j0;
+    }
+    int xoff;
+    {
+        const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
+        const int row = r < p.I ? r : p.I - 1;
+        xoff = (int)(((int64_t)row * p.ldx + 8 * c) * 2);
+    }
+    const int64_t ystep = YK ? 32 : (int64_t)32 * p.ldy;  // elements per leaf
+
+    // Fragment read offsets within a slot.
+    const int i16 = lane & 15, G = lane >> 4;
+    const int xrd = S::Y_BYTES + kt_off(MP == 1 ? 0 : i16, G);
+    int yrd[CB][2];
+#pragma unroll
+    for (int q = 0; q < CB; ++q) {
+        if (YK) {
+            yrd[q][0] = q * 1024 + kt_off(i16, G);
+            yrd[q][1] = 0;
+        } else if (CB == 1) {
+            const int m = i16 >> 2, qq = i16 & 3;
+            yrd[q][0] = nt_row(8 * G + m) + 8 * qq;
+            yrd[q][1] = nt_row(8 * G + 4 + m) + 8 * qq;
+        } else {
+            const int m = i16 >> 2, col = 16 * q + 4 * (i16 & 3), lc = col >> 3;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int r = 8 * G + 4 * h + m;
+                yrd[q][h] = r * 128 + (((lc ^ key8(r)) << 4) | ((col & 7) * 2));
+            }
+        }
+    }
+
+    char *ring = smem + wave * S::WAVE_BYTES;
+    const uint32_t ring_lds =
+        (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char *)ring);
+
+    auto issue = [&](int t) {  // local leaf t into slot t % NB
+        const int leaf = lo + t;
+        const uint32_t slot = ring_lds + (uint32_t)((t & (S::NB - 1)) * S::SLOT);
+        const u32x4 rs = rsrc_at(ybase + (int64_t)leaf * ystep);
+#pragma unroll
+        for (int q = 0; q < CB; ++q)
+            dma16(slot + q * 1024, yoff[q], rs);
+        if (MP == 1) {
+            if (lane < 4)
+                dma16(slot + S::Y_BYTES, xoff, rsrc_at(p.x + (int64_t)leaf * 32));
+        } else {
+            dma16(slot + S::Y_BYTES, xoff, rsrc_at(p.x + (int64_t)leaf * 32));
+        }
+    };
+
+    const int pre = n < S::AHEAD ? n : S::AHEAD;
+    for (int t = 0; t < pre; ++t)
+        issue(t);
+
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    F fz;
+#pragma unroll
+    for (int q = 0; q < CB; ++q)
+        fz.v[0][q] = zero;
+    NodeStack st[CB];
+#pragma unroll
+    for (int q = 0; q < CB; ++q)
+        st[q] = NodeStack{zero, zero, zero, zero, zero, zero, zero, zero};
+    int sp = 0;
+    F root = fz;
+    for (int t = 0; t < n; ++t) {
+        if (t + S::AHEAD < n) {
+            issue(t + S::AHEAD);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(S::OPS * S::AHEAD) : "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        const char *slot = ring + (t & (S::NB - 1)) * S::SLOT;
+        const bf16x8 fx = *reinterpret_cast<const bf16x8 *>(slot + xrd);
+        F cur;
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+            bf16x8 fy;
+            if (YK) {
+                fy = *reinterpret_cast<const bf16x8 *>(slot + yrd[q][0]);
+            } else {
+                const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(slot + yrd[q][0]));
+                const s16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(slot + yrd[q][1]));
+                typedef short s16x8 __attribute__((ext_vector_type(8)));
+                const s16x8 v = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+                fy = __builtin_bit_cast(bf16x8, v);
+            }
+            cur.v[0][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fx, fy, zero, 0, 0, 0);
+        }
+        const int m = merges_after(t, n);
+        for (int k = 0; k < m; ++k) {
+            --sp;
+#pragma unroll
+            for (int q = 0; q < CB; ++q)
+                cur.v[0][q] = merge4(st[q].get(sp), cur.v[0][q]);
+        }
+        if (t + 1 < n) {
+#pragma unroll
+            for (int q = 0; q < CB; ++q)
+                st[q].put(sp, cur.v[0][q]);
+            ++sp;
+        } else {
+            root = cur;
+        }
+    }
+
+    // The eight subtree roots meet in LDS, each in its wave's own ring (the
+    // wave's copies and reads are complete); wave q < CB adds block q's.
+#pragma unroll
+    for (int q = 0; q < CB; ++q)
+        *reinterpret_cast<f32x4 *>(ring + (q * 64 + lane) * 16) = root.v[0][q];
+    __syncthreads();
+    if (wave >= CB)
+        return;
+    f32x4 r[kDecWaves];
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w)
+        r[w] = *reinterpret_cast<const f32x4 *>(smem + w * S::WAVE_BYTES + (wave * 64 + lane) * 16);
+    const f32x4 top = merge4(merge4(merge4(r[0], r[1]), merge4(r[2], r[3])),
+                             merge4(merge4(r[4], r[5]), merge4(r[6], r[7])));
+
+    // Lane 16g + c holds rows 4g .. 4g+3 of column c of the block.  A zero
+    // root is stored as +0.
+    const uint32_t lo2 = pair_bits(round_pair(top[0], top[1]));
+    const uint32_t hi2 = pair_bits(round_pair(top[2], top[3]));
+    const uint16_t v4[4] = {(uint16_t)lo2, (uint16_t)(lo2 >> 16), (uint16_t)hi2,
+                            (uint16_t)(hi2 >> 16)};
+    const int j = j0 + 16 * wave + i16;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int i = 4 * G + v;
+        const uint16_t h = (v4[v] & 0x7FFF) ? v4[v] : (uint16_t)0;
+        if (i < p.I && j < p.J) {
+            if (OUT == OUT_BF16)
+                static_cast<uint16_t *>(p.c)[(int64_t)i * p.ldc + j] = h;
+            else
+                static_cast<float *>(p.c)[(int64_t)i * p.ldc + j] = __uint_as_float((uint32_t)h << 16);
+        }
+    }
+}
+
+template <bool YK, int OUT, int MP, int CB>
+hipError_t launch_decode_one(const MfmaParams &p, hipStream_t st) {
+    typedef DecodeShape<MP, CB> S;
+    const void *fn = reinterpret_cast<const void *>(&mfma_decode_kernel<YK, OUT, MP, CB>);
+    static int max_dynamic = -1;
+    if (max_dynamic < 0) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
+        if (e != hipSuccess)
+            return e;
+        max_dynamic = S::LDS;
+    }
+    const int64_t tiles = (p.J + 16 * CB - 1) / (16 * CB);
+    MfmaParams q = p;
+    q.tiles_j = (int32_t)tiles;
+    hipLaunchKernelGGL((mfma_decode_kernel<YK, OUT, MP, CB>), dim3((unsigned)tiles),
+                       dim3(64 * kDecWaves), S::LDS, st, q);
+    return hipGetLastError();
+}
+
+template <bool YK, int OUT, int CB>
+hipError_t launch_decode_rows(const MfmaParams &p, hipStream_t st) {
+    return p.I == 1 ? launch_decode_one<YK, OUT, 1, CB>(p, st) : launch_decode_one<YK, OUT, 16, CB>(p, st);
+}
+
+template <bool YK, int OUT>
+hipError_t launch_decode_cols(const MfmaParams &p, int cb, hipStream_t st) {
+    return cb == 4 ? launch_decode_rows<YK, OUT, 4>(p, st) : launch_decode_rows<YK, OUT, 1>(p, st);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const MfmaParams &p, bool yk, int out, int cb, hipStream_t st) {
+    if (yk)
+        return out == OUT_BF16 ? launch_decode_cols<true, OUT_BF16>(p, cb, st)
+                               : launch_decode_cols<true, OUT_F32>(p, cb, st);
+    return out == OUT_BF16 ? launch_decode_cols<false, OUT_BF16>(p, cb, st)
+                           : launch_decode_cols<false, OUT_F32>(p, cb, st);
+}
+
+}  // namespace detgemm

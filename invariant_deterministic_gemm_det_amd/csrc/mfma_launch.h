@@ -11,7 +11,7 @@ namespace detgemm {
 
 constexpr int kLdsMax = 160 * 1024;  // LDS per workgroup on gfx950
 
-enum KernelKind { KIND_GENERAL = 0, KIND_FAST = 1, KIND_WIDE = 2 };
+enum KernelKind { KIND_GENERAL = 0, KIND_FAST = 1, KIND_WIDE = 2, KIND_DECODE = 3 };
 
 // Tile configurations.  Every one computes identical bits (same leaf
 // instruction, same lane assignment, same tree); they differ in tile shape and
@@ -27,6 +27,11 @@ enum KernelKind { KIND_GENERAL = 0, KIND_FAST = 1, KIND_WIDE = 2 };
 //      workgroups per compute unit)
 //   7: configuration 5 for leaf counts 3 * 2^a (units of three leaves), groups
 //      of 4 six-leaf nodes
+//   8, 9: configurations 5 and 7 with three stage buffers and early copies
+//  10: at most 16 rows of X: one 16 x 16 output block per workgroup, the
+//      reduction split over 8 waves along the subtrees of depth 3
+//      (mfma_decode.hip)
+//  11: configuration 10 with 16 x 64 output tiles
 struct TileCfg {
     int fm, fn, wm, wn;
     int kind;
@@ -53,8 +58,9 @@ constexpr TileCfg kTileCfgs[] = {
     {2, 2, 2, 2, KIND_GENERAL, 0, 0, 0, 1}, {2, 2, 4, 2, KIND_FAST, 0, 0, 0, 1},
     {2, 2, 2, 2, KIND_FAST, 0, 0, 0, 1},    {4, 2, 2, 4, KIND_WIDE, 2, 4, 1, 1},
     {4, 2, 2, 2, KIND_WIDE, 2, 3, 1, 1},    {4, 2, 2, 4, KIND_WIDE, 2, 2, 1, 3},
-    {4, 2, 2, 4, KIND_WIDE, 3, 4, 1, 1},    {4, 2, 2, 4, KIND_WIDE, 3, 2, 1, 3}};
-constexpr int kNumTileCfgs = 10;
+    {4, 2, 2, 4, KIND_WIDE, 3, 4, 1, 1},    {4, 2, 2, 4, KIND_WIDE, 3, 2, 1, 3},
+    {1, 1, 1, 1, KIND_DECODE, 0, 0, 0, 1},  {1, 4, 1, 1, KIND_DECODE, 0, 0, 0, 1}};
+constexpr int kNumTileCfgs = 12;
 
 struct TreeSel {
     int mode;  // TREE_BLOCK or TREE_STACK
@@ -215,6 +221,9 @@ hipError_t launch_kk_bf16(int cfg, const TreeSel &t, const MfmaParams &p, int64_
 hipError_t launch_nn_bf16(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st);
 hipError_t launch_nn_bf16t(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st);
 hipError_t launch_leaves(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st);
+// Configurations 10 and 11 (X K-major, at most 16 rows, bf16 or fp32 output,
+// cb = column blocks of 16 per workgroup: 1 or 4); defined in mfma_decode.hip.
+hipError_t launch_decode(const MfmaParams &p, bool yk, int out, int cb, hipStream_t st);
 // Grouped forward (wide configurations 5, 7, 8, 9 only); defined in mfma_moe.hip.
 hipError_t launch_moe_grouped(int cfg, const MfmaParams &p, const GroupTable &g, int64_t tiles,
                               hipStream_t st);

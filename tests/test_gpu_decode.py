@@ -1,0 +1,157 @@
+"""GPU parity of the decode kernel (tile configurations 10 and 11: at most 16
+rows of X, the reduction split over the 8 depth-3 subtrees of the mid-split
+tree; 16 or 64 columns per workgroup), through the C-ABI.
+
+Contract (RL-Kernel operator page "Batch-Invariant Deterministic GEMM
+(det_gemm)", sections "Guarantees" and "Ascend NPU backend"): the same leaves
+and the same tree as every other configuration, so the bits must equal those
+of the general kernel (configuration 1, itself checked against the oracle in
+test_gpu_parity.py) on every shape, equal the oracle exactly wherever the
+oracle is exact, and a row's bits must not depend on how many rows share the
+call.
+"""
+import numpy as np
+import pytest
+import torch
+
+import det_workloads as W
+import oracle
+import invariant_deterministic_gemm_det_amd as dg
+from gpu_util import device, say, bits
+
+pytestmark = pytest.mark.gpu
+
+DECODE_CFGS, GENERAL_CFG = (10, 11), 1
+
+
+@pytest.fixture(scope="module")
+def dev():
+    d = device()
+    dg.load_library()
+    dg.det_gemm_debug_force_config(-1)
+    return d
+
+
+def _forced(cfg, f):
+    dg.det_gemm_debug_force_config(cfg)
+    try:
+        return f()
+    finally:
+        dg.det_gemm_debug_force_config(-1)
+
+
+def _ops(A, B, dC):
+    """The four products whose X operand has the row count M."""
+    Bt = B.t().contiguous()
+    return {
+        "fwd": lambda: dg.det_gemm_fwd(A, B),
+        "fwd_rhs_transposed": lambda: dg.det_gemm_fwd_rhs_transposed(A, Bt),
+        "fwd_fp32": lambda: dg.det_gemm_fwd_fp32(A, B),
+        "da": lambda: dg.det_gemm_da(dC, B),   # X = dC [M, N], reduction over N
+    }
+
+
+def _as_bits(t):
+    if t.dtype == torch.float32:
+        return t.cpu().numpy().view(np.uint32)
+    return bits(t)
+
+
+# M, N, K: leaf counts 8 (one leaf per wave), 9, 128, 130, 1000 and 1024 (the
+# deepest per-wave trees); N ragged against the 16-column blocks.
+SHAPES = [(1, 6144, 4096), (16, 6144, 4096), (5, 200, 4096), (3, 136, 288), (1, 64, 256),
+          (2, 48, 32768), (16, 40, 4160), (7, 24, 32000), (1, 8, 1024)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_decode_matches_general_kernel(dev, M, N, K):
+    say("decode kernel vs general kernel", M, N, K)
+    A = W.randn_bf16((M, K), 1.0, 1000 + M + K).to(dev)
+    B = W.randn_bf16((K, N), 0.02, 1001 + N + K).to(dev)
+    dC = W.randn_bf16((M, N), 1.0, 1002 + N).to(dev)
+    ops = _ops(A, B, dC)
+    ran = 0
+    for op, f in ops.items():
+        ref = _as_bits(_forced(GENERAL_CFG, f))
+        auto = _as_bits(f())
+        assert np.array_equal(auto, ref), op
+        da_fits = op != "da" or (N % 32 == 0 and N // 32 >= 8)
+        for cfg in DECODE_CFGS:
+            if not da_fits:
+                with pytest.raises(dg.DetGemmError):
+                    _forced(cfg, f)
+                continue
+            got = _as_bits(_forced(cfg, f))
+            assert np.array_equal(got, ref), (op, cfg)
+            assert np.array_equal(_as_bits(_forced(cfg, f)), ref), (op, cfg, "repeat")
+            ran += 1
+    assert ran >= 6
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 200, 4096), (1, 64, 256), (16, 48, 1024), (1, 24, 8192)])
+def test_decode_integer_regime_bit_exact(dev, M, N, K):
+    """Inputs in {-1, 0, 1}: every leaf and tree add is exact, so the kernel
+    must reproduce the oracle bit for bit."""
+    say("decode kernel, integer regime vs oracle", M, N, K)
+    A = W.int_bf16((M, K), 1100 + K)
+    B = W.int_bf16((K, N), 1101 + N)
+    want = oracle.fwd(bits(A), bits(B))
+    Bt = B.t().contiguous()
+    for cfg in DECODE_CFGS:
+        got = _forced(cfg, lambda: dg.det_gemm_fwd(A.to(dev), B.to(dev)))
+        assert np.array_equal(bits(got), want), cfg
+        got_t = _forced(cfg, lambda: dg.det_gemm_fwd_rhs_transposed(A.to(dev), Bt.to(dev)))
+        assert np.array_equal(bits(got_t), want), cfg
+
+
+def test_decode_rows_invariant_to_batch(dev):
+    """QKV projection (K = 4096, N = 6144): each row of a 16-row call (decode
+    kernel, 16 staged rows), the same row alone (decode kernel, one staged
+    row) and the same row inside a 256-row batch (wide kernel) agree bit for
+    bit."""
+    say("decode rows vs single-row and 256-row calls")
+    K, N = 4096, 6144
+    B = W.randn_bf16((K, N), 0.02, 1200).to(dev)
+    big = W.randn_bf16((256, K), 1.0, 1201).to(dev)
+    X16 = big[100:116].contiguous()
+    c16 = bits(dg.det_gemm_fwd(X16, B))
+    c256 = bits(dg.det_gemm_fwd(big, B))
+    assert np.array_equal(c16, c256[100:116])
+    for i in (0, 7, 15):
+        c1 = bits(dg.det_gemm_fwd(X16[i:i + 1].contiguous(), B))
+        assert np.array_equal(c1[0], c16[i]), i
+    for m in (2, 9):
+        cm = bits(dg.det_gemm_fwd(X16[:m].contiguous(), B))
+        assert np.array_equal(cm, c16[:m]), m
+
+
+def test_decode_lm_head_row(dev):
+    """LM head (K = 4096, N = 151936), one and 16 rows: both decode tile
+    widths against the general kernel over the whole vocabulary."""
+    say("decode kernel, LM head rows")
+    A = W.randn_bf16((16, 4096), 1.0, 1300).to(dev)
+    B = W.randn_bf16((4096, 151936), 0.02, 1301, device=dev)
+    for m in (1, 16):
+        ref = bits(_forced(GENERAL_CFG, lambda: dg.det_gemm_fwd(A[:m], B)))
+        assert np.array_equal(bits(dg.det_gemm_fwd(A[:m], B)), ref), m
+        for cfg in DECODE_CFGS:
+            assert np.array_equal(bits(_forced(cfg, lambda: dg.det_gemm_fwd(A[:m], B))), ref), (m, cfg)
+
+
+@pytest.mark.parametrize("case", ["rows17", "leaves7", "ragged_k", "unaligned", "n_not_8"])
+def test_decode_rejects_unsupported(dev, case):
+    """Forcing configuration 10 or 11 on a problem it does not take is EINVAL;
+    the automatic choice runs another kernel with the same bits."""
+    say("decode kernel rejects", case)
+    M, N, K = {"rows17": (17, 64, 1024), "leaves7": (4, 64, 224), "ragged_k": (4, 64, 1040 + 8),
+               "unaligned": (4, 64, 1024), "n_not_8": (4, 13, 1024)}[case]
+    A = W.randn_bf16((M, K + 8), 1.0, 1400).to(dev)
+    A = A[:, 1:K + 1] if case == "unaligned" else A[:, :K].contiguous()
+    B = W.randn_bf16((K, N), 0.02, 1401).to(dev)
+    for cfg in DECODE_CFGS:
+        with pytest.raises(dg.DetGemmError) as e:
+            _forced(cfg, lambda: dg.det_gemm_fwd(A, B))
+        assert e.value.code == dg.EINVAL
+    auto = bits(dg.det_gemm_fwd(A, B))
+    ref = bits(_forced(GENERAL_CFG, lambda: dg.det_gemm_fwd(A, B)))
+    assert np.array_equal(auto, ref)
