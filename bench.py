@@ -72,6 +72,7 @@ def parse():
     ap.add_argument("--no-rmsnorm", action="store_true", help="skip the RMSNorm leg")
     ap.add_argument("--no-attention", action="store_true", help="skip the decode attention leg")
     ap.add_argument("--no-shard", action="store_true", help="skip the K-shard combination leg")
+    ap.add_argument("--no-small-m", action="store_true", help="skip the decode-shaped products")
     ap.add_argument("--profile-only", action="store_true",
                     help="run only the GPU steps (for rocprofv3 runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -391,6 +392,53 @@ def shard_leg(dev, steps, warmup):
                          "traffic": recorded_traffic("shard")}}
 
 
+def small_m_leg(dev, steps, warmup, decode_only=False):
+    """Decode-shaped forward products (few rows against a full weight), which
+    stream the weight once: time per call and HBM GB/s of the algorithmic bytes
+    (X, W and C once each) against the 8 TB/s roofline.  QKV projection K =
+    4096, N = 6144 with the weight stored [K][N] and [N][K]; LM head K = 4096,
+    N = 151936."""
+    import torch
+    import det_workloads as Wk
+    import invariant_deterministic_gemm_det_amd as dg
+
+    Wq = Wk.qkv_weight(dev)
+    Wqt = Wk.qkv_weight(dev, transposed=True)
+    Xl, Wl = Wk.lm_head_inputs(dev, M=256)
+    Xq = Wk.randn_bf16((128, Wk.QKV_K), 1.0, 9700, dev)
+    cases = [("qkv", "W[K][N]", 1), ("qkv", "W[K][N]", 16), ("qkv", "W[K][N]", 128),
+             ("qkv", "W[N][K]", 1), ("qkv", "W[N][K]", 16), ("lm_head", "W[K][N]", 1),
+             ("lm_head", "W[K][N]", 256)]
+    if decode_only:  # the rows on the decode kernel, one kernel instance each
+        cases = [c for c in cases if c[2] <= 16]
+    rows = []
+    for name, layout, m in cases:
+        if name == "qkv":
+            x, k, n = Xq[:m], Wk.QKV_K, Wk.QKV_N
+            fn = (lambda: dg.det_gemm_fwd(x, Wq)) if layout == "W[K][N]" else \
+                 (lambda: dg.det_gemm_fwd_rhs_transposed(x, Wqt))
+        else:
+            x, k, n = Xl[:m], Xl.shape[1], Wl.shape[1]
+            fn = lambda: dg.det_gemm_fwd(x, Wl)
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / steps
+        nbytes = (m * k + k * n + m * n) * 2
+        gbs = nbytes / (t * 1e-3) / 1e9
+        rows.append({"op": name, "weight": layout, "M": m, "K": k, "N": n, "us": round(t * 1e3, 2),
+                     "GB/s": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                     "kernel": "mfma_decode_kernel" if m <= 16 else "mfma_wide_kernel"})
+    return {"workload": "forward products with 1..256 rows: the weight read once per call",
+            "roofline": "hbm, 8000 GB/s", "rows": rows}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -469,6 +517,8 @@ def main():
             attention_leg(dev, args.steps, args.warmup, False)
         if not args.no_shard:
             shard_leg(dev, args.steps, args.warmup)
+        if not args.no_small_m:
+            small_m_leg(dev, args.steps, args.warmup, decode_only=True)
         if args.copy_calibration:
             # 256 MiB read + 256 MiB written per launch, far beyond the caches
             src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
@@ -507,6 +557,7 @@ def main():
     attn = None if args.no_attention else attention_leg(dev, args.steps, args.warmup,
                                                         not args.no_cpu)
     shard = None if args.no_shard else shard_leg(dev, args.steps, args.warmup)
+    small = None if args.no_small_m else small_m_leg(dev, args.steps, args.warmup)
 
     line = {
         "metric": "det_gemm TFLOP/s and % of bf16 MFMA peak at M=4096,K=4096,N=6144 (1 GPU)",
@@ -538,6 +589,7 @@ def main():
         "rmsnorm": norm,
         "attention_decode": attn,
         "shard_reduce": shard,
+        "small_m": small,
     }
     print(json.dumps(line))
 

@@ -52,7 +52,11 @@ template <int MP, int CB>
 struct DecodeShape {
     static constexpr int Y_BYTES = CB * 1024;
     static constexpr int SLOT = Y_BYTES + MP * 64;        // Y tile, then X tile
-    static constexpr int NB = (MP == 1 && CB == 1) ? 8 : 4;  // ring slots per wave
+    // Ring slots per wave.  Measured: deeper rings do not help (the limit is
+    // how the copies meet the memory system, not the bytes in flight), while
+    // two workgroups per compute unit do: 4 slots for 16-column tiles, 2 for
+    // 64-column ones.
+    static constexpr int NB = CB == 1 ? 4 : 2;
     static constexpr int AHEAD = NB - 1;                  // leaves in flight per wave
     static constexpr int OPS = CB + 1;                    // copies per leaf
     static constexpr int WAVE_BYTES = NB * SLOT;
@@ -85,22 +89,40 @@ __device__ __forceinline__ void dma16(uint32_t lds, int voff, u32x4 rs) {
 
 // The pending left siblings of one 16 x 16 block of a wave, indexed by the
 // wave-uniform depth: eight named registers behind a switch, so that no
-// per-lane scratch array arises.
+// per-lane scratch array arises.  A node waits rounded to bf16 (two packed
+// pairs): its parent's add rounds it to bf16 anyway, so storing it rounded
+// changes nothing and halves the registers.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x2 pack_node(f32x4 v) {
+    const u32x2 o = {pair_bits(round_pair(v[0], v[1])), pair_bits(round_pair(v[2], v[3]))};
+    return o;
+}
+
+__device__ __forceinline__ f32x4 unpack_node(u32x2 h) {
+    const f32x4 o = {__uint_as_float(h[0] << 16), __uint_as_float(h[0] & 0xFFFF0000u),
+                     __uint_as_float(h[1] << 16), __uint_as_float(h[1] & 0xFFFF0000u)};
+    return o;
+}
+
 struct NodeStack {
-    f32x4 s0, s1, s2, s3, s4, s5, s6, s7;
+    u32x2 s0, s1, s2, s3, s4, s5, s6, s7;
     __device__ __forceinline__ f32x4 get(int d) const {
+        u32x2 v;
         switch (d) {
-        case 0: return s0;
-        case 1: return s1;
-        case 2: return s2;
-        case 3: return s3;
-        case 4: return s4;
-        case 5: return s5;
-        case 6: return s6;
-        default: return s7;
+        case 0: v = s0; break;
+        case 1: v = s1; break;
+        case 2: v = s2; break;
+        case 3: v = s3; break;
+        case 4: v = s4; break;
+        case 5: v = s5; break;
+        case 6: v = s6; break;
+        default: v = s7; break;
         }
+        return unpack_node(v);
     }
-    __device__ __forceinline__ void put(int d, f32x4 v) {
+    __device__ __forceinline__ void put(int d, f32x4 x) {
+        const u32x2 v = pack_node(x);
         switch (d) {
         case 0: s0 = v; break;
         case 1: s1 = v; break;
@@ -115,7 +137,7 @@ struct NodeStack {
 };
 
 template <bool YK, int OUT, int MP, int CB>
-__global__ __launch_bounds__(64 * kDecWaves, 2) void mfma_decode_kernel(MfmaParams p) {
+__global__ __launch_bounds__(64 * kDecWaves, 4) void mfma_decode_kernel(MfmaParams p) {
     typedef DecodeShape<MP, CB> S;
     typedef Frag<1, CB> F;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -233,10 +255,11 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void mfma_decode_kernel(MfmaPara
 #pragma unroll
     for (int q = 0; q < CB; ++q)
         fz.v[0][q] = zero;
+    const u32x2 z2 = {0u, 0u};
     NodeStack st[CB];
 #pragma unroll
     for (int q = 0; q < CB; ++q)
-        st[q] = NodeStack{zero, zero, zero, zero, zero, zero, zero, zero};
+        st[q] = NodeStack{z2, z2, z2, z2, z2, z2, z2, z2};
     int sp = 0;
     F root = fz;
     for (int t = 0; t < n; ++t) {
