@@ -185,10 +185,12 @@ bool decode_ok(const Problem &pr) {
 
 // Selection (measured on MI355X; every configuration gives the same bits).
 // At most 16 rows: the decode kernel, whose workgroups split the reduction
-// along the tree; 16 columns per workgroup (N / 16 workgroups, two per
-// compute unit) until 64-column tiles, whose copies read whole 128-byte rows,
-// make one round over the 256 compute units (M = 1, K = 4096: N = 6144 24 us
-// instead of 28 us, N = 151936 293 us instead of 366 us).  Otherwise 128x128
+// along the tree.  Wider tiles read more of each cache line they request (a
+// compute unit keeps a bounded number of line requests in flight), narrower
+// ones spread over more compute units: 64 columns once there are 256 such
+// tiles, 32 columns above 128 such tiles, else 16 (M = 1, K = 4096: N = 6144
+// 18.4 us on 32 columns, 22.4 on 16; N = 151936 222 us on 64 columns, 252 on
+// 32; K = 32768, N = 4096 103 us on 16 columns, 138 on 32).  Otherwise 128x128
 // wide tiles when they make at least four waves of workgroups over the 256
 // compute units, else the 128x64 wide kernel, two workgroups per compute
 // unit, which keeps more units busy on small and mid-size products (M = 1024
@@ -196,8 +198,11 @@ bool decode_ok(const Problem &pr) {
 int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     if (g_force_config >= 0)
         return g_force_config;
-    if (decode_ok(pr))
-        return (pr.J + 63) / 64 >= 256 ? 11 : 10;
+    if (decode_ok(pr)) {
+        if ((pr.J + 63) / 64 >= 256)
+            return 11;
+        return (pr.J + 31) / 32 > 128 ? 12 : 10;
+    }
     int up = 0;
     const int64_t t128 = ((pr.I + 127) / 128) * ((pr.J + 127) / 128);
     if (t128 >= 4 * 256)

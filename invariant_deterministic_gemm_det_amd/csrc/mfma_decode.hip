@@ -30,9 +30,12 @@
 //     c ^ ((r >> 2) & 3): the 16 rows of one quarter-wave's ds_read_b128 land
 //     on all 64 banks.
 //   * Y, column index contiguous (the weight stored [K][N]): the slot holds
-//     32 indices x 16 columns, 32-byte rows; rows with bit 3 set swap 128-byte
-//     halves, so the two 16-lane groups of each half-wave ds_read_b64_tr_b16
-//     (indices r0 .. r0+3 and r0+8 .. r0+11) use disjoint banks.
+//     32 indices x 16 CB columns.  16 columns: 32-byte rows, rows with bit 3
+//     set swap 128-byte halves; 32 columns: 64-byte rows, rows with bit 3 set
+//     swap 32-byte halves; 64 columns: 128-byte rows, 16-byte chunks XORed
+//     as in the direct-to-LDS kernel.  Each way the two 16-lane groups of a
+//     half-wave ds_read_b64_tr_b16 (indices r0 .. r0+3 and r0+8 .. r0+11)
+//     use disjoint banks.
 //   * X: the MP rows the product needs (MP = 1 for a single row, else 16, rows
 //     past the last clamped to it) in the K-major layout above.
 // Workgroup b runs on XCD b mod 8; consecutive column blocks go to the same
@@ -54,9 +57,9 @@ struct DecodeShape {
     static constexpr int SLOT = Y_BYTES + MP * 64;        // Y tile, then X tile
     // Ring slots per wave.  Measured: deeper rings do not help (the limit is
     // how the copies meet the memory system, not the bytes in flight), while
-    // two workgroups per compute unit do: 4 slots for 16-column tiles, 2 for
-    // 64-column ones.
-    static constexpr int NB = CB == 1 ? 4 : 2;
+    // two workgroups per compute unit do: 4 slots for 16- and 32-column
+    // tiles, 2 for 64-column ones.
+    static constexpr int NB = CB == 4 ? 2 : 4;
     static constexpr int AHEAD = NB - 1;                  // leaves in flight per wave
     static constexpr int OPS = CB + 1;                    // copies per leaf
     static constexpr int WAVE_BYTES = NB * SLOT;
@@ -184,6 +187,17 @@ __global__ __launch_bounds__(64 * kDecWaves, 4) void mfma_decode_kernel(MfmaPara
             col = p.J - 8;  // J is a multiple of 8 on this path
         yoff[0] = (int)(((int64_t)r * p.ldy + (col - j0)) * 2);
         ybase = p.y + j0;
+    } else if (CB == 2) {
+        // copy q: reduction rows 16q .. 16q+15, 64 bytes each
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+            const int r = 16 * q + (lane >> 2), c16 = lane & 3;
+            int col = j0 + 16 * ((c16 >> 1) ^ ((r >> 3) & 1)) + 8 * (c16 & 1);
+            if (col >= p.J)
+                col = p.J - 8;
+            yoff[q] = (int)(((int64_t)r * p.ldy + (col - j0)) * 2);
+        }
+        ybase = p.y + j0;
     } else {
         // copy q: reduction rows 8q .. 8q+7, 128 bytes each
 #pragma unroll
@@ -217,6 +231,13 @@ __global__ __launch_bounds__(64 * kDecWaves, 4) void mfma_decode_kernel(MfmaPara
             const int m = i16 >> 2, qq = i16 & 3;
             yrd[q][0] = nt_row(8 * G + m) + 8 * qq;
             yrd[q][1] = nt_row(8 * G + 4 + m) + 8 * qq;
+        } else if (CB == 2) {
+            const int m = i16 >> 2, qq = i16 & 3;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int r = 8 * G + 4 * h + m;
+                yrd[q][h] = r * 64 + ((q ^ ((r >> 3) & 1)) << 5) + 8 * qq;
+            }
         } else {
             const int m = i16 >> 2, col = 16 * q + 4 * (i16 & 3), lc = col >> 3;
 #pragma unroll
@@ -364,7 +385,9 @@ hipError_t launch_decode_rows(const MfmaParams &p, hipStream_t st) {
 
 template <bool YK, int OUT>
 hipError_t launch_decode_cols(const MfmaParams &p, int cb, hipStream_t st) {
-    return cb == 4 ? launch_decode_rows<YK, OUT, 4>(p, st) : launch_decode_rows<YK, OUT, 1>(p, st);
+    if (cb == 4)
+        return launch_decode_rows<YK, OUT, 4>(p, st);
+    return cb == 2 ? launch_decode_rows<YK, OUT, 2>(p, st) : launch_decode_rows<YK, OUT, 1>(p, st);
 }
 
 }  // namespace

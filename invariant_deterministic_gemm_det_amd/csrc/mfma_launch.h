@@ -32,6 +32,7 @@ enum KernelKind { KIND_GENERAL = 0, KIND_FAST = 1, KIND_WIDE = 2, KIND_DECODE = 
 //      reduction split over 8 waves along the subtrees of depth 3
 //      (mfma_decode.hip)
 //  11: configuration 10 with 16 x 64 output tiles
+//  12: configuration 10 with 16 x 32 output tiles
 struct TileCfg {
     int fm, fn, wm, wn;
     int kind;
@@ -59,8 +60,9 @@ constexpr TileCfg kTileCfgs[] = {
     {2, 2, 2, 2, KIND_FAST, 0, 0, 0, 1},    {4, 2, 2, 4, KIND_WIDE, 2, 4, 1, 1},
     {4, 2, 2, 2, KIND_WIDE, 2, 3, 1, 1},    {4, 2, 2, 4, KIND_WIDE, 2, 2, 1, 3},
     {4, 2, 2, 4, KIND_WIDE, 3, 4, 1, 1},    {4, 2, 2, 4, KIND_WIDE, 3, 2, 1, 3},
-    {1, 1, 1, 1, KIND_DECODE, 0, 0, 0, 1},  {1, 4, 1, 1, KIND_DECODE, 0, 0, 0, 1}};
-constexpr int kNumTileCfgs = 12;
+    {1, 1, 1, 1, KIND_DECODE, 0, 0, 0, 1},  {1, 4, 1, 1, KIND_DECODE, 0, 0, 0, 1},
+    {1, 2, 1, 1, KIND_DECODE, 0, 0, 0, 1}};
+constexpr int kNumTileCfgs = 13;
 
 struct TreeSel {
     int mode;  // TREE_BLOCK or TREE_STACK
@@ -221,8 +223,9 @@ hipError_t launch_kk_bf16(int cfg, const TreeSel &t, const MfmaParams &p, int64_
 hipError_t launch_nn_bf16(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st);
 hipError_t launch_nn_bf16t(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st);
 hipError_t launch_leaves(int cfg, const TreeSel &t, const MfmaParams &p, int64_t tiles, hipStream_t st);
-// Configurations 10 and 11 (X K-major, at most 16 rows, bf16 or fp32 output,
-// cb = column blocks of 16 per workgroup: 1 or 4); defined in mfma_decode.hip.
+// Configurations 10, 11 and 12 (X K-major, at most 16 rows, bf16 or fp32
+// output, cb = column blocks of 16 per workgroup: 1, 4 or 2); defined in
+// mfma_decode.hip.
 hipError_t launch_decode(const MfmaParams &p, bool yk, int out, int cb, hipStream_t st);
 // Grouped forward (wide configurations 5, 7, 8, 9 only); defined in mfma_moe.hip.
 hipError_t launch_moe_grouped(int cfg, const MfmaParams &p, const GroupTable &g, int64_t tiles,

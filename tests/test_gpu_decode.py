@@ -1,6 +1,6 @@
-"""GPU parity of the decode kernel (tile configurations 10 and 11: at most 16
+"""GPU parity of the decode kernel (tile configurations 10 to 12: at most 16
 rows of X, the reduction split over the 8 depth-3 subtrees of the mid-split
-tree; 16 or 64 columns per workgroup), through the C-ABI.
+tree; 16, 64 or 32 columns per workgroup), through the C-ABI.
 
 Contract (RL-Kernel operator page "Batch-Invariant Deterministic GEMM
 (det_gemm)", sections "Guarantees" and "Ascend NPU backend"): the same leaves
@@ -21,7 +21,7 @@ from gpu_util import device, say, bits
 
 pytestmark = pytest.mark.gpu
 
-DECODE_CFGS, GENERAL_CFG = (10, 11), 1
+DECODE_CFGS, GENERAL_CFG = (10, 11, 12), 1
 
 
 @pytest.fixture(scope="module")
@@ -140,7 +140,7 @@ def test_decode_lm_head_row(dev):
 
 @pytest.mark.parametrize("case", ["rows17", "leaves7", "ragged_k", "unaligned", "n_not_8"])
 def test_decode_rejects_unsupported(dev, case):
-    """Forcing configuration 10 or 11 on a problem it does not take is EINVAL;
+    """Forcing configuration 10, 11 or 12 on a problem it does not take is EINVAL;
     the automatic choice runs another kernel with the same bits."""
     say("decode kernel rejects", case)
     M, N, K = {"rows17": (17, 64, 1024), "leaves7": (4, 64, 224), "ragged_k": (4, 64, 1040 + 8),
