@@ -15,6 +15,7 @@ oracle timed on a bounded slice of the same products on the host cores.
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -496,8 +497,9 @@ def main():
     ops = {}
     for name, ts in per_op.items():
         avg = sum(ts) / len(ts)
+        med = statistics.median(ts)
         ops[name] = {"ms": round(avg, 4), "tflops": round(flop / (avg * 1e-3) / 1e12, 2),
-                     "min_ms": round(min(ts), 4), "max_ms": round(max(ts), 4)}
+                     "median_ms": round(med, 4), "min_ms": round(min(ts), 4), "max_ms": round(max(ts), 4)}
     dom = max(ops, key=lambda k: ops[k]["ms"])
     achieved = ops[dom]["tflops"]
     # the kernels the library selects for these shapes (wide kernel, 128x128 tiles):
