@@ -424,19 +424,44 @@ def small_m_leg(dev, steps, warmup, decode_only=False):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
+        # A call of a few microseconds is shorter than the host's launch path:
+        # time `steps` calls replayed from a captured graph (kernels back to
+        # back), and the eager calls beside it.
+        out = fn()
+        run = (lambda: dg.det_gemm_fwd(x, Wq, out=out)) if name == "qkv" and layout == "W[K][N]" else \
+              (lambda: dg.det_gemm_fwd_rhs_transposed(x, Wqt, out=out)) if name == "qkv" else \
+              (lambda: dg.det_gemm_fwd(x, Wl, out=out))
+        ref = out.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(steps):
+                run()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "graph replay differs"
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / steps
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "graph replay differs"
         e0.record()
         for _ in range(steps):
             fn()
         e1.record()
         torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) / steps
+        t_eager = e0.elapsed_time(e1) / steps
+        del graph
         nbytes = (m * k + k * n + m * n) * 2
         gbs = nbytes / (t * 1e-3) / 1e9
         rows.append({"op": name, "weight": layout, "M": m, "K": k, "N": n, "us": round(t * 1e3, 2),
+                     "us_eager_calls": round(t_eager * 1e3, 2),
                      "GB/s": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
                      "kernel": "mfma_decode_kernel" if m <= 16 else "mfma_wide_kernel"})
     return {"workload": "forward products with 1..256 rows: the weight read once per call",
+            "timing": "us: per call, calls replayed from a captured graph; us_eager_calls: "
+                      "back-to-back calls through the binding (host launch path included)",
             "roofline": "hbm, 8000 GB/s", "rows": rows}
 
 

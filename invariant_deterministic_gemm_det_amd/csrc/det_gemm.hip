@@ -189,8 +189,10 @@ bool decode_ok(const Problem &pr) {
 // compute unit keeps a bounded number of line requests in flight), narrower
 // ones spread over more compute units: 64 columns once there are 256 such
 // tiles, 32 columns above 128 such tiles, else 16 (M = 1, K = 4096: N = 6144
-// 18.4 us on 32 columns, 22.4 on 16; N = 151936 222 us on 64 columns, 252 on
-// 32; K = 32768, N = 4096 103 us on 16 columns, 138 on 32).  Otherwise 128x128
+// 13.9 us on 32 columns, 19.9 on 16; N = 151936 215 us on 64 columns, 246 on
+// 32; K = 32768, N = 4096 85 us on 16 columns, 94 on 32).  A K-major Y with an
+// even leaf count is read in whole lines at any width and stays on 16 or 32
+// columns (N = 151936: 202 us on 32 columns, 242 on 64).  Otherwise 128x128
 // wide tiles when they make at least four waves of workgroups over the 256
 // compute units, else the 128x64 wide kernel, two workgroups per compute
 // unit, which keeps more units busy on small and mid-size products (M = 1024
@@ -199,7 +201,8 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     if (g_force_config >= 0)
         return g_force_config;
     if (decode_ok(pr)) {
-        if ((pr.J + 63) / 64 >= 256)
+        const bool line_units = pr.yk && (pr.R / 32) % 2 == 0;  // two-leaf copies read whole lines
+        if (!line_units && (pr.J + 63) / 64 >= 256)
             return 11;
         return (pr.J + 31) / 32 > 128 ? 12 : 10;
     }

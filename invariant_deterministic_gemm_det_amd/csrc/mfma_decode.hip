@@ -50,24 +50,29 @@ namespace {
 constexpr int kDecWaves = 8;   // subtrees of depth 3
 
 // CB column blocks of 16 per workgroup (a tile of 16 * CB columns), MP staged
-// rows of X.
-template <int MP, int CB>
+// rows of X, UL leaves per copy unit (2: a K-major Y read as whole 128-byte
+// lines, two leaves of each column).
+template <int MP, int CB, int UL>
 struct DecodeShape {
-    static constexpr int Y_BYTES = CB * 1024;
-    static constexpr int SLOT = Y_BYTES + MP * 64;        // Y tile, then X tile
+    static constexpr int Y_BYTES = CB * 1024 * UL;
+    static constexpr int SLOT = Y_BYTES + MP * 64 * UL;   // Y tile, then X tile
     // Ring slots per wave.  Measured: deeper rings do not help (the limit is
     // how the copies meet the memory system, not the bytes in flight), while
     // two workgroups per compute unit do: 4 slots for 16- and 32-column
-    // tiles, 2 for 64-column ones.
-    static constexpr int NB = CB == 4 ? 2 : 4;
-    static constexpr int AHEAD = NB - 1;                  // leaves in flight per wave
-    static constexpr int OPS = CB + 1;                    // copies per leaf
+    // tiles, 2 for 64-column ones and for the larger two-leaf units.
+    static constexpr int NB = UL == 2 ? ((CB == 1 && MP == 1) ? 4 : 2) : (CB == 4 ? 2 : 4);
+    static constexpr int AHEAD = NB - 1;                  // units in flight per wave
+    static constexpr int OPS = UL == 2 ? 2 * CB + (MP == 1 ? 1 : 2) : CB + 1;  // copies per unit
     static constexpr int WAVE_BYTES = NB * SLOT;
     static constexpr int LDS = kDecWaves * WAVE_BYTES;
 };
 
 __device__ __forceinline__ int kt_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 __device__ __forceinline__ int nt_row(int r) { return (r * 32) ^ (((r >> 3) & 1) << 7); }
+// K-major two-leaf tiles (128-byte rows: 64 reduction indices): chunk c of row
+// r at c ^ ((r >> 1) & 7), the layout of the direct-to-LDS kernel; the 16 rows
+// of one quarter-wave's ds_read_b128 land on all 64 banks.
+__device__ __forceinline__ int kt128(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 // 128-byte rows (64 columns): chunk c of row r at c ^ key8(r); one half-wave's
 // transposed read (rows r0 .. r0+3 and r0+8 .. r0+11, one aligned chunk pair
 // each) then covers disjoint banks.
@@ -90,11 +95,11 @@ __device__ __forceinline__ void dma16(uint32_t lds, int voff, u32x4 rs) {
                  : "memory", "m0");
 }
 
-// The pending left siblings of one 16 x 16 block of a wave, indexed by the
-// wave-uniform depth: eight named registers behind a switch, so that no
-// per-lane scratch array arises.  A node waits rounded to bf16 (two packed
-// pairs): its parent's add rounds it to bf16 anyway, so storing it rounded
-// changes nothing and halves the registers.
+// The pending left siblings of one 16 x 16 block of a wave: one 16-dword
+// register vector indexed by the wave-uniform depth, which the compiler reads
+// and writes with GPR indexing (no branches, no per-lane scratch array).  A
+// node waits rounded to bf16 (two packed pairs): its parent's add rounds it to
+// bf16 anyway, so storing it rounded changes nothing and halves the registers.
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ u32x2 pack_node(f32x4 v) {
@@ -109,39 +114,23 @@ __device__ __forceinline__ f32x4 unpack_node(u32x2 h) {
 }
 
 struct NodeStack {
-    u32x2 s0, s1, s2, s3, s4, s5, s6, s7;
+    typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
+    u32x16 v;   // pair d in elements 2d, 2d + 1; d is wave-uniform
     __device__ __forceinline__ f32x4 get(int d) const {
-        u32x2 v;
-        switch (d) {
-        case 0: v = s0; break;
-        case 1: v = s1; break;
-        case 2: v = s2; break;
-        case 3: v = s3; break;
-        case 4: v = s4; break;
-        case 5: v = s5; break;
-        case 6: v = s6; break;
-        default: v = s7; break;
-        }
-        return unpack_node(v);
+        const u32x2 h = {v[2 * d], v[2 * d + 1]};
+        return unpack_node(h);
     }
     __device__ __forceinline__ void put(int d, f32x4 x) {
-        const u32x2 v = pack_node(x);
-        switch (d) {
-        case 0: s0 = v; break;
-        case 1: s1 = v; break;
-        case 2: s2 = v; break;
-        case 3: s3 = v; break;
-        case 4: s4 = v; break;
-        case 5: s5 = v; break;
-        case 6: s6 = v; break;
-        default: s7 = v; break;
-        }
+        const u32x2 h = pack_node(x);
+        v[2 * d] = h[0];
+        v[2 * d + 1] = h[1];
     }
 };
 
-template <bool YK, int OUT, int MP, int CB>
+template <bool YK, int OUT, int MP, int CB, int UL>
 __global__ __launch_bounds__(64 * kDecWaves, 4) void mfma_decode_kernel(MfmaParams p) {
-    typedef DecodeShape<MP, CB> S;
+    static_assert(UL == 1 || YK, "two-leaf units only for a K-major Y");
+    typedef DecodeShape<MP, CB, UL> S;
     typedef Frag<1, CB> F;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int lane = threadIdx.x & 63;
@@ -165,11 +154,37 @@ __global__ __launch_bounds__(64 * kDecWaves, 4) void mfma_decode_kernel(MfmaPara
     }
     const int n = hi - lo;
 
-    // Per-lane source offsets (bytes) of the copies of a leaf; the leaf's base
+    // Copy units of this wave: the units holding leaves lo .. hi-1 (with
+    // two-leaf units the first and last may hold a neighbour's leaf, which is
+    // read and skipped).
+    const int ulo = lo / UL, nunits = (hi + UL - 1) / UL - ulo;
+
+    // Per-lane source offsets (bytes) of the copies of a unit; the unit's base
     // address moves in the scalar resource.
-    int yoff[CB];
+    int yoff[CB * UL];
+    int xoff2[2] = {0, 0};
     const uint16_t *ybase;
-    if (YK) {
+    if (UL == 2) {
+        // copy 2q + s: columns 16q + 8s .. +7 of the tile, 128 bytes each
+        const int cp = lane & 7;
+#pragma unroll
+        for (int q = 0; q < CB; ++q)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int row = 8 * h + (lane >> 3);            // column within the block
+                const int c = cp ^ ((row >> 1) & 7);
+                const int col = j0 + 16 * q + row < p.J ? j0 + 16 * q + row : p.J - 1;
+                yoff[q * UL + h] = (int)(((int64_t)(col - j0) * p.ldy + 8 * c) * 2);
+            }
+        ybase = p.y + (int64_t)j0 * p.ldy;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {   // X rows 8h .. 8h+7 (MP = 16), or lanes 0..7 of row 0
+            const int row = MP == 1 ? 0 : 8 * h + (lane >> 3);
+            const int c = MP == 1 ? lane : (cp ^ ((row >> 1) & 7));
+            const int rr = row < p.I ? row : p.I - 1;
+            xoff2[h] = (int)(((int64_t)rr * p.ldx + 8 * c) * 2);
+        }
+    } else if (YK) {
         // copy q: columns 16q .. 16q+15 of the tile, K-major slot layout
         const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
 #pragma unroll
@@ -216,7 +231,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 4) void mfma_decode_kernel(MfmaPara
         const int row = r < p.I ? r : p.I - 1;
         xoff = (int)(((int64_t)row * p.ldx + 8 * c) * 2);
     }
-    const int64_t ystep = YK ? 32 : (int64_t)32 * p.ldy;  // elements per leaf
+    const int64_t ystep = YK ? 32 * UL : (int64_t)32 * p.ldy;  // elements per unit
 
     // Fragment read offsets within a slot.
     const int i16 = lane & 15, G = lane >> 4;
@@ -248,55 +263,84 @@ __global__ __launch_bounds__(64 * kDecWaves, 4) void mfma_decode_kernel(MfmaPara
         }
     }
 
+    int xp[2], yp[CB][2];   // two-leaf units: leaf h of the unit
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        xp[h] = S::Y_BYTES + (MP == 1 ? (4 * h + G) * 16 : kt128(i16, 4 * h + G));
+#pragma unroll
+        for (int q = 0; q < CB; ++q)
+            yp[q][h] = q * 2048 + kt128(i16, 4 * h + G);
+    }
+
     char *ring = smem + wave * S::WAVE_BYTES;
     const uint32_t ring_lds =
         (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char *)ring);
 
-    auto issue = [&](int t) {  // local leaf t into slot t % NB
-        const int leaf = lo + t;
-        const uint32_t slot = ring_lds + (uint32_t)((t & (S::NB - 1)) * S::SLOT);
-        const u32x4 rs = rsrc_at(ybase + (int64_t)leaf * ystep);
+    auto issue = [&](int u) {  // local unit u into slot u % NB
+        const int unit = ulo + u;
+        const uint32_t slot = ring_lds + (uint32_t)((u & (S::NB - 1)) * S::SLOT);
+        const u32x4 rs = rsrc_at(ybase + (int64_t)unit * ystep);
+        const u32x4 xs = rsrc_at(p.x + (int64_t)unit * 32 * UL);
+        if (UL == 2) {
 #pragma unroll
-        for (int q = 0; q < CB; ++q)
-            dma16(slot + q * 1024, yoff[q], rs);
-        if (MP == 1) {
-            if (lane < 4)
-                dma16(slot + S::Y_BYTES, xoff, rsrc_at(p.x + (int64_t)leaf * 32));
+            for (int e = 0; e < 2 * CB; ++e)
+                dma16(slot + e * 1024, yoff[e], rs);
+            if (MP == 1) {
+                if (lane < 8)
+                    dma16(slot + S::Y_BYTES, xoff2[0], xs);
+            } else {
+                dma16(slot + S::Y_BYTES, xoff2[0], xs);
+                dma16(slot + S::Y_BYTES + 1024, xoff2[1], xs);
+            }
         } else {
-            dma16(slot + S::Y_BYTES, xoff, rsrc_at(p.x + (int64_t)leaf * 32));
+#pragma unroll
+            for (int q = 0; q < CB; ++q)
+                dma16(slot + q * 1024, yoff[q], rs);
+            if (MP == 1) {
+                if (lane < 4)
+                    dma16(slot + S::Y_BYTES, xoff, xs);
+            } else {
+                dma16(slot + S::Y_BYTES, xoff, xs);
+            }
         }
     };
 
-    const int pre = n < S::AHEAD ? n : S::AHEAD;
-    for (int t = 0; t < pre; ++t)
-        issue(t);
+    const int pre = nunits < S::AHEAD ? nunits : S::AHEAD;
+    for (int u = 0; u < pre; ++u)
+        issue(u);
 
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     F fz;
 #pragma unroll
     for (int q = 0; q < CB; ++q)
         fz.v[0][q] = zero;
-    const u32x2 z2 = {0u, 0u};
     NodeStack st[CB];
 #pragma unroll
     for (int q = 0; q < CB; ++q)
-        st[q] = NodeStack{z2, z2, z2, z2, z2, z2, z2, z2};
+        st[q].v = 0u;
     int sp = 0;
     F root = fz;
-    for (int t = 0; t < n; ++t) {
-        if (t + S::AHEAD < n) {
-            issue(t + S::AHEAD);
+    for (int u = 0; u < nunits; ++u) {
+        if (u + S::AHEAD < nunits) {
+            issue(u + S::AHEAD);
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(S::OPS * S::AHEAD) : "memory");
         } else {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
-        const char *slot = ring + (t & (S::NB - 1)) * S::SLOT;
-        const bf16x8 fx = *reinterpret_cast<const bf16x8 *>(slot + xrd);
+        const char *slot = ring + (u & (S::NB - 1)) * S::SLOT;
+#pragma unroll
+      for (int h = 0; h < UL; ++h) {
+        const int t = (ulo + u) * UL + h - lo;   // local leaf
+        if (t < 0 || t >= n)
+            continue;                            // a neighbour's leaf of a two-leaf unit
+        const bf16x8 fx = *reinterpret_cast<const bf16x8 *>(slot + (UL == 2 ? xp[h] : xrd));
         F cur;
 #pragma unroll
         for (int q = 0; q < CB; ++q) {
             bf16x8 fy;
-            if (YK) {
+            if (UL == 2) {
+                fy = *reinterpret_cast<const bf16x8 *>(slot + yp[q][h]);
+            } else if (YK) {
                 fy = *reinterpret_cast<const bf16x8 *>(slot + yrd[q][0]);
             } else {
                 const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(slot + yrd[q][0]));
@@ -322,6 +366,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 4) void mfma_decode_kernel(MfmaPara
         } else {
             root = cur;
         }
+      }
     }
 
     // The eight subtree roots meet in LDS, each in its wave's own ring (the
@@ -359,10 +404,10 @@ __global__ __launch_bounds__(64 * kDecWaves, 4) void mfma_decode_kernel(MfmaPara
     }
 }
 
-template <bool YK, int OUT, int MP, int CB>
+template <bool YK, int OUT, int MP, int CB, int UL>
 hipError_t launch_decode_one(const MfmaParams &p, hipStream_t st) {
-    typedef DecodeShape<MP, CB> S;
-    const void *fn = reinterpret_cast<const void *>(&mfma_decode_kernel<YK, OUT, MP, CB>);
+    typedef DecodeShape<MP, CB, UL> S;
+    const void *fn = reinterpret_cast<const void *>(&mfma_decode_kernel<YK, OUT, MP, CB, UL>);
     static int max_dynamic = -1;
     if (max_dynamic < 0) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
@@ -373,14 +418,26 @@ hipError_t launch_decode_one(const MfmaParams &p, hipStream_t st) {
     const int64_t tiles = (p.J + 16 * CB - 1) / (16 * CB);
     MfmaParams q = p;
     q.tiles_j = (int32_t)tiles;
-    hipLaunchKernelGGL((mfma_decode_kernel<YK, OUT, MP, CB>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((mfma_decode_kernel<YK, OUT, MP, CB, UL>), dim3((unsigned)tiles),
                        dim3(64 * kDecWaves), S::LDS, st, q);
     return hipGetLastError();
 }
 
+// A K-major Y with an even leaf count is copied in two-leaf units (whole
+// 128-byte lines of each column), on 16- and 32-column tiles (64-column
+// tiles would not fit the unit's registers).
+template <bool YK, int OUT, int MP, int CB>
+hipError_t launch_decode_units(const MfmaParams &p, hipStream_t st) {
+    if constexpr (YK && CB <= 2) {
+        if (p.L % 2 == 0)
+            return launch_decode_one<YK, OUT, MP, CB, 2>(p, st);
+    }
+    return launch_decode_one<YK, OUT, MP, CB, 1>(p, st);
+}
+
 template <bool YK, int OUT, int CB>
 hipError_t launch_decode_rows(const MfmaParams &p, hipStream_t st) {
-    return p.I == 1 ? launch_decode_one<YK, OUT, 1, CB>(p, st) : launch_decode_one<YK, OUT, 16, CB>(p, st);
+    return p.I == 1 ? launch_decode_units<YK, OUT, 1, CB>(p, st) : launch_decode_units<YK, OUT, 16, CB>(p, st);
 }
 
 template <bool YK, int OUT>

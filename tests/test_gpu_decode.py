@@ -57,10 +57,13 @@ def _as_bits(t):
     return bits(t)
 
 
-# M, N, K: leaf counts 8 (one leaf per wave), 9, 128, 130, 1000 and 1024 (the
-# deepest per-wave trees); N ragged against the 16-column blocks.
+# M, N, K: leaf counts 8 (one leaf per wave), 9, 128, 129, 130, 1000 and 1024
+# (the deepest per-wave trees); N ragged against the 16-column blocks.  A
+# K-major Y with an even leaf count is copied two leaves at a time (waves whose
+# range starts or ends inside such a unit: L = 130); odd counts one at a time.
 SHAPES = [(1, 6144, 4096), (16, 6144, 4096), (5, 200, 4096), (3, 136, 288), (1, 64, 256),
-          (2, 48, 32768), (16, 40, 4160), (7, 24, 32000), (1, 8, 1024)]
+          (2, 48, 32768), (16, 40, 4160), (7, 24, 32000), (1, 8, 1024), (2, 64, 4128),
+          (1, 72, 4128)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
