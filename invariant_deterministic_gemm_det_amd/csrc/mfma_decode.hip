@@ -47,24 +47,25 @@ namespace detgemm {
 
 namespace {
 
-constexpr int kDecWaves = 8;   // subtrees of depth 3
-
 // CB column blocks of 16 per workgroup (a tile of 16 * CB columns), MP staged
 // rows of X, UL leaves per copy unit (2: a K-major Y read as whole 128-byte
-// lines, two leaves of each column).
-template <int MP, int CB, int UL>
+// lines, two leaves of each column), W waves (one subtree each: depth 3 or 4).
+template <int MP, int CB, int UL, int W>
 struct DecodeShape {
     static constexpr int Y_BYTES = CB * 1024 * UL;
     static constexpr int SLOT = Y_BYTES + MP * 64 * UL;   // Y tile, then X tile
     // Ring slots per wave.  Measured: deeper rings do not help (the limit is
     // how the copies meet the memory system, not the bytes in flight), while
     // two workgroups per compute unit do: 4 slots for 16- and 32-column
-    // tiles, 2 for 64-column ones and for the larger two-leaf units.
-    static constexpr int NB = UL == 2 ? ((CB == 1 && MP == 1) ? 4 : 2) : (CB == 4 ? 2 : 4);
+    // tiles, 2 for 64-column ones and for the larger two-leaf units; with 16
+    // waves, as many as the LDS holds (at least 2).
+    static constexpr int NB0 = UL == 2 ? ((CB == 1 && MP == 1) ? 4 : 2) : (CB == 4 ? 2 : 4);
+    static constexpr int NB = (NB0 > 2 && W * NB0 * SLOT > 160 * 1024) ? NB0 / 2 : NB0;
     static constexpr int AHEAD = NB - 1;                  // units in flight per wave
     static constexpr int OPS = UL == 2 ? 2 * CB + (MP == 1 ? 1 : 2) : CB + 1;  // copies per unit
     static constexpr int WAVE_BYTES = NB * SLOT;
-    static constexpr int LDS = kDecWaves * WAVE_BYTES;
+    static constexpr int LDS = W * WAVE_BYTES;
+    static constexpr bool kFits = LDS <= 160 * 1024;
 };
 
 __device__ __forceinline__ int kt_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
@@ -127,10 +128,21 @@ struct NodeStack {
     }
 };
 
-template <bool YK, int OUT, int MP, int CB, int UL>
-__global__ __launch_bounds__(64 * kDecWaves, 4) void mfma_decode_kernel(MfmaParams p) {
+// Root of the W subtree roots in the order of the top log2(W) levels.
+template <int LO, int HI>
+__device__ __forceinline__ f32x4 top_levels(const f32x4 *r) {
+    if constexpr (HI - LO == 1)
+        return r[LO];
+    else
+        return merge4(top_levels<LO, (LO + HI) / 2>(r), top_levels<(LO + HI) / 2, HI>(r));
+}
+
+template <bool YK, int OUT, int MP, int CB, int UL, int W>
+__global__ __launch_bounds__(64 * W, W == 16 ? 2 : 4) void mfma_decode_kernel(MfmaParams p) {
     static_assert(UL == 1 || YK, "two-leaf units only for a K-major Y");
-    typedef DecodeShape<MP, CB, UL> S;
+    static_assert(W == 8 || W == 16, "subtrees of depth 3 or 4");
+    typedef DecodeShape<MP, CB, UL, W> S;
+    static_assert(S::kFits, "the rings fit the LDS");
     typedef Frag<1, CB> F;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int lane = threadIdx.x & 63;
@@ -142,10 +154,11 @@ __global__ __launch_bounds__(64 * kDecWaves, 4) void mfma_decode_kernel(MfmaPara
     const int tile = x * q8 + (x < rem ? x : rem) + (b >> 3);
     const int j0 = tile * 16 * CB;
 
-    // Leaf range of this wave: node `wave` at depth 3 of the mid-split tree.
+    // Leaf range of this wave: node `wave` at depth log2(W) of the mid-split
+    // tree.
     int lo = 0, hi = p.L;
 #pragma unroll
-    for (int bit = 2; bit >= 0; --bit) {
+    for (int bit = (W == 16 ? 3 : 2); bit >= 0; --bit) {
         const int mid = lo + (hi - lo) / 2;
         if ((wave >> bit) & 1)
             lo = mid;
@@ -377,12 +390,11 @@ __global__ __launch_bounds__(64 * kDecWaves, 4) void mfma_decode_kernel(MfmaPara
     __syncthreads();
     if (wave >= CB)
         return;
-    f32x4 r[kDecWaves];
+    f32x4 r[W];
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w)
+    for (int w = 0; w < W; ++w)
         r[w] = *reinterpret_cast<const f32x4 *>(smem + w * S::WAVE_BYTES + (wave * 64 + lane) * 16);
-    const f32x4 top = merge4(merge4(merge4(r[0], r[1]), merge4(r[2], r[3])),
-                             merge4(merge4(r[4], r[5]), merge4(r[6], r[7])));
+    const f32x4 top = top_levels<0, W>(r);
 
     // Lane 16g + c holds rows 4g .. 4g+3 of column c of the block.  A zero
     // root is stored as +0.
@@ -404,10 +416,10 @@ __global__ __launch_bounds__(64 * kDecWaves, 4) void mfma_decode_kernel(MfmaPara
     }
 }
 
-template <bool YK, int OUT, int MP, int CB, int UL>
+template <bool YK, int OUT, int MP, int CB, int UL, int W>
 hipError_t launch_decode_one(const MfmaParams &p, hipStream_t st) {
-    typedef DecodeShape<MP, CB, UL> S;
-    const void *fn = reinterpret_cast<const void *>(&mfma_decode_kernel<YK, OUT, MP, CB, UL>);
+    typedef DecodeShape<MP, CB, UL, W> S;
+    const void *fn = reinterpret_cast<const void *>(&mfma_decode_kernel<YK, OUT, MP, CB, UL, W>);
     static int max_dynamic = -1;
     if (max_dynamic < 0) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
@@ -418,9 +430,22 @@ hipError_t launch_decode_one(const MfmaParams &p, hipStream_t st) {
     const int64_t tiles = (p.J + 16 * CB - 1) / (16 * CB);
     MfmaParams q = p;
     q.tiles_j = (int32_t)tiles;
-    hipLaunchKernelGGL((mfma_decode_kernel<YK, OUT, MP, CB, UL>), dim3((unsigned)tiles),
-                       dim3(64 * kDecWaves), S::LDS, st, q);
+    hipLaunchKernelGGL((mfma_decode_kernel<YK, OUT, MP, CB, UL, W>), dim3((unsigned)tiles),
+                       dim3(64 * W), S::LDS, st, q);
     return hipGetLastError();
+}
+
+// When the tiles make at most one round over the 256 compute units, the
+// chain of leaves of each wave sets the time: 16 waves (subtrees of depth 4,
+// half the leaves each) when there are at least 16 leaves and the rings fit.
+template <bool YK, int OUT, int MP, int CB, int UL>
+hipError_t launch_decode_waves(const MfmaParams &p, hipStream_t st) {
+    if constexpr (CB <= 2 && DecodeShape<MP, CB, UL, 16>::kFits) {
+        const int64_t tiles = (p.J + 16 * CB - 1) / (16 * CB);
+        if (p.L >= 16 && tiles <= 256)
+            return launch_decode_one<YK, OUT, MP, CB, UL, 16>(p, st);
+    }
+    return launch_decode_one<YK, OUT, MP, CB, UL, 8>(p, st);
 }
 
 // A K-major Y with an even leaf count is copied in two-leaf units (whole
@@ -430,9 +455,9 @@ template <bool YK, int OUT, int MP, int CB>
 hipError_t launch_decode_units(const MfmaParams &p, hipStream_t st) {
     if constexpr (YK && CB <= 2) {
         if (p.L % 2 == 0)
-            return launch_decode_one<YK, OUT, MP, CB, 2>(p, st);
+            return launch_decode_waves<YK, OUT, MP, CB, 2>(p, st);
     }
-    return launch_decode_one<YK, OUT, MP, CB, 1>(p, st);
+    return launch_decode_waves<YK, OUT, MP, CB, 1>(p, st);
 }
 
 template <bool YK, int OUT, int CB>
