@@ -254,6 +254,31 @@ def fingerprint_leg(dev, steps, warmup, with_cpu):
 NORM_R, NORM_H = 8192, 4096
 
 
+def graph_time(fn, out, steps):
+    """Per-call time of `fn` (which writes `out`) from `steps` calls replayed
+    back to back out of a captured graph: the GPU time of calls shorter than
+    the host's launch path.  Every replay must reproduce the eager bits."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.uint8), ref.view(torch.uint8)), "graph replay differs"
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.uint8), ref.view(torch.uint8)), "graph replay differs"
+    del graph
+    return e0.elapsed_time(e1) / steps
+
+
 def rmsnorm_leg(dev, steps, warmup, with_cpu, decode=True):
     """Batch-invariant RMSNorm (det_norm.h) over 8192 token rows of width 4096
     (the MLP input of the workloads), and a 64-row decode batch."""
@@ -282,11 +307,12 @@ def rmsnorm_leg(dev, steps, warmup, with_cpu, decode=True):
         return sum(t) / len(t)
 
     t_full = timed(lambda: dg.det_rmsnorm(x, w, out=y, rstd=r))
-    t_dec = timed(lambda: dg.det_rmsnorm(x[:64], w, out=y[:64], rstd=r[:64])) if decode else 0.0
+    t_dec = graph_time(lambda: dg.det_rmsnorm(x[:64], w, out=y[:64], rstd=r[:64]), y[:64], steps) \
+        if decode else 0.0
     nbytes = NORM_R * NORM_H * 4 + NORM_H * 2 + NORM_R * 4
     gbs = nbytes / (t_full * 1e-3) / 1e9
     out = {"workload": "RMSNorm of 8192 x 4096 bf16 rows (read x, write y and rstd); "
-                       "decode: 64 rows",
+                       "decode: 64 rows, per call from graph replays of back-to-back calls",
            "ms": round(t_full, 4), "GB/s": round(gbs, 1), "decode_64_rows_us": round(t_dec * 1e3, 2),
            "roofline": {"bound": "hbm", "kernel": "rmsnorm_kernel (8192 x 4096)",
                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -425,34 +451,19 @@ def small_m_leg(dev, steps, warmup, decode_only=False):
             fn()
         torch.cuda.synchronize()
         # A call of a few microseconds is shorter than the host's launch path:
-        # time `steps` calls replayed from a captured graph (kernels back to
-        # back), and the eager calls beside it.
+        # time calls replayed from a captured graph, and the eager calls beside it.
         out = fn()
         run = (lambda: dg.det_gemm_fwd(x, Wq, out=out)) if name == "qkv" and layout == "W[K][N]" else \
               (lambda: dg.det_gemm_fwd_rhs_transposed(x, Wqt, out=out)) if name == "qkv" else \
               (lambda: dg.det_gemm_fwd(x, Wl, out=out))
-        ref = out.clone()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _ in range(steps):
-                run()
-        graph.replay()
-        torch.cuda.synchronize()
-        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "graph replay differs"
+        t = graph_time(run, out, steps)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        graph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) / steps
-        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "graph replay differs"
         e0.record()
         for _ in range(steps):
             fn()
         e1.record()
         torch.cuda.synchronize()
         t_eager = e0.elapsed_time(e1) / steps
-        del graph
         nbytes = (m * k + k * n + m * n) * 2
         gbs = nbytes / (t * 1e-3) / 1e9
         rows.append({"op": name, "weight": layout, "M": m, "K": k, "N": n, "us": round(t * 1e3, 2),
