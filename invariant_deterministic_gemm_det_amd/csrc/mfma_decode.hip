@@ -8,39 +8,44 @@
 // product has only N / 16 output blocks: 384 at N = 6144, too few to keep 256
 // compute units streaming the weights if each block walks the whole reduction
 // alone.  Here the tree itself supplies the parallelism inside a workgroup:
-//   * a workgroup owns one 16 x 16 output block (all rows, 16 columns) and
-//     has 8 waves; wave w evaluates the subtree rooted at node w of depth 3 of
-//     the mid-split tree over the L leaves (L >= 8, so every such node holds at
-//     least one leaf), i.e. a contiguous leaf range of about L / 8 leaves;
+//   * a workgroup owns a 16 x 16 CB output tile (all rows, 16, 32 or 64
+//     columns) and has W = 8 or 16 waves; wave w evaluates the subtree rooted
+//     at node w of depth log2(W) of the mid-split tree over the L leaves
+//     (L >= W, so every such node holds at least one leaf), a contiguous range
+//     of about L / W leaves;
 //   * a wave walks its leaves in ascending order with the streaming post-order
 //     (after leaf t, as many adds as there are inner nodes whose range ends at
 //     t + 1), pending left siblings in registers;
-//   * the 8 subtree roots meet in LDS and the first wave adds them in the
-//     order of the three top levels: ((0+1)+(2+3))+((4+5)+(6+7)).
+//   * the W subtree roots meet in LDS and the first waves (one per 16-column
+//     block) add them in the order of the top log2(W) levels.
 // A leaf is the same v_mfma_f32_16x16x32_bf16 with the same lane assignment as
 // in the other kernels (lane l: X row l % 16 and Y column l % 16 at reduction
 // indices 8(l / 16) .. +7); a tree add is the same round-both-then-add-in-fp32
 // VALU add.  So the bits are those of every other configuration.
 //
 // Data movement, per wave and without workgroup barriers: a private ring of
-// NB leaf slots in LDS, filled by buffer_load_dwordx4 ... lds (16 bytes per
-// lane at M0 + 16 * lane) NB - 1 leaves ahead, drained with s_waitcnt vmcnt.
-//   * Y, reduction index contiguous (the weight stored [N][K]): the slot holds
-//     16 columns x 32 indices, 64-byte rows, 16-byte chunk c of row r at chunk
-//     c ^ ((r >> 2) & 3): the 16 rows of one quarter-wave's ds_read_b128 land
-//     on all 64 banks.
-//   * Y, column index contiguous (the weight stored [K][N]): the slot holds
-//     32 indices x 16 CB columns.  16 columns: 32-byte rows, rows with bit 3
-//     set swap 128-byte halves; 32 columns: 64-byte rows, rows with bit 3 set
-//     swap 32-byte halves; 64 columns: 128-byte rows, 16-byte chunks XORed
-//     as in the direct-to-LDS kernel.  Each way the two 16-lane groups of a
-//     half-wave ds_read_b64_tr_b16 (indices r0 .. r0+3 and r0+8 .. r0+11)
-//     use disjoint banks.
+// NB unit slots in LDS (a unit: one leaf, or two leaves of a K-major Y),
+// filled by buffer_load_dwordx4 ... lds (16 bytes per lane at M0 + 16 * lane)
+// NB - 1 units ahead, drained with s_waitcnt vmcnt.
+//   * Y, reduction index contiguous (the weight stored [N][K]), two-leaf
+//     units (even L): 128-byte rows (one whole cache line per column), chunk c
+//     of row r at c ^ ((r >> 1) & 7); one-leaf units: 64-byte rows, chunk c of
+//     row r at c ^ ((r >> 2) & 3).  Either way the 16 rows of one
+//     quarter-wave's ds_read_b128 land on all 64 banks.
+//   * Y, column index contiguous (the weight stored [K][N]): 32 indices x 16 CB
+//     columns.  16 columns: 32-byte rows, rows with bit 3 set swap 128-byte
+//     halves; 32 columns: 64-byte rows, rows with bit 3 set swap 32-byte
+//     halves; 64 columns: 128-byte rows, 16-byte chunks XORed as in the
+//     direct-to-LDS kernel.  Each way the two 16-lane groups of a half-wave
+//     ds_read_b64_tr_b16 (indices r0 .. r0+3 and r0+8 .. r0+11) use disjoint
+//     banks.
 //   * X: the MP rows the product needs (MP = 1 for a single row, else 16, rows
-//     past the last clamped to it) in the K-major layout above.
-// Workgroup b runs on XCD b mod 8; consecutive column blocks go to the same
-// XCD, so the workgroups that share a 128-byte line of a [K][N] weight share
-// that XCD's L2.
+//     past the last clamped to it) in the K-major layout of the unit.
+// A compute unit serves these copies at a bounded rate of cache-line requests,
+// so wider tiles (more of each requested line used) stream faster and narrower
+// ones reach more compute units; the host picks the width from the tile count.
+// Workgroup b runs on XCD b mod 8; consecutive tiles go to the same XCD, so the
+// workgroups that share a 128-byte line of a [K][N] weight share that XCD's L2.
 #include "mfma_launch.h"
 
 namespace detgemm {
@@ -87,7 +92,7 @@ __device__ __forceinline__ u32x4 rsrc_at(const void *base) {
 
 // One 1 KB (or, with fewer active lanes, smaller) LDS DMA.  Waits for the
 // wave's outstanding LDS reads first: the slot being refilled was read by the
-// previous leaf.  One wait state separates the M0 write from the load.
+// previous unit.  One wait state separates the M0 write from the load.
 __device__ __forceinline__ void dma16(uint32_t lds, int voff, u32x4 rs) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\t"
                  "buffer_load_dwordx4 %1, %2, 0 offen lds"
