@@ -158,3 +158,41 @@ def test_decode_rejects_unsupported(dev, case):
     auto = bits(dg.det_gemm_fwd(A, B))
     ref = bits(_forced(GENERAL_CFG, lambda: dg.det_gemm_fwd(A, B)))
     assert np.array_equal(auto, ref)
+
+
+def test_decode_zero_products_give_positive_zero(dev):
+    """Leaves whose products are all -0 (or +0) are +0 in the definition (the
+    fp32 sum starts at +0), and so is every node above them: the decode
+    kernel stores +0."""
+    say("decode kernel, signed-zero leaves")
+    A = torch.zeros((3, 512), dtype=torch.bfloat16)
+    A[1] = -0.0
+    B = -torch.ones((512, 48), dtype=torch.bfloat16)
+    for cfg in DECODE_CFGS:
+        out = bits(_forced(cfg, lambda: dg.det_gemm_fwd(A.to(dev), B.to(dev))))
+        assert (out == 0).all(), cfg
+        out_t = bits(_forced(cfg, lambda: dg.det_gemm_fwd_rhs_transposed(
+            A.to(dev), B.t().contiguous().to(dev))))
+        assert (out_t == 0).all(), cfg
+
+
+@pytest.mark.parametrize("M,K", [(1, 4096), (5, 1024), (16, 4128)])
+def test_decode_nonfinite_inputs(dev, M, K):
+    """Inf and NaN in X or the weight: every decode configuration gives the
+    general kernel's bits (both layouts of the weight)."""
+    say("decode kernel, non-finite inputs", M, K)
+    N = 200
+    A = W.randn_bf16((M, K), 1.0, 1500 + K)
+    B = W.randn_bf16((K, N), 0.02, 1501 + K)
+    A[0, 17] = float("inf")
+    A[M - 1, K - 3] = float("nan")
+    B[40, 33] = float("-inf")
+    B[K // 2, 150] = float("nan")
+    Ad, Bd, Btd = A.to(dev), B.to(dev), B.t().contiguous().to(dev)
+    ref = bits(_forced(GENERAL_CFG, lambda: dg.det_gemm_fwd(Ad, Bd)))
+    ref_t = bits(_forced(GENERAL_CFG, lambda: dg.det_gemm_fwd_rhs_transposed(Ad, Btd)))
+    assert np.array_equal(ref, ref_t)
+    for cfg in DECODE_CFGS:
+        assert np.array_equal(bits(_forced(cfg, lambda: dg.det_gemm_fwd(Ad, Bd))), ref), cfg
+        assert np.array_equal(bits(_forced(cfg, lambda: dg.det_gemm_fwd_rhs_transposed(Ad, Btd))),
+                              ref), cfg
