@@ -126,6 +126,9 @@ def test_decode_rows_invariant_to_batch(dev):
     for m in (2, 9):
         cm = bits(dg.det_gemm_fwd(X16[:m].contiguous(), B))
         assert np.array_equal(cm, c16[:m]), m
+    for m in (17, 24, 32):   # two decode launches over 16-row blocks
+        cm = bits(dg.det_gemm_fwd(big[100:100 + m].contiguous(), B))
+        assert np.array_equal(cm, c256[100:100 + m]), m
 
 
 def test_decode_lm_head_row(dev):
@@ -196,3 +199,16 @@ def test_decode_nonfinite_inputs(dev, M, K):
         assert np.array_equal(bits(_forced(cfg, lambda: dg.det_gemm_fwd(Ad, Bd))), ref), cfg
         assert np.array_equal(bits(_forced(cfg, lambda: dg.det_gemm_fwd_rhs_transposed(Ad, Btd))),
                               ref), cfg
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 200, 4096), (24, 6144, 4096), (32, 136, 1024), (20, 48, 4128)])
+def test_two_row_blocks_match_general_kernel(dev, M, N, K):
+    """17 to 32 rows run as two decode launches over 16-row blocks: the four
+    X-row products equal the general kernel's bits."""
+    say("17..32 rows as two decode launches vs general kernel", M, N, K)
+    A = W.randn_bf16((M, K), 1.0, 1600 + M + K).to(dev)
+    B = W.randn_bf16((K, N), 0.02, 1601 + N + K).to(dev)
+    dC = W.randn_bf16((M, N), 1.0, 1602 + N).to(dev)
+    for op, f in _ops(A, B, dC).items():
+        ref = _as_bits(_forced(GENERAL_CFG, f))
+        assert np.array_equal(_as_bits(f()), ref), op
