@@ -172,20 +172,23 @@ bool wide_ok(const Problem &pr, const TreeSel &t, const TileCfg &c, int &up) {
     return c.lds_bytes(up) <= kLdsMax;  // the wide kernels use no static LDS
 }
 
-// The decode kernel (configuration 10): X K-major with at most 16 rows, bf16
-// or fp32 output, whole leaves, at least 8 and at most 1024 of them (one leaf
-// or more per wave, at most 8 pending left siblings per wave), 16-byte aligned
-// rows and, for a [K][N] operand Y, whole 8-column chunks.
+// The decode kernels (configurations 10 to 12): X K-major with at most 64
+// rows (at most 32 on 32-column tiles, 16 on 64-column tiles), bf16 or fp32
+// output, whole leaves, at
+// least 8 and at most 1024 of them (one leaf or more per wave, at most 8
+// pending left siblings per wave), 16-byte aligned rows and, for a [K][N]
+// operand Y, whole 8-column chunks.
 bool decode_ok(const Problem &pr) {
     const int64_t L = pr.R / 32;
-    return pr.xk && (pr.out == OUT_BF16 || pr.out == OUT_F32) && pr.I >= 1 && pr.I <= 16 &&
+    return pr.xk && (pr.out == OUT_BF16 || pr.out == OUT_F32) && pr.I >= 1 && pr.I <= 64 &&
            pr.R % 32 == 0 && L >= 8 && L <= 1024 && aligned16(pr.x, pr.ldx) &&
            aligned16(pr.y, pr.ldy) && (pr.yk || pr.J % 8 == 0);
 }
 
 // Selection (measured on MI355X; every configuration gives the same bits).
-// At most 16 rows: the decode kernel, whose workgroups split the reduction
-// along the tree.  Wider tiles read more of each cache line they request (a
+// At most 64 rows: the decode kernel, whose workgroups split the reduction
+// along the tree (17 to 64 rows as 2 or 4 staged row blocks: M = 32,
+// K = 4096, N = 6144 in 16.6 us instead of 40 on the wide kernel).  Wider tiles read more of each cache line they request (a
 // compute unit keeps a bounded number of line requests in flight), narrower
 // ones spread over more compute units: 64 columns once there are 256 such
 // tiles, 32 columns above 128 such tiles, else 16 (M = 1, K = 4096: N = 6144
@@ -202,9 +205,9 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
         return g_force_config;
     if (decode_ok(pr)) {
         const bool line_units = pr.yk && (pr.R / 32) % 2 == 0;  // two-leaf copies read whole lines
-        if (!line_units && (pr.J + 63) / 64 >= 256)
+        if (!line_units && pr.I <= 16 && (pr.J + 63) / 64 >= 256)
             return 11;
-        return (pr.J + 31) / 32 > 128 ? 12 : 10;
+        return pr.I <= 32 && (pr.J + 31) / 32 > 128 ? 12 : 10;
     }
     int up = 0;
     const int64_t t128 = ((pr.I + 127) / 128) * ((pr.J + 127) / 128);
@@ -234,22 +237,6 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
 }
 
 int run_mfma(const Problem &pr, hipStream_t st) {
-    // 17 to 32 rows: the decode kernel on each 16-row block (a row's bits
-    // depend on its own data only, so the split cannot change them).  Two
-    // such launches stream the weight twice and still beat one wide-kernel
-    // launch (M = 32, K = 4096, N = 6144: 28 us instead of 41).
-    if (g_force_config < 0 && pr.I > 16 && pr.I <= 32) {
-        Problem lo = pr, hi = pr;
-        lo.I = 16;
-        hi.I = pr.I - 16;
-        hi.x = pr.x + 16 * pr.ldx;
-        hi.c = pr.out == OUT_F32 ? static_cast<void *>(static_cast<float *>(pr.c) + 16 * pr.ldc)
-                                 : static_cast<void *>(static_cast<uint16_t *>(pr.c) + 16 * pr.ldc);
-        if (decode_ok(lo) && decode_ok(hi)) {
-            const int rc = run_mfma(lo, st);
-            return rc != DET_GEMM_OK ? rc : run_mfma(hi, st);
-        }
-    }
     MfmaParams p;
     std::memset(&p, 0, sizeof p);
     p.x = pr.x;
@@ -268,7 +255,7 @@ int run_mfma(const Problem &pr, hipStream_t st) {
     const int cfg = pick_config(pr, tree, levels);
     const TileCfg &c = kTileCfgs[cfg];
     if (c.kind == KIND_DECODE) {
-        if (!decode_ok(pr))
+        if (!decode_ok(pr) || pr.I > 64 / c.fn)
             return DET_GEMM_EINVAL;  // a forced decode configuration this problem does not fit
         if ((pr.J + 15) / 16 > kMaxDim)
             return DET_GEMM_EINVAL;

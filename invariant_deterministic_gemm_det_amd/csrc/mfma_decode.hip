@@ -53,12 +53,13 @@ namespace detgemm {
 namespace {
 
 // CB column blocks of 16 per workgroup (a tile of 16 * CB columns), MP staged
-// rows of X, UL leaves per copy unit (2: a K-major Y read as whole 128-byte
+// rows of X (1, 16, 32 or 64: MR = 1, 2 or 4 blocks of 16), UL leaves per copy unit (2: a K-major Y read as whole 128-byte
 // lines, two leaves of each column), W waves (one subtree each: depth 3 or 4).
 template <int MP, int CB, int UL, int W>
 struct DecodeShape {
+    static constexpr int MR = MP >= 16 ? MP / 16 : 1;
     static constexpr int Y_BYTES = CB * 1024 * UL;
-    static constexpr int SLOT = Y_BYTES + MP * 64 * UL;   // Y tile, then X tile
+    static constexpr int SLOT = Y_BYTES + MP * 64 * UL;   // Y tile, then the X blocks
     // Ring slots per wave.  Measured: deeper rings do not help (the limit is
     // how the copies meet the memory system, not the bytes in flight), while
     // two workgroups per compute unit do: 4 slots for 16- and 32-column
@@ -67,10 +68,10 @@ struct DecodeShape {
     static constexpr int NB0 = UL == 2 ? ((CB == 1 && MP == 1) ? 4 : 2) : (CB == 4 ? 2 : 4);
     static constexpr int NB = (NB0 > 2 && W * NB0 * SLOT > 160 * 1024) ? NB0 / 2 : NB0;
     static constexpr int AHEAD = NB - 1;                  // units in flight per wave
-    static constexpr int OPS = UL == 2 ? 2 * CB + (MP == 1 ? 1 : 2) : CB + 1;  // copies per unit
+    static constexpr int OPS = UL == 2 ? 2 * CB + (MP == 1 ? 1 : 2 * MR) : CB + MR;  // copies per unit
     static constexpr int WAVE_BYTES = NB * SLOT;
     static constexpr int LDS = W * WAVE_BYTES;
-    static constexpr bool kFits = LDS <= 160 * 1024;
+    static constexpr bool kFits = LDS <= 160 * 1024 && WAVE_BYTES >= MR * CB * 1024;
 };
 
 __device__ __forceinline__ int kt_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
@@ -148,7 +149,8 @@ __global__ __launch_bounds__(64 * W, W == 16 ? 2 : 4) void mfma_decode_kernel(Mf
     static_assert(W == 8 || W == 16, "subtrees of depth 3 or 4");
     typedef DecodeShape<MP, CB, UL, W> S;
     static_assert(S::kFits, "the rings fit the LDS");
-    typedef Frag<1, CB> F;
+    constexpr int MR = S::MR;
+    typedef Frag<(MP >= 16 ? MP / 16 : 1), CB> F;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(64 * W, W == 16 ? 2 : 4) void mfma_decode_kernel(Mf
     // Per-lane source offsets (bytes) of the copies of a unit; the unit's base
     // address moves in the scalar resource.
     int yoff[CB * UL];
-    int xoff2[2] = {0, 0};
+    int xoff2[MR][2] = {};
     const uint16_t *ybase;
     if (UL == 2) {
         // copy 2q + s: columns 16q + 8s .. +7 of the tile, 128 bytes each
@@ -196,12 +198,14 @@ __global__ __launch_bounds__(64 * W, W == 16 ? 2 : 4) void mfma_decode_kernel(Mf
             }
         ybase = p.y + (int64_t)j0 * p.ldy;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {   // X rows 8h .. 8h+7 (MP = 16), or lanes 0..7 of row 0
-            const int row = MP == 1 ? 0 : 8 * h + (lane >> 3);
-            const int c = MP == 1 ? lane : (cp ^ ((row >> 1) & 7));
-            const int rr = row < p.I ? row : p.I - 1;
-            xoff2[h] = (int)(((int64_t)rr * p.ldx + 8 * c) * 2);
-        }
+        for (int a = 0; a < MR; ++a)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {   // X rows 16a + 8h .. +7, or lanes 0..7 of row 0
+                const int row = MP == 1 ? 0 : 8 * h + (lane >> 3);
+                const int c = MP == 1 ? lane : (cp ^ ((row >> 1) & 7));
+                const int rr = 16 * a + row < p.I ? 16 * a + row : p.I - 1;
+                xoff2[a][h] = (int)(((int64_t)rr * p.ldx + 8 * c) * 2);
+            }
     } else if (YK) {
         // copy q: columns 16q .. 16q+15 of the tile, K-major slot layout
         const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
@@ -243,11 +247,12 @@ __global__ __launch_bounds__(64 * W, W == 16 ? 2 : 4) void mfma_decode_kernel(Mf
         }
         ybase = p.y + j0;
     }
-    int xoff;
-    {
+    int xoff[MR];
+#pragma unroll
+    for (int a = 0; a < MR; ++a) {   // X rows 16a .. 16a+15
         const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
-        const int row = r < p.I ? r : p.I - 1;
-        xoff = (int)(((int64_t)row * p.ldx + 8 * c) * 2);
+        const int row = 16 * a + r < p.I ? 16 * a + r : p.I - 1;
+        xoff[a] = (int)(((int64_t)row * p.ldx + 8 * c) * 2);
     }
     const int64_t ystep = YK ? 32 * UL : (int64_t)32 * p.ldy;  // elements per unit
 
@@ -305,10 +310,13 @@ __global__ __launch_bounds__(64 * W, W == 16 ? 2 : 4) void mfma_decode_kernel(Mf
                 dma16(slot + e * 1024, yoff[e], rs);
             if (MP == 1) {
                 if (lane < 8)
-                    dma16(slot + S::Y_BYTES, xoff2[0], xs);
+                    dma16(slot + S::Y_BYTES, xoff2[0][0], xs);
             } else {
-                dma16(slot + S::Y_BYTES, xoff2[0], xs);
-                dma16(slot + S::Y_BYTES + 1024, xoff2[1], xs);
+#pragma unroll
+                for (int a = 0; a < MR; ++a) {
+                    dma16(slot + S::Y_BYTES + a * 2048, xoff2[a][0], xs);
+                    dma16(slot + S::Y_BYTES + a * 2048 + 1024, xoff2[a][1], xs);
+                }
             }
         } else {
 #pragma unroll
@@ -316,9 +324,11 @@ __global__ __launch_bounds__(64 * W, W == 16 ? 2 : 4) void mfma_decode_kernel(Mf
                 dma16(slot + q * 1024, yoff[q], rs);
             if (MP == 1) {
                 if (lane < 4)
-                    dma16(slot + S::Y_BYTES, xoff, xs);
+                    dma16(slot + S::Y_BYTES, xoff[0], xs);
             } else {
-                dma16(slot + S::Y_BYTES, xoff, xs);
+#pragma unroll
+                for (int a = 0; a < MR; ++a)
+                    dma16(slot + S::Y_BYTES + a * 1024, xoff[a], xs);
             }
         }
     };
@@ -330,12 +340,16 @@ __global__ __launch_bounds__(64 * W, W == 16 ? 2 : 4) void mfma_decode_kernel(Mf
     const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
     F fz;
 #pragma unroll
-    for (int q = 0; q < CB; ++q)
-        fz.v[0][q] = zero;
-    NodeStack st[CB];
+    for (int a = 0; a < MR; ++a)
 #pragma unroll
-    for (int q = 0; q < CB; ++q)
-        st[q].v = 0u;
+        for (int q = 0; q < CB; ++q)
+            fz.v[a][q] = zero;
+    NodeStack st[MR][CB];
+#pragma unroll
+    for (int a = 0; a < MR; ++a)
+#pragma unroll
+        for (int q = 0; q < CB; ++q)
+            st[a][q].v = 0u;
     int sp = 0;
     F root = fz;
     for (int u = 0; u < nunits; ++u) {
@@ -351,7 +365,10 @@ __global__ __launch_bounds__(64 * W, W == 16 ? 2 : 4) void mfma_decode_kernel(Mf
         const int t = (ulo + u) * UL + h - lo;   // local leaf
         if (t < 0 || t >= n)
             continue;                            // a neighbour's leaf of a two-leaf unit
-        const bf16x8 fx = *reinterpret_cast<const bf16x8 *>(slot + (UL == 2 ? xp[h] : xrd));
+        bf16x8 fx[MR];
+#pragma unroll
+        for (int a = 0; a < MR; ++a)
+            fx[a] = *reinterpret_cast<const bf16x8 *>(slot + (UL == 2 ? xp[h] + a * 2048 : xrd + a * 1024));
         F cur;
 #pragma unroll
         for (int q = 0; q < CB; ++q) {
@@ -367,19 +384,25 @@ __global__ __launch_bounds__(64 * W, W == 16 ? 2 : 4) void mfma_decode_kernel(Mf
                 const s16x8 v = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
                 fy = __builtin_bit_cast(bf16x8, v);
             }
-            cur.v[0][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fx, fy, zero, 0, 0, 0);
+#pragma unroll
+            for (int a = 0; a < MR; ++a)
+                cur.v[a][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fx[a], fy, zero, 0, 0, 0);
         }
         const int m = merges_after(t, n);
         for (int k = 0; k < m; ++k) {
             --sp;
 #pragma unroll
-            for (int q = 0; q < CB; ++q)
-                cur.v[0][q] = merge4(st[q].get(sp), cur.v[0][q]);
+            for (int a = 0; a < MR; ++a)
+#pragma unroll
+                for (int q = 0; q < CB; ++q)
+                    cur.v[a][q] = merge4(st[a][q].get(sp), cur.v[a][q]);
         }
         if (t + 1 < n) {
 #pragma unroll
-            for (int q = 0; q < CB; ++q)
-                st[q].put(sp, cur.v[0][q]);
+            for (int a = 0; a < MR; ++a)
+#pragma unroll
+                for (int q = 0; q < CB; ++q)
+                    st[a][q].put(sp, cur.v[a][q]);
             ++sp;
         } else {
             root = cur;
@@ -387,13 +410,16 @@ __global__ __launch_bounds__(64 * W, W == 16 ? 2 : 4) void mfma_decode_kernel(Mf
       }
     }
 
-    // The eight subtree roots meet in LDS, each in its wave's own ring (the
-    // wave's copies and reads are complete); wave q < CB adds block q's.
+    // The W subtree roots meet in LDS, each in its wave's own ring (the
+    // wave's copies and reads are complete); wave b < MR * CB adds the roots
+    // of block b = (row block, column block).
 #pragma unroll
-    for (int q = 0; q < CB; ++q)
-        *reinterpret_cast<f32x4 *>(ring + (q * 64 + lane) * 16) = root.v[0][q];
+    for (int a = 0; a < MR; ++a)
+#pragma unroll
+        for (int q = 0; q < CB; ++q)
+            *reinterpret_cast<f32x4 *>(ring + ((a * CB + q) * 64 + lane) * 16) = root.v[a][q];
     __syncthreads();
-    if (wave >= CB)
+    if (wave >= MR * CB)
         return;
     f32x4 r[W];
 #pragma unroll
@@ -407,10 +433,10 @@ __global__ __launch_bounds__(64 * W, W == 16 ? 2 : 4) void mfma_decode_kernel(Mf
     const uint32_t hi2 = pair_bits(round_pair(top[2], top[3]));
     const uint16_t v4[4] = {(uint16_t)lo2, (uint16_t)(lo2 >> 16), (uint16_t)hi2,
                             (uint16_t)(hi2 >> 16)};
-    const int j = j0 + 16 * wave + i16;
+    const int j = j0 + 16 * (wave % CB) + i16;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-        const int i = 4 * G + v;
+        const int i = 16 * (wave / CB) + 4 * G + v;
         const uint16_t h = (v4[v] & 0x7FFF) ? v4[v] : (uint16_t)0;
         if (i < p.I && j < p.J) {
             if (OUT == OUT_BF16)
@@ -467,7 +493,17 @@ hipError_t launch_decode_units(const MfmaParams &p, hipStream_t st) {
 
 template <bool YK, int OUT, int CB>
 hipError_t launch_decode_rows(const MfmaParams &p, hipStream_t st) {
-    return p.I == 1 ? launch_decode_units<YK, OUT, 1, CB>(p, st) : launch_decode_units<YK, OUT, 16, CB>(p, st);
+    if (p.I == 1)
+        return launch_decode_units<YK, OUT, 1, CB>(p, st);
+    if (p.I <= 16)
+        return launch_decode_units<YK, OUT, 16, CB>(p, st);
+    if constexpr (CB <= 2) {   // 17 to 32 rows: two row blocks
+        if (p.I <= 32)
+            return launch_decode_units<YK, OUT, 32, CB>(p, st);
+    }
+    if constexpr (CB == 1)     // 33 to 64 rows: four row blocks on 16-column tiles
+        return launch_decode_units<YK, OUT, 64, CB>(p, st);
+    return hipErrorInvalidValue;
 }
 
 template <bool YK, int OUT>

@@ -126,7 +126,7 @@ def test_decode_rows_invariant_to_batch(dev):
     for m in (2, 9):
         cm = bits(dg.det_gemm_fwd(X16[:m].contiguous(), B))
         assert np.array_equal(cm, c16[:m]), m
-    for m in (17, 24, 32):   # two decode launches over 16-row blocks
+    for m in (17, 24, 32, 40, 64):   # two or four staged row blocks
         cm = bits(dg.det_gemm_fwd(big[100:100 + m].contiguous(), B))
         assert np.array_equal(cm, c256[100:100 + m]), m
 
@@ -144,12 +144,12 @@ def test_decode_lm_head_row(dev):
             assert np.array_equal(bits(_forced(cfg, lambda: dg.det_gemm_fwd(A[:m], B))), ref), (m, cfg)
 
 
-@pytest.mark.parametrize("case", ["rows17", "leaves7", "ragged_k", "unaligned", "n_not_8"])
+@pytest.mark.parametrize("case", ["rows65", "leaves7", "ragged_k", "unaligned", "n_not_8"])
 def test_decode_rejects_unsupported(dev, case):
     """Forcing configuration 10, 11 or 12 on a problem it does not take is EINVAL;
     the automatic choice runs another kernel with the same bits."""
     say("decode kernel rejects", case)
-    M, N, K = {"rows17": (17, 64, 1024), "leaves7": (4, 64, 224), "ragged_k": (4, 64, 1040 + 8),
+    M, N, K = {"rows65": (65, 64, 1024), "leaves7": (4, 64, 224), "ragged_k": (4, 64, 1040 + 8),
                "unaligned": (4, 64, 1024), "n_not_8": (4, 13, 1024)}[case]
     A = W.randn_bf16((M, K + 8), 1.0, 1400).to(dev)
     A = A[:, 1:K + 1] if case == "unaligned" else A[:, :K].contiguous()
@@ -201,14 +201,27 @@ def test_decode_nonfinite_inputs(dev, M, K):
                               ref), cfg
 
 
-@pytest.mark.parametrize("M,N,K", [(17, 200, 4096), (24, 6144, 4096), (32, 136, 1024), (20, 48, 4128)])
-def test_two_row_blocks_match_general_kernel(dev, M, N, K):
-    """17 to 32 rows run as two decode launches over 16-row blocks: the four
-    X-row products equal the general kernel's bits."""
-    say("17..32 rows as two decode launches vs general kernel", M, N, K)
+@pytest.mark.parametrize("M,N,K", [(17, 200, 4096), (24, 6144, 4096), (32, 136, 1024), (20, 48, 4128),
+                                   (32, 40, 32768), (33, 200, 4096), (48, 6144, 4096), (64, 72, 4128),
+                                   (61, 40, 1024)])
+def test_row_blocks_match_general_kernel(dev, M, N, K):
+    """17 to 64 rows: the decode kernel stages 2 or 4 blocks of 16 rows of X
+    (two blocks on 16- and 32-column tiles, four on 16-column tiles; the other
+    widths refuse).  The four X-row products equal the general kernel's bits."""
+    say("17..64 rows on the decode kernel vs general kernel", M, N, K)
     A = W.randn_bf16((M, K), 1.0, 1600 + M + K).to(dev)
     B = W.randn_bf16((K, N), 0.02, 1601 + N + K).to(dev)
     dC = W.randn_bf16((M, N), 1.0, 1602 + N).to(dev)
     for op, f in _ops(A, B, dC).items():
         ref = _as_bits(_forced(GENERAL_CFG, f))
         assert np.array_equal(_as_bits(f()), ref), op
+        da_fits = op != "da" or (N % 32 == 0 and N // 32 >= 8)
+        for cfg, rows in ((10, 64), (12, 32), (11, 16)):
+            if not da_fits:
+                continue
+            if M <= rows:
+                assert np.array_equal(_as_bits(_forced(cfg, f)), ref), (op, cfg)
+            else:
+                with pytest.raises(dg.DetGemmError) as e:
+                    _forced(cfg, f)
+                assert e.value.code == dg.EINVAL
