@@ -433,11 +433,12 @@ def small_m_leg(dev, steps, warmup, decode_only=False):
     Wqt = Wk.qkv_weight(dev, transposed=True)
     Xl, Wl = Wk.lm_head_inputs(dev, M=256)
     Xq = Wk.randn_bf16((128, Wk.QKV_K), 1.0, 9700, dev)
-    cases = [("qkv", "W[K][N]", 1), ("qkv", "W[K][N]", 16), ("qkv", "W[K][N]", 128),
+    cases = [("qkv", "W[K][N]", 1), ("qkv", "W[K][N]", 16), ("qkv", "W[K][N]", 32),
+             ("qkv", "W[K][N]", 64), ("qkv", "W[K][N]", 128),
              ("qkv", "W[N][K]", 1), ("qkv", "W[N][K]", 16), ("lm_head", "W[K][N]", 1),
              ("lm_head", "W[K][N]", 256)]
     if decode_only:  # the rows on the decode kernel, one kernel instance each
-        cases = [c for c in cases if c[2] <= 16]
+        cases = [c for c in cases if c[2] <= 64]
     rows = []
     for name, layout, m in cases:
         if name == "qkv":
@@ -469,8 +470,9 @@ def small_m_leg(dev, steps, warmup, decode_only=False):
         rows.append({"op": name, "weight": layout, "M": m, "K": k, "N": n, "us": round(t * 1e3, 2),
                      "us_eager_calls": round(t_eager * 1e3, 2),
                      "GB/s": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
-                     "kernel": "mfma_decode_kernel" if m <= 16 else "mfma_wide_kernel"})
-    return {"workload": "forward products with 1..256 rows: the weight read once per call",
+                     "kernel": "mfma_decode_kernel" if m <= 64 else "mfma_wide_kernel"})
+    return {"workload": "forward products with 1..256 rows: the weight read once per call "
+                        "(at most 64 rows on the decode kernel)",
             "timing": "us: per call, calls replayed from a captured graph; us_eager_calls: "
                       "back-to-back calls through the binding (host launch path included)",
             "roofline": "hbm, 8000 GB/s", "rows": rows}
