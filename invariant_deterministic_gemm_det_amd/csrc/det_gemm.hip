@@ -173,8 +173,7 @@ bool wide_ok(const Problem &pr, const TreeSel &t, const TileCfg &c, int &up) {
 }
 
 // The decode kernels (configurations 10 to 12): X K-major with at most 64
-// rows (at most 32 on 32-column tiles, 16 on 64-column tiles), bf16 or fp32
-// output, whole leaves, at
+// rows (at most 16 on 64-column tiles), bf16 or fp32 output, whole leaves, at
 // least 8 and at most 1024 of them (one leaf or more per wave, at most 8
 // pending left siblings per wave), 16-byte aligned rows and, for a [K][N]
 // operand Y, whole 8-column chunks.
@@ -188,7 +187,7 @@ bool decode_ok(const Problem &pr) {
 // Selection (measured on MI355X; every configuration gives the same bits).
 // At most 64 rows: the decode kernel, whose workgroups split the reduction
 // along the tree (17 to 64 rows as 2 or 4 staged row blocks: M = 32,
-// K = 4096, N = 6144 in 16.6 us instead of 40 on the wide kernel).  Wider tiles read more of each cache line they request (a
+// K = 4096, N = 6144 in 16.7 us instead of 40 on the wide kernel).  Wider tiles read more of each cache line they request (a
 // compute unit keeps a bounded number of line requests in flight), narrower
 // ones spread over more compute units: 64 columns once there are 256 such
 // tiles, 32 columns above 128 such tiles, else 16 (M = 1, K = 4096: N = 6144
@@ -207,7 +206,7 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
         const bool line_units = pr.yk && (pr.R / 32) % 2 == 0;  // two-leaf copies read whole lines
         if (!line_units && pr.I <= 16 && (pr.J + 63) / 64 >= 256)
             return 11;
-        return pr.I <= 32 && (pr.J + 31) / 32 > 128 ? 12 : 10;
+        return (pr.J + 31) / 32 > 128 ? 12 : 10;
     }
     int up = 0;
     const int64_t t128 = ((pr.I + 127) / 128) * ((pr.J + 127) / 128);
@@ -255,7 +254,7 @@ int run_mfma(const Problem &pr, hipStream_t st) {
     const int cfg = pick_config(pr, tree, levels);
     const TileCfg &c = kTileCfgs[cfg];
     if (c.kind == KIND_DECODE) {
-        if (!decode_ok(pr) || pr.I > 64 / c.fn)
+        if (!decode_ok(pr) || (c.fn == 4 && pr.I > 16))
             return DET_GEMM_EINVAL;  // a forced decode configuration this problem does not fit
         if ((pr.J + 15) / 16 > kMaxDim)
             return DET_GEMM_EINVAL;

@@ -143,8 +143,11 @@ __device__ __forceinline__ f32x4 top_levels(const f32x4 *r) {
         return merge4(top_levels<LO, (LO + HI) / 2>(r), top_levels<(LO + HI) / 2, HI>(r));
 }
 
+// Register budget: 128 VGPRs (two 8-wave workgroups or one 16-wave
+// workgroup per compute unit), or 256 for 4 row blocks x 2 column blocks
+// (one 8-wave workgroup per compute unit).
 template <bool YK, int OUT, int MP, int CB, int UL, int W>
-__global__ __launch_bounds__(64 * W, W == 16 ? 2 : 4) void mfma_decode_kernel(MfmaParams p) {
+__global__ __launch_bounds__(64 * W, (W == 16 || MP * CB > 64) ? 2 : 4) void mfma_decode_kernel(MfmaParams p) {
     static_assert(UL == 1 || YK, "two-leaf units only for a K-major Y");
     static_assert(W == 8 || W == 16, "subtrees of depth 3 or 4");
     typedef DecodeShape<MP, CB, UL, W> S;
@@ -481,10 +484,10 @@ hipError_t launch_decode_waves(const MfmaParams &p, hipStream_t st) {
 
 // A K-major Y with an even leaf count is copied in two-leaf units (whole
 // 128-byte lines of each column), on 16- and 32-column tiles (64-column
-// tiles would not fit the unit's registers).
+// tiles would not fit the unit's registers) when the rings fit the LDS.
 template <bool YK, int OUT, int MP, int CB>
 hipError_t launch_decode_units(const MfmaParams &p, hipStream_t st) {
-    if constexpr (YK && CB <= 2) {
+    if constexpr (YK && CB <= 2 && DecodeShape<MP, CB, 2, 8>::kFits) {
         if (p.L % 2 == 0)
             return launch_decode_waves<YK, OUT, MP, CB, 2>(p, st);
     }
@@ -501,7 +504,7 @@ hipError_t launch_decode_rows(const MfmaParams &p, hipStream_t st) {
         if (p.I <= 32)
             return launch_decode_units<YK, OUT, 32, CB>(p, st);
     }
-    if constexpr (CB == 1)     // 33 to 64 rows: four row blocks on 16-column tiles
+    if constexpr (CB <= 2)     // 33 to 64 rows: four row blocks on 16- and 32-column tiles
         return launch_decode_units<YK, OUT, 64, CB>(p, st);
     return hipErrorInvalidValue;
 }

@@ -205,9 +205,9 @@ def test_decode_nonfinite_inputs(dev, M, K):
                                    (32, 40, 32768), (33, 200, 4096), (48, 6144, 4096), (64, 72, 4128),
                                    (61, 40, 1024)])
 def test_row_blocks_match_general_kernel(dev, M, N, K):
-    """17 to 64 rows: the decode kernel stages 2 or 4 blocks of 16 rows of X
-    (two blocks on 16- and 32-column tiles, four on 16-column tiles; the other
-    widths refuse).  The four X-row products equal the general kernel's bits."""
+    """17 to 64 rows: the decode kernel stages 2 or 4 blocks of 16 rows of X on
+    16- and 32-column tiles (64-column tiles refuse).  The four X-row products
+    equal the general kernel's bits."""
     say("17..64 rows on the decode kernel vs general kernel", M, N, K)
     A = W.randn_bf16((M, K), 1.0, 1600 + M + K).to(dev)
     B = W.randn_bf16((K, N), 0.02, 1601 + N + K).to(dev)
@@ -216,7 +216,7 @@ def test_row_blocks_match_general_kernel(dev, M, N, K):
         ref = _as_bits(_forced(GENERAL_CFG, f))
         assert np.array_equal(_as_bits(f()), ref), op
         da_fits = op != "da" or (N % 32 == 0 and N // 32 >= 8)
-        for cfg, rows in ((10, 64), (12, 32), (11, 16)):
+        for cfg, rows in ((10, 64), (12, 64), (11, 16)):
             if not da_fits:
                 continue
             if M <= rows:
