@@ -157,7 +157,9 @@ int det_gemm_debug_add(const det_bf16 *a, const det_bf16 *b, det_bf16 *out, int6
 /* Inspection: pins the MFMA kernel's tile configuration (0 .. count-1) for
  * subsequent calls on this process, or restores automatic selection (-1).
  * Every configuration computes the same leaves and tree, so the results must
- * not change; tests use this to show it.  Returns the number of
+ * not change; tests use this to show it.  A call whose problem the pinned
+ * configuration does not take (its shape, alignment, leaf count or row count)
+ * returns DET_GEMM_EINVAL without launching.  Returns the number of
  * configurations, or DET_GEMM_EINVAL for an out-of-range value. */
 int det_gemm_debug_force_config(int config);
 
