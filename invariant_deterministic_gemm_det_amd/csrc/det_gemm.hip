@@ -185,30 +185,43 @@ bool decode_ok(const Problem &pr) {
 }
 
 // Selection (measured on MI355X; every configuration gives the same bits).
-// At most 64 rows: the decode kernel, whose workgroups split the reduction
-// along the tree (17 to 64 rows as 2 or 4 staged row blocks: M = 32,
-// K = 4096, N = 6144 in 16.7 us instead of 40 on the wide kernel).  Wider tiles read more of each cache line they request (a
+// At most 16 rows: the decode kernel, whose workgroups split the reduction
+// along the tree.  Wider tiles read more of each cache line they request (a
 // compute unit keeps a bounded number of line requests in flight), narrower
-// ones spread over more compute units: 64 columns once there are 256 such
-// tiles, 32 columns above 128 such tiles, else 16 (M = 1, K = 4096: N = 6144
-// 13.9 us on 32 columns, 19.9 on 16; N = 151936 215 us on 64 columns, 246 on
-// 32; K = 32768, N = 4096 85 us on 16 columns, 94 on 32).  A K-major Y with an
+// ones spread over more compute units: 64 columns once there are more than
+// 128 such tiles, 32 columns above 128 such tiles, else 16 (M = 1, K = 4096:
+// N = 6144 13.9 us on 32 columns, 19.9 on 16; N = 11008 17.5 us on 64
+// columns, 23.9 on 32; N = 151936 215 us on 64 columns, 246 on 32;
+// K = 32768, N = 4096 85 us on 16 columns, 94 on 32).  A K-major Y with an
 // even leaf count is read in whole lines at any width and stays on 16 or 32
-// columns (N = 151936: 202 us on 32 columns, 242 on 64).  Otherwise 128x128
-// wide tiles when they make at least four waves of workgroups over the 256
-// compute units, else the 128x64 wide kernel, two workgroups per compute
-// unit, which keeps more units busy on small and mid-size products (M = 1024
-// at K = 4096, N = 6144: 94 us instead of 111 us).
+// columns (N = 151936: 202 us on 32 columns, 242 on 64).  17 to 64 rows: the
+// decode kernel stages 2 to 4 blocks of 16 rows per tile and re-reads X once
+// per tile, so it wins while the 32-column tiles times the row blocks stay
+// under about 1400 (M = 32, K = 4096, N = 6144: 16.7 us instead of 40 on the
+// wide kernel; N = 18432: 46 us instead of 51); above, the wide kernel
+// (N = 28672: 54 us instead of 65 at M = 32, 54 instead of 83 at M = 64),
+// on 128x128 tiles above 128 column tiles (N = 18432, M = 64: 51 us, 55 on
+// 128x64).  Otherwise 128x128 wide tiles when they make at least four waves
+// of workgroups over the 256 compute units, else the 128x64 wide kernel, two
+// workgroups per compute unit, which keeps more units busy on small and
+// mid-size products (M = 1024 at K = 4096, N = 6144: 94 us instead of 111 us).
 int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     if (g_force_config >= 0)
         return g_force_config;
-    if (decode_ok(pr)) {
-        const bool line_units = pr.yk && (pr.R / 32) % 2 == 0;  // two-leaf copies read whole lines
-        if (!line_units && pr.I <= 16 && (pr.J + 63) / 64 >= 256)
-            return 11;
-        return (pr.J + 31) / 32 > 128 ? 12 : 10;
-    }
     int up = 0;
+    if (decode_ok(pr)) {
+        const int64_t t32 = (pr.J + 31) / 32, blocks = (pr.I + 15) / 16;
+        if (pr.I > 16 && t32 * blocks > 1400) {
+            const int first = (pr.J + 127) / 128 > 128 ? 8 : 6;
+            for (int c : {first, first == 8 ? 6 : 8})
+                if (wide_ok(pr, t, kTileCfgs[c], up))
+                    return c;
+        }
+        const bool line_units = pr.yk && (pr.R / 32) % 2 == 0;  // two-leaf copies read whole lines
+        if (!line_units && pr.I <= 16 && (pr.J + 63) / 64 > 128)
+            return 11;
+        return t32 > 128 ? 12 : 10;
+    }
     const int64_t t128 = ((pr.I + 127) / 128) * ((pr.J + 127) / 128);
     if (t128 >= 4 * 256)
         for (int c : {8, 5, 9, 7})  // three stage buffers with early copies if the LDS holds them

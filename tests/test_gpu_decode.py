@@ -201,13 +201,19 @@ def test_decode_nonfinite_inputs(dev, M, K):
                               ref), cfg
 
 
+# The last four reach past the decode kernel's range of choice: N = 28672 at
+# 17 and 64 rows runs on 128x128 wide tiles, N = 14336 at 64 rows on 128x64
+# wide tiles, and K = 1536 (48 leaves, not a power of two, which the wide
+# kernels need) at N = 28672 stays on the decode kernel.
 @pytest.mark.parametrize("M,N,K", [(17, 200, 4096), (24, 6144, 4096), (32, 136, 1024), (20, 48, 4128),
                                    (32, 40, 32768), (33, 200, 4096), (48, 6144, 4096), (64, 72, 4128),
-                                   (61, 40, 1024)])
+                                   (61, 40, 1024), (17, 28672, 4096), (64, 28672, 4096),
+                                   (64, 14336, 4096), (40, 28672, 1536)])
 def test_row_blocks_match_general_kernel(dev, M, N, K):
     """17 to 64 rows: the decode kernel stages 2 or 4 blocks of 16 rows of X on
-    16- and 32-column tiles (64-column tiles refuse).  The four X-row products
-    equal the general kernel's bits."""
+    16- and 32-column tiles (64-column tiles refuse); the automatic choice
+    moves wide products to the wide kernel.  Every path gives the general
+    kernel's bits on the four X-row products."""
     say("17..64 rows on the decode kernel vs general kernel", M, N, K)
     A = W.randn_bf16((M, K), 1.0, 1600 + M + K).to(dev)
     B = W.randn_bf16((K, N), 0.02, 1601 + N + K).to(dev)
