@@ -236,6 +236,12 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
 }
 
 // One workgroup of 128 threads (one per column) per (query head, sequence).
+// The partials are read kChunk splits at a time, all loads of a chunk issued
+// before its arithmetic, so a sequence waits for memory once per chunk and
+// not once per split; the max and the two sums still run over the splits in
+// ascending order.
+constexpr int kChunk = 16;
+
 __global__ __launch_bounds__(kD) void attn_combine_kernel(const int32_t *lens, int Hq, int Smax,
                                                           int NS, const float *work, uint16_t *O) {
     const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
@@ -249,13 +255,34 @@ __global__ __launch_bounds__(kD) void attn_combine_kernel(const int32_t *lens, i
     }
     const float *w = work + ((int64_t)b * Hq + h) * NS * (kD + 2);
     float M = w[kD];
-    for (int s = 1; s < ns; ++s)
-        M = fmaxf(M, w[s * (kD + 2) + kD]);
+    for (int s0 = 1; s0 < ns; s0 += kChunk) {
+        float m[kChunk];
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i)
+            m[i] = s0 + i < ns ? w[(int64_t)(s0 + i) * (kD + 2) + kD] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i)
+            if (s0 + i < ns)
+                M = fmaxf(M, m[i]);
+    }
     float L = 0.0f, acc = 0.0f;
-    for (int s = 0; s < ns; ++s) {
-        const float f = exp2f(w[s * (kD + 2) + kD] - M);
-        L = fmaf(w[s * (kD + 2) + kD + 1], f, L);
-        acc = fmaf(w[s * (kD + 2) + d], f, acc);
+    for (int s0 = 0; s0 < ns; s0 += kChunk) {
+        float m[kChunk], l[kChunk], v[kChunk];
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            const float *ws = w + (int64_t)(s0 + i) * (kD + 2);
+            const bool in = s0 + i < ns;
+            m[i] = in ? ws[kD] : 0.0f;
+            l[i] = in ? ws[kD + 1] : 0.0f;
+            v[i] = in ? ws[d] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i)
+            if (s0 + i < ns) {
+                const float f = exp2f(m[i] - M);
+                L = fmaf(l[i], f, L);
+                acc = fmaf(v[i], f, acc);
+            }
     }
     o[d] = (uint16_t)pair_bits(round_pair(acc / L, 0.0f));
 }
