@@ -163,6 +163,26 @@ int det_gemm_debug_add(const det_bf16 *a, const det_bf16 *b, det_bf16 *out, int6
  * configurations, or DET_GEMM_EINVAL for an out-of-range value. */
 int det_gemm_debug_force_config(int config);
 
+/* Inspection: the tile configuration (0 .. count-1, the numbering of
+ * det_gemm_debug_force_config) that the MFMA entry point of operation `op`
+ * would run for these arguments, chosen from shape, alignment and leaf count
+ * alone.  The arguments are those of that entry point, in its order (for
+ * det_gemm_fwd: A, lda, B, ldb, C, ldc, M, N, K); the pointers are only
+ * compared and tested for alignment, never dereferenced, and no device is
+ * needed.  op: DET_GEMM_OP_FWD, _FWD_RHS_TRANSPOSED, _FWD_FP32, _DA, _DB or
+ * _DB_TRANSPOSED.  Returns the configuration, the pinned one if
+ * det_gemm_debug_force_config holds one, or the status the entry point would
+ * return before launching: DET_GEMM_EINVAL (also for an empty product, which
+ * launches nothing, and for an unknown op) or DET_GEMM_EKCAP. */
+#define DET_GEMM_OP_FWD 0
+#define DET_GEMM_OP_FWD_RHS_TRANSPOSED 1
+#define DET_GEMM_OP_FWD_FP32 2
+#define DET_GEMM_OP_DA 3
+#define DET_GEMM_OP_DB 4
+#define DET_GEMM_OP_DB_TRANSPOSED 5
+int det_gemm_debug_config(int op, const void *P, int64_t ldp, const void *Q, int64_t ldq,
+                          const void *Out, int64_t ldo, int64_t M, int64_t N, int64_t K);
+
 /* Human-readable text for a status code (static storage). */
 const char *det_gemm_status_string(int status);
 

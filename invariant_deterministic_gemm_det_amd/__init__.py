@@ -28,7 +28,8 @@ _SIX = ("det_gemm_fwd", "det_gemm_fwd_rhs_transposed", "det_gemm_fwd_fp32", "det
         "det_gemm_db", "det_gemm_db_transposed")
 EXPORTS = _SIX + tuple(n.replace("det_gemm_", "det_gemm_strict_") for n in _SIX) + (
     "det_gemm_debug_leaves", "det_gemm_debug_round", "det_gemm_debug_add",
-    "det_gemm_debug_force_config", "det_gemm_status_string", "det_moe_fwd_dprob",
+    "det_gemm_debug_force_config", "det_gemm_debug_config", "det_gemm_status_string",
+    "det_moe_fwd_dprob",
     "det_moe_debug_slots", "det_fingerprint", "det_fingerprint_rows", "det_first_mismatch",
     "det_rmsnorm", "det_attention_decode", "det_gemm_shard_reduce")
 MAX_PARTS = 16
@@ -75,6 +76,8 @@ def load_library(path=LIB_PATH):
     lib.det_gemm_debug_add.restype = ctypes.c_int
     lib.det_gemm_debug_force_config.argtypes = [ctypes.c_int]
     lib.det_gemm_debug_force_config.restype = ctypes.c_int
+    lib.det_gemm_debug_config.argtypes = [ctypes.c_int, p, i64, p, i64, p, i64, i64, i64, i64]
+    lib.det_gemm_debug_config.restype = ctypes.c_int
     lib.det_moe_fwd_dprob.argtypes = [p, i64, p, i64, i64, p, i64, p, i64, p, i64, p, i64, p,
                                       i64, i64, i64, p]
     lib.det_moe_fwd_dprob.restype = ctypes.c_int
@@ -456,6 +459,20 @@ def det_gemm_debug_add(a, b):
                                                _stream(a))
     _check(rc, "det_gemm_debug_add")
     return out
+
+
+OP_FWD, OP_FWD_RHS_TRANSPOSED, OP_FWD_FP32, OP_DA, OP_DB, OP_DB_TRANSPOSED = range(6)
+
+
+def det_gemm_debug_config(op, p, ldp, q, ldq, out, ldo, M, N, K):
+    """The tile configuration the MFMA entry point of `op` (OP_FWD ...) would
+    run for these arguments (addresses as integers, never dereferenced; no
+    device needed)."""
+    rc = load_library().det_gemm_debug_config(int(op), ctypes.c_void_p(p), ldp, ctypes.c_void_p(q),
+                                               ldq, ctypes.c_void_p(out), ldo, M, N, K)
+    if rc < 0:
+        raise DetGemmError(rc, "det_gemm_debug_config")
+    return rc
 
 
 def det_gemm_debug_force_config(config):

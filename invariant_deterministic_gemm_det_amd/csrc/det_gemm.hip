@@ -667,6 +667,23 @@ int det_gemm_debug_force_config(int config) {
     return kNumTileCfgs;
 }
 
+int det_gemm_debug_config(int op, const void *P, int64_t ldp, const void *Q, int64_t ldq,
+                          const void *Out, int64_t ldo, int64_t M, int64_t N, int64_t K) {
+    if (op < OP_FWD || op > OP_DB_T)
+        return DET_GEMM_EINVAL;
+    Problem pr;
+    bool empty;
+    const int rc = build(static_cast<Op>(op), P, ldp, Q, ldq, const_cast<void *>(Out), ldo, M, N,
+                         K, pr, empty);
+    if (rc != DET_GEMM_OK)
+        return rc;
+    if (empty)
+        return DET_GEMM_EINVAL;  // nothing is launched, so no configuration runs
+    int levels = 0;
+    const TreeSel tree = pick_tree((int32_t)((pr.R + 31) / 32), levels);
+    return pick_config(pr, tree, levels);
+}
+
 const char *det_gemm_status_string(int status) {
     switch (status) {
     case DET_GEMM_OK:

@@ -1,0 +1,106 @@
+"""Tile-configuration selection, pinned on the host (no device).
+
+Every configuration computes the same leaves and the same mid-split tree, so
+the choice never changes bits (the GPU tests compare them); these tests pin
+which kernel each problem class runs on, through det_gemm_debug_config, which
+applies the entry point's argument checks and the selection to shape,
+alignment and leaf count without touching memory.  Configurations: 5 to 9
+wide kernels (6: 128x64 tiles; 8: 128x128 two-leaf units; 9: three-leaf
+units), 10 to 12 decode kernels with 16, 64 and 32 columns per workgroup.
+"""
+import pytest
+
+import invariant_deterministic_gemm_det_amd as dg
+
+A_ADDR, B_ADDR, C_ADDR = 0x100000000, 0x200000000, 0x300000000  # disjoint, 256-byte aligned
+
+
+def cfg(op, M, N, K, transposed_rhs=False):
+    """Configuration of a contiguous product: fwd family C[M][N] = A[M][K] B,
+    da dA[M][K] = dC[M][N] B^T, db dB[K][N] = A^T dC."""
+    if op == dg.OP_FWD_RHS_TRANSPOSED:
+        return dg.det_gemm_debug_config(op, A_ADDR, K, B_ADDR, K, C_ADDR, N, M, N, K)
+    if op in (dg.OP_FWD, dg.OP_FWD_FP32):
+        return dg.det_gemm_debug_config(op, A_ADDR, K, B_ADDR, N, C_ADDR, N, M, N, K)
+    if op == dg.OP_DA:
+        return dg.det_gemm_debug_config(op, A_ADDR, N, B_ADDR, N, C_ADDR, K, M, N, K)
+    if op == dg.OP_DB:
+        return dg.det_gemm_debug_config(op, A_ADDR, K, B_ADDR, N, C_ADDR, N, M, N, K)
+    raise ValueError(op)
+
+
+@pytest.fixture(autouse=True)
+def automatic():
+    dg.det_gemm_debug_force_config(-1)
+    yield
+    dg.det_gemm_debug_force_config(-1)
+
+
+def test_step_products_run_on_the_wide_kernel():
+    # M = K = 4096, N = 6144: fwd and db have 128 leaves (two-leaf units),
+    # da reduces over N = 6144, 192 leaves (three-leaf units).
+    assert cfg(dg.OP_FWD, 4096, 6144, 4096) == 8
+    assert cfg(dg.OP_DA, 4096, 6144, 4096) == 9
+    assert cfg(dg.OP_DB, 4096, 6144, 4096) == 8
+    # fewer than four waves of 128x128 workgroups: 128x64 tiles
+    assert cfg(dg.OP_FWD, 1024, 6144, 4096) == 6
+
+
+@pytest.mark.parametrize("M,N,want", [
+    (1, 4096, 10),     # at most 128 tiles of 32 columns
+    (1, 6144, 12),     # QKV: 192 tiles of 32 columns
+    (16, 6144, 12),
+    (1, 8192, 12),     # 128 tiles of 64 columns: still 32 columns
+    (1, 11008, 11),    # 172 tiles of 64 columns
+    (16, 151936, 11),  # LM head
+    (32, 6144, 12),    # two row blocks, 384 (tiles x blocks)
+    (64, 11008, 12),   # 344 x 4 = 1376: decode
+    (64, 14336, 6),    # 448 x 4 = 1792: wide, 112 tiles of 128 columns
+    (17, 28672, 8),    # 896 x 2: wide, 224 tiles of 128 columns
+    (48, 151936, 8),
+])
+def test_small_m_row_major_weight(M, N, want):
+    assert cfg(dg.OP_FWD, M, N, 4096) == want
+    assert cfg(dg.OP_FWD_FP32, M, N, 4096) == want
+
+
+def test_small_m_leaf_count_the_wide_kernel_refuses():
+    # K = 1536: 48 leaves, not a power of two, so 40 rows at N = 28672 stay on
+    # the decode kernel although the wide kernel would be chosen for K = 4096
+    assert cfg(dg.OP_FWD, 40, 28672, 4096) == 8
+    assert cfg(dg.OP_FWD, 40, 28672, 1536) == 12
+
+
+def test_small_m_transposed_weight():
+    # W [N][K] with an even leaf count is read in two-leaf lines at any width:
+    # 32 columns even for the LM head; an odd leaf count takes 64 columns
+    assert cfg(dg.OP_FWD_RHS_TRANSPOSED, 1, 151936, 4096) == 12
+    assert cfg(dg.OP_FWD_RHS_TRANSPOSED, 1, 151936, 4128) == 11
+    assert cfg(dg.OP_FWD_RHS_TRANSPOSED, 1, 6144, 4096) == 12
+
+
+def test_decode_limits():
+    assert cfg(dg.OP_FWD, 65, 6144, 4096) not in (10, 11, 12)   # more than 64 rows
+    assert cfg(dg.OP_FWD, 1, 6144, 224) not in (10, 11, 12)     # 7 leaves
+    assert cfg(dg.OP_FWD, 1, 4096, 32768) == 10   # 1024 leaves, the reduction cap
+    assert cfg(dg.OP_FWD, 1, 6143, 4096) not in (10, 11, 12)    # N not whole 8-column chunks
+
+
+def test_pinned_configuration_is_reported():
+    dg.det_gemm_debug_force_config(3)
+    assert cfg(dg.OP_FWD, 1, 6144, 4096) == 3
+
+
+def test_argument_errors():
+    with pytest.raises(dg.DetGemmError) as e:
+        dg.det_gemm_debug_config(6, A_ADDR, 64, B_ADDR, 64, C_ADDR, 64, 64, 64, 64)
+    assert e.value.code == dg.EINVAL
+    with pytest.raises(dg.DetGemmError) as e:   # empty product: nothing is launched
+        cfg(dg.OP_FWD, 0, 64, 64)
+    assert e.value.code == dg.EINVAL
+    with pytest.raises(dg.DetGemmError) as e:   # reduction past the cap
+        cfg(dg.OP_FWD, 4, 64, 32768 + 32)
+    assert e.value.code == dg.EKCAP
+    with pytest.raises(dg.DetGemmError) as e:   # output overlapping an input
+        dg.det_gemm_debug_config(dg.OP_FWD, A_ADDR, 64, B_ADDR, 64, A_ADDR, 64, 64, 64, 64)
+    assert e.value.code == dg.EINVAL
