@@ -500,9 +500,8 @@ def main():
 
     dev = torch.device("cuda:0")
     dg.load_library()
-    X = Wk.randn_bf16((M, K), 1.0, 4001, dev)
-    W = Wk.randn_bf16((K, N), 0.02, 2001, dev)
-    dC = Wk.randn_bf16((M, N), 1e-3, 4003, dev)
+    X, W, dC = Wk.step_inputs(dev)
+    assert tuple(X.shape) == (M, K) and tuple(W.shape) == (K, N) and tuple(dC.shape) == (M, N)
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     dW = torch.empty((K, N), dtype=torch.bfloat16, device=dev)

@@ -126,6 +126,15 @@ def backward_inputs(device="cpu", M=BWD_M, K=BWD_K, N=BWD_N):
             randn_bf16((M, N), 1e-3, 4003, device))
 
 
+def step_inputs(device="cpu"):
+    """The linear-layer step the benchmark times, at the QKV shape:
+    (X[4096,4096] ~N(0,1), W[4096,6144] ~N(0,0.02), dC[4096,6144] ~N(0,1e-3));
+    fwd C = X W, da dX = dC W^T, db dW = X^T dC."""
+    return (randn_bf16((HEADLINE_M, QKV_K), 1.0, 4001, device),
+            randn_bf16((QKV_K, QKV_N), 0.02, 2001, device),
+            randn_bf16((HEADLINE_M, QKV_N), 1e-3, 4003, device))
+
+
 def lm_head_inputs(device="cpu", M=4096):
     """(X[M,4096] ~N(0,1), Wlm[4096,151936] ~N(0,0.02))."""
     return (randn_bf16((M, LM_K), 1.0, 5001, device),

@@ -19,15 +19,19 @@
  * Conventions for every entry point below:
  *   - det_bf16 is the bf16 bit pattern (uint16_t).  All pointers are DEVICE
  *     pointers; all matrices are row-major with an explicit leading dimension
- *     in elements (ld >= row width, any alignment of the element type).
+ *     in elements (row width <= ld <= 2^23 = DET_GEMM_MAX_LD, any alignment of
+ *     the element type; the upper limit keeps the byte offsets inside one
+ *     operand tile below 2^31).
  *   - The caller owns every buffer; the library allocates no device memory.
  *   - The call is asynchronous on `stream` (a hipStream_t; NULL is the default
  *     stream).  Outputs must not overlap inputs.
  *   - Return value: DET_GEMM_OK, or a negative status.  On any error the call
  *     launches nothing and writes nothing.
  *       DET_GEMM_EINVAL  null pointer with a non-empty shape, negative size,
- *                        leading dimension smaller than the row width, or an
- *                        output range overlapping an input range;
+ *                        leading dimension smaller than the row width or
+ *                        larger than DET_GEMM_MAX_LD, a dimension or tile
+ *                        count beyond 2^31 - 1, or an output range
+ *                        overlapping an input range;
  *       DET_GEMM_EKCAP   reduction length R == 0 or R > 32768 (with a
  *                        non-empty output);
  *       DET_GEMM_EHIP    the HIP runtime reported an error (launch failure or
@@ -38,7 +42,8 @@
  *   - The reduction-internal order of a leaf is whatever the gfx950 bf16 MFMA
  *     does (fixed, shape-independent); the CPU definition adds the 32 products
  *     left to right.  The det_gemm_strict_* entry points add them left to right
- *     as well and are bit-exact to that definition.
+ *     as well and are bit-exact to that definition (for products within fp32's
+ *     normal range; see below).
  */
 #ifndef DET_GEMM_H
 #define DET_GEMM_H
@@ -58,6 +63,7 @@ typedef uint16_t det_bf16;
 
 #define DET_GEMM_LEAF 32
 #define DET_GEMM_MAX_REDUCTION 32768
+#define DET_GEMM_MAX_LD (INT64_C(1) << 23)
 
 /* Forward (page section "Guarantees": C = A @ B).
  * A [M,K] (lda), B [K,N] (ldb), C [M,N] (ldc); reduction over K. */
@@ -88,18 +94,23 @@ int det_gemm_da(const det_bf16 *dC, int64_t lddc, const det_bf16 *B, int64_t ldb
 int det_gemm_db(const det_bf16 *A, int64_t lda, const det_bf16 *dC, int64_t lddc,
                 det_bf16 *dB, int64_t lddb, int64_t M, int64_t N, int64_t K, void *stream);
 
-/* Weight gradient stored in the canonical [N,K] layout (page section "Ascend
- * NPU backend": db_transposed stores the weight gradient born contiguous in
- * [N,K]): dBt [N,K] with dBt[n][k] == dB[k][n] bit for bit. */
+/* Weight gradient written directly in the [N,K] layout that an nn.Linear
+ * weight uses (page section "Ascend NPU backend", entry point
+ * db_transposed): dBt [N,K] with dBt[n][k] == dB[k][n] bit for bit. */
 int det_gemm_db_transposed(const det_bf16 *A, int64_t lda, const det_bf16 *dC, int64_t lddc,
                            det_bf16 *dBt, int64_t lddbt, int64_t M, int64_t N, int64_t K,
                            void *stream);
 
 /* Strict-order variants of the six operations: the same contract with every
  * leaf summed by a scalar fp32 fused multiply-add chain in ascending index
- * order (a bf16 product is exact in fp32, so this is the left-to-right sum of
- * the page's leaf definition).  Bit-exact to the CPU definition; slow by design.
- * Same arguments, ownership and errors as the entry points above. */
+ * order.  A product of two bf16 values has at most 16 significant bits, so it
+ * is exact in fp32 unless it falls below 2^-126 (subnormal range) or above the
+ * fp32 range; for such inputs the fused chain equals the left-to-right sum of
+ * rounded products of the page's leaf definition, and the result is bit-exact
+ * to the CPU definition.  Products that underflow or overflow fp32 are outside
+ * this promise (the fused add rounds once where the definition rounds the
+ * product first).  Slow by design.  Same arguments, ownership and errors as
+ * the entry points above. */
 int det_gemm_strict_fwd(const det_bf16 *A, int64_t lda, const det_bf16 *B, int64_t ldb,
                         det_bf16 *C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                         void *stream);
@@ -153,6 +164,20 @@ int det_gemm_debug_leaves(const det_bf16 *A, int64_t lda, const det_bf16 *B, int
 int det_gemm_debug_round(const float *x, det_bf16 *out, int64_t n, void *stream);
 int det_gemm_debug_add(const det_bf16 *a, const det_bf16 *b, det_bf16 *out, int64_t n,
                        void *stream);
+
+/* Inspection: the tree add exactly as the matrix-core kernels perform it
+ * (page section "Ascend NPU backend", bullet "Reduction tree": nodes are
+ * merged by bf16 adds).  Element-wise out[i] = a[i] (+) b[i], computed in
+ * blocks of 256 pairs by one bf16 MFMA against a constant 0/1 selector matrix
+ * whose products are exact, then rounded to bf16; a block with a non-finite
+ * sum is redone with element-wise fp32 adds, as the kernels redo a tile whose
+ * root is non-finite.  selector 0: the split selector of the wide and
+ * direct-to-LDS kernels (the large-product path); selector 1: the pairwise
+ * selector of the general kernel.  The decode kernel's VALU add is
+ * det_gemm_debug_add.  Device pointers, n elements; asynchronous on stream;
+ * DET_GEMM_EINVAL for n < 0, a null pointer or another selector. */
+int det_gemm_debug_matrix_add(const det_bf16 *a, const det_bf16 *b, det_bf16 *out, int64_t n,
+                              int selector, void *stream);
 
 /* Inspection: pins the MFMA kernel's tile configuration (0 .. count-1) for
  * subsequent calls on this process, or restores automatic selection (-1).

@@ -28,6 +28,7 @@ _SIX = ("det_gemm_fwd", "det_gemm_fwd_rhs_transposed", "det_gemm_fwd_fp32", "det
         "det_gemm_db", "det_gemm_db_transposed")
 EXPORTS = _SIX + tuple(n.replace("det_gemm_", "det_gemm_strict_") for n in _SIX) + (
     "det_gemm_debug_leaves", "det_gemm_debug_round", "det_gemm_debug_add",
+    "det_gemm_debug_matrix_add",
     "det_gemm_debug_force_config", "det_gemm_debug_config", "det_gemm_status_string",
     "det_moe_fwd_dprob",
     "det_moe_debug_slots", "det_fingerprint", "det_fingerprint_rows", "det_first_mismatch",
@@ -74,6 +75,8 @@ def load_library(path=LIB_PATH):
     lib.det_gemm_debug_round.restype = ctypes.c_int
     lib.det_gemm_debug_add.argtypes = [p, p, p, i64, p]
     lib.det_gemm_debug_add.restype = ctypes.c_int
+    lib.det_gemm_debug_matrix_add.argtypes = [p, p, p, i64, ctypes.c_int, p]
+    lib.det_gemm_debug_matrix_add.restype = ctypes.c_int
     lib.det_gemm_debug_force_config.argtypes = [ctypes.c_int]
     lib.det_gemm_debug_force_config.restype = ctypes.c_int
     lib.det_gemm_debug_config.argtypes = [ctypes.c_int, p, i64, p, i64, p, i64, i64, i64, i64]
@@ -131,15 +134,35 @@ def _mat(t, name, dtype=torch.bfloat16):
     return ctypes.c_void_p(t.data_ptr()), ld
 
 
-def _out(out, shape, like, dtype):
+def _same_device(*ts):
+    devs = {t.device for t in ts}
+    if len(devs) != 1:
+        raise ValueError(f"tensors are on different devices: {sorted(map(str, devs))}")
+
+
+def _out(out, shape, like, dtype, contiguous=False, name="output"):
+    """A caller's output tensor, checked against what the C call will write:
+    dtype, device (that of `like`), shape and, for `contiguous`, a dense
+    layout (the C call then writes numel elements from its data pointer).  A
+    2-D output may carry a row stride; its unit column stride is checked where
+    its leading dimension is taken.  None allocates a fresh tensor."""
     if out is None:
         return torch.empty(shape, dtype=dtype, device=like.device)
+    if not isinstance(out, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if out.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, not {out.dtype}")
     if tuple(out.shape) != tuple(shape):
-        raise ValueError(f"output must have shape {tuple(shape)}")
+        raise ValueError(f"{name} must have shape {tuple(shape)}")
+    if contiguous and not out.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not out.is_cuda or out.device != like.device:
+        raise TypeError(f"{name} must be on {like.device}")
     return out
 
 
 def _call(name, P, Q, out, M, N, K, what):
+    _same_device(P, Q, out)
     pp, ldp = _mat(P, "first operand")
     qp, ldq = _mat(Q, "second operand")
     op, ldo = _mat(out, "output", out.dtype)
@@ -236,6 +259,7 @@ def det_gemm_shard_reduce(parts, out=None):
         ptrs.append(pp.value or 0)
     if len(lds) != 1:
         raise ValueError("parts must share one leading dimension")
+    _same_device(*parts)
     out = _out(out, (M, N), parts[0], torch.bfloat16)
     op, ldo = _mat(out, "out")
     arr = (ctypes.c_void_p * len(parts))(*ptrs)
@@ -268,12 +292,16 @@ def det_moe_fwd_dprob(X, W, offsets, G, Y=None, slots=None, dprob=None):
     if len(off) != E + 1:
         raise ValueError("offsets must hold E + 1 entries")
     J = (N + MOE_SLOT - 1) // MOE_SLOT
-    Y = _out(Y, (T, N), X, torch.bfloat16)
-    dprob = _out(dprob, (T,), X, torch.float32)
+    _same_device(X, W, G)
+    Y = _out(Y, (T, N), X, torch.bfloat16, name="Y")
+    dprob = _out(dprob, (T,), X, torch.float32, contiguous=True, name="dprob")
     if slots is None:
         slots = torch.empty((J, T), dtype=torch.float32, device=X.device)
+    if not isinstance(slots, torch.Tensor) or not slots.is_cuda or slots.device != X.device:
+        raise TypeError(f"slots must be a tensor on {X.device}")
     if slots.dtype != torch.float32 or slots.dim() != 2 or slots.shape[0] != J or \
-            slots.shape[1] < T or (J > 0 and T > 1 and slots.stride(1) != 1):
+            slots.shape[1] < T or (J > 0 and T > 1 and slots.stride(1) != 1) or \
+            (J > 1 and slots.stride(0) < T):
         raise ValueError("slots must be float32 [ceil(N/128), >= T] with unit column stride")
     xp, ldx = _mat(X, "X")
     gp, ldg = _mat(G, "G")
@@ -296,8 +324,15 @@ def det_moe_debug_slots(Y, G, slots=None):
     """The slot writer as a kernel of its own over given Y and G: [ceil(N/128), T]."""
     T, N = Y.shape
     J = (N + MOE_SLOT - 1) // MOE_SLOT
+    _same_device(Y, G)
     if slots is None:
         slots = torch.empty((J, T), dtype=torch.float32, device=Y.device)
+    if not isinstance(slots, torch.Tensor) or not slots.is_cuda or slots.device != Y.device:
+        raise TypeError(f"slots must be a tensor on {Y.device}")
+    if slots.dtype != torch.float32 or slots.dim() != 2 or slots.shape[0] != J or \
+            slots.shape[1] < T or (J > 0 and T > 1 and slots.stride(1) != 1) or \
+            (J > 1 and slots.stride(0) < T):
+        raise ValueError("slots must be float32 [ceil(N/128), >= T] with unit column stride")
     yp, ldy = _mat(Y, "Y")
     gp, ldg = _mat(G, "G")
     slot_ld = slots.stride(0) if J > 1 else max(T, 1)
@@ -317,8 +352,9 @@ def det_rmsnorm(x, w, eps=1e-6, out=None, rstd=None):
     R, H = x.shape
     if w.dim() != 1 or w.shape[0] != H or w.dtype != torch.bfloat16 or not w.is_contiguous():
         raise ValueError("w must be a contiguous bf16 vector of H entries")
-    out = _out(out, (R, H), x, torch.bfloat16)
-    rstd = _out(rstd, (R,), x, torch.float32)
+    _same_device(x, w)
+    out = _out(out, (R, H), x, torch.bfloat16, name="out")
+    rstd = _out(rstd, (R,), x, torch.float32, contiguous=True, name="rstd")
     xp, ldx = _mat(x, "x")
     yp, ldy = _mat(out, "y")
     with torch.cuda.device(x.device):
@@ -345,9 +381,16 @@ def det_attention_decode(q, k, v, lens, scale, out=None, work=None):
     if lens.dtype != torch.int32 or not lens.is_cuda or tuple(lens.shape) != (B,):
         raise TypeError("lens must be an int32 GPU tensor [B]")
     NS = (Smax + ATTN_SPLIT - 1) // ATTN_SPLIT
-    out = _out(out, (B, Hq, D), q, torch.bfloat16)
+    _same_device(q, k, v, lens)
+    out = _out(out, (B, Hq, D), q, torch.bfloat16, contiguous=True, name="out")
+    need = B * Hq * NS * (D + 2)
     if work is None:
-        work = torch.empty((max(B * Hq * NS * (D + 2), 1),), dtype=torch.float32, device=q.device)
+        work = torch.empty((max(need, 1),), dtype=torch.float32, device=q.device)
+    if not isinstance(work, torch.Tensor) or work.dtype != torch.float32 or not work.is_cuda or \
+            work.device != q.device or not work.is_contiguous():
+        raise TypeError(f"work must be a contiguous float32 tensor on {q.device}")
+    if work.numel() < need:
+        raise ValueError(f"work must hold at least {need} floats")
     ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t.numel() else 0)
     with torch.cuda.device(q.device):
         rc = load_library().det_attention_decode(ptr(q), ptr(k), ptr(v), ptr(lens), B, Hq, Hkv,
@@ -371,7 +414,7 @@ def det_fingerprint(t, out=None):
     """64-bit digest of the bytes of a contiguous GPU tensor (include/
     det_fingerprint.h); returned in an int64 device tensor [1] holding its bits."""
     p, n = _bytes_of(t, "t")
-    out = _out(out, (1,), t, torch.int64)
+    out = _out(out, (1,), t, torch.int64, contiguous=True)
     with torch.cuda.device(t.device):
         rc = load_library().det_fingerprint(p, n, ctypes.c_void_p(out.data_ptr()), _stream(t))
     _check(rc, "det_fingerprint")
@@ -388,7 +431,7 @@ def det_fingerprint_rows(t, out=None):
         raise ValueError("t needs unit stride along its last dimension")
     es = t.element_size()
     ld = t.stride(0) * es if rows > 1 else cols * es
-    out = _out(out, (rows,), t, torch.int64)
+    out = _out(out, (rows,), t, torch.int64, contiguous=True)
     with torch.cuda.device(t.device):
         rc = load_library().det_fingerprint_rows(
             ctypes.c_void_p(t.data_ptr() if t.numel() else 0), rows, cols * es, ld,
@@ -404,7 +447,8 @@ def det_first_mismatch(a, b, out=None):
     pb, nb = _bytes_of(b, "b")
     if na != nb:
         raise ValueError("a and b differ in byte length")
-    out = _out(out, (1,), a, torch.int64)
+    _same_device(a, b)
+    out = _out(out, (1,), a, torch.int64, contiguous=True)
     with torch.cuda.device(a.device):
         rc = load_library().det_first_mismatch(pa, pb, na, ctypes.c_void_p(out.data_ptr()),
                                                _stream(a))
@@ -458,6 +502,23 @@ def det_gemm_debug_add(a, b):
                                                ctypes.c_void_p(out.data_ptr()), a.numel(),
                                                _stream(a))
     _check(rc, "det_gemm_debug_add")
+    return out
+
+
+def det_gemm_debug_matrix_add(a, b, selector=0):
+    """Device bf16 add of two bf16 tensors as the matrix-core kernels merge
+    tree nodes (selector 0: wide and direct-to-LDS kernels; 1: general kernel)."""
+    a, b = a.contiguous(), b.contiguous()
+    if a.shape != b.shape or a.dtype != torch.bfloat16 or b.dtype != torch.bfloat16:
+        raise TypeError("a and b must be bf16 tensors of one shape")
+    _same_device(a, b)
+    out = torch.empty_like(a)
+    with torch.cuda.device(a.device):
+        rc = load_library().det_gemm_debug_matrix_add(ctypes.c_void_p(a.data_ptr()),
+                                                      ctypes.c_void_p(b.data_ptr()),
+                                                      ctypes.c_void_p(out.data_ptr()), a.numel(),
+                                                      int(selector), _stream(a))
+    _check(rc, "det_gemm_debug_matrix_add")
     return out
 
 

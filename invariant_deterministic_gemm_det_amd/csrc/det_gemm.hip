@@ -29,7 +29,7 @@ using namespace detgemm;
 
 namespace {
 
-constexpr int64_t kMaxLd = int64_t(1) << 23;   // keeps buffer offsets of a tile below 2^31
+constexpr int64_t kMaxLd = DET_GEMM_MAX_LD;   // keeps buffer offsets of a tile below 2^31
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 
 enum Op { OP_FWD, OP_RHS_T, OP_FWD_F32, OP_DA, OP_DB, OP_DB_T, OP_LEAVES };
@@ -433,6 +433,70 @@ __global__ void debug_add_kernel(const uint16_t *a, const uint16_t *b, uint16_t 
     }
 }
 
+// The tree add as the matrix-core kernels run it.  Blocks of 256 pairs, one
+// wave per block: pair k of a block sits at block position (k / 16, k % 16) of
+// both children, i.e. in the lane and register where an MFMA result holds that
+// position (lane 16g + c, register v for position (4g + v, c)); the two
+// children are added by one v_mfma_f32_16x16x32_bf16 against a 0/1 selector,
+// exactly the code of the tree steps:
+//   selector 0: WideMatrixAdd with split_selector (the wide and direct-to-LDS
+//               kernels: each child packed on its own),
+//   selector 1: MatrixAdd with add_selector (the general kernel: the children
+//               packed pairwise by v_cvt_pk).
+// The add moves each sum to the lane and register that the transposed (odd
+// parity) layout uses for the same block position, which is how the store
+// reads it back.  A block with a non-finite sum is redone with element-wise
+// fp32 adds (positions unchanged), as a tile with a non-finite root is.  The
+// result is rounded to bf16 by v_cvt_pk, as a node is before its parent's add.
+__global__ __launch_bounds__(256) void debug_matrix_add_kernel(const uint16_t *a, const uint16_t *b,
+                                                               uint16_t *out, int64_t n,
+                                                               int selector) {
+    const int lane = threadIdx.x & 63;
+    const int64_t base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 256;
+    if (base >= n)
+        return;  // the whole wave
+    const int g = lane >> 4, c = lane & 15;
+    uint32_t av[4], bv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int64_t i = base + (4 * g + v) * 16 + c;
+        av[v] = i < n ? a[i] : 0u;
+        bv[v] = i < n ? b[i] : 0u;
+    }
+    WPacked<1, 1> l, r;
+    l.w[0][0] = u32x2{av[0] | (av[1] << 16), av[2] | (av[3] << 16)};
+    r.w[0][0] = u32x2{bv[0] | (bv[1] << 16), bv[2] | (bv[3] << 16)};
+    Frag<1, 1> s;
+    if (selector == 0) {
+        s = WideMatrixAdd::add<1, 1>(l, r, split_selector(lane));
+    } else {
+        Frag<1, 1> lf, rf;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            lf.v[0][0][v] = __uint_as_float(av[v] << 16);
+            rf.v[0][0][v] = __uint_as_float(bv[v] << 16);
+        }
+        s = MatrixAdd::merge<1, 1>(lf, rf, add_selector(lane));
+    }
+    bool bad = false;
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+        bad |= !(__builtin_fabsf(s.v[0][0][v]) <= 3.40282347e38f);
+    const bool redo = __builtin_amdgcn_ballot_w64(bad) != 0;
+    if (redo)
+        s = WideValuAdd::add<1, 1>(l, r, bf16x8{});
+    const WPacked<1, 1> q = wpack(s);
+    const uint32_t w[2] = {q.w[0][0].x, q.w[0][0].y};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        // odd parity: lane (g, c) register v holds position (c, 4g + v);
+        // element-wise adds keep the even parity (4g + v, c)
+        const int k = redo ? (4 * g + v) * 16 + c : c * 16 + 4 * g + v;
+        if (base + k < n)
+            out[base + k] = (uint16_t)(w[v >> 1] >> (16 * (v & 1)));
+    }
+}
+
 // ---- combination of K-shard partials: each thread takes 8 consecutive
 // columns of one row (16-byte loads when aligned) and evaluates the mid-split
 // tree over the parts, unrolled at compile time for each part count.
@@ -657,6 +721,25 @@ int det_gemm_debug_add(const det_bf16 *a, const det_bf16 *b, det_bf16 *out, int6
         return DET_GEMM_EINVAL;
     hipLaunchKernelGGL(debug_add_kernel, dim3((unsigned)blocks), dim3(256), 0,
                        static_cast<hipStream_t>(stream), a, b, out, n);
+    return hipGetLastError() == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
+}
+
+int det_gemm_debug_matrix_add(const det_bf16 *a, const det_bf16 *b, det_bf16 *out, int64_t n,
+                              int selector, void *stream) {
+    if (n < 0 || (selector != 0 && selector != 1))
+        return DET_GEMM_EINVAL;
+    if (n == 0)
+        return DET_GEMM_OK;
+    if (!a || !b || !out)
+        return DET_GEMM_EINVAL;
+    const int dev = check_device();
+    if (dev != DET_GEMM_OK)
+        return dev;
+    const int64_t blocks = (n + 1023) / 1024;  // 4 waves of 256 pairs
+    if (blocks > kMaxDim)
+        return DET_GEMM_EINVAL;
+    hipLaunchKernelGGL(debug_matrix_add_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a, b, out, n, selector);
     return hipGetLastError() == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
 }
 

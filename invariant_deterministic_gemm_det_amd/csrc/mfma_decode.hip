@@ -1,15 +1,19 @@
-// Decode-shaped forward products: at most 16 rows of X (one token, or a small
+// Decode-shaped forward products: at most 64 rows of X (one token, or a small
 // batch of them, against a weight matrix).  Same leaves, same tree, same bits
 // as every other det_gemm kernel; only the work split differs.
 //
 // The contract (RL-Kernel operator page "Batch-Invariant Deterministic GEMM
 // (det_gemm)", sections on the leaf product-sum and the mid-split reduction
-// tree) forbids splitting the reduction across workgroups, and a 16-row
-// product has only N / 16 output blocks: 384 at N = 6144, too few to keep 256
-// compute units streaming the weights if each block walks the whole reduction
-// alone.  Here the tree itself supplies the parallelism inside a workgroup:
-//   * a workgroup owns a 16 x 16 CB output tile (all rows, 16, 32 or 64
-//     columns) and has W = 8 or 16 waves; wave w evaluates the subtree rooted
+// tree) forbids splitting the reduction across workgroups, and a product of a
+// few rows has only N / 16 output blocks per 16 rows: 384 at N = 6144, too few
+// to keep 256 compute units streaming the weights if each block walks the
+// whole reduction alone.  Here the tree itself supplies the parallelism inside
+// a workgroup:
+//   * a workgroup owns an M x 16 CB output tile: all M rows (staged as 1, 2 or
+//     4 blocks of 16 rows, M <= 16, 32 or 64; 64-column tiles take at most 16
+//     rows) and 16, 32 or 64 columns, one MFMA per row block and column block
+//     with its own tree state.  It has W = 8 or 16 waves; wave w evaluates the
+//     subtree rooted
 //     at node w of depth log2(W) of the mid-split tree over the L leaves
 //     (L >= W, so every such node holds at least one leaf), a contiguous range
 //     of about L / W leaves;
@@ -39,8 +43,9 @@
 //     direct-to-LDS kernel.  Each way the two 16-lane groups of a half-wave
 //     ds_read_b64_tr_b16 (indices r0 .. r0+3 and r0+8 .. r0+11) use disjoint
 //     banks.
-//   * X: the MP rows the product needs (MP = 1 for a single row, else 16, rows
-//     past the last clamped to it) in the K-major layout of the unit.
+//   * X: the MP rows the product needs (MP = 1 for a single row, else 16, 32
+//     or 64, rows past the last clamped to it) in the K-major layout of the
+//     unit.
 // A compute unit serves these copies at a bounded rate of cache-line requests,
 // so wider tiles (more of each requested line used) stream faster and narrower
 // ones reach more compute units; the host picks the width from the tile count.

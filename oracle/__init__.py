@@ -198,9 +198,10 @@ def db_transposed(A, dC):
     return dBt
 
 
-def fwd_detail(A, B):
-    """Forward product plus every element's leaves [M,N,L] and the largest node
-    magnitude of its tree [M,N] (float32)."""
+def fwd_detail(A, B, with_leaves=True):
+    """Forward product plus every element's leaves [M,N,L] (None when
+    with_leaves is false, for products too large to keep them) and the largest
+    node magnitude of its tree [M,N] (float32)."""
     A, lda = _mat(A, "A")
     B, ldb = _mat(B, "B")
     (M, K), (K2, N) = A.shape, B.shape
@@ -208,10 +209,11 @@ def fwd_detail(A, B):
         raise ValueError("inner dimensions differ")
     L = max((K + LEAF - 1) // LEAF, 1)
     C = np.zeros((M, N), np.uint16)
-    leaves = np.zeros((M, N, L), np.uint16)
+    leaves = np.zeros((M, N, L), np.uint16) if with_leaves else None
     big = np.zeros((M, N), np.float32)
     _check(_load().oracle_det_gemm_fwd_detail(_ptr(A), lda, _ptr(B), ldb, _ptr(C), max(N, 1),
-                                              M, N, K, _ptr(leaves), _ptr(big)))
+                                              M, N, K, _ptr(leaves) if with_leaves else None,
+                                              _ptr(big)))
     return C, leaves, big
 
 

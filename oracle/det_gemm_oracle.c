@@ -24,9 +24,12 @@
  * Readings where the page is silent (each one is also listed in the design
  * notes of this repository):
  *   - mid-split of an odd range: the left child takes floor(n/2) leaves;
- *   - a leaf starts from +0.0f and adds products in ascending reduction index;
- *     a product of two bf16 values is exact in fp32, so multiply-then-add and
- *     fused multiply-add agree;
+ *   - a leaf starts from +0.0f and accumulates products in ascending reduction
+ *     index, one multiply-accumulate per step (the exact product added, the
+ *     sum rounded once: the fused chain of the strict kernel, and the MAC
+ *     order the Ascend section describes); a product of two bf16 values is
+ *     exact in fp32 unless it underflows, so this equals rounding each product
+ *     and adding for every product in fp32's normal range;
  *   - a "bf16 add" is the fp32 sum of the two bf16 values rounded once to bf16
  *     (this equals the correctly rounded bf16 sum);
  *   - a partial last leaf (R % 32 != 0) holds only the remaining products;
@@ -34,7 +37,7 @@
  *   - R == 0 or R > 32768 is rejected; an empty output (I == 0 or J == 0) is a
  *     successful no-op.
  *
- * Build: plain C99, -O2 -fno-fast-math -ffp-contract=off, OpenMP over output
+ * Build: plain C99, -O2 -fno-fast-math -ffp-contract=off -mfma, OpenMP over output
  * rows only (each output element is computed start to finish by one thread, in
  * the order above, so the thread count never changes a bit).
  *
@@ -90,15 +93,18 @@ static uint16_t add_bf16(uint16_t a, uint16_t b) {
     return round_bf16(s);
 }
 
-/* One leaf: the products x[r]*y[r] for r in [r0, r1), added one by one in
- * ascending r to an fp32 sum that starts at +0, then rounded once to bf16. */
+/* One leaf: the products x[r]*y[r] for r in [r0, r1), accumulated one by one
+ * in ascending r into an fp32 sum that starts at +0 (each step a multiply-
+ * accumulate: the exact product is added and the sum rounded once, fmaf),
+ * then rounded once to bf16.  A product of two bf16 values has at most 16
+ * significant bits, so for products in fp32's normal range this is the same
+ * as rounding each product to fp32 and adding; the two differ only for
+ * products below 2^-126. */
 static uint16_t leaf(const uint16_t *x, int64_t sx, const uint16_t *y, int64_t sy,
                      int64_t r0, int64_t r1) {
     float s = 0.0f;
-    for (int64_t r = r0; r < r1; ++r) {
-        float p = widen(x[r * sx]) * widen(y[r * sy]);
-        s = s + p;
-    }
+    for (int64_t r = r0; r < r1; ++r)
+        s = fmaf(widen(x[r * sx]), widen(y[r * sy]), s);
     return round_bf16(s);
 }
 
@@ -278,11 +284,11 @@ int oracle_num_threads(void) {
  *
  * Reading notes "Bitwise-Deterministic Pretraining at Scale: How Megatron Core
  * Finds and Removes Every Flipped Bit", section "Kernel redesign: the
- * grouped-GEMM epilogue": in the epilogue of the MoE grouped GEMM several
- * N-tiles contribute to the same per-token value dprob[token]; instead of
- * atomic adds (whose order varies from run to run), every N-tile writes a
- * private slot and, once all writers are done, the slots are combined by a
- * fixed reduction tree.
+ * grouped-GEMM epilogue": a per-token value dprob[token] of the MoE grouped
+ * GEMM's epilogue gathers contributions from several output column tiles.
+ * Atomic accumulation would add them in whatever order the tiles finish; the
+ * deterministic form keeps one private partial per column tile and reduces
+ * those partials in a fixed tree after the last tile has written its own.
  *
  * What is computed here:
  *   - rows of X are grouped by expert: expert e owns rows [off[e], off[e+1]);

@@ -65,3 +65,24 @@ def tolerance_report(got, want, big):
     beyond = int((err > lim).sum())
     ratio = float(np.max(err / lim)) if err.size else 0.0
     return hist, beyond, ratio
+
+
+def leaf_bound_ok(lg, lv, x_bits, y_bits):
+    """Device leaves lg against the oracle's lv ([M, N, L] bf16 patterns) for
+    operands x [M, K], y [K, N] (bf16 patterns): each side is the exact leaf
+    sum plus at most 31 (sequential) or 32 (any order) fp32 roundings of
+    partial sums, then one bf16 rounding, so
+    |leaf_gpu - leaf_oracle| <= spacing(max |leaf|) + 64 * 2^-24 * sum_r |x_r y_r|.
+    Returns (all within the bound, max ulp distance)."""
+    M, K = x_bits.shape
+    N = y_bits.shape[1]
+    Lk = (K + 31) // 32
+    x = np.zeros((M, Lk * 32))
+    x[:, :K] = bf16_value(x_bits)
+    y = np.zeros((Lk * 32, N))
+    y[:K] = bf16_value(y_bits)
+    x, y = x.reshape(M, Lk, 32), y.reshape(Lk, 32, N)
+    mag = np.einsum("mlk,lkn->mnl", np.abs(x), np.abs(y))
+    lgv, lvv = bf16_value(lg), bf16_value(lv)
+    lim = bf16_spacing(np.maximum(np.abs(lgv), np.abs(lvv))) + 64 * 2.0 ** -24 * mag
+    return bool((np.abs(lgv - lvv) <= lim).all()), int(ulp_distance(lg, lv).max())

@@ -104,6 +104,58 @@ def test_device_add_all_bf16_pairs(dev):
           "(the only normal-range pair that differs)")
 
 
+@pytest.mark.parametrize("selector", [0, 1])
+def test_device_matrix_add_all_bf16_pairs(dev, selector):
+    """Every pair of bf16 values through the tree add the matrix-core kernels
+    run (det_gemm_debug_matrix_add: one bf16 MFMA against a 0/1 selector per
+    block of 256 pairs, rounded by v_cvt_pk; a block with a non-finite sum
+    redone element-wise), against the oracle's bf16 add.  Pairs whose sum is
+    finite are sent in blocks of their own, so every one of them goes through
+    the matrix core; the rest (non-finite operands, overflowing sums) go
+    through the element-wise redo, as a tile with a non-finite root does.
+    Subnormal operands or sums are counted, not asserted (outside the promise);
+    NaN results are compared as NaN; (-0) + (-0) is excluded as in the VALU
+    add's test (no tree node is ever -0)."""
+    say(f"debug_matrix_add selector {selector}: all 2^32 bf16 pairs vs oracle.add_bf16")
+    a_host = np.tile(np.arange(65536, dtype=np.uint16), 256)
+    a_dev = torch.from_numpy(a_host.view(np.int16)).to(dev)
+    a_bf = a_dev.view(torch.bfloat16)
+    a_f = a_bf.float()
+    tiny = lambda v: (v != 0) & (v.abs() < 2.0 ** -126)
+    sub_a = tiny(a_f)
+    sub_diff = 0
+    mfma_pairs = 0
+    for b0 in range(0, 65536, 256):
+        b_host = np.repeat(np.arange(b0, b0 + 256, dtype=np.uint16), 65536)
+        b_dev = torch.from_numpy(b_host.view(np.int16)).to(dev)
+        b_bf = b_dev.view(torch.bfloat16)
+        b_f = b_bf.float()
+        fin = torch.isfinite(a_f + b_f)         # partition only; the expectation is the oracle's
+        res = torch.empty_like(a_dev)
+        for part in (fin, ~fin):
+            idx = torch.nonzero(part).flatten()
+            if idx.numel():
+                res[idx] = dg.det_gemm_debug_matrix_add(a_bf[idx], b_bf[idx], selector).view(torch.int16)
+        mfma_pairs += int(fin.sum())
+        ref = torch.from_numpy(oracle.add_bf16(a_host, b_host).view(np.int16)).to(dev)
+        ri, oi = ref.to(torch.int32) & 0xFFFF, res.to(torch.int32) & 0xFFFF
+        ref_nan = ((ri & 0x7F80) == 0x7F80) & ((ri & 0x7F) != 0)
+        our_nan = ((oi & 0x7F80) == 0x7F80) & ((oi & 0x7F) != 0)
+        exact = a_bf.double() + b_bf.double()
+        sub = sub_a | tiny(b_f) | tiny(exact)
+        both_neg_zero = (a_dev == -32768) & (b_dev == -32768)
+        assert bool((ref_nan == our_nan).all()), f"NaN-ness differs near b0={b0:#x}"
+        bad = (res != ref) & ~ref_nan & ~sub & ~both_neg_zero
+        if bool(bad.any()):
+            idx = torch.nonzero(bad).flatten()[:8]
+            pairs = [(hex(int(a_dev[i]) & 0xFFFF), hex(int(b_dev[i]) & 0xFFFF),
+                      hex(int(res[i]) & 0xFFFF), hex(int(ref[i]) & 0xFFFF)) for i in idx]
+            raise AssertionError(f"matrix-core add differs from the oracle (a, b, ours, oracle): {pairs}")
+        sub_diff += int(((res != ref) & ~ref_nan & sub).sum())
+    print(f"pairs through the matrix core: {mfma_pairs}; pairs involving subnormals added "
+          f"differently: {sub_diff}")
+
+
 # ---------------------------------------------------------------- helpers
 
 def _inputs(M, N, K, seed, sigma=1.0):

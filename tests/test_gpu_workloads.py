@@ -20,7 +20,7 @@ import torch
 import det_workloads as Wk
 import oracle
 import invariant_deterministic_gemm_det_amd as dg
-from gpu_util import device, say, bits, tolerance_report
+from gpu_util import device, say, bits, tolerance_report, ulp_distance, leaf_bound_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -169,3 +169,63 @@ def test_simulated_tp2(dev, shape):
     assert _same(dg.det_gemm_fwd_fp32(X, Bm), merged.float())
     if shape == "deep":
         _oracle_check(full[:2], X[:2], Bm)
+
+
+# ---------------------------------------------------------------- every element at the step shape
+
+# Elements allowed beyond the literal 2-ulp bound, as a fraction of the
+# product.  A leaf the matrix core sums in its own internal order can land one
+# bf16 step (more for a leaf whose products cancel) from the sequential leaf;
+# where the tree then cancels down to a root much smaller than that leaf, one
+# step of the leaf is several steps of the root.  Each such element is checked
+# structurally instead: the kernel's own leaves for it are within the rigorous
+# leaf bound of the oracle's, and the oracle's tree over the kernel's leaves
+# gives the kernel's output bit for bit -- the leaf-internal order is then the
+# only difference.
+BEYOND_2ULP_FRACTION = 1e-4
+
+
+@pytest.mark.parametrize("op", ["fwd", "da", "db"])
+def test_step_products_every_element(dev, op):
+    """The three products of the benchmark step (M = K = 4096, N = 6144, the
+    seeds and entry points the benchmark uses, so the same tile
+    configurations), every output element against the oracle: within 2 bf16
+    ulp of the oracle's element, except a counted few (at most a fraction
+    1e-4) that cancellation pushes beyond it, each of which must be explained
+    by its leaves alone (see BEYOND_2ULP_FRACTION)."""
+    X, W, dC = Wk.step_inputs(dev)
+    say("step product", op, "every element vs the oracle (M=K=4096, N=6144)")
+    # the product as a forward contraction P[I,R] @ Q[R,J] (same products, same order)
+    if op == "fwd":
+        got = dg.det_gemm_fwd(X, W)
+        P, Q = X, W
+    elif op == "da":     # dX = dC W^T
+        got = dg.det_gemm_da(dC, W)
+        P, Q = dC, W.t().contiguous()
+    else:                # dW = X^T dC
+        got = dg.det_gemm_db(X, dC)
+        P, Q = X.t().contiguous(), dC
+    want, _, big = oracle.fwd_detail(bits(P), bits(Q), with_leaves=False)
+    g = bits(got)
+    hist, _, _ = tolerance_report(g, want, big)
+    far = ulp_distance(g, want) > 2
+    over = int(far.sum())
+    print(f"  {op}: ulp histogram {hist}; beyond 2 ulp: {over} of {g.size} ({over / g.size:.2e})")
+    assert over <= BEYOND_2ULP_FRACTION * g.size
+    if over == 0:
+        return
+    ri, cj = np.nonzero(far)
+    rows, cols = np.unique(ri), np.unique(cj)
+    Pr = P[torch.as_tensor(rows, device=dev)].contiguous()
+    Qc = Q[:, torch.as_tensor(cols, device=dev)].contiguous()
+    lg = bits(dg.det_gemm_debug_leaves(Pr, Qc))
+    _, lv, _ = oracle.fwd_detail(bits(Pr), bits(Qc))
+    ok, worst = leaf_bound_ok(lg, lv, bits(Pr), bits(Qc))
+    roots, _ = oracle.tree_from_leaves(lg)
+    r_at = np.searchsorted(rows, ri)
+    c_at = np.searchsorted(cols, cj)
+    print(f"  {op}: leaves of those elements' rows and columns: within the leaf bound {ok}, "
+          f"worst leaf distance {worst} ulp")
+    assert ok
+    assert np.array_equal(roots[r_at, c_at], g[ri, cj]), \
+        "an element beyond 2 ulp is not the oracle's tree over the kernel's leaves"

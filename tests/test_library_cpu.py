@@ -202,3 +202,69 @@ def test_shard_reduce_argument_errors_without_device(lib):
     assert f(parts, 3, 64, ctypes.c_void_p(0x200000000), 64, 4, 64, NULL) == dg.EINVAL  # overlap
     assert f(parts, 3, 64, out, 64, 0, 64, NULL) == dg.OK               # empty
     assert f(None, 3, 64, out, 64, 4, 64, NULL) == dg.EINVAL
+
+
+def test_leading_dimension_limit(lib):
+    """Leading dimensions above DET_GEMM_MAX_LD = 2^23 are refused before any
+    device work (the tile byte offsets must stay below 2^31)."""
+    big = (1 << 23) + 8
+    far = ctypes.c_void_p(0x40000000000)
+    assert _fwd(lib, 4, 4, 8, lda=big, C=far) == dg.EINVAL
+    assert _fwd(lib, 4, 4, 8, ldb=big, C=far) == dg.EINVAL
+    assert _fwd(lib, 4, 4, 8, ldc=big, C=far) == dg.EINVAL
+    hdr = open(HEADER).read()
+    assert "DET_GEMM_MAX_LD" in hdr and "(INT64_C(1) << 23)" in hdr
+
+
+def test_debug_matrix_add_argument_errors(lib):
+    out = ctypes.c_void_p(0x900000000)
+    f = lib.det_gemm_debug_matrix_add
+    assert f(FAKE, FAKE, out, -1, 0, NULL) == dg.EINVAL
+    assert f(FAKE, FAKE, out, 16, 2, NULL) == dg.EINVAL      # unknown selector
+    assert f(NULL, FAKE, out, 16, 0, NULL) == dg.EINVAL
+    assert f(FAKE, FAKE, out, 0, 1, NULL) == dg.OK
+
+
+# ---------------------------------------------------------------- the Python binding
+
+def _t(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+def test_binding_checks_caller_outputs_before_any_launch():
+    """A caller's output must have the dtype, shape and layout the C call
+    writes: a bf16 buffer for an fp32 product (half the bytes) or a float32
+    buffer for a bf16 product is refused, as are outputs on another device,
+    undersized work buffers and non-contiguous vectors."""
+    import torch
+    A, B = _t((4, 64), torch.bfloat16), _t((64, 8), torch.bfloat16)
+    with pytest.raises(TypeError, match="dtype"):
+        dg.det_gemm_fwd_fp32(A, B, out=_t((4, 8), torch.bfloat16))
+    with pytest.raises(TypeError, match="dtype"):
+        dg.det_gemm_fwd(A, B, out=_t((4, 8), torch.float32))
+    with pytest.raises(ValueError, match="shape"):
+        dg.det_gemm_fwd(A, B, out=_t((4, 9), torch.bfloat16))
+    with pytest.raises(TypeError, match="must be on"):          # CPU tensor output
+        dg.det_gemm_fwd(A, B, out=_t((4, 8), torch.bfloat16))
+    with pytest.raises(TypeError, match="torch tensor"):
+        dg.det_gemm_fwd(A, B, out=[0] * 32)
+    x, w = _t((4, 64), torch.bfloat16), _t((64,), torch.bfloat16)
+    with pytest.raises(TypeError, match="dtype"):
+        dg.det_rmsnorm(x, w, rstd=_t((4,), torch.float16))
+    with pytest.raises(ValueError, match="contiguous"):
+        dg.det_rmsnorm(x, w, rstd=_t((8,), torch.float32)[::2])
+    with pytest.raises(TypeError, match="dtype"):
+        dg._out(_t((4,), torch.int32), (4,), x, torch.int64, contiguous=True)
+
+
+def test_binding_refuses_host_tensors():
+    """No CPU fallback: host tensors never reach the library."""
+    import torch
+    q = _t((2, 8, 128), torch.bfloat16)
+    k = _t((2, 2, 64, 128), torch.bfloat16)
+    lens = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        dg.det_attention_decode(q, k, k, lens, 0.1)
+    with pytest.raises(TypeError):
+        dg.det_gemm_fwd(_t((4, 64), torch.bfloat16), _t((64, 8), torch.bfloat16))
