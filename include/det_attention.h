@@ -58,6 +58,30 @@ int det_attention_decode(const det_bf16 *Q, const det_bf16 *K, const det_bf16 *V
                          const int32_t *lens, int64_t B, int64_t Hq, int64_t Hkv, int64_t Smax,
                          int64_t D, float scale, float *work, det_bf16 *O, void *stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * computation and the same kernels as det_attention_decode, bit for bit, with
+ * the per-split partials in a fixed device array of DET_ATTN_SCRATCH_FLOATS
+ * floats (32 MiB) that the library holds on every device it runs on until the
+ * process ends, instead of a work buffer.  The call allocates nothing: no
+ * hipMalloc, no hipFree, no allocating library routine.  The caller still
+ * passes Q, K, V, lens and O as above.
+ *   - A problem whose partials need more than the array,
+ *     B * Hq * ceil(Smax / 256) * (D + 2) > DET_ATTN_SCRATCH_FLOATS, is
+ *     refused with DET_ATTN_ESCRATCH before anything is launched (the
+ *     64-sequence, 32-head, Smax = 4096 decode batch needs 4.3 M floats).
+ *   - Every call on one device shares that device's array: calls that may
+ *     run at the same time on one device (other streams, other threads)
+ *     race and must be serialised by the caller.  Nothing in the array has
+ *     to start at zero: each call writes every partial it reads.
+ *   - Other errors as det_attention_decode. */
+#define DET_ATTN_SCRATCH_FLOATS (INT64_C(8) << 20)
+#define DET_ATTN_ESCRATCH (-4)
+int det_attention_decode_noalloc(const det_bf16 *Q, const det_bf16 *K, const det_bf16 *V,
+                                 const int32_t *lens, int64_t B, int64_t Hq, int64_t Hkv,
+                                 int64_t Smax, int64_t D, float scale, det_bf16 *O,
+                                 void *stream);
+
 #ifdef __cplusplus
 }
 #endif

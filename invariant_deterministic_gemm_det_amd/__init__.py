@@ -20,7 +20,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdet_gemm.so")
 
-OK, EINVAL, EKCAP, EHIP = 0, -1, -2, -3
+OK, EINVAL, EKCAP, EHIP, ESCRATCH = 0, -1, -2, -3, -4
 MAX_REDUCTION = 32768
 LEAF = 32
 
@@ -32,7 +32,9 @@ EXPORTS = _SIX + tuple(n.replace("det_gemm_", "det_gemm_strict_") for n in _SIX)
     "det_gemm_debug_force_config", "det_gemm_debug_config", "det_gemm_status_string",
     "det_moe_fwd_dprob",
     "det_moe_debug_slots", "det_fingerprint", "det_fingerprint_rows", "det_first_mismatch",
-    "det_rmsnorm", "det_attention_decode", "det_gemm_shard_reduce")
+    "det_rmsnorm", "det_attention_decode", "det_attention_decode_noalloc",
+    "det_gemm_shard_reduce")
+ATTN_SCRATCH_FLOATS = 8 << 20
 MAX_PARTS = 16
 ATTN_SPLIT = 256
 MOE_SLOT = 128
@@ -97,6 +99,9 @@ def load_library(path=LIB_PATH):
     lib.det_attention_decode.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, ctypes.c_float, p,
                                          p, p]
     lib.det_attention_decode.restype = ctypes.c_int
+    lib.det_attention_decode_noalloc.argtypes = [p, p, p, p, i64, i64, i64, i64, i64,
+                                                 ctypes.c_float, p, p]
+    lib.det_attention_decode_noalloc.restype = ctypes.c_int
     lib.det_gemm_shard_reduce.argtypes = [p, i64, i64, p, i64, i64, i64, p]
     lib.det_gemm_shard_reduce.restype = ctypes.c_int
     lib.det_gemm_status_string.argtypes = [ctypes.c_int]
@@ -397,6 +402,33 @@ def det_attention_decode(q, k, v, lens, scale, out=None, work=None):
                                                  Smax, D, ctypes.c_float(scale), ptr(work),
                                                  ptr(out), _stream(q))
     _check(rc, "det_attention_decode")
+    return out
+
+
+def det_attention_decode_noalloc(q, k, v, lens, scale, out):
+    """det_attention_decode without a work buffer (include/det_attention.h):
+    the library keeps the per-split partials in a fixed device array, so the C
+    call allocates nothing.  `out` [B,Hq,128] bf16 is required; calls that can
+    overlap on one device race on the shared array."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous bf16 GPU tensor")
+    B, Hq, D = q.shape
+    _, Hkv, Smax, D2 = k.shape
+    if tuple(v.shape) != tuple(k.shape) or D2 != D or k.shape[0] != B:
+        raise ValueError("q, k, v disagree in shape")
+    if lens.dtype != torch.int32 or not lens.is_cuda or tuple(lens.shape) != (B,):
+        raise TypeError("lens must be an int32 GPU tensor [B]")
+    if out is None:
+        raise ValueError("out is required: this entry point allocates nothing")
+    _same_device(q, k, v, lens)
+    out = _out(out, (B, Hq, D), q, torch.bfloat16, contiguous=True, name="out")
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t.numel() else 0)
+    with torch.cuda.device(q.device):
+        rc = load_library().det_attention_decode_noalloc(ptr(q), ptr(k), ptr(v), ptr(lens), B, Hq,
+                                                         Hkv, Smax, D, ctypes.c_float(scale),
+                                                         ptr(out), _stream(q))
+    _check(rc, "det_attention_decode_noalloc")
     return out
 
 

@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "bf16_device.h"
 #include "det_attention.h"
@@ -292,18 +293,45 @@ bool disjoint(const void *a, int64_t na, const void *b, int64_t nb) {
     return na <= 0 || nb <= 0 || a0 + (uintptr_t)na <= b0 || b0 + (uintptr_t)nb <= a0;
 }
 
-}  // namespace
+// ---- the allocation-free variant: the per-split partials in a file-scope
+// device array instead of a caller's buffer.  Each device the library runs on
+// holds its own copy until the process ends; its address on a device is taken
+// once, with that device current, and used from then on (the array's name is a
+// host-side stand-in, not a device address).
+constexpr int64_t kScratchFloats = DET_ATTN_SCRATCH_FLOATS;
+static __device__ __align__(256) float scratch[kScratchFloats];
 
-extern "C" int det_attention_decode(const det_bf16 *Q, const det_bf16 *K, const det_bf16 *V,
-                                    const int32_t *lens, int64_t B, int64_t Hq, int64_t Hkv,
-                                    int64_t Smax, int64_t D, float scale, float *work,
-                                    det_bf16 *O, void *stream) {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch[kMaxDevices];
+
+// The current device's copy of `scratch`, or nullptr on a runtime error.
+float *scratch_on_current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return nullptr;
+        g_scratch[dev] = static_cast<float *>(p);
+    }
+    return g_scratch[dev];
+}
+
+// Shape checks shared by both entry points; NS receives the split count.
+int check_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t Smax, int64_t D, int64_t &NS) {
     if (B < 0 || Hq < 1 || Hkv < 1 || Smax < 0 || D != kD || Hq % Hkv != 0 ||
         Hq / Hkv > kGMax || B > 65535 || Hkv > 65535 || Hq > 65535 || Smax > (1 << 24))
         return DET_GEMM_EINVAL;
-    if (B == 0)
-        return DET_GEMM_OK;
-    const int64_t NS = (Smax + kSplit - 1) / kSplit;
+    NS = (Smax + kSplit - 1) / kSplit;
+    return DET_GEMM_OK;
+}
+
+int run_attention(const det_bf16 *Q, const det_bf16 *K, const det_bf16 *V, const int32_t *lens,
+                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Smax, int64_t NS, float scale,
+                  float *work, det_bf16 *O, void *stream) {
     if (!Q || !lens || !O || (NS > 0 && (!K || !V || !work)))
         return DET_GEMM_EINVAL;
     const int64_t qb = B * Hq * kD * 2, kvb = B * Hkv * Smax * kD * 2;
@@ -339,4 +367,36 @@ extern "C" int det_attention_decode(const det_bf16 *Q, const det_bf16 *K, const 
     hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)Hq, (unsigned)B), dim3(kD), 0, st, lens,
                        (int)Hq, (int)Smax, (int)NS, work, O);
     return hipGetLastError() == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
+}
+
+}  // namespace
+
+extern "C" int det_attention_decode(const det_bf16 *Q, const det_bf16 *K, const det_bf16 *V,
+                                    const int32_t *lens, int64_t B, int64_t Hq, int64_t Hkv,
+                                    int64_t Smax, int64_t D, float scale, float *work,
+                                    det_bf16 *O, void *stream) {
+    int64_t NS = 0;
+    const int rc = check_shape(B, Hq, Hkv, Smax, D, NS);
+    if (rc != DET_GEMM_OK || B == 0)
+        return rc;
+    return run_attention(Q, K, V, lens, B, Hq, Hkv, Smax, NS, scale, work, O, stream);
+}
+
+extern "C" int det_attention_decode_noalloc(const det_bf16 *Q, const det_bf16 *K,
+                                            const det_bf16 *V, const int32_t *lens, int64_t B,
+                                            int64_t Hq, int64_t Hkv, int64_t Smax, int64_t D,
+                                            float scale, det_bf16 *O, void *stream) {
+    int64_t NS = 0;
+    const int rc = check_shape(B, Hq, Hkv, Smax, D, NS);
+    if (rc != DET_GEMM_OK || B == 0)
+        return rc;
+    // B, Hq <= 65535 and NS <= 2^16: the product fits in int64
+    if (B * Hq * NS * (kD + 2) > kScratchFloats)
+        return DET_ATTN_ESCRATCH;
+    if (check_device() != DET_GEMM_OK)
+        return DET_GEMM_EHIP;
+    float *work = scratch_on_current_device();
+    if (!work)
+        return DET_GEMM_EHIP;
+    return run_attention(Q, K, V, lens, B, Hq, Hkv, Smax, NS, scale, work, O, stream);
 }

@@ -19,6 +19,7 @@
 #include <cstring>
 #include <vector>
 
+#include "det_attention.h"
 #include "det_gemm.h"
 #include "det_moe.h"
 #include "mfma_launch.h"
@@ -777,6 +778,8 @@ const char *det_gemm_status_string(int status) {
         return "reduction length must be in [1, 32768]";
     case DET_GEMM_EHIP:
         return "HIP runtime error or no gfx950 device";
+    case DET_ATTN_ESCRATCH:
+        return "problem needs more scratch than the library's fixed device array holds";
     default:
         return "unknown status";
     }

@@ -268,3 +268,16 @@ def test_binding_refuses_host_tensors():
         dg.det_attention_decode(q, k, k, lens, 0.1)
     with pytest.raises(TypeError):
         dg.det_gemm_fwd(_t((4, 64), torch.bfloat16), _t((64, 8), torch.bfloat16))
+
+
+def test_attention_noalloc_refuses_oversize_without_device(lib):
+    """det_attention_decode_noalloc: a problem whose per-split partials exceed
+    the fixed device array is refused before any device work."""
+    f = lib.det_attention_decode_noalloc
+    A = ctypes.c_void_p(0x100000000)
+    s = ctypes.c_float(0.1)
+    o = ctypes.c_void_p(0x900000000)
+    assert f(FAKE, A, A, FAKE, 65535, 32, 8, 4096, 128, s, o, NULL) == dg.ESCRATCH
+    assert f(FAKE, A, A, FAKE, 2, 8, 2, 64, 64, s, o, NULL) == dg.EINVAL   # D != 128
+    assert f(FAKE, A, A, FAKE, 0, 8, 2, 64, 128, s, o, NULL) == dg.OK      # no sequences
+    assert b"scratch" in lib.det_gemm_status_string(dg.ESCRATCH)
