@@ -27,6 +27,8 @@ M, K, N = 4096, 4096, 6144
 COPY_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles",
                             "hbm_traffic_per_launch.md")
+ISSUE_FILE = os.path.join(ROOT, "profiles", "det_gemm_step_M4096_K4096_N6144_sq_counters.md")
+CLOCK_MHZ_PEAK = 2400.0     # the clock the published peak assumes
 CSRC = os.path.join(ROOT, "invariant_deterministic_gemm_det_amd", "csrc")
 
 
@@ -41,23 +43,55 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def recorded_traffic(op):
-    """HBM bytes per launch of `op` from the rocprofv3 counter summary, or None when
-    the summary is missing or was taken on different kernel sources."""
+def profile_fields(path):
+    """The machine-readable `- key: value` lines of a rocprofv3 summary under
+    profiles/, or {} when the file is missing or was taken on other kernel
+    sources (its kernel_source_sha256 differs from the current sources)."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             lines = f.read().splitlines()
     except OSError:
-        return None
+        return {}
     fields = {}
     for ln in lines:
         if ln.startswith("- ") and ": " in ln:
             k, v = ln[2:].split(": ", 1)
             fields[k.strip()] = v.strip().strip("`")
     if fields.get("kernel_source_sha256") != kernel_source_hash():
-        return None
-    v = fields.get(f"hbm_bytes_per_launch_{op}")
+        return {}
+    return fields
+
+
+def recorded_traffic(op):
+    """HBM bytes per launch of `op` from the rocprofv3 counter summary, or None when
+    the summary is missing or was taken on different kernel sources."""
+    v = profile_fields(TRAFFIC_FILE).get(f"hbm_bytes_per_launch_{op}")
     return int(v) if v else None
+
+
+def recorded_issue(op):
+    """From the matrix-core / VALU counter pass of the step kernels: the shader
+    clock under load (SQ_BUSY_CYCLES per shader engine / kernel duration, MHz)
+    and the non-MFMA VALU instructions per 16x16 block and leaf, or {}."""
+    f = profile_fields(ISSUE_FILE)
+    out = {}
+    if f.get(f"sclk_mhz_{op}"):
+        out["sclk_mhz"] = float(f[f"sclk_mhz_{op}"])
+    if f.get(f"valu_per_block_leaf_{op}"):
+        out["valu_per_block_leaf"] = float(f[f"valu_per_block_leaf_{op}"])
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def parse():
@@ -105,7 +139,7 @@ def cpu_baseline(X, W, dC, target_s):
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * N * K + 2.0 * rows * K * N + 2.0 * rows * N * M
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 3),
+            "seconds": round(dt, 3), "cpu_model": cpu_model(), "nproc": os.cpu_count(),
             "sample": f"CPU oracle on {rows} output rows of each product: fwd C[:{rows}], "
                       f"da dX[:{rows}], db dW[:{rows}] of the M=4096 K=4096 N=6144 step"}
 
@@ -486,6 +520,28 @@ def small_m_leg(dev, steps, warmup, decode_only=False):
             "roofline": "hbm, 8000 GB/s", "rows": rows}
 
 
+def strict_leg(X, W, rows):
+    """The strict-order kernel (det_gemm_strict_fwd: one scalar fp32 FMA chain
+    per leaf, bit-exact to the oracle) on a row slice of the forward product,
+    timed with HIP events on the launch stream."""
+    import torch
+    import invariant_deterministic_gemm_det_amd as dg
+    x = X[:rows]
+    out = dg.det_gemm_fwd(x, W, strict=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        dg.det_gemm_fwd(x, W, out=out, strict=True)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 3
+    flop = 2.0 * rows * N * K
+    return {"kernel": "strict_kernel (K1)", "sample": f"fwd on {rows} rows of the step shape "
+            f"(M={rows}, K={K}, N={N})", "ms": round(ms, 4),
+            "tflops": round(flop / (ms * 1e-3) / 1e12, 3)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -505,6 +561,7 @@ def main():
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     dW = torch.empty((K, N), dtype=torch.bfloat16, device=dev)
+    flop = 2.0 * M * N * K
 
     def step(ev=None):
         if ev:
@@ -519,41 +576,34 @@ def main():
         if ev:
             ev[3].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    per_op = {"fwd": [], "da": [], "db": []}
-    for ev in events:
-        per_op["fwd"].append(ev[0].elapsed_time(ev[1]))
-        per_op["da"].append(ev[1].elapsed_time(ev[2]))
-        per_op["db"].append(ev[2].elapsed_time(ev[3]))
-    flop = 2.0 * M * N * K
-    ms_step = wall * 1e3 / args.steps
-    value = 3 * flop / (ms_step * 1e-3) / 1e12
-    ops = {}
-    for name, ts in per_op.items():
-        avg = sum(ts) / len(ts)
-        med = statistics.median(ts)
-        ops[name] = {"ms": round(avg, 4), "tflops": round(flop / (avg * 1e-3) / 1e12, 2),
-                     "median_ms": round(med, 4), "min_ms": round(min(ts), 4), "max_ms": round(max(ts), 4)}
-    dom = max(ops, key=lambda k: ops[k]["ms"])
-    achieved = ops[dom]["tflops"]
-    # the kernels the library selects for these shapes (wide kernel, 128x128 tiles):
-    # L = 128 for fwd (R = K) and db (R = M), L = 192 = 3 * 64 for da (R = N)
-    kernel_names = {"fwd": "mfma_wide_kernel<K-major X, MN-major Y, bf16 out, 2-leaf units>",
-                    "da": "mfma_wide_kernel<K-major X, K-major Y, bf16 out, 3-leaf units>",
-                    "db": "mfma_wide_kernel<MN-major X, MN-major Y, bf16 out, 2-leaf units>"}
+    def timed_step_loop():
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                  for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(events[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per_op = {"fwd": [], "da": [], "db": []}
+        for ev in events:
+            per_op["fwd"].append(ev[0].elapsed_time(ev[1]))
+            per_op["da"].append(ev[1].elapsed_time(ev[2]))
+            per_op["db"].append(ev[2].elapsed_time(ev[3]))
+        ops = {}
+        for name, ts in per_op.items():
+            avg = sum(ts) / len(ts)
+            med = statistics.median(ts)
+            ops[name] = {"ms": round(avg, 4), "tflops": round(flop / (avg * 1e-3) / 1e12, 2),
+                         "median_ms": round(med, 4), "min_ms": round(min(ts), 4),
+                         "max_ms": round(max(ts), 4)}
+        return wall, ops
 
     if args.profile_only:
+        _, ops = timed_step_loop()
         if not args.no_moe:
             moe_leg(dev, args.steps, args.warmup, False, context=False)
         if not args.no_fingerprint:
@@ -576,6 +626,33 @@ def main():
         print(json.dumps({"profile_only": True, "ops": ops}))
         return
 
+    # The CPU oracle first, then the other GPU legs, then the headline step: the
+    # step is timed once the device has been under load for a while (its clocks
+    # at their loaded level), not straight after the host-bound oracle leg.
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(X, W, dC, args.cpu_seconds)
+    moe = None if args.no_moe else moe_leg(dev, args.steps, args.warmup, not args.no_cpu)
+    fp = None if args.no_fingerprint else fingerprint_leg(dev, args.steps, args.warmup,
+                                                          not args.no_cpu)
+    norm = None if args.no_rmsnorm else rmsnorm_leg(dev, args.steps, args.warmup, not args.no_cpu)
+    attn = None if args.no_attention else attention_leg(dev, args.steps, args.warmup,
+                                                        not args.no_cpu)
+    shard = None if args.no_shard else shard_leg(dev, args.steps, args.warmup)
+    small = None if args.no_small_m else small_m_leg(dev, args.steps, args.warmup)
+    strict = strict_leg(X, W, 256)
+
+    wall, ops = timed_step_loop()
+    ms_step = wall * 1e3 / args.steps
+    value = 3 * flop / (ms_step * 1e-3) / 1e12
+    dom = max(ops, key=lambda k: ops[k]["ms"])
+    achieved = ops[dom]["tflops"]
+    # the kernels the library selects for these shapes (wide kernel, 128x128 tiles):
+    # L = 128 for fwd (R = K) and db (R = M), L = 192 = 3 * 64 for da (R = N)
+    kernel_names = {"fwd": "mfma_wide_kernel<K-major X, MN-major Y, bf16 out, 2-leaf units>",
+                    "da": "mfma_wide_kernel<K-major X, K-major Y, bf16 out, 3-leaf units>",
+                    "db": "mfma_wide_kernel<MN-major X, MN-major Y, bf16 out, 2-leaf units>"}
+
     # context, not the metric: the nondeterministic library GEMM on the forward shape
     ctx = {}
     try:
@@ -594,17 +671,24 @@ def main():
     except Exception as e:  # context only
         ctx = {"torch_matmul_error": str(e)[:120]}
 
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(X, W, dC, args.cpu_seconds)
-    moe = None if args.no_moe else moe_leg(dev, args.steps, args.warmup, not args.no_cpu)
-    fp = None if args.no_fingerprint else fingerprint_leg(dev, args.steps, args.warmup,
-                                                          not args.no_cpu)
-    norm = None if args.no_rmsnorm else rmsnorm_leg(dev, args.steps, args.warmup, not args.no_cpu)
-    attn = None if args.no_attention else attention_leg(dev, args.steps, args.warmup,
-                                                        not args.no_cpu)
-    shard = None if args.no_shard else shard_leg(dev, args.steps, args.warmup)
-    small = None if args.no_small_m else small_m_leg(dev, args.steps, args.warmup)
+    # Ceilings of the dominant kernel (from the committed counter pass of the
+    # same kernels): the clock the chip held under this load, the share of the
+    # published peak at that clock, and the two issue ceilings per 16x16 block
+    # and leaf -- the matrix core (a leaf MFMA and a tree-add MFMA of 16 cycles
+    # each: at most half of its cycles are leaf products) and the VALU issue
+    # port (v non-MFMA VALU instructions plus the two MFMA issues, 4 cycles
+    # each, against the 16 cycles of the leaf MFMA).
+    issue = recorded_issue(dom)
+    ceilings = {"mfma_leaf_share": 0.5}
+    at_clock = None
+    if "sclk_mhz" in issue:
+        peak_at_clock = PEAK_BF16_TFLOPS * issue["sclk_mhz"] / CLOCK_MHZ_PEAK
+        at_clock = {"sclk_mhz": issue["sclk_mhz"], "peak_tflops": round(peak_at_clock, 1),
+                    "pct_of_peak_at_measured_clock": round(100 * achieved / peak_at_clock, 2)}
+    if "valu_per_block_leaf" in issue:
+        v = issue["valu_per_block_leaf"]
+        ceilings["valu_issue"] = round(16.0 / (4.0 * (v + 2.0)), 4)
+        ceilings["valu_per_block_leaf"] = v
 
     line = {
         "metric": "det_gemm TFLOP/s and % of bf16 MFMA peak at M=4096,K=4096,N=6144 (1 GPU)",
@@ -628,7 +712,9 @@ def main():
         "roofline": {"bound": "mfma", "kernel": f"{dom}: {kernel_names[dom]}",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": recorded_traffic(dom)},
+                     "traffic": recorded_traffic(dom),
+                     "at_measured_clock": at_clock, "ceilings": ceilings},
+        "strict_k1": strict,
         "cpu_baseline": cpu,
         "context": ctx,
         "moe_grouped_gemm": moe,

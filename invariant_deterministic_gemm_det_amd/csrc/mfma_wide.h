@@ -178,14 +178,108 @@ __device__ __forceinline__ float slot_tree8(const float (&pr)[8]) {
     return v;
 }
 
+// Byte offset of byte `byte` of staged row r.  Padded (SWZ false): rows
+// 2 * COLS + 16 bytes apart.  Swizzled (SWZ true): rows 2 * COLS bytes apart,
+// 16-byte chunk c of row r stored at chunk c ^ (r mod 16) (at most 16 chunks
+// per row), which spreads the 16 rows of one write over the banks as the
+// padding does, in exactly ROWS * COLS * 2 bytes.
+template <int COLS, bool SWZ>
+__device__ __forceinline__ int staged_off(int r, int byte) {
+    if constexpr (SWZ) {
+        constexpr int CHM = (COLS / 8 < 16 ? COLS / 8 : 16) - 1;
+        return r * (COLS * 2) + ((((byte >> 4) ^ (r & CHM)) << 4) | (byte & 15));
+    } else {
+        return r * (COLS * 2 + 16) + byte;
+    }
+}
+
+// Publishes each wave's non-finite flag through one dword per wave of `flags`
+// (LDS) with one barrier, which also publishes whatever the waves wrote to the
+// LDS before it.  Returns whether any wave's flag is set; in that case a second
+// barrier has retired every wave's read of the flags, so the caller may reuse
+// the LDS.
+template <int NW>
+__device__ __forceinline__ bool publish_nonfinite(int *flags, bool nonfinite) {
+    static_assert(NW % 4 == 0, "flags are read four at a time");
+    const bool any = __builtin_amdgcn_ballot_w64(nonfinite) != 0;
+    if ((threadIdx.x & 63) == 0)
+        flags[threadIdx.x >> 6] = any ? 1 : 0;
+    __syncthreads();
+    uint32_t r = 0;
+#pragma unroll
+    for (int q = 0; q < NW; q += 4) {
+        const uint4 f = *reinterpret_cast<const uint4 *>(flags + q);
+        r |= f.x | f.y | f.z | f.w;
+    }
+    if (r != 0) {
+        __syncthreads();
+        return true;
+    }
+    return false;
+}
+
+// Two rounded roots packed in a dword, with a zero of either sign stored as
+// +0: within a half, x & 0x7FFF is nonzero exactly when adding 0x7FFF to it
+// carries into bit 15 (no carry crosses into the other half), which selects
+// the mask 0xFFFF or 0 for that half.
+__device__ __forceinline__ uint32_t plus_zero_pair(uint32_t w) {
+    const uint32_t nz = (((w & 0x7FFF7FFFu) + 0x7FFF7FFFu) & 0x80008000u) >> 15;
+    return w & (nz * 0xFFFFu);
+}
+
+// Whether either bf16 of a packed pair is Inf or NaN (exponent all ones).
+__device__ __forceinline__ bool pair_nonfinite(uint32_t w) {
+    const uint32_t e = (w & 0x7F807F80u) ^ 0x7F807F80u;
+    return (e & 0xFFFFu) == 0 || (e >> 16) == 0;
+}
+
+// Writes a tile's roots to the staged rows.  ROWROW: the lane's four values of
+// a block lie in one staged row (one 8-byte write), else in four rows.
+// Returns whether a rounded root of this lane is Inf or NaN (a non-finite
+// fp32 root stays non-finite when rounded).
+template <bool T, bool ROWROW, int FM, int FN, int COLS, bool SWZ>
+__device__ __forceinline__ bool stage_roots(const Frag<FM, FN> &root, int wm, int wn, int lane,
+                                            char *lds) {
+    const int g = lane >> 4, c = lane & 15;
+    bool nonfinite = false;
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+            const uint32_t lo = plus_zero_pair(pair_bits(round_pair(root.v[a][b][0], root.v[a][b][1])));
+            const uint32_t hi = plus_zero_pair(pair_bits(round_pair(root.v[a][b][2], root.v[a][b][3])));
+            nonfinite |= pair_nonfinite(lo) | pair_nonfinite(hi);
+            const int rb = wm * FM * 16 + a * 16, cb = wn * FN * 16 + b * 16;  // block origin (i, j)
+            if constexpr (ROWROW) {
+                const int r = T ? cb + c : rb + c;
+                const int col = T ? rb + 4 * g : cb + 4 * g;
+                *reinterpret_cast<uint2 *>(lds + staged_off<COLS, SWZ>(r, col * 2)) = make_uint2(lo, hi);
+            } else {
+                const uint16_t v4[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi,
+                                        (uint16_t)(hi >> 16)};
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = T ? cb + 4 * g + v : rb + 4 * g + v;
+                    const int col = T ? rb + c : cb + c;
+                    *reinterpret_cast<uint16_t *>(lds + staged_off<COLS, SWZ>(r, col * 2)) = v4[v];
+                }
+            }
+        }
+    return nonfinite;
+}
+
 // EPI: also the slots of the epilogue (operands in the EpiInfo at the start of
-// the dynamic LDS; this tile's rows start at its row r0).
-template <int OUT, int FM, int FN, int BM, int BN, int NW, bool EPI = false>
-__device__ __forceinline__ void store_staged(const MfmaParams &p, const Frag<FM, FN> &root, bool odd,
-                                             int i0, int j0, int wm, int wn, int lane, char *lds) {
+// the dynamic LDS; this tile's rows start at its row r0).  FLAGS: the
+// non-finite check of the rounded roots rides on the staging barrier
+// (publish_nonfinite); a tile with a non-finite root is then not stored and
+// true is returned.
+template <int OUT, int FM, int FN, int BM, int BN, int NW, bool EPI = false, bool SWZ = false,
+          bool FLAGS = false>
+__device__ __forceinline__ bool store_staged(const MfmaParams &p, const Frag<FM, FN> &root, bool odd,
+                                             int i0, int j0, int wm, int wn, int lane, char *lds,
+                                             int *flags = nullptr) {
     constexpr bool T = OUT == OUT_BF16_T;
     constexpr int ROWS = T ? BN : BM, COLS = T ? BM : BN;  // of the staged block
-    constexpr int RS = COLS * 2 + 16;                      // LDS row stride, bytes
     // Per-token epilogue: a row's slot is reduced by 16 lanes holding 8
     // columns each; a wave takes 4 rows per pass.  The G chunks are loaded
     // first, so that their latency overlaps the staging.
@@ -230,34 +324,18 @@ __device__ __forceinline__ void store_staged(const MfmaParams &p, const Frag<FM,
             }
         }
     }
-    const int g = lane >> 4, c = lane & 15;
-#pragma unroll
-    for (int a = 0; a < FM; ++a)
-#pragma unroll
-        for (int b = 0; b < FN; ++b) {
-            uint16_t v4[4];
-            quad_bits(root, a, b, v4);
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                v4[v] = (v4[v] & 0x7FFF) ? v4[v] : (uint16_t)0;
-            const int rb = wm * FM * 16 + a * 16, cb = wn * FN * 16 + b * 16;  // block origin (i, j)
-            // the lane's four values: odd parity (rb + c, cb + 4g + v), even (rb + 4g + v, cb + c);
-            // they are contiguous in a staged row when that row is i (odd, not T) or j (even, T)
-            if (odd != T) {
-                const int r = T ? cb + c : rb + c;
-                const int col = T ? rb + 4 * g : cb + 4 * g;
-                const uint2 w = make_uint2(v4[0] | ((uint32_t)v4[1] << 16), v4[2] | ((uint32_t)v4[3] << 16));
-                *reinterpret_cast<uint2 *>(lds + r * RS + col * 2) = w;
-            } else {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int r = T ? cb + 4 * g + v : rb + 4 * g + v;
-                    const int col = T ? rb + c : cb + c;
-                    *reinterpret_cast<uint16_t *>(lds + r * RS + col * 2) = v4[v];
-                }
-            }
-        }
-    __syncthreads();
+    // the lane's four values of a block: odd parity (rb + c, cb + 4g + v), even
+    // (rb + 4g + v, cb + c); they are contiguous in a staged row when that row
+    // is i (odd, not T) or j (even, T).  One uniform branch on the parity, so
+    // each variant is straight-line code.
+    const bool staged_nonfinite = odd != T ? stage_roots<T, true, FM, FN, COLS, SWZ>(root, wm, wn, lane, lds)
+                                           : stage_roots<T, false, FM, FN, COLS, SWZ>(root, wm, wn, lane, lds);
+    if constexpr (FLAGS) {
+        if (publish_nonfinite<NW>(flags, staged_nonfinite))
+            return true;
+    } else {
+        __syncthreads();
+    }
     // read out: 16-byte chunks of staged rows
     const int row0 = T ? j0 : i0, col0 = T ? i0 : j0;
     const int rows_ok = (T ? p.J : p.I) - row0, cols_ok = (T ? p.I : p.J) - col0;
@@ -269,7 +347,7 @@ __device__ __forceinline__ void store_staged(const MfmaParams &p, const Frag<FM,
         const int r = q / CH, ch = q % CH;
         if (r >= rows_ok)
             continue;
-        const uint4 w = *reinterpret_cast<const uint4 *>(lds + r * RS + ch * 16);
+        const uint4 w = *reinterpret_cast<const uint4 *>(lds + staged_off<COLS, SWZ>(r, ch * 16));
         uint16_t *dst = out + (int64_t)(row0 + r) * p.ldc + col0 + ch * 8;
         if (p.cvec && ch * 8 + 8 <= cols_ok) {
             *reinterpret_cast<uint4 *>(dst) = w;
@@ -290,7 +368,7 @@ __device__ __forceinline__ void store_staged(const MfmaParams &p, const Frag<FM,
 #pragma unroll
             for (int k = 0; k < EP; ++k) {
                 const int r = erow + k * 4 * NW;
-                const uint4 yq = *reinterpret_cast<const uint4 *>(lds + r * RS + c8 * 2);
+                const uint4 yq = *reinterpret_cast<const uint4 *>(lds + staged_off<COLS, SWZ>(r, c8 * 2));
                 const uint32_t yw[4] = {yq.x, yq.y, yq.z, yq.w};
                 const uint32_t gw[4] = {gq[k].x, gq[k].y, gq[k].z, gq[k].w};
                 float pr[8];
@@ -306,6 +384,7 @@ __device__ __forceinline__ void store_staged(const MfmaParams &p, const Frag<FM,
             }
         }
     }
+    return false;
 }
 
 // With NBUF >= 3 the copies are issued early: before the barrier that opens
@@ -403,6 +482,14 @@ struct WideEngine {
         }
         S = p.R / 64;
         park_lane = lds_ + threadIdx.x * 8;
+    }
+
+    // Stage buffer k (0 or 1) of the two that nothing can still read or fill
+    // once every wave is past the barrier of the last stage S - 1: those of
+    // stages S - 3 and S - 2 (or never used), all copies done (NBUF >= 3).
+    __device__ __forceinline__ char *free_buffer(int k) const {
+        static_assert(NBUF >= 3, "two free stage buffers at the end of the tile");
+        return smem + ((unsigned)(S + k) % NBUF) * BUF;
     }
 
     __device__ __forceinline__ void issue(int s) {
@@ -737,26 +824,47 @@ struct WideTree {
     // stored (true is returned, the caller recomputes it); element-wise adds
     // always store.  The barrier of the check also frees the LDS for staging.
     __device__ __forceinline__ bool finish_root(const F &root) {
-        bool nonfinite = false;
-        if constexpr (Arith::kTransposes) {
+        const int wave = threadIdx.x >> 6;
+        const auto fp32_nonfinite = [&]() {
+            bool nonfinite = false;
+            if constexpr (Arith::kTransposes) {
 #pragma unroll
-            for (int a = 0; a < E::kFM; ++a)
+                for (int a = 0; a < E::kFM; ++a)
 #pragma unroll
-                for (int b = 0; b < E::kFN; ++b)
+                    for (int b = 0; b < E::kFN; ++b)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        nonfinite |= !(__builtin_fabsf(root.v[a][b][v]) <= 3.40282347e38f);
-        }
-        if (e.any_in_workgroup(nonfinite))
-            return true;
-        if constexpr (E::kOUT == OUT_F32) {
-            store(root);
+                        for (int v = 0; v < 4; ++v)
+                            nonfinite |= !(__builtin_fabsf(root.v[a][b][v]) <= 3.40282347e38f);
+            }
+            return nonfinite;
+        };
+        if constexpr (E::kEarly) {
+            // One barrier: the staged tile goes to one free stage buffer, the
+            // wave flags to the other (see WideEngine::free_buffer).
+            int *flags = reinterpret_cast<int *>(e.free_buffer(1));
+            if constexpr (E::kOUT == OUT_F32) {
+                if (publish_nonfinite<E::NW>(flags, fp32_nonfinite()))
+                    return true;
+                store(root);
+                return false;
+            } else {
+                // element-wise adds never need the recomputation
+                return store_staged<E::kOUT, E::kFM, E::kFN, E::BM, E::BN, E::NW, EPI, true,
+                                    Arith::kTransposes>(
+                    p, root, odd, i0, j0, wave % E::kWM, wave / E::kWM, threadIdx.x & 63,
+                    e.free_buffer(0), flags);
+            }
         } else {
-            const int wave = threadIdx.x >> 6;
-            store_staged<E::kOUT, E::kFM, E::kFN, E::BM, E::BN, E::NW, EPI>(
-                p, root, odd, i0, j0, wave % E::kWM, wave / E::kWM, threadIdx.x & 63, e.lds);
+            if (e.any_in_workgroup(fp32_nonfinite()))
+                return true;
+            if constexpr (E::kOUT == OUT_F32) {
+                store(root);
+            } else {
+                store_staged<E::kOUT, E::kFM, E::kFN, E::BM, E::BN, E::NW, EPI>(
+                    p, root, odd, i0, j0, wave % E::kWM, wave / E::kWM, threadIdx.x & 63, e.lds);
+            }
+            return false;
         }
-        return false;
     }
 
     // Stage U of group t: the fragment reads of the stage, the tree work of
