@@ -348,7 +348,7 @@ def rmsnorm_leg(dev, steps, warmup, with_cpu, decode=True):
     out = {"workload": "RMSNorm of 8192 x 4096 bf16 rows (read x, write y and rstd); "
                        "decode: 64 rows, per call from graph replays of back-to-back calls",
            "ms": round(t_full, 4), "GB/s": round(gbs, 1), "decode_64_rows_us": round(t_dec * 1e3, 2),
-           "roofline": {"bound": "hbm", "kernel": "rmsnorm_kernel (8192 x 4096)",
+           "roofline": {"bound": "hbm", "kernel": "rmsnorm_fixed_kernel<16> (8192 x 4096)",
                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": recorded_traffic("norm")}}
     if with_cpu:

@@ -9,10 +9,10 @@
  * never done here.
  *
  * What is computed for each row x[0..H) (bf16), weight w[0..H) (bf16), eps:
- *   lane partials  p_t, t < 256: lane t owns the 8-element chunks c with
- *                  c mod 256 == t and adds x_i^2 over its elements in
- *                  ascending i, in fp32 from +0;
- *   ss             the pairwise tree of fp32 adds over p_0 .. p_255;
+ *   squares        x_i^2 in fp32;
+ *   ss             the mid-split tree of fp32 adds over the H squares (a
+ *                  range of n splits into floor(n/2) on the left and the rest
+ *                  on the right), an order that depends on H alone;
  *   rstd           1 / sqrt(ss / H + eps), each operation rounded once (fp32);
  *   y_i            bf16 (nearest even) of (x_i * rstd) * w_i in fp32.
  * One workgroup owns one row, so a row's bits never depend on R, on the other

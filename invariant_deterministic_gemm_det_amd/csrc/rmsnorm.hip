@@ -4,15 +4,26 @@
 // batch-invariant kernel design, RMSNorm: each row is reduced by one
 // workgroup with one fixed strategy, never split across workgroups.
 //
-// One workgroup of 256 threads per row; thread t is lane t of the definition:
-// it reads its 8-element chunks t, t + 256, ... with 16-byte loads, sums their
-// squares in ascending order, and keeps up to four chunks in registers for the
-// output pass (rows of up to 8192 elements are read from HBM once).  The
-// 256 lane sums meet in the pairwise tree: six shuffle levels inside each
-// wave, then (wave 0 + wave 1) + (wave 2 + wave 3).  Square root and division
-// are rounded to nearest as the definition requires (the runtime's fp32
-// square root and division are not guaranteed to be): a candidate from fp64,
-// moved to the fp32 neighbour while that is closer, decided exactly in fp64.
+// The sum of squares is the mid-split tree of fp32 adds over the row's H
+// squares.  One workgroup of 256 threads per row evaluates it from the nodes
+// of depth 8: thread t takes node t (bits of t from the top: 0 = left child),
+// a contiguous range of about H / 256 elements, and evaluates that subtree
+// itself; the 256 node sums then meet in the top 8 levels, six shuffle levels
+// inside each wave and (wave 0 + wave 1) + (wave 2 + wave 3).  A node of one
+// element has no children, so for H < 256 some positions of depth 8 are empty
+// and a parent with an empty right child is its left child.
+//   * H = 256 * M with M in the instantiated set: every node holds exactly M
+//     elements, [M t, M t + M); the thread loads them with the widest aligned
+//     loads, evaluates the subtree at compile time in registers, and writes
+//     its own outputs from the kept values (the row is read from HBM once).
+//   * any other H: each thread walks its range in ascending order with the
+//     streaming post-order of the mid-split tree (a stack of pending left
+//     subtrees in LDS), then the output pass reads the row again in 16-byte
+//     chunks.
+// Square root and division are rounded to nearest as the definition requires
+// (the runtime's fp32 square root and division are not guaranteed to be): a
+// candidate from fp64, moved to the fp32 neighbour while that is closer,
+// decided exactly in fp64.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -27,7 +38,7 @@ namespace {
 
 constexpr int kLanes = 256;
 constexpr int kChunk = 8;
-constexpr int kKeep = 4;
+constexpr int kStack = 16;   // pending left subtrees of a node's walk: ranges below 2^15
 
 __device__ __forceinline__ float bf(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -53,15 +64,6 @@ __device__ __forceinline__ void store_chunk(uint16_t *row, int c, int H, uint4 v
         row[8 * c + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
 }
 
-__device__ __forceinline__ float chunk_sumsq(float p, uint4 v) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float x = bf((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-        p = __fadd_rn(p, __fmul_rn(x, x));
-    }
-    return p;
-}
 
 __device__ __forceinline__ uint4 chunk_out(uint4 xv, uint4 wv, float rs) {
     const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, ww[4] = {wv.x, wv.y, wv.z, wv.w};
@@ -117,45 +119,186 @@ __device__ __forceinline__ float div_rn(float a, float b) {
     return q;
 }
 
-template <bool VEC>
-__global__ __launch_bounds__(kLanes) void rmsnorm_kernel(const uint16_t *x, int64_t ldx,
-                                                         const uint16_t *w, float eps, uint16_t *y,
-                                                         int64_t ldy, float *rstd, int H) {
+__device__ __forceinline__ float square(uint32_t bits16) {
+    const float x = bf(bits16);
+    return __fmul_rn(x, x);
+}
+
+// Mid-split tree of fp32 adds over the compile-time range s[LO, HI).
+template <int LO, int HI, int M>
+__device__ __forceinline__ float tree_sum(const float (&s)[M]) {
+    if constexpr (HI - LO == 1) {
+        return s[LO];
+    } else {
+        constexpr int MID = LO + (HI - LO) / 2;
+        return __fadd_rn(tree_sum<LO, MID>(s), tree_sum<MID, HI>(s));
+    }
+}
+
+// The top 8 levels over the 256 node sums (one per thread) and the row's
+// rstd; `empty`: this thread's position of depth 8 holds no node (H < 256).
+// Both threads of a pair compute the same parent (fp32 addition commutes).
+__device__ __forceinline__ float row_rstd(float p, bool empty, int H, float eps) {
     __shared__ float part[kLanes / 64];
+    __shared__ int part_empty[kLanes / 64];
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const float q = __shfl_xor(p, m, 64);
+        const bool qe = __shfl_xor(empty ? 1 : 0, m, 64) != 0;
+        p = empty ? q : (qe ? p : __fadd_rn(p, q));
+        empty = empty && qe;
+    }
+    if ((t & 63) == 0) {
+        part[t >> 6] = p;
+        part_empty[t >> 6] = empty ? 1 : 0;
+    }
+    __syncthreads();
+    const auto join = [](float a, bool ae, float b, bool be, bool &e) {
+        e = ae && be;
+        return ae ? b : (be ? a : __fadd_rn(a, b));
+    };
+    bool e01, e23, e;
+    const float s01 = join(part[0], part_empty[0] != 0, part[1], part_empty[1] != 0, e01);
+    const float s23 = join(part[2], part_empty[2] != 0, part[3], part_empty[3] != 0, e23);
+    const float ss = join(s01, e01, s23, e23, e);
+    return div_rn(1.0f, sqrt_rn(__fadd_rn(div_rn(ss, (float)H), eps)));
+}
+
+// H = 256 * M.  G: elements per load (8, 4, 2 or 1; VEC false: 1).
+template <int M, bool VEC>
+__global__ __launch_bounds__(kLanes) void rmsnorm_fixed_kernel(const uint16_t *x, int64_t ldx,
+                                                               const uint16_t *w, float eps,
+                                                               uint16_t *y, int64_t ldy,
+                                                               float *rstd) {
+    constexpr int G = !VEC ? 1 : (M % 8 == 0 ? 8 : (M % 4 == 0 ? 4 : (M % 2 == 0 ? 2 : 1)));
+    constexpr int H = kLanes * M;
+    const int64_t r = blockIdx.x;
+    const int i0 = M * threadIdx.x;
+    const uint16_t *xr = x + r * ldx + i0;
+    uint32_t xv[(M + 1) / 2];  // the thread's elements, two per word
+#pragma unroll
+    for (int k = 0; k < M; k += G) {
+        if constexpr (G == 8) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(xr + k);
+            xv[k / 2] = q.x, xv[k / 2 + 1] = q.y, xv[k / 2 + 2] = q.z, xv[k / 2 + 3] = q.w;
+        } else if constexpr (G == 4) {
+            const uint2 q = *reinterpret_cast<const uint2 *>(xr + k);
+            xv[k / 2] = q.x, xv[k / 2 + 1] = q.y;
+        } else if constexpr (G == 2) {
+            xv[k / 2] = *reinterpret_cast<const uint32_t *>(xr + k);
+        } else {
+            const uint32_t h = xr[k];
+            xv[k / 2] = (k & 1) ? (xv[k / 2] | (h << 16)) : h;
+        }
+    }
+    float sq[M];
+#pragma unroll
+    for (int k = 0; k < M; ++k)
+        sq[k] = square((xv[k / 2] >> (16 * (k & 1))) & 0xFFFFu);
+    const float rs = row_rstd(tree_sum<0, M>(sq), false, H, eps);
+    if (threadIdx.x == 0 && rstd)
+        rstd[r] = rs;
+    const uint16_t *wr = w + i0;
+    uint16_t *yr = y + r * ldy + i0;
+    if constexpr (G >= 2) {
+        // G elements of w in, G of y out per access, like the loads of x
+#pragma unroll
+        for (int k = 0; k < M; k += G) {
+            uint32_t wk[G / 2], o[G / 2];
+            if constexpr (G == 8) {
+                const uint4 q = *reinterpret_cast<const uint4 *>(wr + k);
+                wk[0] = q.x, wk[1] = q.y, wk[2] = q.z, wk[3] = q.w;
+            } else if constexpr (G == 4) {
+                const uint2 q = *reinterpret_cast<const uint2 *>(wr + k);
+                wk[0] = q.x, wk[1] = q.y;
+            } else {
+                wk[0] = *reinterpret_cast<const uint32_t *>(wr + k);
+            }
+#pragma unroll
+            for (int h = 0; h < G / 2; ++h) {
+                const uint32_t xk = xv[k / 2 + h];
+                const float a = __fmul_rn(__fmul_rn(bf(xk & 0xFFFFu), rs), bf(wk[h] & 0xFFFFu));
+                const float b = __fmul_rn(__fmul_rn(bf(xk >> 16), rs), bf(wk[h] >> 16));
+                o[h] = pair_bits(round_pair(a, b));
+            }
+            if constexpr (G == 8)
+                *reinterpret_cast<uint4 *>(yr + k) = make_uint4(o[0], o[1], o[2], o[3]);
+            else if constexpr (G == 4)
+                *reinterpret_cast<uint2 *>(yr + k) = make_uint2(o[0], o[1]);
+            else
+                *reinterpret_cast<uint32_t *>(yr + k) = o[0];
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < M; ++k) {
+            const float xk = bf((xv[k / 2] >> (16 * (k & 1))) & 0xFFFFu);
+            const float v = __fmul_rn(__fmul_rn(xk, rs), bf(wr[k]));
+            yr[k] = (uint16_t)pair_bits(round_pair(v, 0.0f));
+        }
+    }
+}
+
+// Number of inner nodes of the mid-split tree over [0, n) whose range ends
+// at i + 1: the adds that follow leaf i in the post-order walk.
+__device__ __forceinline__ int merges_after(int i, int n) {
+    int lo = 0, hi = n, count = 0;
+    while (hi - lo > 1) {
+        if (hi == i + 1)
+            ++count;
+        const int mid = lo + (hi - lo) / 2;
+        if (i < mid)
+            hi = mid;
+        else
+            lo = mid;
+    }
+    return count;
+}
+
+// Any H: node ranges from the splits, subtrees by the streaming walk.
+template <bool VEC>
+__global__ __launch_bounds__(kLanes) void rmsnorm_any_kernel(const uint16_t *x, int64_t ldx,
+                                                             const uint16_t *w, float eps,
+                                                             uint16_t *y, int64_t ldy,
+                                                             float *rstd, int H) {
+    __shared__ float stack[kStack][kLanes];
     const int64_t r = blockIdx.x;
     const int t = threadIdx.x;
     const uint16_t *xr = x + r * ldx;
-    const int chunks = (H + kChunk - 1) / kChunk;
-    uint4 keep[kKeep];
-    float p = 0.0f;
+    // node t of depth 8: take the left (bit 0) or right (bit 1) child 8 times
+    int lo = 0, hi = H;
+    bool empty = false;
 #pragma unroll
-    for (int k = 0; k < kKeep; ++k) {
-        const int c = t + k * kLanes;
-        keep[k] = c < chunks ? load_chunk<VEC>(xr, c, H) : make_uint4(0u, 0u, 0u, 0u);
+    for (int d = 7; d >= 0; --d) {
+        const int bit = (t >> d) & 1;
+        if (hi - lo >= 2) {
+            const int mid = lo + (hi - lo) / 2;
+            if (bit)
+                lo = mid;
+            else
+                hi = mid;
+        } else if (bit) {
+            empty = true;  // a leaf has no right child
+        }
     }
-#pragma unroll
-    for (int k = 0; k < kKeep; ++k)
-        p = chunk_sumsq(p, keep[k]);  // zero chunks add +0: no change
-    for (int c = t + kKeep * kLanes; c < chunks; c += kLanes)
-        p = chunk_sumsq(p, load_chunk<VEC>(xr, c, H));
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1)
-        p = __fadd_rn(p, __shfl_xor(p, m, 64));
-    if ((t & 63) == 0)
-        part[t >> 6] = p;
-    __syncthreads();
-    const float ss = __fadd_rn(__fadd_rn(part[0], part[1]), __fadd_rn(part[2], part[3]));
-    const float rs = div_rn(1.0f, sqrt_rn(__fadd_rn(div_rn(ss, (float)H), eps)));
+    float p = 0.0f;
+    if (!empty) {
+        const int n = hi - lo;
+        int sp = 0;
+        for (int i = 0; i < n; ++i) {
+            float v = square(xr[lo + i]);
+            for (int m = merges_after(i, n); m > 0; --m)
+                v = __fadd_rn(stack[--sp][t], v);
+            stack[sp++][t] = v;
+        }
+        p = stack[0][t];
+    }
+    const float rs = row_rstd(p, empty, H, eps);
     if (t == 0 && rstd)
         rstd[r] = rs;
     uint16_t *yr = y + r * ldy;
-#pragma unroll
-    for (int k = 0; k < kKeep; ++k) {
-        const int c = t + k * kLanes;
-        if (c < chunks)
-            store_chunk<VEC>(yr, c, H, chunk_out(keep[k], load_chunk<VEC>(w, c, H), rs));
-    }
-    for (int c = t + kKeep * kLanes; c < chunks; c += kLanes)
+    const int chunks = (H + kChunk - 1) / kChunk;
+    for (int c = t; c < chunks; c += kLanes)
         store_chunk<VEC>(yr, c, H, chunk_out(load_chunk<VEC>(xr, c, H), load_chunk<VEC>(w, c, H), rs));
 }
 
@@ -168,6 +311,39 @@ bool overlap(const void *a, int64_t na, const void *b, int64_t nb) {
         return false;
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
     return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+// The node sizes M (H = 256 * M) with a compile-time kernel: model widths
+// from 256 to 16384 that are multiples of 256 * 4, and the small ones.
+template <int... Ms>
+struct MList {};
+using kFixedList = MList<1, 2, 4, 8, 12, 16, 20, 24, 28, 32, 40, 48, 56, 64>;
+constexpr kFixedList kFixed{};
+
+// Whether the row base and leading dimension allow loads of G elements.
+bool aligned_to(const void *p, int64_t ld, int64_t R, int G) {
+    return (reinterpret_cast<uintptr_t>(p) % (2 * G)) == 0 && (R <= 1 || ld % G == 0);
+}
+
+template <int M>
+void launch_m(const uint16_t *x, int64_t ldx, const uint16_t *w, float eps, uint16_t *y,
+              int64_t ldy, float *rstd, int64_t R, hipStream_t st) {
+    constexpr int G = M % 8 == 0 ? 8 : (M % 4 == 0 ? 4 : (M % 2 == 0 ? 2 : 1));
+    const bool vec = aligned_to(x, ldx, R, G) && aligned_to(y, ldy, R, G) && aligned_to(w, 0, 1, G);
+    if (vec)
+        hipLaunchKernelGGL((rmsnorm_fixed_kernel<M, true>), dim3((unsigned)R), dim3(kLanes), 0, st, x,
+                           ldx, w, eps, y, ldy, rstd);
+    else
+        hipLaunchKernelGGL((rmsnorm_fixed_kernel<M, false>), dim3((unsigned)R), dim3(kLanes), 0, st, x,
+                           ldx, w, eps, y, ldy, rstd);
+}
+
+template <int... Ms>
+bool launch_fixed(MList<Ms...>, int M, const uint16_t *x, int64_t ldx, const uint16_t *w,
+                  float eps, uint16_t *y, int64_t ldy, float *rstd, int64_t R, hipStream_t st) {
+    bool done = false;
+    ((M == Ms && !done ? (launch_m<Ms>(x, ldx, w, eps, y, ldy, rstd, R, st), done = true) : false), ...);
+    return done;
 }
 
 }  // namespace
@@ -190,13 +366,16 @@ extern "C" int det_rmsnorm(const det_bf16 *x, int64_t ldx, const det_bf16 *w, fl
     if (dev != DET_GEMM_OK)
         return dev;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)R), block(kLanes);
+    if (H % kLanes == 0 && launch_fixed(kFixed, (int)(H / kLanes), x, ldx, w, eps, y, ldy, rstd, R, st))
+        return hipGetLastError() == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
     const bool vec = aligned16(x, R > 1 ? ldx : 8) && aligned16(y, R > 1 ? ldy : 8) &&
                      aligned16(w, 8);
     if (vec)
-        hipLaunchKernelGGL(rmsnorm_kernel<true>, dim3((unsigned)R), dim3(kLanes), 0, st, x, ldx, w,
-                           eps, y, ldy, rstd, (int)H);
+        hipLaunchKernelGGL(rmsnorm_any_kernel<true>, grid, block, 0, st, x, ldx, w, eps, y, ldy, rstd,
+                           (int)H);
     else
-        hipLaunchKernelGGL(rmsnorm_kernel<false>, dim3((unsigned)R), dim3(kLanes), 0, st, x, ldx,
-                           w, eps, y, ldy, rstd, (int)H);
+        hipLaunchKernelGGL(rmsnorm_any_kernel<false>, grid, block, 0, st, x, ldx, w, eps, y, ldy,
+                           rstd, (int)H);
     return hipGetLastError() == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
 }

@@ -466,51 +466,58 @@ int64_t oracle_first_mismatch(const void *a, const void *b, int64_t nbytes) {
  * size (no split reduction, which would trade invariance for parallelism).
  *
  * What is computed for a row x[0..H) with weight w[0..H) (bf16) and eps:
- *   lane partials  p_t, t < 256: lane t owns the 8-element chunks c with
- *                  c mod 256 == t (elements 8c .. 8c+7) and adds x_i^2 for
- *                  its elements in ascending i, in fp32 from +0 (each square
- *                  of a bf16 value is exact in fp32);
- *   ss             the mid-split (here: pairwise) tree of fp32 adds over
- *                  p_0 .. p_255;
+ *   squares        s_i = x_i * x_i in fp32 (exact unless it leaves fp32's
+ *                  normal range);
+ *   ss             the mid-split tree of fp32 adds over s_0 .. s_{H-1}: a
+ *                  range of n squares splits into floor(n/2) on the left and
+ *                  the rest on the right, the two sums are added in fp32 (the
+ *                  tree shape of det_gemm's leaves, over single elements);
  *   rstd           1 / sqrt(ss / H + eps), each operation rounded once (fp32);
  *   y_i            bf16 rounding (nearest even) of (x_i * rstd) * w_i, both
  *                  products in fp32.
- * The lane count, the chunk width and the orders are this design's reading:
- * the page fixes only that the strategy must not depend on the batch.
+ * The summation order is this design's reading: the page fixes only that the
+ * strategy must not depend on the batch.  The mid-split tree depends on H
+ * alone (not on a thread count or a chunk width), and has depth ceil(log2 H).
  */
-#define ORACLE_RMS_LANES 256
-#define ORACLE_RMS_CHUNK 8
-
-static float rms_sumsq(const uint16_t *x, int64_t H) {
-    float p[ORACLE_RMS_LANES];
-    for (int t = 0; t < ORACLE_RMS_LANES; ++t)
-        p[t] = 0.0f;
+/* ss of one row; s is scratch space for H floats. */
+static float rms_sumsq(const uint16_t *x, int64_t H, float *s) {
     for (int64_t i = 0; i < H; ++i) {
-        int t = (int)((i / ORACLE_RMS_CHUNK) % ORACLE_RMS_LANES);
         float v = widen(x[i]);
-        p[t] = p[t] + v * v;
+        s[i] = v * v;
     }
-    return tree_f32(p, 0, ORACLE_RMS_LANES);
+    return tree_f32(s, 0, H);
 }
 
 int oracle_rmsnorm(const uint16_t *x, int64_t ldx, const uint16_t *w, float eps, uint16_t *y,
                    int64_t ldy, float *rstd, float *sumsq, int64_t R, int64_t H) {
     if (R < 0 || H < 1 || (R > 1 && (ldx < H || ldy < H)))
         return ORACLE_EINVAL;
-#pragma omp parallel for schedule(static)
-    for (int64_t r = 0; r < R; ++r) {
-        const uint16_t *xr = x + r * ldx;
-        float ss = rms_sumsq(xr, H);
-        float mean = ss / (float)H;
-        float rs = 1.0f / sqrtf(mean + eps);
-        for (int64_t i = 0; i < H; ++i) {
-            float v = widen(xr[i]) * rs;
-            y[r * ldy + i] = round_bf16(v * widen(w[i]));
+    int failed = 0;
+#pragma omp parallel
+    {
+        float *s = (float *)malloc((size_t)H * sizeof(float));
+        if (!s) {
+#pragma omp atomic write
+            failed = 1;
         }
-        if (rstd)
-            rstd[r] = rs;
-        if (sumsq)
-            sumsq[r] = ss;
+#pragma omp for schedule(static)
+        for (int64_t r = 0; r < R; ++r) {
+            if (!s)
+                continue;
+            const uint16_t *xr = x + r * ldx;
+            float ss = rms_sumsq(xr, H, s);
+            float mean = ss / (float)H;
+            float rs = 1.0f / sqrtf(mean + eps);
+            for (int64_t i = 0; i < H; ++i) {
+                float v = widen(xr[i]) * rs;
+                y[r * ldy + i] = round_bf16(v * widen(w[i]));
+            }
+            if (rstd)
+                rstd[r] = rs;
+            if (sumsq)
+                sumsq[r] = ss;
+        }
+        free(s);
     }
-    return ORACLE_OK;
+    return failed ? ORACLE_ENOMEM : ORACLE_OK;
 }

@@ -34,7 +34,8 @@ def _check(x, w, eps):
 
 
 @pytest.mark.parametrize("R,H", [(1, 1), (3, 7), (5, 8), (64, 4096), (33, 5120), (9, 8200),
-                                 (4, 20000), (2, 2049)])
+                                 (4, 20000), (2, 2049), (3, 256), (2, 768), (5, 3072),
+                                 (3, 16384), (2, 7168), (4, 255), (3, 257)])
 def test_rmsnorm_matches_oracle(dev, R, H):
     say("rmsnorm R", R, "H", H)
     x = Wk.randn_bf16((R, H), 2.0, 9000 + H, dev)
@@ -42,14 +43,19 @@ def test_rmsnorm_matches_oracle(dev, R, H):
     _check(x, w, 1e-6)
 
 
-def test_rmsnorm_hand_order_cases(dev):
-    """The oracle's hand-derived sums of squares reach rstd on the device."""
-    H = 4096
-    x = torch.zeros((2, H), dtype=torch.bfloat16)
-    x[0, 0], x[0, 2048], x[0, 1024], x[0, 1536] = 4096.0, 1.0, 1.0, 1.0
-    x[1, 0], x[1, 2], x[1, 3] = 4096.0, 1.0, 1.0
+@pytest.mark.parametrize("H,ones", [(3, (1, 2)), (4, (2, 3)), (6, (3, 5)), (2048, (1024, 1536)),
+                                    (2048, (1023, 1024)), (4096, (2048, 3072)), (4096, (5, 6))])
+def test_rmsnorm_hand_order_cases(dev, H, ones):
+    """The oracle's hand-derived tree shapes (4096^2 = 2^24 next to ones whose
+    sum survives only if they meet first) reach rstd on the device; each H
+    runs on the kernel it selects (a node per thread for H = 256 * M, the
+    walk over computed node ranges otherwise)."""
+    x = torch.zeros((1, H), dtype=torch.bfloat16)
+    x[0, 0] = 4096.0
+    x[0, ones[0]] = 1.0
+    x[0, ones[1]] = 1.0
     w = torch.ones(H, dtype=torch.bfloat16)
-    say("rmsnorm hand order cases")
+    say("rmsnorm hand order case H", H, "ones at", ones)
     _check(x.to(dev), w.to(dev), 0.0)
 
 

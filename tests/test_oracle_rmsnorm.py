@@ -3,14 +3,16 @@ Nondeterminism in LLM Inference", batch-invariant kernel design, RMSNorm: one
 row per core, the same reduction whatever the batch size).
 
 Definition (a reading; the page fixes only that the strategy is constant):
-lane t of 256 sums, in fp32 and ascending order, the squares of the elements
-of its 8-element chunks (chunk c belongs to lane c mod 256); the 256 lane sums
-are joined by the pairwise tree; rstd = 1/sqrt(ss/H + eps); y = bf16((x*rstd)*w).
+the squares x_i^2 (fp32) are summed by the mid-split tree of fp32 adds over
+the row's H positions (a range of n splits into floor(n/2) on the left, the
+rest on the right); rstd = 1/sqrt(ss/H + eps); y = bf16((x*rstd)*w).  The
+order depends on H alone.
 
-Pins: hand-derived sums of squares whose value depends on each part of the
-order (in-lane sequential, chunk-to-lane assignment, pairwise across lanes),
-a closed form (constant rows of a power of two), and float64 within the
-rounding bounds on random rows.
+Pins: hand-derived sums of squares whose value depends on the tree shape
+(pairwise rather than sequential, the split in the middle of the range, the
+odd split taking floor(n/2) on the left), a closed form (constant rows of a
+power of two), and float64 within the rounding bound of a depth-ceil(log2 H)
+tree on random rows.
 """
 import numpy as np
 import pytest
@@ -36,37 +38,37 @@ def _row(H, entries):
 ONES = lambda H: np.full(H, bf(1.0), np.uint16)
 
 
-# (H, {index: value}, expected sum of squares, why)
+# (H, {index: value}, expected sum of squares, why).  4096^2 = 2^24, where the
+# fp32 spacing is 2: 2^24 + 1 is a tie that goes to the even 2^24.
 CASES = [
-    (8, {0: 4096.0, 2: 1.0, 3: 1.0}, 16777216.0,
-     "one chunk, one lane: 2^24 + 0 + 1 + 1 added in order; each + 1 is a tie "
-     "between 2^24 and 2^24 + 2 and goes to the even 2^24 (a pairwise sum would "
-     "give (2^24 + 0) + (1 + 1) = 2^24 + 2)"),
+    (4, {0: 4096.0, 2: 1.0, 3: 1.0}, 16777218.0,
+     "squares (2^24, 0, 1, 1): the tree adds (2^24 + 0) + (1 + 1) = 2^24 + 2 exactly; "
+     "a left-to-right sum would give ((2^24 + 0) + 1) + 1 = 2^24"),
+    (3, {0: 4096.0, 1: 1.0, 2: 1.0}, 16777218.0,
+     "squares (2^24, 1, 1), odd range: floor(3/2) = 1 on the left, so "
+     "2^24 + (1 + 1) = 2^24 + 2; the other split, (2^24 + 1) + 1, gives 2^24"),
     (2048, {0: 4096.0, 1024: 1.0, 1536: 1.0}, 16777218.0,
-     "chunks 0, 128, 192 sit in lanes 0, 128, 192; the pairwise tree over 256 "
-     "lanes joins lanes 128..191 and 192..255 first (1 + 1 = 2), then adds 2^24: "
-     "2^24 + 2 exactly (a single lane or lanes in sequence would give 2^24)"),
+     "the right half [1024, 2048) sums to 1 + 1 = 2 before meeting the left "
+     "half's 2^24: 2^24 + 2; a sum in index order gives 2^24"),
+    (2048, {0: 4096.0, 1023: 1.0, 1024: 1.0}, 16777216.0,
+     "the two ones sit on either side of the root's split: the left half is "
+     "2^24 + 1 -> 2^24 (tie to even), the right half 1, and 2^24 + 1 -> 2^24"),
 ]
 
 
-def test_sum_of_squares_in_lane_order():
-    H, e, want, _ = CASES[0]
-    assert oracle.rmsnorm(_row(H, e), ONES(H), 0.0)[2][0] == np.float32(want)
+@pytest.mark.parametrize("case", CASES, ids=[f"H{c[0]}_{i}" for i, c in enumerate(CASES)])
+def test_sum_of_squares_tree_shape(case):
+    H, e, want, why = case
+    ss = oracle.rmsnorm(_row(H, e), ONES(H), 0.0)[2][0]
+    assert ss == np.float32(want), why
 
 
-def test_sum_of_squares_across_lanes_pairwise():
-    H, e, want, _ = CASES[1]
-    assert oracle.rmsnorm(_row(H, e), ONES(H), 0.0)[2][0] == np.float32(want)
-
-
-def test_chunk_to_lane_assignment_wraps_at_256():
-    # element 2048 = chunk 256 belongs to lane 0 together with element 0: the
-    # lane adds 2^24 + 1 -> 2^24 (tie to even), and the ones in lanes 128 and
-    # 192 meet first (1 + 1 = 2): 2^24 + 2.  If chunk 256 had a lane of its own
-    # (more than 256 lanes), the total would be 2^24 + 3 -> 2^24 + 4 (nearest).
-    H = 4096
-    x = _row(H, {0: 4096.0, 2048: 1.0, 1024: 1.0, 1536: 1.0})
-    assert oracle.rmsnorm(x, ONES(H), 0.0)[2][0] == np.float32(16777218.0)
+def test_sum_of_squares_split_is_in_the_middle():
+    """H = 6: splits 3 | 3, then 1 | 2.  Squares (2^24, 0, 0, 1, 0, 1): the
+    right half (1 + (0 + 1)) = 2 meets the left half 2^24: 2^24 + 2.  A
+    power-of-two split 4 | 2 would give (2^24 + 1) + 1 -> 2^24."""
+    x = _row(6, {0: 4096.0, 3: 1.0, 5: 1.0})
+    assert oracle.rmsnorm(x, ONES(6), 0.0)[2][0] == np.float32(16777218.0)
 
 
 @pytest.mark.parametrize("H,k", [(64, 3), (4096, -2), (5000, 5)])
@@ -92,8 +94,8 @@ def test_float64_bounds(H):
     y, rstd, ss = oracle.rmsnorm(x, w, eps)
     xv, wv = val(x).astype(np.float64), val(w).astype(np.float64)
     ss64 = (xv * xv).sum(axis=1)
-    # fp32 sums of non-negative terms: relative error below (depth) * 2^-24
-    depth = 8 + int(np.ceil(H / (8 * 256))) * 8
+    # fp32 tree of non-negative terms: relative error below (depth) * 2^-24
+    depth = max(1, int(np.ceil(np.log2(H))))
     assert np.all(np.abs(ss - ss64) <= depth * 2.0 ** -24 * ss64)
     r64 = 1 / np.sqrt(ss64 / H + eps)
     assert np.all(np.abs(rstd - r64) <= (depth + 4) * 2.0 ** -24 * r64)
