@@ -407,6 +407,31 @@ def attention_leg(dev, steps, warmup, with_cpu):
            "roofline": {"bound": "hbm", "kernel": "attn_split_kernel + attn_combine_kernel",
                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": recorded_traffic("attn")}}
+    # chunked prefill with the decode arithmetic: 4 sequences of 4096 cached
+    # positions, the last 512 of each as the chunk (causal rows)
+    PB, PC = 4, 512
+    pq = Wk.randn_bf16((PB * PC, ATT_HQ, ATT_D), 1.0, 2203, dev)
+    plens = torch.arange(ATT_S - PC + 1, ATT_S + 1, dtype=torch.int32, device=dev).repeat(PB)
+    poff = [i * PC for i in range(PB + 1)]
+    pk, pv = k[:PB].contiguous(), v[:PB].contiguous()
+    pwork = torch.empty(PB * PC * ATT_HQ * ns * (ATT_D + 2), dtype=torch.float32, device=dev)
+    po = torch.empty((PB * PC, ATT_HQ, ATT_D), dtype=torch.bfloat16, device=dev)
+    pfn = lambda: dg.det_attention_prefill(pq, pk, pv, poff, plens, scale, out=po, work=pwork)
+    for _ in range(max(1, warmup // 2)):
+        pfn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        pfn()
+    e1.record()
+    torch.cuda.synchronize()
+    tp = e0.elapsed_time(e1) / 5
+    flops = 4.0 * float(plens.sum().item()) * ATT_HQ * ATT_D
+    out["prefill"] = {"workload": f"{PB} sequences x {PC}-row causal chunks at positions "
+                                  f"{ATT_S - PC}..{ATT_S - 1}, 32/8 heads, head dim 128, the "
+                                  "decode arithmetic per row",
+                      "ms": round(tp, 4), "tflops": round(flops / (tp * 1e-3) / 1e12, 2)}
     if with_cpu:
         from oracle.attention import attention_decode
         sel = [0, 1]

@@ -58,6 +58,28 @@ int det_attention_decode(const det_bf16 *Q, const det_bf16 *K, const det_bf16 *V
                          const int32_t *lens, int64_t B, int64_t Hq, int64_t Hkv, int64_t Smax,
                          int64_t D, float scale, float *work, det_bf16 *O, void *stream);
 
+/* Chunked prefill with the decode arithmetic (same section: a query's result
+ * must not depend on how the sequence is cut into chunks, nor on whether its
+ * keys came from the cache or from the current chunk).  Query rows Q [NQ, Hq,
+ * D] (bf16, contiguous) are grouped by sequence: the rows of sequence b are
+ * row_offsets[b] .. row_offsets[b+1] - 1 (row_offsets: a HOST array of B + 1
+ * entries, 0 first and NQ last, nondecreasing).  Row r attends the first
+ * lens[r] positions of its sequence's K and V [B, Hkv, Smax, D] (lens: DEVICE
+ * int32 [NQ], clamped into [0, Smax]); a causal chunk at positions p0 .. p0 +
+ * C - 1 is the rows with lens p0 + 1 .. p0 + C.  Every (row, head) is
+ * computed exactly as det_attention_decode computes a query of that length
+ * (same splits, same orders), so O [NQ, Hq, D] holds, bit for bit, what a
+ * decode call would return for each row -- whatever the chunk sizes, the
+ * other rows or their order.  work: a caller-owned fp32 buffer of
+ * NQ * Hq * ceil(Smax / 256) * (D + 2) floats.  Rows of one sequence are
+ * processed 8 / G at a time, so each split of keys and values is read once
+ * per such tile.  B <= 128, NQ <= 65535; other conditions and errors as
+ * det_attention_decode.  NQ == 0 is a no-op. */
+int det_attention_prefill(const det_bf16 *Q, const det_bf16 *K, const det_bf16 *V,
+                          const int64_t *row_offsets, const int32_t *lens, int64_t NQ, int64_t B,
+                          int64_t Hq, int64_t Hkv, int64_t Smax, int64_t D, float scale,
+                          float *work, det_bf16 *O, void *stream);
+
 /* For callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
  * computation and the same kernels as det_attention_decode, bit for bit, with

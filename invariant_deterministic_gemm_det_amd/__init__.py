@@ -32,7 +32,7 @@ EXPORTS = _SIX + tuple(n.replace("det_gemm_", "det_gemm_strict_") for n in _SIX)
     "det_gemm_debug_force_config", "det_gemm_debug_config", "det_gemm_status_string",
     "det_moe_fwd_dprob",
     "det_moe_debug_slots", "det_fingerprint", "det_fingerprint_rows", "det_first_mismatch",
-    "det_rmsnorm", "det_attention_decode", "det_attention_decode_noalloc",
+    "det_rmsnorm", "det_attention_decode", "det_attention_decode_noalloc", "det_attention_prefill",
     "det_gemm_shard_reduce")
 ATTN_SCRATCH_FLOATS = 8 << 20
 MAX_PARTS = 16
@@ -99,6 +99,9 @@ def load_library(path=LIB_PATH):
     lib.det_attention_decode.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, ctypes.c_float, p,
                                          p, p]
     lib.det_attention_decode.restype = ctypes.c_int
+    lib.det_attention_prefill.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i64,
+                                          ctypes.c_float, p, p, p]
+    lib.det_attention_prefill.restype = ctypes.c_int
     lib.det_attention_decode_noalloc.argtypes = [p, p, p, p, i64, i64, i64, i64, i64,
                                                  ctypes.c_float, p, p]
     lib.det_attention_decode_noalloc.restype = ctypes.c_int
@@ -402,6 +405,46 @@ def det_attention_decode(q, k, v, lens, scale, out=None, work=None):
                                                  Smax, D, ctypes.c_float(scale), ptr(work),
                                                  ptr(out), _stream(q))
     _check(rc, "det_attention_decode")
+    return out
+
+
+def det_attention_prefill(q, k, v, row_offsets, lens, scale, out=None, work=None):
+    """Chunked prefill with the decode arithmetic (include/det_attention.h):
+    q [NQ,Hq,128] query rows grouped by sequence (rows of sequence b:
+    row_offsets[b] .. row_offsets[b+1]-1, host integers), k and v
+    [B,Hkv,Smax,128] bf16 (contiguous), lens [NQ] int32 on the device (keys
+    each row attends).  Returns o [NQ,Hq,128] bf16: row r equals what
+    det_attention_decode returns for its query with length lens[r]."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous bf16 GPU tensor")
+    NQ, Hq, D = q.shape
+    B, Hkv, Smax, D2 = k.shape
+    if tuple(v.shape) != tuple(k.shape) or D2 != D:
+        raise ValueError("q, k, v disagree in shape")
+    off = [int(x) for x in row_offsets]
+    if len(off) != B + 1:
+        raise ValueError("row_offsets must hold B + 1 entries")
+    if lens.dtype != torch.int32 or not lens.is_cuda or tuple(lens.shape) != (NQ,):
+        raise TypeError("lens must be an int32 GPU tensor [NQ]")
+    _same_device(q, k, v, lens)
+    NS = (Smax + ATTN_SPLIT - 1) // ATTN_SPLIT
+    out = _out(out, (NQ, Hq, D), q, torch.bfloat16, contiguous=True, name="out")
+    need = NQ * Hq * NS * (D + 2)
+    if work is None:
+        work = torch.empty((max(need, 1),), dtype=torch.float32, device=q.device)
+    if not isinstance(work, torch.Tensor) or work.dtype != torch.float32 or not work.is_cuda or \
+            work.device != q.device or not work.is_contiguous():
+        raise TypeError(f"work must be a contiguous float32 tensor on {q.device}")
+    if work.numel() < need:
+        raise ValueError(f"work must hold at least {need} floats")
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr() if t.numel() else 0)
+    off_arr = (ctypes.c_int64 * (B + 1))(*off)
+    with torch.cuda.device(q.device):
+        rc = load_library().det_attention_prefill(ptr(q), ptr(k), ptr(v), off_arr, ptr(lens), NQ,
+                                                  B, Hq, Hkv, Smax, D, ctypes.c_float(scale),
+                                                  ptr(work), ptr(out), _stream(q))
+    _check(rc, "det_attention_prefill")
     return out
 
 

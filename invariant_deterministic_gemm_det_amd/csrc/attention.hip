@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstring>
 #include <mutex>
 
 #include "bf16_device.h"
@@ -64,24 +65,68 @@ __device__ __forceinline__ void put_tile(char *tile, const uint4 (&v)[kPer]) {
 
 __device__ __forceinline__ bf16x2 as_pair(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
 
-// GM: a power of two >= G (the register arrays are sized by it).
-template <int GM>
+// Query rows of a prefill launch, grouped by sequence: sequence q owns rows
+// row_start[q] .. row_start[q] + rows[q] - 1 and the launch's tiles
+// tile_start[q] .. tile_start[q + 1] - 1, each of `qt` consecutive rows (the
+// last one of a sequence possibly fewer).
+constexpr int kMaxPrefillSeqs = 128;
+struct PrefillTiles {
+    int32_t seqs, qt;
+    int32_t tile_start[kMaxPrefillSeqs + 1];
+    int32_t row_start[kMaxPrefillSeqs];
+    int32_t rows[kMaxPrefillSeqs];
+};
+
+// GM: the virtual heads of a workgroup, a power of two (the register arrays
+// are sized by it).  Decode (PF false): workgroup z is sequence z, and its
+// virtual heads are the G query heads of key/value head y.  Prefill (PF true):
+// workgroup z is a tile of query rows of one sequence, and its virtual heads
+// are the G heads of each of those rows (rows * G <= GM); every virtual head
+// has its own length, and the arithmetic of each one is that of a decode
+// query with that length.
+template <int GM, bool PF>
 __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     const uint16_t *Q, const uint16_t *K, const uint16_t *V, const int32_t *lens, int Hq, int Hkv,
-    int Smax, int G, int NS, float scale_log2, float *work) {
+    int Smax, int G, int NS, float scale_log2, float *work, PrefillTiles pt) {
     __shared__ __attribute__((aligned(16))) float sc[GM][kSplit];
     __shared__ __attribute__((aligned(16))) char tile[kTile * kRowBytes];
     __shared__ float red[GM][kThreads / 64];
 
-    const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int s = blockIdx.x, kvh = blockIdx.y;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    int len = lens[b];
-    len = len < 0 ? 0 : (len > Smax ? Smax : len);
     const int j0 = s * kSplit;
-    if (j0 >= len)
+    int seq = blockIdx.z, row0 = blockIdx.z, VG = G;  // sequence, first query row, virtual heads
+    if constexpr (PF) {
+        int lo = 0, hi = pt.seqs;  // the last sequence whose first tile is <= z
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (pt.tile_start[mid] <= (int)blockIdx.z)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        seq = lo;
+        const int k = blockIdx.z - pt.tile_start[lo];
+        row0 = pt.row_start[lo] + k * pt.qt;
+        const int nrows = pt.rows[lo] - k * pt.qt < pt.qt ? pt.rows[lo] - k * pt.qt : pt.qt;
+        VG = nrows * G;
+    }
+    // per virtual head v: its query row and head, and its positions in this split
+    int nv[GM];
+    int n = 0;
+#pragma unroll
+    for (int v = 0; v < GM; ++v) {
+        nv[v] = 0;
+        if (v < VG) {
+            int len = lens[row0 + v / G];
+            len = len < 0 ? 0 : (len > Smax ? Smax : len);
+            nv[v] = len - j0 <= 0 ? 0 : (len - j0 < kSplit ? len - j0 : kSplit);
+            n = nv[v] > n ? nv[v] : n;
+        }
+    }
+    if (n == 0)
         return;  // the whole workgroup: no barrier is reached
-    const int n = len - j0 < kSplit ? len - j0 : kSplit;
-    const int64_t head = ((int64_t)b * Hkv + kvh) * Smax;
+    const int64_t head = ((int64_t)seq * Hkv + kvh) * Smax;
     const uint16_t *Kh = K + (head + j0) * kD, *Vh = V + (head + j0) * kD;
 
     // ---- scores: thread t takes position r = t / 4 of a tile and the 32-wide
@@ -95,9 +140,9 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (g < G)
+            if (g < VG)
                 v = *reinterpret_cast<const uint4 *>(
-                    Q + ((int64_t)b * Hq + kvh * G + g) * kD + pp * 32 + c * 8);
+                    Q + ((int64_t)(row0 + g / G) * Hq + kvh * G + g % G) * kD + pp * 32 + c * 8);
             qp[g][4 * c] = v.x;
             qp[g][4 * c + 1] = v.y;
             qp[g][4 * c + 2] = v.z;
@@ -133,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
         const int j = sub * kTile + r;
 #pragma unroll
         for (int g = 0; g < GM; ++g) {
-            if (g < G) {
+            if (g < VG) {
                 float part = 0.0f;
 #pragma unroll
                 for (int c = 0; c < 16; ++c)
@@ -142,14 +187,14 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
                 float v = part + __shfl_xor(part, 1, 64);
                 v = v + __shfl_xor(v, 2, 64);
                 if (pp == 0)
-                    sc[g][j] = j < n ? v * scale_log2 : -__builtin_inff();
+                    sc[g][j] = j < nv[g] ? v * scale_log2 : -__builtin_inff();
             }
         }
     }
     uint4 nxt[kPer];
     fetch_tile(nxt, Vh, 0, n);  // the first value tile, in flight through the softmax
     // slots past the last tile read are empty
-    for (int i = t; i < G * kSplit; i += kThreads)
+    for (int i = t; i < VG * kSplit; i += kThreads)
         if (i % kSplit >= ntiles * kTile)
             sc[i / kSplit][i % kSplit] = -__builtin_inff();
     __syncthreads();
@@ -157,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     float m[GM], l[GM];
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
-        if (g >= G)
+        if (g >= VG)
             break;
         float x = sc[g][t];
 #pragma unroll
@@ -169,10 +214,10 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     __syncthreads();
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
-        if (g >= G)
+        if (g >= VG)
             break;
         m[g] = fmaxf(fmaxf(red[g][0], red[g][1]), fmaxf(red[g][2], red[g][3]));
-        const float p = t < n ? exp2f(sc[g][t] - m[g]) : 0.0f;
+        const float p = t < nv[g] ? exp2f(sc[g][t] - m[g]) : 0.0f;
         sc[g][t] = p;
         float x = p;
 #pragma unroll
@@ -183,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     __syncthreads();  // every max read from red before it is reused
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
-        if (g >= G)
+        if (g >= VG)
             break;
         if (lane == 0)
             red[g][wave] = l[g];
@@ -192,7 +237,16 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     // 2 (o % 64) and 2 (o % 64) + 1); positions in ascending order, four
     // weights read at a time
     float acc[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-    const int npairs = G * (kD / 2);
+    const int npairs = VG * (kD / 2);
+    int nown[2];  // the length of the virtual head of output pair i (static selects)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int g = (t + i * kThreads) >> 6;
+        nown[i] = 0;
+#pragma unroll
+        for (int v = 0; v < GM; ++v)
+            nown[i] = v == g ? nv[v] : nown[i];
+    }
     for (int sub = 0; sub < ntiles; ++sub) {
         __syncthreads();
         put_tile(tile, nxt);
@@ -212,8 +266,13 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
                     for (int u = 0; u < 4; ++u) {
                         const uint32_t vv =
                             *reinterpret_cast<const uint32_t *>(tile + (rr + u) * kRowBytes + dp * 4);
-                        acc[i][0] = fmaf(wv[u], bfv(vv & 0xFFFFu), acc[i][0]);
-                        acc[i][1] = fmaf(wv[u], bfv(vv >> 16), acc[i][1]);
+                        // Prefill: the value rows of a longer row of the tile, past
+                        // this head's length, are skipped (a decode query of that
+                        // length sees zero rows there, which leave acc unchanged).
+                        if (!PF || sub * kTile + rr + u < nown[i]) {
+                            acc[i][0] = fmaf(wv[u], bfv(vv & 0xFFFFu), acc[i][0]);
+                            acc[i][1] = fmaf(wv[u], bfv(vv >> 16), acc[i][1]);
+                        }
                     }
                 }
             }
@@ -225,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
         const int o = t + i * kThreads;
         if (o < npairs) {
             const int g = o >> 6, dp = o & 63;
-            float *w = work + (((int64_t)b * Hq + kvh * G + g) * NS + s) * (kD + 2);
+            float *w = work + (((int64_t)(row0 + g / G) * Hq + kvh * G + g % G) * NS + s) * (kD + 2);
             w[2 * dp] = acc[i][0];
             w[2 * dp + 1] = acc[i][1];
             if (dp == 0) {
@@ -351,18 +410,20 @@ int run_attention(const det_bf16 *Q, const det_bf16 *K, const det_bf16 *V, const
     if (NS > 0) {
         const dim3 grid((unsigned)NS, (unsigned)Hkv, (unsigned)B);
         const float sl = scale * kLog2e;
+        PrefillTiles none;
+        std::memset(&none, 0, sizeof none);
         if (G == 1)
-            hipLaunchKernelGGL(attn_split_kernel<1>, grid, dim3(kThreads), 0, st, Q, K, V, lens,
-                               (int)Hq, (int)Hkv, (int)Smax, G, (int)NS, sl, work);
+            hipLaunchKernelGGL((attn_split_kernel<1, false>), grid, dim3(kThreads), 0, st, Q, K, V,
+                               lens, (int)Hq, (int)Hkv, (int)Smax, G, (int)NS, sl, work, none);
         else if (G == 2)
-            hipLaunchKernelGGL(attn_split_kernel<2>, grid, dim3(kThreads), 0, st, Q, K, V, lens,
-                               (int)Hq, (int)Hkv, (int)Smax, G, (int)NS, sl, work);
+            hipLaunchKernelGGL((attn_split_kernel<2, false>), grid, dim3(kThreads), 0, st, Q, K, V,
+                               lens, (int)Hq, (int)Hkv, (int)Smax, G, (int)NS, sl, work, none);
         else if (G <= 4)
-            hipLaunchKernelGGL(attn_split_kernel<4>, grid, dim3(kThreads), 0, st, Q, K, V, lens,
-                               (int)Hq, (int)Hkv, (int)Smax, G, (int)NS, sl, work);
+            hipLaunchKernelGGL((attn_split_kernel<4, false>), grid, dim3(kThreads), 0, st, Q, K, V,
+                               lens, (int)Hq, (int)Hkv, (int)Smax, G, (int)NS, sl, work, none);
         else
-            hipLaunchKernelGGL(attn_split_kernel<8>, grid, dim3(kThreads), 0, st, Q, K, V, lens,
-                               (int)Hq, (int)Hkv, (int)Smax, G, (int)NS, sl, work);
+            hipLaunchKernelGGL((attn_split_kernel<8, false>), grid, dim3(kThreads), 0, st, Q, K, V,
+                               lens, (int)Hq, (int)Hkv, (int)Smax, G, (int)NS, sl, work, none);
     }
     hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)Hq, (unsigned)B), dim3(kD), 0, st, lens,
                        (int)Hq, (int)Smax, (int)NS, work, O);
@@ -380,6 +441,67 @@ extern "C" int det_attention_decode(const det_bf16 *Q, const det_bf16 *K, const 
     if (rc != DET_GEMM_OK || B == 0)
         return rc;
     return run_attention(Q, K, V, lens, B, Hq, Hkv, Smax, NS, scale, work, O, stream);
+}
+
+extern "C" int det_attention_prefill(const det_bf16 *Q, const det_bf16 *K, const det_bf16 *V,
+                                     const int64_t *row_offsets, const int32_t *lens, int64_t NQ,
+                                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Smax, int64_t D,
+                                     float scale, float *work, det_bf16 *O, void *stream) {
+    int64_t NS = 0;
+    int rc = check_shape(B, Hq, Hkv, Smax, D, NS);
+    if (rc != DET_GEMM_OK)
+        return rc;
+    if (NQ < 0 || NQ > 65535 || B > kMaxPrefillSeqs || !row_offsets)
+        return DET_GEMM_EINVAL;
+    if (row_offsets[0] != 0 || row_offsets[B] != NQ)
+        return DET_GEMM_EINVAL;
+    for (int64_t b = 0; b < B; ++b)
+        if (row_offsets[b + 1] < row_offsets[b])
+            return DET_GEMM_EINVAL;
+    if (NQ == 0)
+        return DET_GEMM_OK;
+    if (!Q || !lens || !O || (NS > 0 && (!K || !V || !work)))
+        return DET_GEMM_EINVAL;
+    const int64_t qb = NQ * Hq * kD * 2, kvb = B * Hkv * Smax * kD * 2;
+    const int64_t wb = NQ * Hq * NS * (kD + 2) * 4;
+    if (!disjoint(O, qb, Q, qb) || !disjoint(O, qb, K, kvb) || !disjoint(O, qb, V, kvb) ||
+        !disjoint(O, qb, lens, NQ * 4) || !disjoint(O, qb, work, wb) ||
+        !disjoint(work, wb, Q, qb) || !disjoint(work, wb, K, kvb) || !disjoint(work, wb, V, kvb) ||
+        !disjoint(work, wb, lens, NQ * 4))
+        return DET_GEMM_EINVAL;
+    if (((reinterpret_cast<uintptr_t>(K) | reinterpret_cast<uintptr_t>(V)) & 15) != 0)
+        return DET_GEMM_EINVAL;  // 16-byte rows
+    const int dev = check_device();
+    if (dev != DET_GEMM_OK)
+        return dev;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int G = (int)(Hq / Hkv);
+    if (NS > 0) {
+        // tiles of qt consecutive rows of one sequence: qt * G <= 8 virtual heads
+        PrefillTiles pt;
+        std::memset(&pt, 0, sizeof pt);
+        pt.seqs = (int32_t)B;
+        pt.qt = kGMax / G;
+        int64_t tiles = 0;
+        for (int64_t b = 0; b < B; ++b) {
+            const int64_t rows = row_offsets[b + 1] - row_offsets[b];
+            pt.tile_start[b] = (int32_t)tiles;
+            pt.row_start[b] = (int32_t)row_offsets[b];
+            pt.rows[b] = (int32_t)rows;
+            tiles += (rows + pt.qt - 1) / pt.qt;
+        }
+        pt.tile_start[B] = (int32_t)tiles;
+        if (tiles > 65535)
+            return DET_GEMM_EINVAL;
+        if (tiles > 0)
+            hipLaunchKernelGGL((attn_split_kernel<kGMax, true>),
+                               dim3((unsigned)NS, (unsigned)Hkv, (unsigned)tiles), dim3(kThreads), 0,
+                               st, Q, K, V, lens, (int)Hq, (int)Hkv, (int)Smax, G, (int)NS,
+                               scale * kLog2e, work, pt);
+    }
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)Hq, (unsigned)NQ), dim3(kD), 0, st, lens,
+                       (int)Hq, (int)Smax, (int)NS, work, O);
+    return hipGetLastError() == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
 }
 
 extern "C" int det_attention_decode_noalloc(const det_bf16 *Q, const det_bf16 *K,

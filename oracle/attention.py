@@ -39,3 +39,16 @@ def attention_decode(q, k, v, lens, scale):
             w = np.exp(s - s.max())
             o[b, h] = (w / w.sum()) @ vv
     return o
+
+
+def attention_prefill(q, k, v, row_offsets, lens, scale):
+    """Query rows q [NQ, Hq, D] grouped by sequence (row_offsets, B + 1
+    entries), k and v [B, Hkv, Smax, D], lens [NQ]: row r attends the first
+    lens[r] positions of its sequence.  Returns o [NQ, Hq, D] float64 (the
+    same definition, one query row at a time)."""
+    NQ = q.shape[0]
+    o = np.zeros(q.shape)
+    for b in range(len(row_offsets) - 1):
+        for r in range(int(row_offsets[b]), int(row_offsets[b + 1])):
+            o[r] = attention_decode(q[r:r + 1], k[b:b + 1], v[b:b + 1], [lens[r]], scale)[0]
+    return o

@@ -106,3 +106,61 @@ def test_decode_workload_full_size(dev):
         assert torch.equal(ob[0].view(torch.int16), o[b].view(torch.int16))
     sel = [0, 63]
     _within(o[sel], q[sel], k[sel], v[sel], L[sel])
+
+
+# ---------------------------------------------------------------- chunked prefill
+
+def _decode_one(q_row, k, v, b, n, dev):
+    """det_attention_decode of one query row against sequence b's first n positions."""
+    return dg.det_attention_decode(q_row[None].contiguous(), k[b:b + 1].contiguous(),
+                                   v[b:b + 1].contiguous(),
+                                   torch.tensor([n], dtype=torch.int32, device=dev), SCALE)[0]
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (32, 8), (16, 2)])
+def test_prefill_rows_equal_decode(dev, Hq, Hkv):
+    """A causal chunk at positions 300 .. 369 of a 700-position sequence (and
+    rows of a second sequence in the same call): every row equals, bit for
+    bit, the decode call for its query with its length (the chunk's own keys
+    counted as cached)."""
+    say("attention prefill rows vs decode", Hq, Hkv)
+    B, Smax = 2, 700
+    k = Wk.randn_bf16((B, Hkv, Smax, D), 1.0, 3001 + Hq, dev)
+    v = Wk.randn_bf16((B, Hkv, Smax, D), 1.0, 3002 + Hq, dev)
+    lens = list(range(301, 371)) + [1, 256, 257, 700, 513]
+    offsets = [0, 70, 75]
+    q = Wk.randn_bf16((75, Hq, D), 1.0, 3003 + Hq, dev)
+    L = torch.tensor(lens, dtype=torch.int32, device=dev)
+    o = dg.det_attention_prefill(q, k, v, offsets, L, SCALE)
+    for r in [0, 1, 17, 63, 69, 70, 71, 72, 73, 74]:
+        b = 0 if r < 70 else 1
+        want = _decode_one(q[r], k, v, b, lens[r], dev)
+        assert torch.equal(o[r].view(torch.int16), want.view(torch.int16)), (r, lens[r])
+
+
+@pytest.mark.parametrize("chunk", [1, 64, 512])
+def test_prefill_chunk_size_invariance(dev, chunk):
+    """Prefill of positions 0 .. 1099 of one sequence in chunks of 1, 64 and
+    512 rows (one call per chunk, the cache holding the whole sequence) gives
+    the bits of the unchunked call, and agrees with the float64 oracle."""
+    say("attention prefill chunks of", chunk)
+    Hq, Hkv, S = 32, 8, 1100
+    k = Wk.randn_bf16((1, Hkv, S, D), 1.0, 3101, dev)
+    v = Wk.randn_bf16((1, Hkv, S, D), 1.0, 3102, dev)
+    q = Wk.randn_bf16((S, Hq, D), 1.0, 3103, dev)
+    lens = torch.arange(1, S + 1, dtype=torch.int32, device=dev)
+    whole = dg.det_attention_prefill(q, k, v, [0, S], lens, SCALE)
+    parts = []
+    for a in range(0, S, chunk):
+        e = min(S, a + chunk)
+        parts.append(dg.det_attention_prefill(q[a:e].contiguous(), k, v, [0, e - a],
+                                              lens[a:e].contiguous(), SCALE))
+    assert torch.equal(torch.cat(parts).view(torch.int16), whole.view(torch.int16))
+    if chunk == 64:
+        rows = [0, 255, 256, 1099]
+        from oracle.attention import attention_prefill
+        want = attention_prefill(bits(q[rows]), bits(k), bits(v), [0, len(rows)],
+                                 [r + 1 for r in rows], SCALE)
+        got = (bits(whole[rows]).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        vmax = np.abs((bits(v).astype(np.uint32) << 16).view(np.float32)).max()
+        assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 2e-5 * vmax)

@@ -281,3 +281,18 @@ def test_attention_noalloc_refuses_oversize_without_device(lib):
     assert f(FAKE, A, A, FAKE, 2, 8, 2, 64, 64, s, o, NULL) == dg.EINVAL   # D != 128
     assert f(FAKE, A, A, FAKE, 0, 8, 2, 64, 128, s, o, NULL) == dg.OK      # no sequences
     assert b"scratch" in lib.det_gemm_status_string(dg.ESCRATCH)
+
+
+def test_attention_prefill_argument_errors_without_device(lib):
+    """det_attention_prefill: grouping and shape errors before any device work."""
+    f = lib.det_attention_prefill
+    A = ctypes.c_void_p(0x100000000)
+    o, w = ctypes.c_void_p(0x900000000), ctypes.c_void_p(0xA00000000)
+    s = ctypes.c_float(0.1)
+    off = lambda *v: (ctypes.c_int64 * len(v))(*v)
+    assert f(FAKE, A, A, off(0, 3, 4), FAKE, 5, 2, 8, 2, 64, 128, s, w, o, NULL) == dg.EINVAL  # last != NQ
+    assert f(FAKE, A, A, off(1, 3, 5), FAKE, 5, 2, 8, 2, 64, 128, s, w, o, NULL) == dg.EINVAL  # first != 0
+    assert f(FAKE, A, A, off(0, 4, 3), FAKE, 3, 2, 8, 2, 64, 128, s, w, o, NULL) == dg.EINVAL  # decreasing
+    assert f(FAKE, A, A, off(0, 3, 5), FAKE, 5, 2, 8, 2, 64, 64, s, w, o, NULL) == dg.EINVAL   # D != 128
+    assert f(FAKE, A, A, None, FAKE, 5, 2, 8, 2, 64, 128, s, w, o, NULL) == dg.EINVAL          # no offsets
+    assert f(FAKE, A, A, off(0, 0), FAKE, 0, 1, 8, 2, 64, 128, s, w, o, NULL) == dg.OK         # no rows

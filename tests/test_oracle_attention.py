@@ -3,7 +3,7 @@ page of "Defeating Nondeterminism in LLM Inference", batch-invariant kernel
 design, attention)."""
 import numpy as np
 
-from oracle.attention import attention_decode
+from oracle.attention import attention_decode, attention_prefill
 
 
 def bf(x):
@@ -63,3 +63,22 @@ def test_length_masks_the_tail_and_zero_length():
     v2[0, :, 7:] = bf(np.full((1, 3, 4), 1e3, np.float32))
     assert np.array_equal(attention_decode(q, k2, v2, [7, 0], 0.5), o)
     assert np.all(o[1] == 0)
+
+
+def test_prefill_rows_each_attend_their_own_prefix():
+    """Equal keys give uniform weights, so row r's output is the mean of the
+    first lens[r] values of its sequence, whatever the other rows."""
+    rng = np.random.default_rng(11)
+    B, Hkv, G, Smax, D = 2, 2, 2, 9, 8
+    k = np.zeros((B, Hkv, Smax, D), np.uint16)                   # all keys +0: equal scores
+    v = bf(rng.standard_normal((B, Hkv, Smax, D)).astype(np.float32))
+    offsets = [0, 3, 7]
+    lens = [1, 4, 9, 2, 5, 5, 7]
+    q = bf(rng.standard_normal((7, Hkv * G, D)).astype(np.float32))
+    o = attention_prefill(q, k, v, offsets, lens, 0.3)
+    V = val(v)
+    for b in range(B):
+        for r in range(offsets[b], offsets[b + 1]):
+            for h in range(Hkv * G):
+                np.testing.assert_allclose(o[r, h], V[b, h // G, :lens[r]].mean(axis=0), rtol=1e-12,
+                                           atol=1e-12)
