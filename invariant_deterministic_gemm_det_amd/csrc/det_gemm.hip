@@ -180,7 +180,7 @@ bool wide_ok(const Problem &pr, const TreeSel &t, const TileCfg &c, int &up) {
 // operand Y, whole 8-column chunks.
 bool decode_ok(const Problem &pr) {
     const int64_t L = pr.R / 32;
-    return pr.xk && (pr.out == OUT_BF16 || pr.out == OUT_F32) && pr.I >= 1 && pr.I <= 64 &&
+    return pr.xk && (pr.out == OUT_BF16 || pr.out == OUT_F32) && pr.I >= 1 && pr.I <= 128 &&
            pr.R % 32 == 0 && L >= 8 && L <= 1024 && aligned16(pr.x, pr.ldx) &&
            aligned16(pr.y, pr.ldy) && (pr.yk || pr.J % 8 == 0);
 }
@@ -199,7 +199,9 @@ bool decode_ok(const Problem &pr) {
 // decode kernel stages 2 to 4 blocks of 16 rows per tile and re-reads X once
 // per tile, so it wins while the 32-column tiles times the row blocks stay
 // under about 1400 (M = 32, K = 4096, N = 6144: 16.7 us instead of 40 on the
-// wide kernel; N = 18432: 46 us instead of 51); above, the wide kernel
+// wide kernel; N = 18432: 46 us instead of 51), or 600 for 65 to 128 rows on
+// 16-column tiles (M = 128, N = 2048: 20 us; N = 6144: 48 us instead of 40 on
+// the wide kernel); above, the wide kernel
 // (N = 28672: 54 us instead of 65 at M = 32, 54 instead of 83 at M = 64),
 // on 128x128 tiles above 128 column tiles (N = 18432, M = 64: 51 us, 55 on
 // 128x64).  Otherwise 128x128 wide tiles when they make at least four waves
@@ -212,12 +214,14 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     int up = 0;
     if (decode_ok(pr)) {
         const int64_t t32 = (pr.J + 31) / 32, blocks = (pr.I + 15) / 16;
-        if (pr.I > 16 && t32 * blocks > 1400) {
+        if ((pr.I > 16 && t32 * blocks > 1400) || (pr.I > 64 && t32 * blocks > 600)) {
             const int first = (pr.J + 127) / 128 > 128 ? 8 : 6;
             for (int c : {first, first == 8 ? 6 : 8})
                 if (wide_ok(pr, t, kTileCfgs[c], up))
                     return c;
         }
+        if (pr.I > 64)
+            return 10;  // eight row blocks: 16-column tiles only
         const bool line_units = pr.yk && (pr.R / 32) % 2 == 0;  // two-leaf copies read whole lines
         if (!line_units && pr.I <= 16 && (pr.J + 63) / 64 > 128)
             return 11;
@@ -268,7 +272,7 @@ int run_mfma(const Problem &pr, hipStream_t st) {
     const int cfg = pick_config(pr, tree, levels);
     const TileCfg &c = kTileCfgs[cfg];
     if (c.kind == KIND_DECODE) {
-        if (!decode_ok(pr) || (c.fn == 4 && pr.I > 16))
+        if (!decode_ok(pr) || (c.fn == 4 && pr.I > 16) || (c.fn == 2 && pr.I > 64))
             return DET_GEMM_EINVAL;  // a forced decode configuration this problem does not fit
         if ((pr.J + 15) / 16 > kMaxDim)
             return DET_GEMM_EINVAL;

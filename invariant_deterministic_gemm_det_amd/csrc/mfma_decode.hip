@@ -70,13 +70,20 @@ struct DecodeShape {
     // two workgroups per compute unit do: 4 slots for 16- and 32-column
     // tiles, 2 for 64-column ones and for the larger two-leaf units; with 16
     // waves, as many as the LDS holds (at least 2).
+    // With 4 waves (one per SIMD) each ring takes a quarter of the LDS: as
+    // many slots as fit, at most 8.
     static constexpr int NB0 = UL == 2 ? ((CB == 1 && MP == 1) ? 4 : 2) : (CB == 4 ? 2 : 4);
-    static constexpr int NB = (NB0 > 2 && W * NB0 * SLOT > 160 * 1024) ? NB0 / 2 : NB0;
+    static constexpr int NB4 = (160 * 1024) / (4 * SLOT) < 8 ? (160 * 1024) / (4 * SLOT) : 8;
+    static constexpr int NB = W == 4 ? NB4 : (NB0 > 2 && W * NB0 * SLOT > 160 * 1024) ? NB0 / 2 : NB0;
     static constexpr int AHEAD = NB - 1;                  // units in flight per wave
     static constexpr int OPS = UL == 2 ? 2 * CB + (MP == 1 ? 1 : 2 * MR) : CB + MR;  // copies per unit
     static constexpr int WAVE_BYTES = NB * SLOT;
     static constexpr int LDS = W * WAVE_BYTES;
-    static constexpr bool kFits = LDS <= 160 * 1024 && WAVE_BYTES >= MR * CB * 1024;
+    static constexpr int BPW = (MR * CB + W - 1) / W;      // output blocks per wave at the end
+    static constexpr bool kFits = NB >= 2 && LDS <= 160 * 1024 && WAVE_BYTES >= MR * CB * 1024;
+    // Waves per SIMD the register allocation must allow: two workgroups per
+    // compute unit when their rings fit the LDS twice, and at most four.
+    static constexpr int OCC = (W / 4) * (2 * LDS <= 160 * 1024 ? 2 : 1) < 4 ? (W / 4) * (2 * LDS <= 160 * 1024 ? 2 : 1) : 4;
 };
 
 __device__ __forceinline__ int kt_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
@@ -132,6 +139,10 @@ struct NodeStack {
         const u32x2 h = {v[2 * d], v[2 * d + 1]};
         return unpack_node(h);
     }
+    __device__ __forceinline__ u32x2 raw(int d) const {
+        const u32x2 h = {v[2 * d], v[2 * d + 1]};
+        return h;
+    }
     __device__ __forceinline__ void put(int d, f32x4 x) {
         const u32x2 h = pack_node(x);
         v[2 * d] = h[0];
@@ -148,13 +159,37 @@ __device__ __forceinline__ f32x4 top_levels(const f32x4 *r) {
         return merge4(top_levels<LO, (LO + HI) / 2>(r), top_levels<(LO + HI) / 2, HI>(r));
 }
 
-// Register budget: 128 VGPRs (two 8-wave workgroups or one 16-wave
-// workgroup per compute unit), or 256 for 4 row blocks x 2 column blocks
-// (one 8-wave workgroup per compute unit).
+// Where leaf t of the mid-split tree over [0, n) stands: the number of inner
+// nodes whose range ends at it (the adds that follow it in post-order) and
+// the parity of its depth (root: depth 0).
+struct LeafPlan {
+    int merges;
+    int odd;
+};
+
+__device__ __forceinline__ LeafPlan leaf_plan(int t, int n) {
+    int lo = 0, hi = n, merges = 0, depth = 0;
+    while (hi - lo > 1) {
+        if (hi == t + 1)
+            ++merges;
+        const int mid = lo + (hi - lo) / 2;
+        if (t < mid)
+            hi = mid;
+        else
+            lo = mid;
+        ++depth;
+    }
+    return LeafPlan{merges, depth & 1};
+}
+
+// Register budget: 128 VGPRs when four waves share a SIMD (two 8-wave
+// workgroups or one 16-wave workgroup per compute unit), else 256.
 template <bool YK, int OUT, int MP, int CB, int UL, int W>
-__global__ __launch_bounds__(64 * W, (W == 16 || MP * CB > 64) ? 2 : 4) void mfma_decode_kernel(MfmaParams p) {
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(DecodeShape<MP, CB, UL, W>::OCC,
+                                                                       DecodeShape<MP, CB, UL, W>::OCC)))
+void mfma_decode_kernel(MfmaParams p) {
     static_assert(UL == 1 || YK, "two-leaf units only for a K-major Y");
-    static_assert(W == 8 || W == 16, "subtrees of depth 3 or 4");
+    static_assert(W == 4 || W == 8 || W == 16, "subtrees of depth 2, 3 or 4");
     typedef DecodeShape<MP, CB, UL, W> S;
     static_assert(S::kFits, "the rings fit the LDS");
     constexpr int MR = S::MR;
@@ -173,7 +208,7 @@ __global__ __launch_bounds__(64 * W, (W == 16 || MP * CB > 64) ? 2 : 4) void mfm
     // tree.
     int lo = 0, hi = p.L;
 #pragma unroll
-    for (int bit = (W == 16 ? 3 : 2); bit >= 0; --bit) {
+    for (int bit = (W == 16 ? 3 : W == 8 ? 2 : 1); bit >= 0; --bit) {
         const int mid = lo + (hi - lo) / 2;
         if ((wave >> bit) & 1)
             lo = mid;
@@ -309,7 +344,7 @@ __global__ __launch_bounds__(64 * W, (W == 16 || MP * CB > 64) ? 2 : 4) void mfm
 
     auto issue = [&](int u) {  // local unit u into slot u % NB
         const int unit = ulo + u;
-        const uint32_t slot = ring_lds + (uint32_t)((u & (S::NB - 1)) * S::SLOT);
+        const uint32_t slot = ring_lds + (uint32_t)((u % S::NB) * S::SLOT);
         const u32x4 rs = rsrc_at(ybase + (int64_t)unit * ystep);
         const u32x4 xs = rsrc_at(p.x + (int64_t)unit * 32 * UL);
         if (UL == 2) {
@@ -341,116 +376,186 @@ __global__ __launch_bounds__(64 * W, (W == 16 || MP * CB > 64) ? 2 : 4) void mfm
         }
     };
 
-    const int pre = nunits < S::AHEAD ? nunits : S::AHEAD;
-    for (int u = 0; u < pre; ++u)
-        issue(u);
+    // The wave's subtree, in ascending leaf order.  Matrix-core adds (MA):
+    // a tree add is the selector MFMA of the wide kernel, whose result lands
+    // transposed; a leaf at odd depth below the wave's root is computed with
+    // swapped operands (the same products and sums, transposed), so that the
+    // two children of every add share a layout and the wave's root comes out
+    // in the plain layout.  Element-wise adds (not MA): merge4, positions
+    // never move.
+    const bf16x8 sel = split_selector(lane);
+    auto subtree = [&](auto matrix_add) {
+        constexpr bool MA = decltype(matrix_add)::value;
+        const int pre = nunits < S::AHEAD ? nunits : S::AHEAD;
+        for (int u = 0; u < pre; ++u)
+            issue(u);
 
-    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    F fz;
-#pragma unroll
-    for (int a = 0; a < MR; ++a)
-#pragma unroll
-        for (int q = 0; q < CB; ++q)
-            fz.v[a][q] = zero;
-    NodeStack st[MR][CB];
-#pragma unroll
-    for (int a = 0; a < MR; ++a)
-#pragma unroll
-        for (int q = 0; q < CB; ++q)
-            st[a][q].v = 0u;
-    int sp = 0;
-    F root = fz;
-    for (int u = 0; u < nunits; ++u) {
-        if (u + S::AHEAD < nunits) {
-            issue(u + S::AHEAD);
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(S::OPS * S::AHEAD) : "memory");
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
-        const char *slot = ring + (u & (S::NB - 1)) * S::SLOT;
-#pragma unroll
-      for (int h = 0; h < UL; ++h) {
-        const int t = (ulo + u) * UL + h - lo;   // local leaf
-        if (t < 0 || t >= n)
-            continue;                            // a neighbour's leaf of a two-leaf unit
-        bf16x8 fx[MR];
+        const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        NodeStack st[MR][CB];
 #pragma unroll
         for (int a = 0; a < MR; ++a)
-            fx[a] = *reinterpret_cast<const bf16x8 *>(slot + (UL == 2 ? xp[h] + a * 2048 : xrd + a * 1024));
-        F cur;
 #pragma unroll
-        for (int q = 0; q < CB; ++q) {
-            bf16x8 fy;
-            if (UL == 2) {
-                fy = *reinterpret_cast<const bf16x8 *>(slot + yp[q][h]);
-            } else if (YK) {
-                fy = *reinterpret_cast<const bf16x8 *>(slot + yrd[q][0]);
+            for (int q = 0; q < CB; ++q)
+                st[a][q].v = 0u;
+        int sp = 0;
+        for (int u = 0; u < nunits; ++u) {
+            if (u + S::AHEAD < nunits) {
+                issue(u + S::AHEAD);
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(S::OPS * S::AHEAD) : "memory");
             } else {
-                const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(slot + yrd[q][0]));
-                const s16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(slot + yrd[q][1]));
-                typedef short s16x8 __attribute__((ext_vector_type(8)));
-                const s16x8 v = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
-                fy = __builtin_bit_cast(bf16x8, v);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
+            const char *slot = ring + (u % S::NB) * S::SLOT;
 #pragma unroll
-            for (int a = 0; a < MR; ++a)
-                cur.v[a][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fx[a], fy, zero, 0, 0, 0);
+            for (int h = 0; h < UL; ++h) {
+                const int t = (ulo + u) * UL + h - lo;   // local leaf
+                if (t < 0 || t >= n)
+                    continue;                            // a neighbour's leaf of a two-leaf unit
+                const LeafPlan lp = leaf_plan(t, n);
+                bf16x8 fx[MR];
+#pragma unroll
+                for (int a = 0; a < MR; ++a)
+                    fx[a] = *reinterpret_cast<const bf16x8 *>(slot + (UL == 2 ? xp[h] + a * 2048 : xrd + a * 1024));
+                bf16x8 fy[CB];
+#pragma unroll
+                for (int q = 0; q < CB; ++q) {
+                    if (UL == 2) {
+                        fy[q] = *reinterpret_cast<const bf16x8 *>(slot + yp[q][h]);
+                    } else if (YK) {
+                        fy[q] = *reinterpret_cast<const bf16x8 *>(slot + yrd[q][0]);
+                    } else {
+                        const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(slot + yrd[q][0]));
+                        const s16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(slot + yrd[q][1]));
+                        typedef short s16x8 __attribute__((ext_vector_type(8)));
+                        const s16x8 v = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+                        fy[q] = __builtin_bit_cast(bf16x8, v);
+                    }
+                }
+                F cur;
+                if (MA && lp.odd) {
+#pragma unroll
+                    for (int q = 0; q < CB; ++q)
+#pragma unroll
+                        for (int a = 0; a < MR; ++a)
+                            cur.v[a][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fy[q], fx[a], zero, 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < CB; ++q)
+#pragma unroll
+                        for (int a = 0; a < MR; ++a)
+                            cur.v[a][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fx[a], fy[q], zero, 0, 0, 0);
+                }
+                for (int k = 0; k < lp.merges; ++k) {
+                    --sp;
+#pragma unroll
+                    for (int a = 0; a < MR; ++a)
+#pragma unroll
+                        for (int q = 0; q < CB; ++q) {
+                            if constexpr (MA) {
+                                const u32x4 A = __builtin_shufflevector(st[a][q].raw(sp), pack_node(cur.v[a][q]),
+                                                                        0, 1, 2, 3);
+                                cur.v[a][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    __builtin_bit_cast(bf16x8, A), sel, zero, 0, 0, 0);
+                            } else {
+                                cur.v[a][q] = merge4(st[a][q].get(sp), cur.v[a][q]);
+                            }
+                        }
+                }
+                if (t + 1 < n) {
+#pragma unroll
+                    for (int a = 0; a < MR; ++a)
+#pragma unroll
+                        for (int q = 0; q < CB; ++q)
+                            st[a][q].put(sp, cur.v[a][q]);
+                    ++sp;
+                } else {
+                    // The wave's root goes to the start of its own ring: its
+                    // copies are complete (the last unit waited for all of
+                    // them) and nothing reads the ring after this leaf.
+#pragma unroll
+                    for (int a = 0; a < MR; ++a)
+#pragma unroll
+                        for (int q = 0; q < CB; ++q)
+                            *reinterpret_cast<f32x4 *>(ring + ((a * CB + q) * 64 + lane) * 16) = cur.v[a][q];
+                }
+            }
         }
-        const int m = merges_after(t, n);
-        for (int k = 0; k < m; ++k) {
-            --sp;
-#pragma unroll
-            for (int a = 0; a < MR; ++a)
-#pragma unroll
-                for (int q = 0; q < CB; ++q)
-                    cur.v[a][q] = merge4(st[a][q].get(sp), cur.v[a][q]);
-        }
-        if (t + 1 < n) {
-#pragma unroll
-            for (int a = 0; a < MR; ++a)
-#pragma unroll
-                for (int q = 0; q < CB; ++q)
-                    st[a][q].put(sp, cur.v[a][q]);
-            ++sp;
-        } else {
-            root = cur;
-        }
-      }
-    }
+    };
 
-    // The W subtree roots meet in LDS, each in its wave's own ring (the
-    // wave's copies and reads are complete); wave b < MR * CB adds the roots
-    // of block b = (row block, column block).
+    // The W subtree roots meet in LDS, each in its wave's own ring; wave w
+    // adds the roots of blocks b = w, w + W, ... (b = row block * CB + column
+    // block) in the order of the top levels, with element-wise adds.
+    constexpr int BPW = S::BPW;
+    f32x4 top[BPW];
+    auto meet = [&]() {
+        __syncthreads();
 #pragma unroll
-    for (int a = 0; a < MR; ++a)
+        for (int k = 0; k < BPW; ++k) {
+            const int b = wave + k * W;
+            top[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (b < MR * CB) {
+                f32x4 r[W];
 #pragma unroll
-        for (int q = 0; q < CB; ++q)
-            *reinterpret_cast<f32x4 *>(ring + ((a * CB + q) * 64 + lane) * 16) = root.v[a][q];
+                for (int w = 0; w < W; ++w)
+                    r[w] = *reinterpret_cast<const f32x4 *>(smem + w * S::WAVE_BYTES + (b * 64 + lane) * 16);
+                top[k] = top_levels<0, W>(r);
+            }
+        }
+    };
+
+    subtree(std::true_type{});
+    meet();
+    // A non-finite value in a matrix-core add spreads NaN over the other sums
+    // of its row, and every non-finite node leaves a non-finite root: a tile
+    // with a non-finite root is recomputed with element-wise adds (exact IEEE
+    // behaviour).  The flags are one dword per wave at the start of the LDS,
+    // written once every root has been read.
+    bool bad = false;
+#pragma unroll
+    for (int k = 0; k < BPW; ++k)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            bad |= !(__builtin_fabsf(top[k][v]) <= 3.40282347e38f);
+    const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
     __syncthreads();
-    if (wave >= MR * CB)
-        return;
-    f32x4 r[W];
+    int *flags = reinterpret_cast<int *>(smem);
+    if (lane == 0)
+        flags[wave] = wave_bad ? 1 : 0;
+    __syncthreads();
+    int any = 0;
 #pragma unroll
-    for (int w = 0; w < W; ++w)
-        r[w] = *reinterpret_cast<const f32x4 *>(smem + w * S::WAVE_BYTES + (wave * 64 + lane) * 16);
-    const f32x4 top = top_levels<0, W>(r);
+    for (int w = 0; w < W; w += 4) {
+        const uint4 f = *reinterpret_cast<const uint4 *>(flags + w);
+        any |= (int)(f.x | f.y | f.z | f.w);
+    }
+    if (any) {
+        __syncthreads();   // every wave has read the flags before the rings refill
+        subtree(std::false_type{});
+        meet();
+    }
 
     // Lane 16g + c holds rows 4g .. 4g+3 of column c of the block.  A zero
     // root is stored as +0.
-    const uint32_t lo2 = pair_bits(round_pair(top[0], top[1]));
-    const uint32_t hi2 = pair_bits(round_pair(top[2], top[3]));
-    const uint16_t v4[4] = {(uint16_t)lo2, (uint16_t)(lo2 >> 16), (uint16_t)hi2,
-                            (uint16_t)(hi2 >> 16)};
-    const int j = j0 + 16 * (wave % CB) + i16;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int i = 16 * (wave / CB) + 4 * G + v;
-        const uint16_t h = (v4[v] & 0x7FFF) ? v4[v] : (uint16_t)0;
-        if (i < p.I && j < p.J) {
-            if (OUT == OUT_BF16)
-                static_cast<uint16_t *>(p.c)[(int64_t)i * p.ldc + j] = h;
-            else
-                static_cast<float *>(p.c)[(int64_t)i * p.ldc + j] = __uint_as_float((uint32_t)h << 16);
+    for (int k = 0; k < BPW; ++k) {
+        const int b = wave + k * W;
+        if (b >= MR * CB)
+            break;
+        const uint32_t lo2 = pair_bits(round_pair(top[k][0], top[k][1]));
+        const uint32_t hi2 = pair_bits(round_pair(top[k][2], top[k][3]));
+        const uint16_t v4[4] = {(uint16_t)lo2, (uint16_t)(lo2 >> 16), (uint16_t)hi2,
+                                (uint16_t)(hi2 >> 16)};
+        const int j = j0 + 16 * (b % CB) + i16;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = 16 * (b / CB) + 4 * G + v;
+            const uint16_t h = (v4[v] & 0x7FFF) ? v4[v] : (uint16_t)0;
+            if (i < p.I && j < p.J) {
+                if (OUT == OUT_BF16)
+                    static_cast<uint16_t *>(p.c)[(int64_t)i * p.ldc + j] = h;
+                else
+                    static_cast<float *>(p.c)[(int64_t)i * p.ldc + j] = __uint_as_float((uint32_t)h << 16);
+            }
         }
     }
 }
@@ -477,8 +582,13 @@ hipError_t launch_decode_one(const MfmaParams &p, hipStream_t st) {
 // When the tiles make at most one round over the 256 compute units, the
 // chain of leaves of each wave sets the time: 16 waves (subtrees of depth 4,
 // half the leaves each) when there are at least 16 leaves and the rings fit.
+#ifndef DET_DECODE_WAVES
+#define DET_DECODE_WAVES 0
+#endif
 template <bool YK, int OUT, int MP, int CB, int UL>
 hipError_t launch_decode_waves(const MfmaParams &p, hipStream_t st) {
+    if constexpr (DET_DECODE_WAVES == 4 && DecodeShape<MP, CB, UL, 4>::kFits)
+        return launch_decode_one<YK, OUT, MP, CB, UL, 4>(p, st);
     if constexpr (CB <= 2 && DecodeShape<MP, CB, UL, 16>::kFits) {
         const int64_t tiles = (p.J + 16 * CB - 1) / (16 * CB);
         if (p.L >= 16 && tiles <= 256)
@@ -509,8 +619,12 @@ hipError_t launch_decode_rows(const MfmaParams &p, hipStream_t st) {
         if (p.I <= 32)
             return launch_decode_units<YK, OUT, 32, CB>(p, st);
     }
-    if constexpr (CB <= 2)     // 33 to 64 rows: four row blocks on 16- and 32-column tiles
-        return launch_decode_units<YK, OUT, 64, CB>(p, st);
+    if constexpr (CB <= 2) {   // 33 to 64 rows: four row blocks on 16- and 32-column tiles
+        if (p.I <= 64)
+            return launch_decode_units<YK, OUT, 64, CB>(p, st);
+    }
+    if constexpr (CB == 1)     // 65 to 128 rows: eight row blocks on 16-column tiles
+        return launch_decode_units<YK, OUT, 128, CB>(p, st);
     return hipErrorInvalidValue;
 }
 

@@ -1,6 +1,8 @@
-"""GPU parity of the decode kernel (tile configurations 10 to 12: at most 16
-rows of X, the reduction split over the 8 depth-3 subtrees of the mid-split
-tree; 16, 64 or 32 columns per workgroup), through the C-ABI.
+"""GPU parity of the decode kernel (tile configurations 10 to 12: at most 128,
+16 or 64 rows of X on 16-, 64- or 32-column tiles, the reduction split over the
+8 or 16 subtrees of the mid-split tree at depth 3 or 4, tree adds on the matrix
+core with an element-wise recomputation of tiles whose root is not finite),
+through the C-ABI.
 
 Contract (RL-Kernel operator page "Batch-Invariant Deterministic GEMM
 (det_gemm)", sections "Guarantees" and "Ascend NPU backend"): the same leaves
@@ -126,7 +128,7 @@ def test_decode_rows_invariant_to_batch(dev):
     for m in (2, 9):
         cm = bits(dg.det_gemm_fwd(X16[:m].contiguous(), B))
         assert np.array_equal(cm, c16[:m]), m
-    for m in (17, 24, 32, 40, 64):   # two or four staged row blocks
+    for m in (17, 24, 32, 40, 64, 65, 100, 128):   # two, four or eight staged row blocks
         cm = bits(dg.det_gemm_fwd(big[100:100 + m].contiguous(), B))
         assert np.array_equal(cm, c256[100:100 + m]), m
 
@@ -144,12 +146,12 @@ def test_decode_lm_head_row(dev):
             assert np.array_equal(bits(_forced(cfg, lambda: dg.det_gemm_fwd(A[:m], B))), ref), (m, cfg)
 
 
-@pytest.mark.parametrize("case", ["rows65", "leaves7", "ragged_k", "unaligned", "n_not_8"])
+@pytest.mark.parametrize("case", ["rows129", "leaves7", "ragged_k", "unaligned", "n_not_8"])
 def test_decode_rejects_unsupported(dev, case):
     """Forcing configuration 10, 11 or 12 on a problem it does not take is EINVAL;
     the automatic choice runs another kernel with the same bits."""
     say("decode kernel rejects", case)
-    M, N, K = {"rows65": (65, 64, 1024), "leaves7": (4, 64, 224), "ragged_k": (4, 64, 1040 + 8),
+    M, N, K = {"rows129": (129, 64, 1024), "leaves7": (4, 64, 224), "ragged_k": (4, 64, 1040 + 8),
                "unaligned": (4, 64, 1024), "n_not_8": (4, 13, 1024)}[case]
     A = W.randn_bf16((M, K + 8), 1.0, 1400).to(dev)
     A = A[:, 1:K + 1] if case == "unaligned" else A[:, :K].contiguous()
@@ -179,10 +181,14 @@ def test_decode_zero_products_give_positive_zero(dev):
         assert (out_t == 0).all(), cfg
 
 
-@pytest.mark.parametrize("M,K", [(1, 4096), (5, 1024), (16, 4128)])
+ROW_LIMITS = ((10, 128), (12, 64), (11, 16))
+
+
+@pytest.mark.parametrize("M,K", [(1, 4096), (5, 1024), (16, 4128), (40, 4096), (128, 1024),
+                                 (100, 4128)])
 def test_decode_nonfinite_inputs(dev, M, K):
-    """Inf and NaN in X or the weight: every decode configuration gives the
-    general kernel's bits (both layouts of the weight)."""
+    """Inf and NaN in X or the weight: every decode configuration that takes M
+    rows gives the general kernel's bits (both layouts of the weight)."""
     say("decode kernel, non-finite inputs", M, K)
     N = 200
     A = W.randn_bf16((M, K), 1.0, 1500 + K)
@@ -195,7 +201,34 @@ def test_decode_nonfinite_inputs(dev, M, K):
     ref = bits(_forced(GENERAL_CFG, lambda: dg.det_gemm_fwd(Ad, Bd)))
     ref_t = bits(_forced(GENERAL_CFG, lambda: dg.det_gemm_fwd_rhs_transposed(Ad, Btd)))
     assert np.array_equal(ref, ref_t)
-    for cfg in DECODE_CFGS:
+    for cfg, rows in ROW_LIMITS:
+        if M > rows:
+            continue
+        assert np.array_equal(bits(_forced(cfg, lambda: dg.det_gemm_fwd(Ad, Bd))), ref), cfg
+        assert np.array_equal(bits(_forced(cfg, lambda: dg.det_gemm_fwd_rhs_transposed(Ad, Btd))),
+                              ref), cfg
+
+
+@pytest.mark.parametrize("M", [1, 16, 64, 128])
+def test_decode_tree_overflow(dev, M):
+    """Finite leaves whose tree adds overflow: in columns 5 and 37 every leaf
+    is 32 * 2^122 = 2^127 (exact), so the first add of two leaves is 2^128,
+    +Inf in fp32 and bf16, and so is the root; the other columns stay finite.
+    The decode configurations give the general kernel's bits, and those
+    columns are +Inf."""
+    say("decode kernel, overflow in the tree adds", M)
+    K, N = 1024, 72
+    A = torch.ones((M, K), dtype=torch.bfloat16)
+    B = W.randn_bf16((K, N), 0.02, 1510 + M)
+    B[:, 5] = 2.0 ** 122
+    B[:, 37] = 2.0 ** 122
+    Ad, Bd, Btd = A.to(dev), B.to(dev), B.t().contiguous().to(dev)
+    ref = bits(_forced(GENERAL_CFG, lambda: dg.det_gemm_fwd(Ad, Bd)))
+    assert (ref[:, [5, 37]] == 0x7F80).all()
+    assert ((ref[:, [c for c in range(N) if c not in (5, 37)]] & 0x7F80) != 0x7F80).all()
+    for cfg, rows in ROW_LIMITS:
+        if M > rows:
+            continue
         assert np.array_equal(bits(_forced(cfg, lambda: dg.det_gemm_fwd(Ad, Bd))), ref), cfg
         assert np.array_equal(bits(_forced(cfg, lambda: dg.det_gemm_fwd_rhs_transposed(Ad, Btd))),
                               ref), cfg
@@ -207,14 +240,17 @@ def test_decode_nonfinite_inputs(dev, M, K):
 # kernels need) at N = 28672 stays on the decode kernel.
 @pytest.mark.parametrize("M,N,K", [(17, 200, 4096), (24, 6144, 4096), (32, 136, 1024), (20, 48, 4128),
                                    (32, 40, 32768), (33, 200, 4096), (48, 6144, 4096), (64, 72, 4128),
-                                   (61, 40, 1024), (17, 28672, 4096), (64, 28672, 4096),
+                                   (61, 40, 1024), (65, 200, 4096), (80, 6144, 4096),
+                                   (100, 40, 1024), (128, 72, 4128), (128, 6144, 4096),
+                                   (17, 28672, 4096), (64, 28672, 4096),
                                    (64, 14336, 4096), (40, 28672, 1536)])
 def test_row_blocks_match_general_kernel(dev, M, N, K):
-    """17 to 64 rows: the decode kernel stages 2 or 4 blocks of 16 rows of X on
-    16- and 32-column tiles (64-column tiles refuse); the automatic choice
+    """17 to 128 rows: the decode kernel stages 2 or 4 blocks of 16 rows of X on
+    16- and 32-column tiles, and 8 blocks on 16-column tiles (wider tiles
+    refuse what they do not take); the automatic choice
     moves wide products to the wide kernel.  Every path gives the general
     kernel's bits on the four X-row products."""
-    say("17..64 rows on the decode kernel vs general kernel", M, N, K)
+    say("17..128 rows on the decode kernel vs general kernel", M, N, K)
     A = W.randn_bf16((M, K), 1.0, 1600 + M + K).to(dev)
     B = W.randn_bf16((K, N), 0.02, 1601 + N + K).to(dev)
     dC = W.randn_bf16((M, N), 1.0, 1602 + N).to(dev)
@@ -222,7 +258,7 @@ def test_row_blocks_match_general_kernel(dev, M, N, K):
         ref = _as_bits(_forced(GENERAL_CFG, f))
         assert np.array_equal(_as_bits(f()), ref), op
         da_fits = op != "da" or (N % 32 == 0 and N // 32 >= 8)
-        for cfg, rows in ((10, 64), (12, 64), (11, 16)):
+        for cfg, rows in ROW_LIMITS:
             if not da_fits:
                 continue
             if M <= rows:
