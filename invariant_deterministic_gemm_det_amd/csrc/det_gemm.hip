@@ -158,23 +158,29 @@ bool fast_ok(const Problem &pr, const TreeSel &t) {
 
 // The wide kernel: the fast kernel's operand conditions and a leaf count
 // L = 2 * tb * 2^k with at least one group of 2^gl nodes of 2 * tb leaves
-// (with exactly one group, the group root is the root).  `up` receives the
-// levels above the groups.
+// (with exactly one group, the group root is the root); a tree split at its
+// root over two wave groups needs units of one leaf, a K-major X, a
+// row-major output and a group of stages in each half.  `up` receives the
+// levels above the groups (of one half for a split tree).
 bool wide_ok(const Problem &pr, const TreeSel &t, const TileCfg &c, int &up) {
     const int64_t L = (pr.R + 31) / 32;
-    if (!fast_ok(pr, t) || L % (2 * c.tb) != 0)
+    const bool split = c.ks > 1;
+    if (!fast_ok(pr, t) || L % (2 * c.tb) != 0 ||
+        (split && (!pr.xk || c.tb != 1 || pr.out == OUT_BF16_T)))
         return false;
     const int64_t S = L / (2 * c.tb), G = int64_t(1) << c.gl;  // nodes of 2 * tb leaves
-    if ((S & (S - 1)) != 0 || S < G)
+    const int64_t SG = split ? S / 2 : S;                      // stages of one wave group
+    if ((S & (S - 1)) != 0 || SG < G)
         return false;
     up = 0;
-    while ((G << up) < S)
+    while ((G << up) < SG)
         ++up;
     return c.lds_bytes(up) <= kLdsMax;  // the wide kernels use no static LDS
 }
 
-// The decode kernels (configurations 10 to 12): X K-major with at most 64
-// rows (at most 16 on 64-column tiles), bf16 or fp32 output, whole leaves, at
+// The decode kernels (configurations 10 to 12): X K-major with at most 128
+// rows (at most 64 on 32-column tiles, 16 on 64-column tiles), bf16 or fp32
+// output, whole leaves, at
 // least 8 and at most 1024 of them (one leaf or more per wave, at most 8
 // pending left siblings per wave), 16-byte aligned rows and, for a [K][N]
 // operand Y, whole 8-column chunks.
@@ -201,7 +207,13 @@ bool decode_ok(const Problem &pr) {
 // under about 1400 (M = 32, K = 4096, N = 6144: 16.7 us instead of 40 on the
 // wide kernel; N = 18432: 46 us instead of 51), or 600 for 65 to 128 rows on
 // 16-column tiles (M = 128, N = 2048: 20 us; N = 6144: 48 us instead of 40 on
-// the wide kernel); above, the wide kernel
+// the wide kernel).  Before those, 33 to 128 rows go to the 32-column wide
+// tiles with the tree split at its root over two wave groups, 64x32 while
+// they fit one round over the compute units (K = 4096: M = 128, N = 2048
+// 17 us instead of 20 on the decode kernel; M = 64, N = 6144 19 us instead of
+// 21), else 128x32 (M = 128, N = 6144: 24 us instead of 40 on the wide
+// kernel); up to 64 rows the decode kernel keeps at most 128 column tiles
+// (M = 64, N = 2048: 13 us, 17 on 64x32).  Otherwise the wide kernel
 // (N = 28672: 54 us instead of 65 at M = 32, 54 instead of 83 at M = 64),
 // on 128x128 tiles above 128 column tiles (N = 18432, M = 64: 51 us, 55 on
 // 128x64).  Otherwise 128x128 wide tiles when they make at least four waves
@@ -214,6 +226,17 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     int up = 0;
     if (decode_ok(pr)) {
         const int64_t t32 = (pr.J + 31) / 32, blocks = (pr.I + 15) / 16;
+        // 33 to 128 rows: the 32-column wide tiles that split the tree over
+        // two wave groups, while their tiles make at most one round over the
+        // compute units (and, up to 64 rows, once the decode kernel has more
+        // than 128 column tiles)
+        if (pr.I > 32) {
+            const int64_t t64 = (pr.I + 63) / 64 * t32, t128 = (pr.I + 127) / 128 * t32;
+            if (t64 <= 256 && (pr.I > 64 || t32 > 128) && wide_ok(pr, t, kTileCfgs[14], up))
+                return 14;
+            if (pr.I > 64 && t128 <= 256 && wide_ok(pr, t, kTileCfgs[13], up))
+                return 13;
+        }
         if ((pr.I > 16 && t32 * blocks > 1400) || (pr.I > 64 && t32 * blocks > 600)) {
             const int first = (pr.J + 127) / 128 > 128 ? 8 : 6;
             for (int c : {first, first == 8 ? 6 : 8})
@@ -920,7 +943,8 @@ int moe_entry(const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw, in
         int cfg = -1, up = 0;
         if (g_force_config >= 0) {
             if (kTileCfgs[g_force_config].kind == KIND_WIDE) {
-                if (g_force_config == 6 || !wide_ok(base, tree, kTileCfgs[g_force_config], up))
+                if (kTileCfgs[g_force_config].bn() != kSlot ||
+                    !wide_ok(base, tree, kTileCfgs[g_force_config], up))
                     return DET_GEMM_EINVAL;
                 cfg = g_force_config;
             }

@@ -582,13 +582,8 @@ hipError_t launch_decode_one(const MfmaParams &p, hipStream_t st) {
 // When the tiles make at most one round over the 256 compute units, the
 // chain of leaves of each wave sets the time: 16 waves (subtrees of depth 4,
 // half the leaves each) when there are at least 16 leaves and the rings fit.
-#ifndef DET_DECODE_WAVES
-#define DET_DECODE_WAVES 0
-#endif
 template <bool YK, int OUT, int MP, int CB, int UL>
 hipError_t launch_decode_waves(const MfmaParams &p, hipStream_t st) {
-    if constexpr (DET_DECODE_WAVES == 4 && DecodeShape<MP, CB, UL, 4>::kFits)
-        return launch_decode_one<YK, OUT, MP, CB, UL, 4>(p, st);
     if constexpr (CB <= 2 && DecodeShape<MP, CB, UL, 16>::kFits) {
         const int64_t tiles = (p.J + 16 * CB - 1) / (16 * CB);
         if (p.L >= 16 && tiles <= 256)

@@ -30,17 +30,22 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // XOR applied to the 16-byte chunk index of an MN-major tile row (one
-// reduction index).  NC = chunks per row: 8 (128-byte rows, two rows per LDS
-// bank sweep) or 16 (256-byte rows).  One transposed fragment read touches, per
-// 32 lanes, the reduction rows r0 + {0..3, 8..11} (r0 a multiple of 4), each at
-// the same aligned pair of chunks; the XOR (always even, so pairs stay pairs)
-// sends those rows to disjoint banks.
+// reduction index).  NC = chunks per row: 4 (64-byte rows, four rows per LDS
+// bank sweep), 8 (128-byte rows, two rows per sweep) or 16 (256-byte rows).
+// One transposed fragment read touches, per 32 lanes, the reduction rows
+// r0 + {0..3, 8..11} (r0 a multiple of 4), each at the same aligned pair of
+// chunks; the XOR (always even, so pairs stay pairs) sends those rows to
+// disjoint banks.  With 64-byte rows, rows r0 .. r0+3 already fill one sweep
+// with their pairs in disjoint banks, and rows r0+8 .. r0+11 take the other
+// pair of each row.
 template <int NC>
 __device__ __forceinline__ int mn_key(int r) {
     if constexpr (NC >= 16)
         return 2 * ((r & 3) | (((r >> 3) & 1) << 2));
-    else
+    else if constexpr (NC == 8)
         return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1));
+    else
+        return 2 * ((r >> 3) & 1);
 }
 
 template <bool KMAJOR, int NR, int NW>

@@ -38,6 +38,7 @@ struct TileCfg {
     int kind;
     int nbuf, gl, ru;  // wide kernel: stage buffers, static group levels, register levels
     int tb;            // wide kernel: leaves per unit (1 or 3)
+    int ks;            // wide kernel: wave groups splitting the tree at its root (0 or 1: none, 2)
     int bm() const { return 16 * fm * wm; }
     int bn() const { return 16 * fn * wn; }
     int nw() const { return wm * wn; }
@@ -49,7 +50,7 @@ struct TileCfg {
     int lds_bytes(int levels) const {
         const int park = fm * fn * nw() * 64 * 8;
         if (kind == KIND_WIDE)
-            return nbuf * (bm() + bn()) * 128 + (levels > ru ? levels - ru : 0) * park;
+            return (ks > 1 ? ks : 1) * (nbuf * (bm() + bn()) * 128 + (levels > ru ? levels - ru : 0) * park);
         const int parked = kind == KIND_FAST ? (levels > 1 ? levels - 1 : 0) : levels;
         return (kind == KIND_FAST ? 3 : 2) * (bm() + bn()) * 128 + parked * park;
     }
@@ -61,8 +62,9 @@ constexpr TileCfg kTileCfgs[] = {
     {4, 2, 2, 2, KIND_WIDE, 2, 3, 1, 1},    {4, 2, 2, 4, KIND_WIDE, 2, 2, 1, 3},
     {4, 2, 2, 4, KIND_WIDE, 3, 4, 1, 1},    {4, 2, 2, 4, KIND_WIDE, 3, 2, 1, 3},
     {1, 1, 1, 1, KIND_DECODE, 0, 0, 0, 1},  {1, 4, 1, 1, KIND_DECODE, 0, 0, 0, 1},
-    {1, 2, 1, 1, KIND_DECODE, 0, 0, 0, 1}};
-constexpr int kNumTileCfgs = 13;
+    {1, 2, 1, 1, KIND_DECODE, 0, 0, 0, 1},  {2, 2, 4, 1, KIND_WIDE, 4, 3, 2, 1, 2},
+    {2, 1, 2, 2, KIND_WIDE, 6, 3, 2, 1, 2}};
+constexpr int kNumTileCfgs = 15;
 
 struct TreeSel {
     int mode;  // TREE_BLOCK or TREE_STACK
@@ -130,6 +132,36 @@ hipError_t launch_wide(const MfmaParams &p, int64_t tiles, hipStream_t st) {
         if (lds > max_dynamic)
             return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL(kernel, dim3((unsigned)tiles), dim3(64 * WM * WN), lds, st, p);
+        return hipGetLastError();
+    }
+}
+
+// K-split wide kernel (X K-major, row-major bf16 or fp32 output): two wave
+// groups per workgroup, p.levels counted in one group's subtree.
+template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU, int OCC>
+hipError_t launch_wide_split(const MfmaParams &p, int64_t tiles, hipStream_t st) {
+    if constexpr (!XK || (OUT != OUT_BF16 && OUT != OUT_F32)) {
+        return hipErrorInvalidValue;
+    } else {
+        typedef WideEngine<true, YK, OUT, FM, FN, WM, WN, NBUF> E;
+        void (*kernel)(MfmaParams) = &mfma_wide_split_kernel<YK, OUT, FM, FN, WM, WN, NBUF, GL, RU, OCC>;
+        const void *fn = reinterpret_cast<const void *>(kernel);
+        static int max_dynamic = -1;
+        if (max_dynamic < 0) {
+            hipFuncAttributes attr;
+            hipError_t e = hipFuncGetAttributes(&attr, fn);
+            if (e != hipSuccess)
+                return e;
+            const int room = kLdsMax - (int)attr.sharedSizeBytes;
+            e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, room);
+            if (e != hipSuccess)
+                return e;
+            max_dynamic = room;
+        }
+        const int lds = 2 * E::lds_bytes(p.levels > RU ? p.levels - RU : 0);
+        if (lds > max_dynamic)
+            return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(kernel, dim3((unsigned)tiles), dim3(128 * WM * WN), lds, st, p);
         return hipGetLastError();
     }
 }
@@ -211,6 +243,14 @@ hipError_t launch_layout(int cfg, const TreeSel &t, const MfmaParams &p, int64_t
         return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 1, 4, 1, 2>(p, tiles, st);
     case 9:
         return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 3, 2, 1, 2>(p, tiles, st);
+    // Narrow tiles for 17 to 128 rows (X K-major, row-major output), the tree
+    // split at its root over two wave groups (half the stages per tile):
+    // 128x32 on 2 x 4 waves of 2 x 2 blocks with four stage buffers per group,
+    // 64x32 on 2 x 4 waves of 2 x 1 blocks with six.
+    case 13:
+        return launch_wide_split<XK, YK, OUT, 2, 2, 4, 1, 4, 3, 2, 2>(p, tiles, st);
+    case 14:
+        return launch_wide_split<XK, YK, OUT, 2, 1, 2, 2, 6, 3, 2, 2>(p, tiles, st);
     default:
         return hipErrorInvalidValue;
     }

@@ -268,6 +268,35 @@ __device__ __forceinline__ bool stage_roots(const Frag<FM, FN> &root, int wm, in
     return nonfinite;
 }
 
+// Copies a staged block of ROWS rows of COLS bf16 values to the output rows
+// row0 .. and columns col0 .. (only the first rows_ok rows and cols_ok
+// columns exist), 16 bytes per thread and pass; `tid` < 64 * NW.
+template <int ROWS, int COLS, int NW, bool SWZ>
+__device__ __forceinline__ void read_out_staged(const MfmaParams &p, const char *lds, int row0, int col0,
+                                                int rows_ok, int cols_ok, int tid) {
+    uint16_t *out = static_cast<uint16_t *>(p.c);
+    constexpr int CH = COLS / 8;  // chunks per row
+    static_assert(ROWS * CH % (64 * NW) == 0, "the passes cover the staged rows");
+#pragma unroll
+    for (int k = 0; k < ROWS * CH / (64 * NW); ++k) {
+        const int q = tid + k * 64 * NW;
+        const int r = q / CH, ch = q % CH;
+        if (r >= rows_ok)
+            continue;
+        const uint4 w = *reinterpret_cast<const uint4 *>(lds + staged_off<COLS, SWZ>(r, ch * 16));
+        uint16_t *dst = out + (int64_t)(row0 + r) * p.ldc + col0 + ch * 8;
+        if (p.cvec && ch * 8 + 8 <= cols_ok) {
+            *reinterpret_cast<uint4 *>(dst) = w;
+        } else {
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (ch * 8 + e < cols_ok)
+                    dst[e] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+}
+
 // EPI: also the slots of the epilogue (operands in the EpiInfo at the start of
 // the dynamic LDS; this tile's rows start at its row r0).  FLAGS: the
 // non-finite check of the rounded roots rides on the staging barrier
@@ -339,26 +368,7 @@ __device__ __forceinline__ bool store_staged(const MfmaParams &p, const Frag<FM,
     // read out: 16-byte chunks of staged rows
     const int row0 = T ? j0 : i0, col0 = T ? i0 : j0;
     const int rows_ok = (T ? p.J : p.I) - row0, cols_ok = (T ? p.I : p.J) - col0;
-    uint16_t *out = static_cast<uint16_t *>(p.c);
-    constexpr int CH = COLS / 8;  // chunks per row
-#pragma unroll
-    for (int k = 0; k < ROWS * CH / (64 * NW); ++k) {
-        const int q = threadIdx.x + k * 64 * NW;
-        const int r = q / CH, ch = q % CH;
-        if (r >= rows_ok)
-            continue;
-        const uint4 w = *reinterpret_cast<const uint4 *>(lds + staged_off<COLS, SWZ>(r, ch * 16));
-        uint16_t *dst = out + (int64_t)(row0 + r) * p.ldc + col0 + ch * 8;
-        if (p.cvec && ch * 8 + 8 <= cols_ok) {
-            *reinterpret_cast<uint4 *>(dst) = w;
-        } else {
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (ch * 8 + e < cols_ok)
-                    dst[e] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
-        }
-    }
+    read_out_staged<ROWS, COLS, NW, SWZ>(p, lds, row0, col0, rows_ok, cols_ok, threadIdx.x);
     // Slots from the staged rows (the values just stored).  Columns past the
     // last one hold the product +0, as the slot definition requires (not y * 0,
     // which is -0 for negative y).
@@ -456,10 +466,13 @@ struct WideEngine {
     // LDS: the parked tree levels first (`parked` of them), so that a lane's
     // slots are within the immediate offset of one address register, then the
     // NBUF stage buffers.
-    __device__ __forceinline__ WideEngine(const MfmaParams &p, char *lds_, int parked, int i0, int j0)
+    // tid0: the first thread of the engine's waves (a workgroup may hold two
+    // engines, one per wave group).
+    __device__ __forceinline__ WideEngine(const MfmaParams &p, char *lds_, int parked, int i0, int j0,
+                                          int tid0 = 0)
         : lds(lds_), smem(lds_ + parked * PARK_LEVEL) {
         const int lane = threadIdx.x & 63;
-        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int wave = __builtin_amdgcn_readfirstlane((threadIdx.x - tid0) >> 6);
         const int wm = wave % WM, wn = wave / WM;
         producer = wave < NP;
         sx.init(p.x, p.ldx, i0, p.I, producer ? wave : 0, lane);
@@ -481,7 +494,7 @@ struct WideEngine {
                 yoff[b] = XB + mnmajor_offset<BN>(wn * FN * 16 + b * 16, lane);
         }
         S = p.R / 64;
-        park_lane = lds_ + threadIdx.x * 8;
+        park_lane = lds_ + (threadIdx.x - tid0) * 8;
     }
 
     // Stage buffer k (0 or 1) of the two that nothing can still read or fill
@@ -962,11 +975,10 @@ struct WideTree {
         return finish_root(final_chain(wpack(add(c.u0, u1))));
     }
 
-    // Requires S = e.S = TB * G * 2^nup.  Computes and stores the tile;
-    // returns whether a root was non-finite.
-    __device__ __forceinline__ bool run() {
-        if constexpr (TB == 3)
-            return run3();
+    // Requires S = e.S = G * 2^nup (units of one leaf).  Computes the root
+    // (unrounded fp32, in the layout of its parity) without storing it.
+    __device__ __forceinline__ F run_root() {
+        static_assert(TB == 1, "units of one leaf");
         const int T = e.S >> GL;
         e.prologue();
         P x0;
@@ -980,7 +992,16 @@ struct WideTree {
             }
         for (int t = 0; t < T; ++t)
             stage<0>(t, x0, l1);
-        return finish(x0, l1);
+        return final_chain(wpack(add(x0, wpack(l1))));
+    }
+
+    // Requires S = e.S = TB * G * 2^nup.  Computes and stores the tile;
+    // returns whether a root was non-finite.
+    __device__ __forceinline__ bool run() {
+        if constexpr (TB == 3)
+            return run3();
+        else
+            return finish_root(run_root());
     }
 };
 
@@ -1046,6 +1067,134 @@ template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, i
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void mfma_wide_kernel(MfmaParams p) {
     wide_tile<XK, YK, OUT, FM, FN, WM, WN, NBUF, TB, GL, RU, false>(p, blockIdx.x);
+}
+
+// ---- K-split tiles (X K-major, bf16 or fp32 output, L a power of two): the
+// workgroup holds two wave groups of WM x WN waves, each with its own engine
+// and stage buffers.  Group g evaluates the subtree of the root's child g --
+// for L = 2^a the mid-split root splits at L / 2, so that child holds leaves
+// g L/2 .. (g+1) L/2 - 1 --, which halves the chain of stages a tile waits
+// for.  The two subtree roots meet in LDS and group 0 performs the root's
+// add, then rounds and stores the tile.  Both groups run the same number of
+// stages, so every workgroup barrier is reached by all waves.  With
+// matrix-core adds, a tile with a non-finite root returns true (not stored).
+template <class Arith, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU>
+__device__ __forceinline__ bool split_tile(const MfmaParams &p, int tile) {
+    typedef WideEngine<true, YK, OUT, FM, FN, WM, WN, NBUF> E;
+    typedef typename E::P P;
+    typedef typename E::F F;
+    constexpr int NW = E::NW;
+    static_assert(OUT == OUT_BF16 || OUT == OUT_F32, "row-major output");
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = wave / NW, lw = wave % NW;
+    const int wm = lw % WM, wn = lw / WM;
+    const int i0 = (tile / p.tiles_j) * E::BM;
+    const int j0 = (tile % p.tiles_j) * E::BN;
+    const int parked = p.levels > RU ? p.levels - RU : 0;
+    const int group_bytes = E::lds_bytes(parked);
+
+    // this group's half of the reduction
+    MfmaParams q = p;
+    const int half = p.R / 2;
+    q.R = half;
+    q.L = p.L / 2;
+    if (g == 1) {
+        q.x = p.x + half;
+        q.y = YK ? p.y + half : p.y + (int64_t)half * p.ldy;
+    }
+    E e(q, smem + g * group_bytes, parked, i0, j0, g * 64 * NW);
+    const bf16x8 sel = split_selector(lane);
+    WideTree<E, Arith, 1, GL, RU, false> tree(e, q, sel, i0, j0, false);
+    const P mine = wpack(tree.run_root());
+
+    // Every wave is past its last stage (its copies and reads are complete):
+    // group 1 hands its root, rounded and packed, to group 0 through the
+    // start of its own LDS region.
+    __syncthreads();
+    u32x2 *xchg = reinterpret_cast<u32x2 *>(smem + group_bytes) + lw * 64 + lane;
+    if (g == 1) {
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+                xchg[(a * FN + b) * NW * 64] = mine.w[a][b];
+    }
+    __syncthreads();
+
+    // the root: left child (group 0) + right child (group 1); its layout
+    // parity is that of the whole tree's height
+    const bool odd = Arith::kTransposes && (tree_height_rt(p.L) & 1) != 0;
+    F root;
+    bool nonfinite = false;
+    char *staged = smem + parked * E::PARK_LEVEL;   // group 0's first stage buffer
+    int *flags = reinterpret_cast<int *>(staged + E::BUF);  // its second
+    if (g == 0) {
+        P other;
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+                other.w[a][b] = xchg[(a * FN + b) * NW * 64];
+        root = Arith::add(mine, other, sel);
+        if constexpr (OUT == OUT_F32) {
+            if constexpr (Arith::kTransposes) {
+#pragma unroll
+                for (int a = 0; a < FM; ++a)
+#pragma unroll
+                    for (int b = 0; b < FN; ++b)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            nonfinite |= !(__builtin_fabsf(root.v[a][b][v]) <= 3.40282347e38f);
+            }
+        } else {
+            nonfinite = odd ? stage_roots<false, true, FM, FN, E::BN, true>(root, wm, wn, lane, staged)
+                            : stage_roots<false, false, FM, FN, E::BN, true>(root, wm, wn, lane, staged);
+        }
+    }
+    if constexpr (Arith::kTransposes) {
+        if (publish_nonfinite<2 * NW>(flags, nonfinite))
+            return true;
+    } else {
+        __syncthreads();
+    }
+    if (g == 0) {
+        if constexpr (OUT == OUT_F32)
+            store_root<OUT>(p, root, odd, i0, j0, wm, wn, lane);
+        else
+            read_out_staged<E::BM, E::BN, NW, true>(p, staged, i0, j0, p.I - i0, p.J - j0, threadIdx.x);
+    }
+    return false;
+}
+
+// The same tile with element-wise adds, for tiles whose matrix-core root was
+// not finite (kept out of line, as wide_valu_tile).
+template <bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU>
+__device__ __attribute__((noinline)) void split_valu_tile(MfmaParams q, int tile_arg) {
+    MfmaParams p = q;
+    p.x = uniform_ptr(q.x);
+    p.y = uniform_ptr(q.y);
+    p.c = uniform_ptr(q.c);
+    p.ldx = uniform64(q.ldx);
+    p.ldy = uniform64(q.ldy);
+    p.ldc = uniform64(q.ldc);
+    p.I = __builtin_amdgcn_readfirstlane(q.I);
+    p.J = __builtin_amdgcn_readfirstlane(q.J);
+    p.R = __builtin_amdgcn_readfirstlane(q.R);
+    p.L = __builtin_amdgcn_readfirstlane(q.L);
+    p.tiles_j = __builtin_amdgcn_readfirstlane(q.tiles_j);
+    p.levels = __builtin_amdgcn_readfirstlane(q.levels);
+    p.cvec = __builtin_amdgcn_readfirstlane(q.cvec);
+    split_tile<WideValuAdd, YK, OUT, FM, FN, WM, WN, NBUF, GL, RU>(p, __builtin_amdgcn_readfirstlane(tile_arg));
+}
+
+// p.levels: the levels above the groups of one subtree.
+template <bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU, int OCC>
+__global__ __launch_bounds__(128 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void mfma_wide_split_kernel(MfmaParams p) {
+    if (split_tile<WideMatrixAdd, YK, OUT, FM, FN, WM, WN, NBUF, GL, RU>(p, blockIdx.x))
+        split_valu_tile<YK, OUT, FM, FN, WM, WN, NBUF, GL, RU>(p, blockIdx.x);
 }
 
 // ---- grouped launch (MoE grouped GEMM): the row-major X is cut into

@@ -182,6 +182,7 @@ def test_decode_zero_products_give_positive_zero(dev):
 
 
 ROW_LIMITS = ((10, 128), (12, 64), (11, 16))
+NARROW_WIDE_CFGS = (13, 14)   # 32-column wide tiles, the tree split at its root
 
 
 @pytest.mark.parametrize("M,K", [(1, 4096), (5, 1024), (16, 4128), (40, 4096), (128, 1024),
@@ -267,3 +268,15 @@ def test_row_blocks_match_general_kernel(dev, M, N, K):
                 with pytest.raises(dg.DetGemmError) as e:
                     _forced(cfg, f)
                 assert e.value.code == dg.EINVAL
+        # 32-column wide tiles: power-of-two leaf counts of at least 32 whose
+        # parked levels fit the LDS (the reduction runs over K, or over N for
+        # da); at K = 1024 and 4096 they all run
+        R = N if op == "da" else K
+        pow2 = R % 64 == 0 and (R // 32) & (R // 32 - 1) == 0
+        for cfg in NARROW_WIDE_CFGS:
+            try:
+                got = _as_bits(_forced(cfg, f))
+            except dg.DetGemmError as err:
+                assert err.code == dg.EINVAL and (not pow2 or R not in (1024, 4096)), (op, cfg)
+                continue
+            assert pow2 and np.array_equal(got, ref), (op, cfg)

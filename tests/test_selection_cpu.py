@@ -6,7 +6,9 @@ which kernel each problem class runs on, through det_gemm_debug_config, which
 applies the entry point's argument checks and the selection to shape,
 alignment and leaf count without touching memory.  Configurations: 5 to 9
 wide kernels (6: 128x64 tiles; 8: 128x128 two-leaf units; 9: three-leaf
-units), 10 to 12 decode kernels with 16, 64 and 32 columns per workgroup.
+units), 10 to 12 decode kernels with 16, 64 and 32 columns per workgroup, 13
+and 14 the 128x32 and 64x32 wide tiles whose tree is split at its root over
+two wave groups.
 """
 import pytest
 
@@ -80,7 +82,7 @@ def test_small_m_transposed_weight():
 
 
 def test_decode_limits():
-    assert cfg(dg.OP_FWD, 65, 6144, 4096) not in (10, 11, 12)   # more than 64 rows
+    assert cfg(dg.OP_FWD, 129, 6144, 4096) not in (10, 11, 12)  # more than 128 rows
     assert cfg(dg.OP_FWD, 1, 6144, 224) not in (10, 11, 12)     # 7 leaves
     assert cfg(dg.OP_FWD, 1, 4096, 32768) == 10   # 1024 leaves, the reduction cap
     assert cfg(dg.OP_FWD, 1, 6143, 4096) not in (10, 11, 12)    # N not whole 8-column chunks
@@ -104,3 +106,28 @@ def test_argument_errors():
     with pytest.raises(dg.DetGemmError) as e:   # output overlapping an input
         dg.det_gemm_debug_config(dg.OP_FWD, A_ADDR, 64, B_ADDR, 64, A_ADDR, 64, 64, 64, 64)
     assert e.value.code == dg.EINVAL
+
+
+@pytest.mark.parametrize("M,N,want", [
+    (128, 6144, 13),   # QKV at 128 rows: 192 tiles of 128x32
+    (65, 6144, 13),
+    (64, 6144, 14),    # 192 tiles of 64x32
+    (48, 6144, 14),
+    (40, 6144, 14),
+    (32, 6144, 12),    # up to 32 rows: the decode kernel
+    (128, 2048, 14),   # 2 x 64 tiles of 64x32
+    (128, 4096, 14),   # 2 x 128 = 256 tiles: one round over the compute units
+    (64, 2048, 10),    # at most 128 column tiles: the decode kernel
+    (128, 14336, 6),   # 448 tiles of 128x32: the 128x64 wide kernel
+])
+def test_narrow_split_tiles(M, N, want):
+    assert cfg(dg.OP_FWD, M, N, 4096) == want
+    assert cfg(dg.OP_FWD_FP32, M, N, 4096) == want
+    assert cfg(dg.OP_FWD_RHS_TRANSPOSED, M, N, 4096) == want
+
+
+def test_narrow_split_tiles_need_a_power_of_two_leaf_count():
+    # K = 4128: 129 leaves; neither the split tiles nor the wide kernel take it
+    assert cfg(dg.OP_FWD, 128, 6144, 4128) == 10
+    # da at 128 rows reduces over N = 4096 (128 leaves) into 6144 columns
+    assert cfg(dg.OP_DA, 128, 4096, 6144) == 13
