@@ -496,9 +496,10 @@ def small_m_leg(dev, steps, warmup, decode_only=False):
              ("qkv", "W[K][N]", 64), ("qkv", "W[K][N]", 128),
              ("qkv", "W[N][K]", 1), ("qkv", "W[N][K]", 16), ("lm_head", "W[K][N]", 1),
              ("lm_head", "W[K][N]", 32), ("lm_head", "W[K][N]", 256)]
-    if decode_only:  # the rows on the decode kernel, one kernel instance each (the LM
-        # head at 32 rows is wide enough in N to run on the wide kernel)
-        cases = [c for c in cases if c[2] <= 16 or (c[0] == "qkv" and c[2] <= 64)]
+    if decode_only:  # the rows on the decode kernel and the split 32-column tiles, one
+        # kernel instance each (the LM head at 32 rows is wide enough in N to run on the
+        # wide kernel)
+        cases = [c for c in cases if c[2] <= 16 or (c[0] == "qkv" and c[2] <= 128)]
     rows = []
     for name, layout, m in cases:
         if name == "qkv":
@@ -531,7 +532,8 @@ def small_m_leg(dev, steps, warmup, decode_only=False):
         cfg = dg.det_gemm_debug_config(dg.OP_FWD_RHS_TRANSPOSED if transposed else dg.OP_FWD,
                                        x.data_ptr(), x.stride(0), w.data_ptr(), w.stride(0),
                                        out.data_ptr(), out.stride(0), m, n, k)
-        kernel = "mfma_decode_kernel" if cfg >= 10 else "mfma_wide_kernel" if cfg >= 5 else "mfma_kernel"
+        kernel = ("mfma_wide_split_kernel" if cfg >= 13 else "mfma_decode_kernel" if cfg >= 10
+                  else "mfma_wide_kernel" if cfg >= 5 else "mfma_kernel")
         nbytes = (m * k + k * n + m * n) * 2
         gbs = nbytes / (t * 1e-3) / 1e9
         rows.append({"op": name, "weight": layout, "M": m, "K": k, "N": n, "us": round(t * 1e3, 2),
@@ -539,7 +541,8 @@ def small_m_leg(dev, steps, warmup, decode_only=False):
                      "GB/s": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
                      "kernel": kernel, "config": cfg})
     return {"workload": "forward products with 1..256 rows: the weight read once per call "
-                        "(at most 64 rows on the decode kernel, unless wide in N)",
+                        "(the decode kernel, 32-column wide tiles whose tree is split over two "
+                        "wave groups from 33 to 128 rows, the wide kernel when wide in N)",
             "timing": "us: per call, calls replayed from a captured graph; us_eager_calls: "
                       "back-to-back calls through the binding (host launch path included)",
             "roofline": "hbm, 8000 GB/s", "rows": rows}
