@@ -548,6 +548,35 @@ def small_m_leg(dev, steps, warmup, decode_only=False):
             "roofline": "hbm, 8000 GB/s", "rows": rows}
 
 
+def issue_probe_leg(iters=4000):
+    """The instruction mix of one pipeline stage of the 128x128 wide kernel
+    (per wave: 32 MFMAs, 64 bf16 conversions, each conversion feeding the next
+    MFMA; 8 waves per compute unit), without memory traffic, on all 256
+    compute units: its time per stage bounds the kernel's main loop from
+    below.  The MFMAs alone give the matrix-core rate at the clock the chip
+    holds under this load: 2 waves x 32 MFMAs of 16 cycles (the published
+    bf16 peak over 1024 SIMDs at 2.4 GHz) per SIMD and stage."""
+    import torch
+    import invariant_deterministic_gemm_det_amd as dg
+    dev = torch.device("cuda:0")
+    sink = torch.empty(256 * 512, dtype=torch.float32, device=dev)
+    dg.det_gemm_debug_issue_probe(1, 100, sink)
+    torch.cuda.synchronize()
+    out = {}
+    for mode, name in ((0, "mfma_only"), (1, "stage_mix")):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dg.det_gemm_debug_issue_probe(mode, iters, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        out[name] = {"ms": round(ms, 4), "ns_per_stage": round(ms * 1e6 / iters, 2)}
+    mhz = 2 * 32 * 16 / (out["mfma_only"]["ns_per_stage"] * 1e-3)
+    out["sclk_mhz_implied"] = round(mhz, 1)
+    out["stage_mix_cycles"] = round(out["stage_mix"]["ns_per_stage"] * mhz * 1e-3, 1)
+    return out
+
+
 def strict_leg(X, W, rows):
     """The strict-order kernel (det_gemm_strict_fwd: one scalar fp32 FMA chain
     per leaf, bit-exact to the oracle) on a row slice of the forward product,
@@ -709,9 +738,30 @@ def main():
     issue = recorded_issue(dom)
     ceilings = {"mfma_leaf_share": 0.5}
     at_clock = None
+    # The issue probe (live, this run): the stage's instruction mix alone, in
+    # TFLOP/s of the whole chip at 2 * 128 * 128 * 64 flops per compute unit
+    # and stage, at the clock the probe held.
+    try:
+        probe = issue_probe_leg()
+        flops_stage = 2.0 * 128 * 128 * 64 * 256   # leaf flops of one stage on every compute unit
+        ceil = flops_stage / (probe["stage_mix"]["ns_per_stage"] * 1e-9) / 1e12
+        probe["stage_mix_ceiling_tflops"] = round(ceil, 1)
+        probe["mfma_only_ceiling_tflops"] = round(
+            flops_stage / (probe["mfma_only"]["ns_per_stage"] * 1e-9) / 1e12, 1)
+        probe["frac_of_stage_mix_ceiling"] = round(achieved / ceil, 4)
+        ceilings["issue_probe"] = probe
+    except Exception as e:  # a ceiling, not the measurement
+        ceilings["issue_probe_error"] = str(e)[:120]
     if "sclk_mhz" in issue:
         peak_at_clock = PEAK_BF16_TFLOPS * issue["sclk_mhz"] / CLOCK_MHZ_PEAK
-        at_clock = {"sclk_mhz": issue["sclk_mhz"], "peak_tflops": round(peak_at_clock, 1),
+        at_clock = {"sclk_mhz": issue["sclk_mhz"], "source": "counter pass under profiles/",
+                    "peak_tflops": round(peak_at_clock, 1),
+                    "pct_of_peak_at_measured_clock": round(100 * achieved / peak_at_clock, 2)}
+    elif "issue_probe" in ceilings:
+        mhz = ceilings["issue_probe"]["sclk_mhz_implied"]
+        peak_at_clock = PEAK_BF16_TFLOPS * mhz / CLOCK_MHZ_PEAK
+        at_clock = {"sclk_mhz": mhz, "source": "MFMA rate of the issue probe, this run",
+                    "peak_tflops": round(peak_at_clock, 1),
                     "pct_of_peak_at_measured_clock": round(100 * achieved / peak_at_clock, 2)}
     if "valu_per_block_leaf" in issue:
         v = issue["valu_per_block_leaf"]

@@ -179,6 +179,18 @@ int det_gemm_debug_add(const det_bf16 *a, const det_bf16 *b, det_bf16 *out, int6
 int det_gemm_debug_matrix_add(const det_bf16 *a, const det_bf16 *b, det_bf16 *out, int64_t n,
                               int selector, void *stream);
 
+/* Issue-rate probe (inspection; no page defines it -- it measures the chip the
+ * kernels run on).  Runs `workgroups` workgroups of 512 threads (two waves
+ * per SIMD) on `stream`; each wave loops `iters` times over the instruction
+ * mix of one pipeline stage of the 128x128 wide kernel without memory
+ * traffic: 32 v_mfma_f32_16x16x32_bf16 and 64 v_cvt_pk_bf16_f32 per wave and
+ * iteration, each conversion rounding an MFMA result that the next MFMA
+ * consumes (mode 1), or the MFMAs alone (mode 0).  The caller times the
+ * launch (e.g. with events on `stream`).  sink: device float[workgroups *
+ * 512], written with meaningless values.  EINVAL: mode outside 0..1,
+ * iters < 1, workgroups < 1, or sink null. */
+int det_gemm_debug_issue_probe(int mode, int iters, int workgroups, float *sink, void *stream);
+
 /* Inspection: pins the MFMA kernel's tile configuration (0 .. count-1) for
  * subsequent calls on this process, or restores automatic selection (-1).
  * Every configuration computes the same leaves and tree, so the results must

@@ -28,7 +28,7 @@ _SIX = ("det_gemm_fwd", "det_gemm_fwd_rhs_transposed", "det_gemm_fwd_fp32", "det
         "det_gemm_db", "det_gemm_db_transposed")
 EXPORTS = _SIX + tuple(n.replace("det_gemm_", "det_gemm_strict_") for n in _SIX) + (
     "det_gemm_debug_leaves", "det_gemm_debug_round", "det_gemm_debug_add",
-    "det_gemm_debug_matrix_add",
+    "det_gemm_debug_matrix_add", "det_gemm_debug_issue_probe",
     "det_gemm_debug_force_config", "det_gemm_debug_config", "det_gemm_status_string",
     "det_moe_fwd_dprob",
     "det_moe_debug_slots", "det_fingerprint", "det_fingerprint_rows", "det_first_mismatch",
@@ -79,6 +79,8 @@ def load_library(path=LIB_PATH):
     lib.det_gemm_debug_add.restype = ctypes.c_int
     lib.det_gemm_debug_matrix_add.argtypes = [p, p, p, i64, ctypes.c_int, p]
     lib.det_gemm_debug_matrix_add.restype = ctypes.c_int
+    lib.det_gemm_debug_issue_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, p, p]
+    lib.det_gemm_debug_issue_probe.restype = ctypes.c_int
     lib.det_gemm_debug_force_config.argtypes = [ctypes.c_int]
     lib.det_gemm_debug_force_config.restype = ctypes.c_int
     lib.det_gemm_debug_config.argtypes = [ctypes.c_int, p, i64, p, i64, p, i64, i64, i64, i64]
@@ -595,6 +597,21 @@ def det_gemm_debug_matrix_add(a, b, selector=0):
                                                       int(selector), _stream(a))
     _check(rc, "det_gemm_debug_matrix_add")
     return out
+
+
+def det_gemm_debug_issue_probe(mode, iters, sink):
+    """Launch the issue-rate probe on the current stream of sink's device:
+    mode 0 the MFMAs of one wide-kernel stage alone, 1 the stage's MFMAs and
+    conversions; one workgroup per 512 elements of `sink` (contiguous float32,
+    overwritten)."""
+    if sink.dtype != torch.float32 or not sink.is_contiguous() or sink.numel() < 512:
+        raise TypeError("sink must be a contiguous float32 tensor of at least 512 elements")
+    if sink.device.type != "cuda":
+        raise ValueError("sink must be a device tensor")
+    with torch.cuda.device(sink.device):
+        rc = load_library().det_gemm_debug_issue_probe(int(mode), int(iters), sink.numel() // 512,
+                                                       ctypes.c_void_p(sink.data_ptr()), _stream(sink))
+    _check(rc, "det_gemm_debug_issue_probe")
 
 
 OP_FWD, OP_FWD_RHS_TRANSPOSED, OP_FWD_FP32, OP_DA, OP_DB, OP_DB_TRANSPOSED = range(6)

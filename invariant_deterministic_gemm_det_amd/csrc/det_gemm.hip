@@ -461,6 +461,63 @@ __global__ void debug_add_kernel(const uint16_t *a, const uint16_t *b, uint16_t 
     }
 }
 
+// Issue-rate probe (inspection): the instruction mix of one pipeline stage of
+// the 128x128 wide kernel without any memory traffic.  Per wave and
+// iteration, four rounds of 8 independent v_mfma_f32_16x16x32_bf16 whose
+// results are each rounded to bf16 by two v_cvt_pk_bf16_f32 and fed back as
+// the next round's A operand (a tree add consumes its children rounded):
+// 32 MFMAs and 64 conversions, the per-stage counts of a wave of that kernel.
+// MODE 0: the MFMAs alone (accumulating chains); 1: both, dependent as above.
+// 512 threads per workgroup (two waves per SIMD, as the wide kernel).  Values
+// stay bounded (B holds 1/32); each thread writes one float of `sink`.
+template <int MODE>
+__global__ __launch_bounds__(512) void issue_probe_kernel(float *sink, int iters) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t one32 = 0x3D003D00u;  // bf16 1/32, twice
+    const u32x4 bw = {one32, one32, one32, one32};
+    const bf16x8 B = __builtin_bit_cast(bf16x8, bw);
+    const u32x4 bw1 = {one32, 0u, one32, 0u};   // a second weight: different products
+    const bf16x8 B1 = __builtin_bit_cast(bf16x8, bw1);
+    u32x4 A[8];
+    f32x4 acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t w = 0x3F803F80u + (uint32_t)((lane + k) & 7);
+        A[k] = u32x4{w, w, w, w};
+        acc[k] = f32x4{1.0f + k, 1.0f, 1.0f, (float)lane};
+    }
+    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if constexpr (MODE == 0) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[k]), B,
+                                                                     acc[k], 0, 0, 0);
+            } else {
+                // A of MFMAs 2q and 2q + 1: the rounded results of the previous
+                // round's MFMAs 2q and 2q + 1 (as a tree add's two children)
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[k >> 1]),
+                                                                     (k & 1) ? B1 : B, zero, 0, 0, 0);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    A[q] = u32x4{pair_bits(round_pair(acc[2 * q][0], acc[2 * q][1])),
+                                 pair_bits(round_pair(acc[2 * q][2], acc[2 * q][3])),
+                                 pair_bits(round_pair(acc[2 * q + 1][0], acc[2 * q + 1][1])),
+                                 pair_bits(round_pair(acc[2 * q + 1][2], acc[2 * q + 1][3]))};
+            }
+        }
+    }
+    float v = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        v += acc[k][0] + acc[k][1] + acc[k][2] + acc[k][3] + __uint_as_float(A[k][0] & 0x3FFFFFFFu);
+    sink[(int64_t)blockIdx.x * 512 + threadIdx.x] = v;
+}
+
 // The tree add as the matrix-core kernels run it.  Blocks of 256 pairs, one
 // wave per block: pair k of a block sits at block position (k / 16, k % 16) of
 // both children, i.e. in the lane and register where an MFMA result holds that
@@ -768,6 +825,20 @@ int det_gemm_debug_matrix_add(const det_bf16 *a, const det_bf16 *b, det_bf16 *ou
         return DET_GEMM_EINVAL;
     hipLaunchKernelGGL(debug_matrix_add_kernel, dim3((unsigned)blocks), dim3(256), 0,
                        static_cast<hipStream_t>(stream), a, b, out, n, selector);
+    return hipGetLastError() == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
+}
+
+int det_gemm_debug_issue_probe(int mode, int iters, int workgroups, float *sink, void *stream) {
+    if (mode < 0 || mode > 1 || iters < 1 || workgroups < 1 || !sink)
+        return DET_GEMM_EINVAL;
+    const int dev = check_device();
+    if (dev != DET_GEMM_OK)
+        return dev;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (mode == 0)
+        hipLaunchKernelGGL(issue_probe_kernel<0>, dim3((unsigned)workgroups), dim3(512), 0, st, sink, iters);
+    else
+        hipLaunchKernelGGL(issue_probe_kernel<1>, dim3((unsigned)workgroups), dim3(512), 0, st, sink, iters);
     return hipGetLastError() == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
 }
 

@@ -225,6 +225,16 @@ def test_debug_matrix_add_argument_errors(lib):
     assert f(FAKE, FAKE, out, 0, 1, NULL) == dg.OK
 
 
+def test_issue_probe_argument_errors(lib):
+    sink = ctypes.c_void_p(0x900000000)
+    f = lib.det_gemm_debug_issue_probe
+    assert f(2, 10, 256, sink, NULL) == dg.EINVAL      # unknown mode
+    assert f(-1, 10, 256, sink, NULL) == dg.EINVAL
+    assert f(0, 0, 256, sink, NULL) == dg.EINVAL       # no iterations
+    assert f(1, 10, 0, sink, NULL) == dg.EINVAL        # no workgroups
+    assert f(1, 10, 256, NULL, NULL) == dg.EINVAL
+
+
 # ---------------------------------------------------------------- the Python binding
 
 def _t(shape, dtype):
