@@ -169,7 +169,7 @@ bool wide_ok(const Problem &pr, const TreeSel &t, const TileCfg &c, int &up) {
         (split && (!pr.xk || c.tb != 1 || pr.out == OUT_BF16_T)))
         return false;
     const int64_t S = L / (2 * c.tb), G = int64_t(1) << c.gl;  // nodes of 2 * tb leaves
-    const int64_t SG = split ? S / 2 : S;                      // stages of one wave group
+    const int64_t SG = split ? S / c.ks : S;                   // stages of one wave group
     if ((S & (S - 1)) != 0 || SG < G)
         return false;
     up = 0;
@@ -212,8 +212,12 @@ bool decode_ok(const Problem &pr) {
 // they fit one round over the compute units (K = 4096: M = 128, N = 2048
 // 17 us instead of 20 on the decode kernel; M = 64, N = 6144 19 us instead of
 // 21), else 128x32 (M = 128, N = 6144: 24 us instead of 40 on the wide
-// kernel); up to 64 rows the decode kernel keeps at most 128 column tiles
-// (M = 64, N = 2048: 13 us, 17 on 64x32).  Otherwise the wide kernel
+// kernel); up to 64 rows the decode kernel keeps at most 128 and more than
+// 192 column tiles (M = 64, N = 2048: 13 us, 17 on 64x32; N = 8192: 22.5 us,
+// 23.3 on 64x32).  A K-major Y (whole 128-byte lines
+// per column and stage) takes 64x32 tiles on four wave groups instead, at
+// any column count that fits one round (M = 64, N = 6144: 14.1 us instead of
+// 16.3; M = 128, N = 2048: 12.9 instead of 15.8).  Otherwise the wide kernel
 // (N = 28672: 54 us instead of 65 at M = 32, 54 instead of 83 at M = 64),
 // on 128x128 tiles above 128 column tiles (N = 18432, M = 64: 51 us, 55 on
 // 128x64).  Otherwise 128x128 wide tiles when they make at least four waves
@@ -227,12 +231,15 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     if (decode_ok(pr)) {
         const int64_t t32 = (pr.J + 31) / 32, blocks = (pr.I + 15) / 16;
         // 33 to 128 rows: the 32-column wide tiles that split the tree over
-        // two wave groups, while their tiles make at most one round over the
-        // compute units (and, up to 64 rows, once the decode kernel has more
-        // than 128 column tiles)
+        // wave groups, while their tiles make at most one round over the
+        // compute units (and, up to 64 rows of a [K][N] weight, while the
+        // decode kernel has 129 to 192 column tiles)
         if (pr.I > 32) {
             const int64_t t64 = (pr.I + 63) / 64 * t32, t128 = (pr.I + 127) / 128 * t32;
-            if (t64 <= 256 && (pr.I > 64 || t32 > 128) && wide_ok(pr, t, kTileCfgs[14], up))
+            if (pr.yk && t64 <= 256 && wide_ok(pr, t, kTileCfgs[15], up))
+                return 15;
+            if (t64 <= 256 && (pr.I > 64 || (t32 > 128 && t32 <= 192)) &&
+                wide_ok(pr, t, kTileCfgs[14], up))
                 return 14;
             if (pr.I > 64 && t128 <= 256 && wide_ok(pr, t, kTileCfgs[13], up))
                 return 13;

@@ -63,8 +63,8 @@ constexpr TileCfg kTileCfgs[] = {
     {4, 2, 2, 4, KIND_WIDE, 3, 4, 1, 1},    {4, 2, 2, 4, KIND_WIDE, 3, 2, 1, 3},
     {1, 1, 1, 1, KIND_DECODE, 0, 0, 0, 1},  {1, 4, 1, 1, KIND_DECODE, 0, 0, 0, 1},
     {1, 2, 1, 1, KIND_DECODE, 0, 0, 0, 1},  {2, 2, 4, 1, KIND_WIDE, 4, 3, 2, 1, 2},
-    {2, 1, 2, 2, KIND_WIDE, 6, 3, 2, 1, 2}};
-constexpr int kNumTileCfgs = 15;
+    {2, 1, 2, 2, KIND_WIDE, 6, 3, 2, 1, 2},  {2, 1, 2, 2, KIND_WIDE, 3, 3, 2, 1, 4}};
+constexpr int kNumTileCfgs = 16;
 
 struct TreeSel {
     int mode;  // TREE_BLOCK or TREE_STACK
@@ -136,15 +136,16 @@ hipError_t launch_wide(const MfmaParams &p, int64_t tiles, hipStream_t st) {
     }
 }
 
-// K-split wide kernel (X K-major, row-major bf16 or fp32 output): two wave
+// K-split wide kernel (X K-major, row-major bf16 or fp32 output): KS wave
 // groups per workgroup, p.levels counted in one group's subtree.
-template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU, int OCC>
+template <bool XK, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU, int KS,
+          int OCC>
 hipError_t launch_wide_split(const MfmaParams &p, int64_t tiles, hipStream_t st) {
     if constexpr (!XK || (OUT != OUT_BF16 && OUT != OUT_F32)) {
         return hipErrorInvalidValue;
     } else {
         typedef WideEngine<true, YK, OUT, FM, FN, WM, WN, NBUF> E;
-        void (*kernel)(MfmaParams) = &mfma_wide_split_kernel<YK, OUT, FM, FN, WM, WN, NBUF, GL, RU, OCC>;
+        void (*kernel)(MfmaParams) = &mfma_wide_split_kernel<YK, OUT, FM, FN, WM, WN, NBUF, GL, RU, KS, OCC>;
         const void *fn = reinterpret_cast<const void *>(kernel);
         static int max_dynamic = -1;
         if (max_dynamic < 0) {
@@ -158,10 +159,10 @@ hipError_t launch_wide_split(const MfmaParams &p, int64_t tiles, hipStream_t st)
                 return e;
             max_dynamic = room;
         }
-        const int lds = 2 * E::lds_bytes(p.levels > RU ? p.levels - RU : 0);
+        const int lds = KS * E::lds_bytes(p.levels > RU ? p.levels - RU : 0);
         if (lds > max_dynamic)
             return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(kernel, dim3((unsigned)tiles), dim3(128 * WM * WN), lds, st, p);
+        hipLaunchKernelGGL(kernel, dim3((unsigned)tiles), dim3(64 * KS * WM * WN), lds, st, p);
         return hipGetLastError();
     }
 }
@@ -243,14 +244,17 @@ hipError_t launch_layout(int cfg, const TreeSel &t, const MfmaParams &p, int64_t
         return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 1, 4, 1, 2>(p, tiles, st);
     case 9:
         return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 3, 2, 1, 2>(p, tiles, st);
-    // Narrow tiles for 17 to 128 rows (X K-major, row-major output), the tree
-    // split at its root over two wave groups (half the stages per tile):
+    // Narrow tiles for 33 to 128 rows (X K-major, row-major output), the tree
+    // split over wave groups (the stages per tile divided by their number):
     // 128x32 on 2 x 4 waves of 2 x 2 blocks with four stage buffers per group,
-    // 64x32 on 2 x 4 waves of 2 x 1 blocks with six.
+    // 64x32 on 2 x 4 waves of 2 x 1 blocks with six, and 64x32 on 4 x 4 waves
+    // (four waves per SIMD) with three.
     case 13:
-        return launch_wide_split<XK, YK, OUT, 2, 2, 4, 1, 4, 3, 2, 2>(p, tiles, st);
+        return launch_wide_split<XK, YK, OUT, 2, 2, 4, 1, 4, 3, 2, 2, 2>(p, tiles, st);
     case 14:
-        return launch_wide_split<XK, YK, OUT, 2, 1, 2, 2, 6, 3, 2, 2>(p, tiles, st);
+        return launch_wide_split<XK, YK, OUT, 2, 1, 2, 2, 6, 3, 2, 2, 2>(p, tiles, st);
+    case 15:
+        return launch_wide_split<XK, YK, OUT, 2, 1, 2, 2, 3, 3, 2, 4, 4>(p, tiles, st);
     default:
         return hipErrorInvalidValue;
     }

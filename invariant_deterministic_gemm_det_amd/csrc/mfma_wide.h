@@ -1070,20 +1070,24 @@ void mfma_wide_kernel(MfmaParams p) {
 }
 
 // ---- K-split tiles (X K-major, bf16 or fp32 output, L a power of two): the
-// workgroup holds two wave groups of WM x WN waves, each with its own engine
-// and stage buffers.  Group g evaluates the subtree of the root's child g --
-// for L = 2^a the mid-split root splits at L / 2, so that child holds leaves
-// g L/2 .. (g+1) L/2 - 1 --, which halves the chain of stages a tile waits
-// for.  The two subtree roots meet in LDS and group 0 performs the root's
-// add, then rounds and stores the tile.  Both groups run the same number of
-// stages, so every workgroup barrier is reached by all waves.  With
-// matrix-core adds, a tile with a non-finite root returns true (not stored).
-template <class Arith, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU>
+// workgroup holds KS = 2 or 4 wave groups of WM x WN waves, each with its own
+// engine and stage buffers.  For L = 2^a the mid-split tree's nodes of depth
+// log2 KS are the KS equal quarters (halves) of the leaves: group g evaluates
+// the subtree over leaves g L/KS .. (g+1) L/KS - 1, which divides the chain
+// of stages a tile waits for by KS.  The subtree roots meet in LDS and group 0
+// performs the adds of the top log2 KS levels ((0 + 1) for KS = 2,
+// (0 + 1) + (2 + 3) for KS = 4), then rounds and stores the tile.  All groups
+// run the same number of stages, so every workgroup barrier is reached by all
+// waves.  With matrix-core adds, a tile with a non-finite root returns true
+// (not stored).
+template <class Arith, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU,
+          int KS>
 __device__ __forceinline__ bool split_tile(const MfmaParams &p, int tile) {
     typedef WideEngine<true, YK, OUT, FM, FN, WM, WN, NBUF> E;
     typedef typename E::P P;
     typedef typename E::F F;
     constexpr int NW = E::NW;
+    static_assert(KS == 2 || KS == 4, "two or four wave groups");
     static_assert(OUT == OUT_BF16 || OUT == OUT_F32, "row-major output");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int lane = threadIdx.x & 63;
@@ -1095,49 +1099,58 @@ __device__ __forceinline__ bool split_tile(const MfmaParams &p, int tile) {
     const int parked = p.levels > RU ? p.levels - RU : 0;
     const int group_bytes = E::lds_bytes(parked);
 
-    // this group's half of the reduction
+    // this group's part of the reduction
     MfmaParams q = p;
-    const int half = p.R / 2;
-    q.R = half;
-    q.L = p.L / 2;
-    if (g == 1) {
-        q.x = p.x + half;
-        q.y = YK ? p.y + half : p.y + (int64_t)half * p.ldy;
-    }
+    const int part = p.R / KS;
+    q.R = part;
+    q.L = p.L / KS;
+    q.x = p.x + g * part;
+    q.y = YK ? p.y + g * part : p.y + (int64_t)(g * part) * p.ldy;
     E e(q, smem + g * group_bytes, parked, i0, j0, g * 64 * NW);
     const bf16x8 sel = split_selector(lane);
     WideTree<E, Arith, 1, GL, RU, false> tree(e, q, sel, i0, j0, false);
     const P mine = wpack(tree.run_root());
 
     // Every wave is past its last stage (its copies and reads are complete):
-    // group 1 hands its root, rounded and packed, to group 0 through the
-    // start of its own LDS region.
+    // groups 1 .. KS-1 hand their roots, rounded and packed, to group 0, each
+    // through the start of its own LDS region.
     __syncthreads();
-    u32x2 *xchg = reinterpret_cast<u32x2 *>(smem + group_bytes) + lw * 64 + lane;
-    if (g == 1) {
+    const int slot = lw * 64 + lane;
+    if (g > 0) {
+        u32x2 *x = reinterpret_cast<u32x2 *>(smem + g * group_bytes) + slot;
 #pragma unroll
         for (int a = 0; a < FM; ++a)
 #pragma unroll
             for (int b = 0; b < FN; ++b)
-                xchg[(a * FN + b) * NW * 64] = mine.w[a][b];
+                x[(a * FN + b) * NW * 64] = mine.w[a][b];
     }
     __syncthreads();
+    auto root_of = [&](int h) {
+        const u32x2 *x = reinterpret_cast<const u32x2 *>(smem + h * group_bytes) + slot;
+        P r;
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b)
+                r.w[a][b] = x[(a * FN + b) * NW * 64];
+        return r;
+    };
 
-    // the root: left child (group 0) + right child (group 1); its layout
-    // parity is that of the whole tree's height
+    // the top levels, left child first; the root's layout parity is that of
+    // the whole tree's height
     const bool odd = Arith::kTransposes && (tree_height_rt(p.L) & 1) != 0;
     F root;
     bool nonfinite = false;
-    char *staged = smem + parked * E::PARK_LEVEL;   // group 0's first stage buffer
+    char *staged = smem + parked * E::PARK_LEVEL;           // group 0's first stage buffer
     int *flags = reinterpret_cast<int *>(staged + E::BUF);  // its second
     if (g == 0) {
-        P other;
-#pragma unroll
-        for (int a = 0; a < FM; ++a)
-#pragma unroll
-            for (int b = 0; b < FN; ++b)
-                other.w[a][b] = xchg[(a * FN + b) * NW * 64];
-        root = Arith::add(mine, other, sel);
+        if constexpr (KS == 2) {
+            root = Arith::add(mine, root_of(1), sel);
+        } else {
+            const P left = wpack(Arith::add(mine, root_of(1), sel));
+            const P right = wpack(Arith::add(root_of(2), root_of(3), sel));
+            root = Arith::add(left, right, sel);
+        }
         if constexpr (OUT == OUT_F32) {
             if constexpr (Arith::kTransposes) {
 #pragma unroll
@@ -1154,7 +1167,7 @@ __device__ __forceinline__ bool split_tile(const MfmaParams &p, int tile) {
         }
     }
     if constexpr (Arith::kTransposes) {
-        if (publish_nonfinite<2 * NW>(flags, nonfinite))
+        if (publish_nonfinite<KS * NW>(flags, nonfinite))
             return true;
     } else {
         __syncthreads();
@@ -1170,7 +1183,7 @@ __device__ __forceinline__ bool split_tile(const MfmaParams &p, int tile) {
 
 // The same tile with element-wise adds, for tiles whose matrix-core root was
 // not finite (kept out of line, as wide_valu_tile).
-template <bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU>
+template <bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU, int KS>
 __device__ __attribute__((noinline)) void split_valu_tile(MfmaParams q, int tile_arg) {
     MfmaParams p = q;
     p.x = uniform_ptr(q.x);
@@ -1186,15 +1199,15 @@ __device__ __attribute__((noinline)) void split_valu_tile(MfmaParams q, int tile
     p.tiles_j = __builtin_amdgcn_readfirstlane(q.tiles_j);
     p.levels = __builtin_amdgcn_readfirstlane(q.levels);
     p.cvec = __builtin_amdgcn_readfirstlane(q.cvec);
-    split_tile<WideValuAdd, YK, OUT, FM, FN, WM, WN, NBUF, GL, RU>(p, __builtin_amdgcn_readfirstlane(tile_arg));
+    split_tile<WideValuAdd, YK, OUT, FM, FN, WM, WN, NBUF, GL, RU, KS>(p, __builtin_amdgcn_readfirstlane(tile_arg));
 }
 
-// p.levels: the levels above the groups of one subtree.
-template <bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU, int OCC>
-__global__ __launch_bounds__(128 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+// p.levels: the levels above the groups of stages of one wave group's subtree.
+template <bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU, int KS, int OCC>
+__global__ __launch_bounds__(64 * KS * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void mfma_wide_split_kernel(MfmaParams p) {
-    if (split_tile<WideMatrixAdd, YK, OUT, FM, FN, WM, WN, NBUF, GL, RU>(p, blockIdx.x))
-        split_valu_tile<YK, OUT, FM, FN, WM, WN, NBUF, GL, RU>(p, blockIdx.x);
+    if (split_tile<WideMatrixAdd, YK, OUT, FM, FN, WM, WN, NBUF, GL, RU, KS>(p, blockIdx.x))
+        split_valu_tile<YK, OUT, FM, FN, WM, WN, NBUF, GL, RU, KS>(p, blockIdx.x);
 }
 
 // ---- grouped launch (MoE grouped GEMM): the row-major X is cut into

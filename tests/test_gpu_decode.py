@@ -182,7 +182,9 @@ def test_decode_zero_products_give_positive_zero(dev):
 
 
 ROW_LIMITS = ((10, 128), (12, 64), (11, 16))
-NARROW_WIDE_CFGS = (13, 14)   # 32-column wide tiles, the tree split at its root
+# 32-column wide tiles with the tree split over wave groups, and the least
+# leaf count each takes (a group of 8 stages of 2 leaves per wave group)
+NARROW_WIDE_CFGS = {13: 32, 14: 32, 15: 64}
 
 
 @pytest.mark.parametrize("M,K", [(1, 4096), (5, 1024), (16, 4128), (40, 4096), (128, 1024),
@@ -268,15 +270,16 @@ def test_row_blocks_match_general_kernel(dev, M, N, K):
                 with pytest.raises(dg.DetGemmError) as e:
                     _forced(cfg, f)
                 assert e.value.code == dg.EINVAL
-        # 32-column wide tiles: power-of-two leaf counts of at least 32 whose
-        # parked levels fit the LDS (the reduction runs over K, or over N for
-        # da); at K = 1024 and 4096 they all run
+        # 32-column wide tiles: power-of-two leaf counts from the least each
+        # takes, whose parked levels fit the LDS (the reduction runs over K, or
+        # over N for da); up to 128 leaves they all run
         R = N if op == "da" else K
         pow2 = R % 64 == 0 and (R // 32) & (R // 32 - 1) == 0
-        for cfg in NARROW_WIDE_CFGS:
+        for cfg, least in NARROW_WIDE_CFGS.items():
+            runs = pow2 and least <= R // 32 <= 128
             try:
                 got = _as_bits(_forced(cfg, f))
             except dg.DetGemmError as err:
-                assert err.code == dg.EINVAL and (not pow2 or R not in (1024, 4096)), (op, cfg)
+                assert err.code == dg.EINVAL and not runs, (op, cfg)
                 continue
             assert pow2 and np.array_equal(got, ref), (op, cfg)

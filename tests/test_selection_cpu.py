@@ -8,7 +8,7 @@ alignment and leaf count without touching memory.  Configurations: 5 to 9
 wide kernels (6: 128x64 tiles; 8: 128x128 two-leaf units; 9: three-leaf
 units), 10 to 12 decode kernels with 16, 64 and 32 columns per workgroup, 13
 and 14 the 128x32 and 64x32 wide tiles whose tree is split at its root over
-two wave groups.
+two wave groups, 15 the 64x32 tiles on four wave groups.
 """
 import pytest
 
@@ -108,22 +108,23 @@ def test_argument_errors():
     assert e.value.code == dg.EINVAL
 
 
-@pytest.mark.parametrize("M,N,want", [
-    (128, 6144, 13),   # QKV at 128 rows: 192 tiles of 128x32
-    (65, 6144, 13),
-    (64, 6144, 14),    # 192 tiles of 64x32
-    (48, 6144, 14),
-    (40, 6144, 14),
-    (32, 6144, 12),    # up to 32 rows: the decode kernel
-    (128, 2048, 14),   # 2 x 64 tiles of 64x32
-    (128, 4096, 14),   # 2 x 128 = 256 tiles: one round over the compute units
-    (64, 2048, 10),    # at most 128 column tiles: the decode kernel
-    (128, 14336, 6),   # 448 tiles of 128x32: the 128x64 wide kernel
+@pytest.mark.parametrize("M,N,want,want_t", [
+    (128, 6144, 13, 13),   # QKV at 128 rows: 192 tiles of 128x32 (384 of 64x32)
+    (65, 6144, 13, 13),
+    (64, 6144, 14, 15),    # 192 tiles of 64x32; a K-major weight on four wave groups
+    (48, 6144, 14, 15),
+    (40, 6144, 14, 15),
+    (32, 6144, 12, 12),    # up to 32 rows: the decode kernel
+    (128, 2048, 14, 15),   # 2 x 64 tiles of 64x32
+    (128, 4096, 14, 15),   # 2 x 128 = 256 tiles: one round over the compute units
+    (64, 2048, 10, 15),    # at most 128 column tiles: the decode kernel for W [K][N]
+    (48, 8192, 12, 15),    # 256 column tiles: the decode kernel for W [K][N]
+    (128, 14336, 6, 6),    # 448 tiles of 128x32: the 128x64 wide kernel
 ])
-def test_narrow_split_tiles(M, N, want):
+def test_narrow_split_tiles(M, N, want, want_t):
     assert cfg(dg.OP_FWD, M, N, 4096) == want
     assert cfg(dg.OP_FWD_FP32, M, N, 4096) == want
-    assert cfg(dg.OP_FWD_RHS_TRANSPOSED, M, N, 4096) == want
+    assert cfg(dg.OP_FWD_RHS_TRANSPOSED, M, N, 4096) == want_t
 
 
 def test_narrow_split_tiles_need_a_power_of_two_leaf_count():
