@@ -217,7 +217,11 @@ bool decode_ok(const Problem &pr) {
 // 23.3 on 64x32).  A K-major Y (whole 128-byte lines
 // per column and stage) takes 64x32 tiles on four wave groups instead, at
 // any column count that fits one round (M = 64, N = 6144: 14.1 us instead of
-// 16.3; M = 128, N = 2048: 12.9 instead of 15.8).  Otherwise the wide kernel
+// 16.3; M = 128, N = 2048: 12.9 instead of 15.8), and 65 to 128 rows of a
+// [K][N] weight with 129 to 256 column tiles take 64x64 tiles on four wave
+// groups, whose weight copies are whole lines (M = 128, N = 6144: 22.8 us
+// instead of 24.1 on 128x32; N = 8192: 23.0 instead of 25.8).  Otherwise the
+// wide kernel
 // (N = 28672: 54 us instead of 65 at M = 32, 54 instead of 83 at M = 64),
 // on 128x128 tiles above 128 column tiles (N = 18432, M = 64: 51 us, 55 on
 // 128x64).  Otherwise 128x128 wide tiles when they make at least four waves
@@ -241,6 +245,11 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
             if (t64 <= 256 && (pr.I > 64 || (t32 > 128 && t32 <= 192)) &&
                 wide_ok(pr, t, kTileCfgs[14], up))
                 return 14;
+            // 65 to 128 rows of a [K][N] weight with 129 to 256 column tiles:
+            // 64x64 tiles on four wave groups read whole 128-byte weight lines
+            if (pr.I > 64 && !pr.yk && t32 > 128 && t32 <= 256 &&
+                (pr.I + 63) / 64 * ((pr.J + 63) / 64) <= 256 && wide_ok(pr, t, kTileCfgs[16], up))
+                return 16;
             if (pr.I > 64 && t128 <= 256 && wide_ok(pr, t, kTileCfgs[13], up))
                 return 13;
         }

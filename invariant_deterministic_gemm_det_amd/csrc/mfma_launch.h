@@ -63,8 +63,9 @@ constexpr TileCfg kTileCfgs[] = {
     {4, 2, 2, 4, KIND_WIDE, 3, 4, 1, 1},    {4, 2, 2, 4, KIND_WIDE, 3, 2, 1, 3},
     {1, 1, 1, 1, KIND_DECODE, 0, 0, 0, 1},  {1, 4, 1, 1, KIND_DECODE, 0, 0, 0, 1},
     {1, 2, 1, 1, KIND_DECODE, 0, 0, 0, 1},  {2, 2, 4, 1, KIND_WIDE, 4, 3, 2, 1, 2},
-    {2, 1, 2, 2, KIND_WIDE, 6, 3, 2, 1, 2},  {2, 1, 2, 2, KIND_WIDE, 3, 3, 2, 1, 4}};
-constexpr int kNumTileCfgs = 16;
+    {2, 1, 2, 2, KIND_WIDE, 6, 3, 2, 1, 2},  {2, 1, 2, 2, KIND_WIDE, 3, 3, 2, 1, 4},
+    {2, 2, 2, 2, KIND_WIDE, 2, 3, 2, 1, 4}};
+constexpr int kNumTileCfgs = 17;
 
 struct TreeSel {
     int mode;  // TREE_BLOCK or TREE_STACK
@@ -248,13 +249,16 @@ hipError_t launch_layout(int cfg, const TreeSel &t, const MfmaParams &p, int64_t
     // split over wave groups (the stages per tile divided by their number):
     // 128x32 on 2 x 4 waves of 2 x 2 blocks with four stage buffers per group,
     // 64x32 on 2 x 4 waves of 2 x 1 blocks with six, and 64x32 on 4 x 4 waves
-    // (four waves per SIMD) with three.
+    // (four waves per SIMD) with three; 64x64 on 4 x 4 waves of 2 x 2 blocks
+    // with two.
     case 13:
         return launch_wide_split<XK, YK, OUT, 2, 2, 4, 1, 4, 3, 2, 2, 2>(p, tiles, st);
     case 14:
         return launch_wide_split<XK, YK, OUT, 2, 1, 2, 2, 6, 3, 2, 2, 2>(p, tiles, st);
     case 15:
         return launch_wide_split<XK, YK, OUT, 2, 1, 2, 2, 3, 3, 2, 4, 4>(p, tiles, st);
+    case 16:
+        return launch_wide_split<XK, YK, OUT, 2, 2, 2, 2, 2, 3, 2, 4, 4>(p, tiles, st);
     default:
         return hipErrorInvalidValue;
     }

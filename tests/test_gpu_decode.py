@@ -182,9 +182,9 @@ def test_decode_zero_products_give_positive_zero(dev):
 
 
 ROW_LIMITS = ((10, 128), (12, 64), (11, 16))
-# 32-column wide tiles with the tree split over wave groups, and the least
+# 32- and 64-column wide tiles with the tree split over wave groups, and the least
 # leaf count each takes (a group of 8 stages of 2 leaves per wave group)
-NARROW_WIDE_CFGS = {13: 32, 14: 32, 15: 64}
+NARROW_WIDE_CFGS = {13: 32, 14: 32, 15: 64, 16: 64}
 
 
 @pytest.mark.parametrize("M,K", [(1, 4096), (5, 1024), (16, 4128), (40, 4096), (128, 1024),

@@ -383,14 +383,14 @@ def test_mfma_tile_configs_identical(dev, K):
 
 # Tile configurations 3 and 4 are the direct-to-LDS kernels (whole 64-index
 # stages, 16-byte aligned rows, 8-row chunks of operands whose row index is
-# contiguous), 5 to 9 and 13 to 15 the wide kernels (the same, and leaf counts
-# 2^a or 3 * 2^a; 13 to 15 are the 32-column tiles that split the tree over two
-# or four wave groups, X K-major only); 2 is the general kernel they must
+# contiguous), 5 to 9 and 13 to 16 the wide kernels (the same, and leaf counts
+# 2^a or 3 * 2^a; 13 to 16 are the 32- and 64-column tiles that split the tree
+# over two or four wave groups, X K-major only); 2 is the general kernel they must
 # reproduce bit for bit.
 FAST_SHAPES = [(200, 192, 256), (256, 136, 768), (320, 256, 4096), (128, 64, 12288),
                (72, 64, 32768), (512, 512, 1024), (264, 392, 8192), (768, 384, 1536),
                (384, 768, 6144)]
-GENERAL_CFG, FAST_CFGS = 2, (3, 4, 5, 6, 7, 8, 9, 13, 14, 15)
+GENERAL_CFG, FAST_CFGS = 2, (3, 4, 5, 6, 7, 8, 9, 13, 14, 15, 16)
 
 
 def _six_forced(cfg, A, B, dC):
@@ -527,7 +527,7 @@ def test_wide_kernel_nonfinite_inputs(dev, K):
     Ad, Bd, dCd = A.to(dev), B.to(dev), dC.to(dev)
     ref = _six_forced(GENERAL_CFG, Ad, Bd, dCd)
     ran = 0
-    for cfg in (5, 6, 7, 8, 9, 13, 14, 15):
+    for cfg in (5, 6, 7, 8, 9, 13, 14, 15, 16):
         got = _six_forced(cfg, Ad, Bd, dCd)
         for op, g in got.items():
             if g is None:

@@ -8,7 +8,7 @@ alignment and leaf count without touching memory.  Configurations: 5 to 9
 wide kernels (6: 128x64 tiles; 8: 128x128 two-leaf units; 9: three-leaf
 units), 10 to 12 decode kernels with 16, 64 and 32 columns per workgroup, 13
 and 14 the 128x32 and 64x32 wide tiles whose tree is split at its root over
-two wave groups, 15 the 64x32 tiles on four wave groups.
+two wave groups, 15 and 16 the 64x32 and 64x64 tiles on four wave groups.
 """
 import pytest
 
@@ -109,8 +109,11 @@ def test_argument_errors():
 
 
 @pytest.mark.parametrize("M,N,want,want_t", [
-    (128, 6144, 13, 13),   # QKV at 128 rows: 192 tiles of 128x32 (384 of 64x32)
-    (65, 6144, 13, 13),
+    (128, 6144, 16, 13),   # QKV at 128 rows: 192 tiles of 64x64 (W [K][N]) or 128x32
+    (65, 6144, 16, 13),
+    (128, 8192, 16, 13),
+    (96, 8192, 16, 13),
+    (128, 10240, 6, 6),    # 320 column tiles of 32: more than one round; 128x64 wide
     (64, 6144, 14, 15),    # 192 tiles of 64x32; a K-major weight on four wave groups
     (48, 6144, 14, 15),
     (40, 6144, 14, 15),
