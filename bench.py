@@ -542,8 +542,8 @@ def small_m_leg(dev, steps, warmup, decode_only=False):
                      "GB/s": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
                      "kernel": kernel, "config": cfg})
     return {"workload": "forward products with 1..256 rows: the weight read once per call "
-                        "(the decode kernel, 32-column wide tiles whose tree is split over two "
-                        "wave groups from 33 to 128 rows, the wide kernel when wide in N)",
+                        "(the decode kernel; from 33 to 128 rows, narrow wide tiles whose tree is "
+                        "split over two or four wave groups; the wide kernel when wide in N)",
             "timing": "us: per call, calls replayed from a captured graph; us_eager_calls: "
                       "back-to-back calls through the binding (host launch path included)",
             "roofline": "hbm, 8000 GB/s", "rows": rows}

@@ -159,9 +159,9 @@ bool fast_ok(const Problem &pr, const TreeSel &t) {
 // The wide kernel: the fast kernel's operand conditions and a leaf count
 // L = 2 * tb * 2^k with at least one group of 2^gl nodes of 2 * tb leaves
 // (with exactly one group, the group root is the root); a tree split at its
-// root over two wave groups needs units of one leaf, a K-major X, a
-// row-major output and a group of stages in each half.  `up` receives the
-// levels above the groups (of one half for a split tree).
+// root over two or four wave groups needs units of one leaf, a K-major X, a
+// row-major output and a group of stages in each part.  `up` receives the
+// levels above the groups (of one part for a split tree).
 bool wide_ok(const Problem &pr, const TreeSel &t, const TileCfg &c, int &up) {
     const int64_t L = (pr.R + 31) / 32;
     const bool split = c.ks > 1;
@@ -234,7 +234,7 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     int up = 0;
     if (decode_ok(pr)) {
         const int64_t t32 = (pr.J + 31) / 32, blocks = (pr.I + 15) / 16;
-        // 33 to 128 rows: the 32-column wide tiles that split the tree over
+        // 33 to 128 rows: the narrow wide tiles that split the tree over
         // wave groups, while their tiles make at most one round over the
         // compute units (and, up to 64 rows of a [K][N] weight, while the
         // decode kernel has 129 to 192 column tiles)

@@ -270,7 +270,7 @@ def test_row_blocks_match_general_kernel(dev, M, N, K):
                 with pytest.raises(dg.DetGemmError) as e:
                     _forced(cfg, f)
                 assert e.value.code == dg.EINVAL
-        # 32-column wide tiles: power-of-two leaf counts from the least each
+        # narrow split wide tiles: power-of-two leaf counts from the least each
         # takes, whose parked levels fit the LDS (the reduction runs over K, or
         # over N for da); up to 128 leaves they all run
         R = N if op == "da" else K
