@@ -645,8 +645,19 @@ struct WideEngine {
         return wpack(l);
     }
 
+    // This lane's first slot of parked level `slot`.  The level's offset is
+    // made opaque, so that the address is formed where it is used: past the
+    // 16-bit offset field (two levels) the compiler would otherwise keep one
+    // address register per fragment and level alive through the whole loop,
+    // for branches that run once or twice per tile.
+    __device__ __forceinline__ char *park_slot(int slot) const {
+        int off = slot * PARK_LEVEL;
+        asm volatile("" : "+s"(off));
+        return park_lane + off;
+    }
+
     __device__ __forceinline__ void park(int slot, const P &v) {
-        char *base = park_lane + slot * PARK_LEVEL;
+        char *base = park_slot(slot);
 #pragma unroll
         for (int a = 0; a < FM; ++a)
 #pragma unroll
@@ -655,7 +666,7 @@ struct WideEngine {
     }
 
     __device__ __forceinline__ P unpark(int slot) const {
-        const char *base = park_lane + slot * PARK_LEVEL;
+        const char *base = park_slot(slot);
         P v;
 #pragma unroll
         for (int a = 0; a < FM; ++a)
@@ -911,36 +922,32 @@ struct WideTree {
     // matrix-core adds the single leaves a0 and b1 are computed with swapped
     // operands, so they are laid out like the two-leaf nodes they meet.
     struct Carry {
-        P a0, a1, b0, b1, u0, c0, c1;
+        P a0, a1, b0, b1, u0, c0, c1, u1;
     };
 
-    // Tree work that finishes super-stage U of group t: the second unit and
-    // the six-leaf node.
-    template <int U>
-    __device__ __forceinline__ void step3(const Carry &c, int t) {
-        const P u1 = wpack(add(c.b1, wpack(add(c.c0, c.c1))));
-        climb_low<U, 0>(wpack(add(c.u0, u1)), t);
-    }
-
-    // Super-stage U of group t: stages A, B, C.
-    //   A: finish super-stage U - 1 (group t - 1's last one for U = 0, with the
-    //      zero-leaf convention of the one-leaf schedule), then leaves a0, a1;
-    //   B: leaves b0, b1;
-    //   C: the first unit, then leaves c0, c1.
+    // Super-stage U of group t: stages A, B, C.  The tree work of super-stage
+    // U - 1 (group t - 1's last one for U = 0, with the zero-leaf convention
+    // of the one-leaf schedule) is spread over the stages so that each has
+    // adds to cover the latency of its first fragment reads:
+    //   A: the second unit u1 = b1 (+) (c0 (+) c1), then leaves a0, a1;
+    //   B: the six-leaf node u0 (+) u1 climbs, then leaves b0, b1;
+    //   C: the first unit u0 = a0 (+) (a1 (+) b0), then leaves c0, c1.
     template <int U>
     __device__ __forceinline__ void stage3(int t, Carry &c) {
         const int s = 3 * (t * G + U);
         e.template begin<U & 1>(s);
-        if constexpr (U == 0)
-            step3<G - 1>(c, t > 0 ? t - 1 : 0);
-        else
-            step3<U - 1>(c, t);
+        c.u1 = wpack(add(c.b1, wpack(add(c.c0, c.c1))));
         e.template read<1>();
         c.a0 = e.template leaf<0, Arith::kTransposes>();
         c.a1 = e.template leaf<1, false>();
+        pin_p(c.u1);
         pin_p(c.a0);
         pin_p(c.a1);
         e.template begin<(U + 1) & 1>(s + 1);
+        if constexpr (U == 0)
+            climb_low<G - 1, 0>(wpack(add(c.u0, c.u1)), t > 0 ? t - 1 : 0);
+        else
+            climb_low<U - 1, 0>(wpack(add(c.u0, c.u1)), t);
         e.template read<1>();
         c.b0 = e.template leaf<0, false>();
         c.b1 = e.template leaf<1, Arith::kTransposes>();
@@ -967,7 +974,7 @@ struct WideTree {
 #pragma unroll
             for (int b = 0; b < E::kFN; ++b) {
                 c.a0.w[a][b] = c.a1.w[a][b] = c.b0.w[a][b] = c.b1.w[a][b] = u32x2{0u, 0u};
-                c.u0.w[a][b] = c.c0.w[a][b] = c.c1.w[a][b] = u32x2{0u, 0u};
+                c.u0.w[a][b] = c.c0.w[a][b] = c.c1.w[a][b] = c.u1.w[a][b] = u32x2{0u, 0u};
             }
         for (int t = 0; t < T; ++t)
             stage3<0>(t, c);
