@@ -1,4 +1,4 @@
-// Decode-shaped forward products: at most 64 rows of X (one token, or a small
+// Decode-shaped forward products: at most 128 rows of X (one token, or a small
 // batch of them, against a weight matrix).  Same leaves, same tree, same bits
 // as every other det_gemm kernel; only the work split differs.
 //
@@ -9,23 +9,27 @@
 // to keep 256 compute units streaming the weights if each block walks the
 // whole reduction alone.  Here the tree itself supplies the parallelism inside
 // a workgroup:
-//   * a workgroup owns an M x 16 CB output tile: all M rows (staged as 1, 2 or
-//     4 blocks of 16 rows, M <= 16, 32 or 64; 64-column tiles take at most 16
-//     rows) and 16, 32 or 64 columns, one MFMA per row block and column block
-//     with its own tree state.  It has W = 8 or 16 waves; wave w evaluates the
-//     subtree rooted
-//     at node w of depth log2(W) of the mid-split tree over the L leaves
-//     (L >= W, so every such node holds at least one leaf), a contiguous range
-//     of about L / W leaves;
+//   * a workgroup owns an M x 16 CB output tile: all M rows (staged as 1, 2, 4
+//     or 8 blocks of 16 rows: M <= 16, 32, 64 or 128; 32-column tiles take at
+//     most 64 rows, 64-column tiles at most 16) and 16, 32 or 64 columns, one
+//     MFMA per row block and column block with its own tree state.  It has
+//     W = 4, 8 or 16 waves; wave w evaluates the subtree rooted at node w of
+//     depth log2(W) of the mid-split tree over the L leaves (L >= W, so every
+//     such node holds at least one leaf), a contiguous range of about L / W
+//     leaves;
 //   * a wave walks its leaves in ascending order with the streaming post-order
 //     (after leaf t, as many adds as there are inner nodes whose range ends at
 //     t + 1), pending left siblings in registers;
-//   * the W subtree roots meet in LDS and the first waves (one per 16-column
+//   * the W subtree roots meet in LDS and the first waves (one per 16 x 16
 //     block) add them in the order of the top log2(W) levels.
 // A leaf is the same v_mfma_f32_16x16x32_bf16 with the same lane assignment as
 // in the other kernels (lane l: X row l % 16 and Y column l % 16 at reduction
-// indices 8(l / 16) .. +7); a tree add is the same round-both-then-add-in-fp32
-// VALU add.  So the bits are those of every other configuration.
+// indices 8(l / 16) .. +7).  Inside a wave's subtree a tree add is the
+// selector MFMA of the wide kernel (a leaf at odd depth is computed with
+// swapped operands, so both children of every add share a layout); the top
+// levels use the element-wise VALU add; a tile whose root is not finite is
+// recomputed with element-wise adds throughout.  Both adds give the exactly
+// rounded bf16 sum, so the bits are those of every other configuration.
 //
 // Data movement, per wave and without workgroup barriers: a private ring of
 // NB unit slots in LDS (a unit: one leaf, or two leaves of a K-major Y),
@@ -43,9 +47,9 @@
 //     direct-to-LDS kernel.  Each way the two 16-lane groups of a half-wave
 //     ds_read_b64_tr_b16 (indices r0 .. r0+3 and r0+8 .. r0+11) use disjoint
 //     banks.
-//   * X: the MP rows the product needs (MP = 1 for a single row, else 16, 32
-//     or 64, rows past the last clamped to it) in the K-major layout of the
-//     unit.
+//   * X: the MP rows the product needs (MP = 1 for a single row, else 16, 32,
+//     64 or 128, rows past the last clamped to it) in the K-major layout of
+//     the unit.
 // A compute unit serves these copies at a bounded rate of cache-line requests,
 // so wider tiles (more of each requested line used) stream faster and narrower
 // ones reach more compute units; the host picks the width from the tile count.
@@ -58,8 +62,9 @@ namespace detgemm {
 namespace {
 
 // CB column blocks of 16 per workgroup (a tile of 16 * CB columns), MP staged
-// rows of X (1, 16, 32 or 64: MR = 1, 2 or 4 blocks of 16), UL leaves per copy unit (2: a K-major Y read as whole 128-byte
-// lines, two leaves of each column), W waves (one subtree each: depth 3 or 4).
+// rows of X (1, 16, 32, 64 or 128: MR = 1, 2, 4 or 8 blocks of 16), UL leaves
+// per copy unit (2: a K-major Y read as whole 128-byte lines, two leaves of
+// each column), W waves (one subtree each: depth 2, 3 or 4).
 template <int MP, int CB, int UL, int W>
 struct DecodeShape {
     static constexpr int MR = MP >= 16 ? MP / 16 : 1;
