@@ -306,3 +306,16 @@ def test_attention_prefill_argument_errors_without_device(lib):
     assert f(FAKE, A, A, off(0, 3, 5), FAKE, 5, 2, 8, 2, 64, 64, s, w, o, NULL) == dg.EINVAL   # D != 128
     assert f(FAKE, A, A, None, FAKE, 5, 2, 8, 2, 64, 128, s, w, o, NULL) == dg.EINVAL          # no offsets
     assert f(FAKE, A, A, off(0, 0), FAKE, 0, 1, 8, 2, 64, 128, s, w, o, NULL) == dg.OK         # no rows
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus N > 1 exits with status 2 and says so
+    before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
