@@ -13,7 +13,7 @@
 //     or 8 blocks of 16 rows: M <= 16, 32, 64 or 128; 32-column tiles take at
 //     most 64 rows, 64-column tiles at most 16) and 16, 32 or 64 columns, one
 //     MFMA per row block and column block with its own tree state.  It has
-//     W = 4, 8 or 16 waves; wave w evaluates the subtree rooted at node w of
+//     W = 8 or 16 waves; wave w evaluates the subtree rooted at node w of
 //     depth log2(W) of the mid-split tree over the L leaves (L >= W, so every
 //     such node holds at least one leaf), a contiguous range of about L / W
 //     leaves;
@@ -64,7 +64,7 @@ namespace {
 // CB column blocks of 16 per workgroup (a tile of 16 * CB columns), MP staged
 // rows of X (1, 16, 32, 64 or 128: MR = 1, 2, 4 or 8 blocks of 16), UL leaves
 // per copy unit (2: a K-major Y read as whole 128-byte lines, two leaves of
-// each column), W waves (one subtree each: depth 2, 3 or 4).
+// each column), W waves (one subtree each: depth 3 or 4).
 template <int MP, int CB, int UL, int W>
 struct DecodeShape {
     static constexpr int MR = MP >= 16 ? MP / 16 : 1;
@@ -75,11 +75,8 @@ struct DecodeShape {
     // two workgroups per compute unit do: 4 slots for 16- and 32-column
     // tiles, 2 for 64-column ones and for the larger two-leaf units; with 16
     // waves, as many as the LDS holds (at least 2).
-    // With 4 waves (one per SIMD) each ring takes a quarter of the LDS: as
-    // many slots as fit, at most 8.
     static constexpr int NB0 = UL == 2 ? ((CB == 1 && MP == 1) ? 4 : 2) : (CB == 4 ? 2 : 4);
-    static constexpr int NB4 = (160 * 1024) / (4 * SLOT) < 8 ? (160 * 1024) / (4 * SLOT) : 8;
-    static constexpr int NB = W == 4 ? NB4 : (NB0 > 2 && W * NB0 * SLOT > 160 * 1024) ? NB0 / 2 : NB0;
+    static constexpr int NB = (NB0 > 2 && W * NB0 * SLOT > 160 * 1024) ? NB0 / 2 : NB0;
     static constexpr int AHEAD = NB - 1;                  // units in flight per wave
     static constexpr int OPS = UL == 2 ? 2 * CB + (MP == 1 ? 1 : 2 * MR) : CB + MR;  // copies per unit
     static constexpr int WAVE_BYTES = NB * SLOT;
@@ -194,7 +191,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(DecodeSh
                                                                        DecodeShape<MP, CB, UL, W>::OCC)))
 void mfma_decode_kernel(MfmaParams p) {
     static_assert(UL == 1 || YK, "two-leaf units only for a K-major Y");
-    static_assert(W == 4 || W == 8 || W == 16, "subtrees of depth 2, 3 or 4");
+    static_assert(W == 8 || W == 16, "subtrees of depth 3 or 4");
     typedef DecodeShape<MP, CB, UL, W> S;
     static_assert(S::kFits, "the rings fit the LDS");
     constexpr int MR = S::MR;
