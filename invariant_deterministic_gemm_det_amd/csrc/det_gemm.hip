@@ -102,6 +102,21 @@ int check_device() {
     return state == 1 ? DET_GEMM_OK : DET_GEMM_EHIP;
 }
 
+// Compute units of the current device (read once per device); 0 if unknown.
+std::atomic<int> g_device_cus[64];
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 0;
+    int n = g_device_cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0)
+            n = 0;
+        g_device_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 }  // namespace detgemm
 
 namespace {
@@ -1067,6 +1082,25 @@ int moe_entry(const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw, in
             }
             g.tile_start[E] = (int32_t)tiles;
             g.y_stride = w_stride;
+            // Tail balancing: one workgroup of these tiles fills a compute
+            // unit, so when the last round would keep at most half of the
+            // units busy, its tiles run as two half-height tiles each (the
+            // tree split over two wave groups, half the stages each): every
+            // unit then ends after about the same share of the work.  Bits do
+            // not depend on the tile shape.
+            g.split_from = (int32_t)tiles;
+            g.split_levels = 0;
+            if (kTileCfgs[cfg].tb == 1) {
+                const int64_t cus = device_cus();
+                const int64_t r = cus > 0 ? tiles % cus : 0;
+                const TileCfg h{4, 2, 1, 4, KIND_WIDE, 3, kTileCfgs[cfg].gl, kTileCfgs[cfg].ru, 1, 2};
+                int uph = 0;
+                if (tiles > cus && r > 0 && 2 * r <= cus && wide_ok(base, tree, h, uph) &&
+                    h.lds_bytes(uph) + kEpiLds <= kLdsMax) {
+                    g.split_from = (int32_t)(tiles - r);
+                    g.split_levels = uph;
+                }
+            }
             MfmaParams p;
             std::memset(&p, 0, sizeof p);
             p.x = X;

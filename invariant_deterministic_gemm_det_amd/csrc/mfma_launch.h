@@ -189,10 +189,20 @@ hipError_t launch_wide_grouped(const MfmaParams &p, const GroupTable &g, int64_t
             return e;
         max_dynamic = room;
     }
-    const int lds = kEpiLds + E::lds_bytes(p.levels > RU ? p.levels - RU : 0);
+    int lds = kEpiLds + E::lds_bytes(p.levels > RU ? p.levels - RU : 0);
+    int64_t blocks = tiles;
+    if (g.split_from < tiles) {
+        // half-height tail tiles: two wave groups of four 64 x 32 waves
+        typedef WideEngine<true, false, OUT_BF16, 4, 2, 1, 4, 3> H;
+        if (TB != 1 || g.split_from < 0)
+            return hipErrorInvalidValue;
+        const int half = kEpiLds + 2 * H::lds_bytes(g.split_levels > RU ? g.split_levels - RU : 0);
+        lds = half > lds ? half : lds;
+        blocks = tiles + (tiles - g.split_from);
+    }
     if (lds > max_dynamic)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)tiles), dim3(64 * WM * WN), lds, st, p, g);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(64 * WM * WN), lds, st, p, g);
     return hipGetLastError();
 }
 

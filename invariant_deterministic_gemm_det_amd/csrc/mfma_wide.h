@@ -139,6 +139,12 @@ struct GroupTable {
     int64_t ldg;
     float *slots;
     int64_t slot_ld;
+    // Tail balancing: tiles split_from .. tile_start[groups]-1 each run as two
+    // half-height tiles (workgroups split_from + 2 (t - split_from) and the
+    // next), whose trees are split at the root over two wave groups
+    // (split_levels: the levels above the groups of stages of one wave group).
+    int32_t split_from;
+    int32_t split_levels;
 };
 
 // What the epilogue of a grouped tile needs, written by the workgroup at the
@@ -1086,23 +1092,24 @@ void mfma_wide_kernel(MfmaParams p) {
 // (0 + 1) + (2 + 3) for KS = 4), then rounds and stores the tile.  All groups
 // run the same number of stages, so every workgroup barrier is reached by all
 // waves.  With matrix-core adds, a tile with a non-finite root returns true
-// (not stored).
+// (not stored).  The tile's origin is (i0, j0); `lds` is the start of the
+// groups' LDS.  EPI (grouped launches, bf16 out): group 0 also writes the
+// per-token slots of the tile (store_staged), group 1 meets its barrier.
 template <class Arith, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU,
-          int KS>
-__device__ __forceinline__ bool split_tile(const MfmaParams &p, int tile) {
+          int KS, bool EPI = false>
+__device__ __forceinline__ bool split_tile_at(const MfmaParams &p, int i0, int j0, char *lds) {
     typedef WideEngine<true, YK, OUT, FM, FN, WM, WN, NBUF> E;
     typedef typename E::P P;
     typedef typename E::F F;
     constexpr int NW = E::NW;
     static_assert(KS == 2 || KS == 4, "two or four wave groups");
     static_assert(OUT == OUT_BF16 || OUT == OUT_F32, "row-major output");
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    static_assert(!EPI || (OUT == OUT_BF16 && KS == 2), "slots: bf16 tiles on two wave groups");
+    char *const smem = lds;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = wave / NW, lw = wave % NW;
     const int wm = lw % WM, wn = lw / WM;
-    const int i0 = (tile / p.tiles_j) * E::BM;
-    const int j0 = (tile % p.tiles_j) * E::BN;
     const int parked = p.levels > RU ? p.levels - RU : 0;
     const int group_bytes = E::lds_bytes(parked);
 
@@ -1150,6 +1157,22 @@ __device__ __forceinline__ bool split_tile(const MfmaParams &p, int tile) {
     bool nonfinite = false;
     char *staged = smem + parked * E::PARK_LEVEL;           // group 0's first stage buffer
     int *flags = reinterpret_cast<int *>(staged + E::BUF);  // its second
+    if constexpr (EPI) {
+        // staging, slots and store by group 0 (store_staged over its NW
+        // waves); group 1 takes part in the one barrier, whose flags are
+        // group 0's
+        if (g == 0) {
+            const F r = Arith::add(mine, root_of(1), sel);
+            return store_staged<OUT, FM, FN, E::BM, E::BN, NW, true, true, Arith::kTransposes>(
+                p, r, odd, i0, j0, wm, wn, lane, staged, flags);
+        }
+        if constexpr (Arith::kTransposes) {
+            return publish_nonfinite<NW>(flags, false);
+        } else {
+            __syncthreads();
+            return false;
+        }
+    }
     if (g == 0) {
         if constexpr (KS == 2) {
             root = Arith::add(mine, root_of(1), sel);
@@ -1188,6 +1211,15 @@ __device__ __forceinline__ bool split_tile(const MfmaParams &p, int tile) {
     return false;
 }
 
+template <class Arith, bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU,
+          int KS>
+__device__ __forceinline__ bool split_tile(const MfmaParams &p, int tile) {
+    typedef WideEngine<true, YK, OUT, FM, FN, WM, WN, NBUF> E;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    return split_tile_at<Arith, YK, OUT, FM, FN, WM, WN, NBUF, GL, RU, KS>(
+        p, (tile / p.tiles_j) * E::BM, (tile % p.tiles_j) * E::BN, smem);
+}
+
 // The same tile with element-wise adds, for tiles whose matrix-core root was
 // not finite (kept out of line, as wide_valu_tile).
 template <bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU, int KS>
@@ -1222,10 +1254,52 @@ void mfma_wide_split_kernel(MfmaParams p) {
 // y + e * y_stride; one launch covers the tiles of every group, group e owning
 // tiles tile_start[e] .. tile_start[e+1]-1.  The same tile code runs on the
 // group's rows, so each row gets the bits of an ungrouped product.
+//
+// Half-height tiles (tail balancing, tiles of 128 x 128 in units of one leaf):
+// 64 x 128, four 64 x 32 waves per wave group, two wave groups splitting the
+// tree at its root, each over half the stages, so a half takes about half a
+// tile's time.  A half holds whole 128-column slot rows, so group 0 writes the
+// slots as a whole tile does.
+template <int GL, int RU>
+__device__ __attribute__((noinline)) void grouped_half_valu(MfmaParams q, int i0, int j0) {
+    extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
+    MfmaParams p = q;
+    p.x = uniform_ptr(q.x);
+    p.y = uniform_ptr(q.y);
+    p.c = uniform_ptr(q.c);
+    p.ldx = uniform64(q.ldx);
+    p.ldy = uniform64(q.ldy);
+    p.ldc = uniform64(q.ldc);
+    p.I = __builtin_amdgcn_readfirstlane(q.I);
+    p.J = __builtin_amdgcn_readfirstlane(q.J);
+    p.R = __builtin_amdgcn_readfirstlane(q.R);
+    p.L = __builtin_amdgcn_readfirstlane(q.L);
+    p.tiles_j = __builtin_amdgcn_readfirstlane(q.tiles_j);
+    p.levels = __builtin_amdgcn_readfirstlane(q.levels);
+    p.cvec = __builtin_amdgcn_readfirstlane(q.cvec);
+    split_tile_at<WideValuAdd, false, OUT_BF16, 4, 2, 1, 4, 3, GL, RU, 2, true>(
+        p, __builtin_amdgcn_readfirstlane(i0), __builtin_amdgcn_readfirstlane(j0), dyn_lds + kEpiLds);
+}
+
+template <int GL, int RU>
+__device__ __forceinline__ void grouped_half_tile(MfmaParams q, int idx, int h, int levels) {
+    extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
+    const int i0 = (idx / q.tiles_j) * 128 + h * 64;
+    const int j0 = (idx % q.tiles_j) * 128;
+    if (i0 >= q.I)
+        return;  // the lower half of a group's last row tile may hold no rows
+    q.levels = levels;
+    if (split_tile_at<WideMatrixAdd, false, OUT_BF16, 4, 2, 1, 4, 3, GL, RU, 2, true>(
+            q, i0, j0, dyn_lds + kEpiLds))
+        grouped_half_valu<GL, RU>(q, i0, j0);
+}
+
 template <int FM, int FN, int WM, int WN, int NBUF, int TB, int GL, int RU, int OCC>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void mfma_wide_grouped_kernel(MfmaParams p, GroupTable g) {
-    const int t = blockIdx.x;
+    const int b = blockIdx.x;
+    const bool half = b >= g.split_from;
+    const int t = half ? g.split_from + ((b - g.split_from) >> 1) : b;
     int lo = 0, hi = g.groups;  // the last group whose first tile is <= t
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -1248,6 +1322,13 @@ void mfma_wide_grouped_kernel(MfmaParams p, GroupTable g) {
         info->ldg = g.ldg;
         info->slot_ld = g.slot_ld;
         info->r0 = r0;
+    }
+    if constexpr (TB == 1) {
+        static_assert(FM * WM == 8 && FN * WN == 8 && WM * WN == 8, "halves of 128 x 128 tiles");
+        if (half) {
+            grouped_half_tile<GL, RU>(q, t - g.tile_start[lo], (b - g.split_from) & 1, g.split_levels);
+            return;
+        }
     }
     wide_tile<true, false, OUT_BF16, FM, FN, WM, WN, NBUF, TB, GL, RU, true>(q, t - g.tile_start[lo]);
 }

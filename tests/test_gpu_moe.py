@@ -199,7 +199,8 @@ def test_nonfinite_rows(dev):
 def test_moe_full_size_workload(dev):
     """The benchmark's workload: 4096 tokens, top-2 of 8 experts (8192 rows),
     K = 2048, N = 4096.  Two runs agree bitwise; sampled rows against the
-    oracle; one expert against det_gemm_fwd."""
+    oracle; two experts against det_gemm_fwd (the last one's final row tiles
+    run as half-height tail tiles)."""
     inp = Wk.moe_inputs(dev)
     say("MoE full size: rows", inp.offsets[-1], "segments", np.diff(inp.offsets).tolist())
     Y, dprob, slots = dg.det_moe_fwd_dprob(inp.x, inp.w, inp.offsets, inp.g)
@@ -207,10 +208,12 @@ def test_moe_full_size_workload(dev):
     assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16))
     assert torch.equal(dprob.view(torch.int32), d2.view(torch.int32))
     assert torch.equal(slots.view(torch.int32), s2.view(torch.int32))
-    e = 3
-    r = slice(inp.offsets[e], inp.offsets[e + 1])
-    assert torch.equal(dg.det_gemm_fwd(inp.x[r], inp.w[e]).view(torch.int16),
-                       Y[r].view(torch.int16))
+    # expert 3, and expert 7, whose last row tiles run as half-height tiles
+    # (2176 tiles: the 128 past the eighth round of 256 are split)
+    for e in (3, 7):
+        r = slice(inp.offsets[e], inp.offsets[e + 1])
+        assert torch.equal(dg.det_gemm_fwd(inp.x[r], inp.w[e]).view(torch.int16),
+                           Y[r].view(torch.int16))
     # sampled rows: Y within tolerance of the oracle, epilogue exact
     off = inp.offsets
     rows = [0, off[1] - 1, off[4] + 5, off[-1] - 1]
@@ -223,3 +226,36 @@ def test_moe_full_size_workload(dev):
     assert np.array_equal(_fbits(slots[:, rows]), _np_fbits(s_or))
     # the whole epilogue on the device's Y
     _check_epilogue(Y, inp.g, slots, dprob)
+
+
+def test_tail_tiles_split_in_half(dev):
+    """11 row tiles x 32 column tiles = 352 tiles on 256 compute units: the 96
+    past the last full round run as half-height tiles whose tree is split over
+    two wave groups (an expert of 60 rows: its lower half holds no rows; one of
+    100: a ragged half).  Y equals det_gemm_fwd per expert bitwise, the
+    epilogue equals the oracle's on the device's Y, and both equal the
+    per-expert products with the slot kernel; a non-finite input inside a half
+    tile takes the element-wise recomputation."""
+    say("MoE tail tiles split in half")
+    X, W, G, off = _case([300, 200, 500, 100, 60], 2048, 4096, 7500, dev)
+    Y, dprob, slots = dg.det_moe_fwd_dprob(X, W, off, G)
+    assert torch.equal(Y.view(torch.int16), _per_expert_fwd(X, W, off).view(torch.int16))
+    _check_epilogue(Y, G, slots, dprob)
+    dg.det_gemm_debug_force_config(3)
+    try:
+        Y3, d3, s3 = dg.det_moe_fwd_dprob(X, W, off, G)
+    finally:
+        dg.det_gemm_debug_force_config(-1)
+    assert torch.equal(Y3.view(torch.int16), Y.view(torch.int16))
+    assert torch.equal(s3.view(torch.int32), slots.view(torch.int32))
+    assert torch.equal(d3.view(torch.int32), dprob.view(torch.int32))
+    # a non-finite input in the lower half of expert 3's only row tile
+    X[off[3] + 70, 11] = float("inf")
+    Yn, dn, sn = dg.det_moe_fwd_dprob(X, W, off, G)
+    assert torch.equal(Yn.view(torch.int16), _per_expert_fwd(X, W, off).view(torch.int16))
+    s_or, d_or = oracle.moe_dprob(bits(Yn), bits(G))
+    got = sn.cpu().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(s_or))
+    ok = ~np.isnan(s_or)
+    assert np.array_equal(_fbits(sn)[ok], _np_fbits(s_or)[ok])
+    assert np.isnan(s_or).any()
