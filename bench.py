@@ -502,7 +502,8 @@ def small_m_leg(dev, steps, warmup, decode_only=False):
     Xq = Wk.randn_bf16((128, Wk.QKV_K), 1.0, 9700, dev)
     cases = [("qkv", "W[K][N]", 1), ("qkv", "W[K][N]", 16), ("qkv", "W[K][N]", 32),
              ("qkv", "W[K][N]", 64), ("qkv", "W[K][N]", 128),
-             ("qkv", "W[N][K]", 1), ("qkv", "W[N][K]", 16), ("qkv", "W[N][K]", 64),
+             ("qkv", "W[N][K]", 1), ("qkv", "W[N][K]", 16), ("qkv", "W[N][K]", 32),
+             ("qkv", "W[N][K]", 64),
              ("qkv", "W[N][K]", 128), ("lm_head", "W[K][N]", 1),
              ("lm_head", "W[K][N]", 32), ("lm_head", "W[K][N]", 256)]
     if decode_only:  # the rows on the decode kernel and the split 32-column tiles, one

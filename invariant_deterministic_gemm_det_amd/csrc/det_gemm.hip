@@ -232,7 +232,10 @@ bool decode_ok(const Problem &pr) {
 // 23.3 on 64x32).  A K-major Y (whole 128-byte lines
 // per column and stage) takes 64x32 tiles on four wave groups instead, at
 // any column count that fits one round (M = 64, N = 6144: 14.1 us instead of
-// 16.3; M = 128, N = 2048: 12.9 instead of 15.8), and 65 to 128 rows of a
+// 16.3; M = 128, N = 2048: 12.9 instead of 15.8), as do 17 to 32 rows of it
+// with 129 to 256 column tiles (M = 32, N = 6144: 13.6 us instead of 15.0 on
+// the decode kernel; at most 16 rows, or at most 128 column tiles, the decode
+// kernel stays faster), and 65 to 128 rows of a
 // [K][N] weight with 129 to 256 column tiles take 64x64 tiles on four wave
 // groups, whose weight copies are whole lines (M = 128, N = 6144: 22.8 us
 // instead of 24.1 on 128x32; N = 8192: 23.0 instead of 25.8).  Otherwise the
@@ -253,6 +256,12 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
         // wave groups, while their tiles make at most one round over the
         // compute units (and, up to 64 rows of a [K][N] weight, while the
         // decode kernel has 129 to 192 column tiles)
+        // 17 to 32 rows of a K-major Y with 129 to 256 column tiles: the
+        // 64x32 tiles on four wave groups (the decode kernel's two row blocks
+        // wait on longer chains)
+        if (pr.I > 16 && pr.I <= 32 && pr.yk && t32 > 128 && t32 <= 256 &&
+            wide_ok(pr, t, kTileCfgs[15], up))
+            return 15;
         if (pr.I > 32) {
             const int64_t t64 = (pr.I + 63) / 64 * t32, t128 = (pr.I + 127) / 128 * t32;
             if (pr.yk && t64 <= 256 && wide_ok(pr, t, kTileCfgs[15], up))

@@ -117,7 +117,7 @@ def test_argument_errors():
     (64, 6144, 14, 15),    # 192 tiles of 64x32; a K-major weight on four wave groups
     (48, 6144, 14, 15),
     (40, 6144, 14, 15),
-    (32, 6144, 12, 12),    # up to 32 rows: the decode kernel
+    (32, 6144, 12, 15),    # up to 32 rows: the decode kernel for W [K][N]
     (128, 2048, 14, 15),   # 2 x 64 tiles of 64x32
     (128, 4096, 14, 15),   # 2 x 128 = 256 tiles: one round over the compute units
     (64, 2048, 10, 15),    # at most 128 column tiles: the decode kernel for W [K][N]
@@ -128,6 +128,19 @@ def test_narrow_split_tiles(M, N, want, want_t):
     assert cfg(dg.OP_FWD, M, N, 4096) == want
     assert cfg(dg.OP_FWD_FP32, M, N, 4096) == want
     assert cfg(dg.OP_FWD_RHS_TRANSPOSED, M, N, 4096) == want_t
+
+
+@pytest.mark.parametrize("M,N,want_t", [
+    (32, 6144, 15),    # 17 to 32 rows, 192 column tiles of 32: four wave groups
+    (17, 6144, 15),
+    (24, 8192, 15),    # 256 column tiles
+    (16, 6144, 12),    # at most 16 rows: the decode kernel
+    (32, 4096, 10),    # at most 128 column tiles: the decode kernel
+    (32, 10240, 12),   # more than one round of 64x32 tiles: the decode kernel
+])
+def test_split_tiles_for_17_to_32_rows_of_a_k_major_weight(M, N, want_t):
+    assert cfg(dg.OP_FWD_RHS_TRANSPOSED, M, N, 4096) == want_t
+    assert cfg(dg.OP_FWD, M, N, 4096) in (10, 11, 12)   # a [K][N] weight keeps the decode kernel
 
 
 def test_narrow_split_tiles_need_a_power_of_two_leaf_count():
