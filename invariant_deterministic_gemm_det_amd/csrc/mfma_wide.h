@@ -595,12 +595,15 @@ struct WideEngine {
         return __builtin_bit_cast(bf16x8, v);
     }
 
-    // The two leaves of the current stage: the first rounded and packed per
-    // block, the second as fp32.
-    __device__ __forceinline__ void leaves(P &x0, F &l1) {
+    // The two leaves of the current stage, each rounded and packed per block.
+    // The second leaf's conversions follow its MFMAs in the same stage (they
+    // overlap the MFMAs still in flight), so the next stage opens with the
+    // pair's matrix-core add on packed operands rather than with conversions
+    // that both waves of a SIMD would run at once.
+    __device__ __forceinline__ void leaves(P &x0, P &x1) {
         const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
         read<1>();
-        F l0;
+        F l0, l1;
 #pragma unroll
         for (int a = 0; a < FM; ++a)
 #pragma unroll
@@ -612,6 +615,7 @@ struct WideEngine {
             for (int b = 0; b < FN; ++b)
                 l1.v[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[1][a], fb[1][b], zero, 0, 0, 0);
         x0 = wpack(l0);
+        x1 = wpack(l1);
     }
 
     // Workgroup-wide OR of a flag, through one dword per wave at the end of
@@ -837,17 +841,17 @@ struct WideTree {
         }
     }
 
-    // Tree work of stage U of group t, whose leaves are x0 (rounded, packed)
-    // and l1 (fp32): their pair add, rounded, climbs while it is a right child.
+    // Tree work of stage U of group t, whose leaves are x0 and x1 (rounded,
+    // packed): their pair add, rounded, climbs while it is a right child.
     template <int U>
-    __device__ __forceinline__ void step(const P &x0, const F &l1, int t) {
-        climb_low<U, 0>(wpack(add(x0, wpack(l1))), t);
+    __device__ __forceinline__ void step(const P &x0, const P &x1, int t) {
+        climb_low<U, 0>(wpack(add(x0, x1)), t);
     }
 
     // Tree work of the last stage, then the root is rounded and stored.
     // Returns whether the root has a non-finite value.
-    __device__ __forceinline__ bool finish(const P &x0, const F &l1) {
-        return finish_root(final_chain(wpack(add(x0, wpack(l1)))));
+    __device__ __forceinline__ bool finish(const P &x0, const P &x1) {
+        return finish_root(final_chain(wpack(add(x0, x1))));
     }
 
     // With matrix-core adds, a tile whose root has a non-finite value is not
@@ -899,7 +903,7 @@ struct WideTree {
 
     // Stage U of group t: the fragment reads of the stage, the tree work of
     // the previous stage (which covers the latency of the reads), then the
-    // stage's leaves, which wait across the barrier (l0 packed, l1 as fp32).
+    // stage's leaves, which wait across the barrier, packed.
     // `pin` keeps the leaves where they are computed: without it the compiler
     // sinks their MFMAs into the next stage, behind its barrier.
     //
@@ -908,17 +912,17 @@ struct WideTree {
     // of the first upper slot, which group 0's own root overwrites before any
     // read (group 1 reads it); a branch here would split the stage's code.
     template <int U>
-    __device__ __forceinline__ void stage(int t, P &x0, F &l1) {
+    __device__ __forceinline__ void stage(int t, P &x0, P &x1) {
         e.template begin<U & 1>(t * G + U);
         if constexpr (U == 0)
-            step<G - 1>(x0, l1, t > 0 ? t - 1 : 0);
+            step<G - 1>(x0, x1, t > 0 ? t - 1 : 0);
         else
-            step<U - 1>(x0, l1, t);
-        e.leaves(x0, l1);
+            step<U - 1>(x0, x1, t);
+        e.leaves(x0, x1);
         pin_p(x0);
-        pin_f(l1);
+        pin_p(x1);
         if constexpr (U + 1 < G)
-            stage<U + 1>(t, x0, l1);
+            stage<U + 1>(t, x0, x1);
     }
 
     // ---- L = 3 * 2^a.  The mid-split tree is the perfect tree over units of
@@ -995,17 +999,17 @@ struct WideTree {
         const int T = e.S >> GL;
         e.prologue();
         P x0;
-        F l1;
+        P x1;
 #pragma unroll
         for (int a = 0; a < E::kFM; ++a)
 #pragma unroll
             for (int b = 0; b < E::kFN; ++b) {
                 x0.w[a][b] = u32x2{0u, 0u};
-                l1.v[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                x1.w[a][b] = u32x2{0u, 0u};
             }
         for (int t = 0; t < T; ++t)
-            stage<0>(t, x0, l1);
-        return final_chain(wpack(add(x0, wpack(l1))));
+            stage<0>(t, x0, x1);
+        return final_chain(wpack(add(x0, x1)));
     }
 
     // Requires S = e.S = TB * G * 2^nup.  Computes and stores the tile;
