@@ -339,6 +339,14 @@ int run_mfma(const Problem &pr, hipStream_t st) {
             return DET_GEMM_EINVAL;  // a forced decode configuration this problem does not fit
         if ((pr.J + 15) / 16 > kMaxDim)
             return DET_GEMM_EINVAL;
+        // A weight larger than the 256 MB Infinity Cache cannot stay there
+        // from one call to the next: its copies are non-temporal when each
+        // workgroup reads whole cache lines of it (a K-major Y, or 64-column
+        // tiles of a [K][N] Y).  Measured on the LM head (K = 4096,
+        // N = 151936): 188 us instead of 213 at M = 1.  A weight the cache
+        // holds keeps its copies cacheable (QKV, [K][N]: 13.7 us instead of
+        // 18.0).  Bits do not depend on it.
+        p.ynt = (pr.yk || c.fn == 4) && pr.J * pr.R * 2 > (int64_t(256) << 20) ? 1 : 0;
         const hipError_t e = launch_decode(p, pr.yk, pr.out, c.fn, st);
         return e == hipSuccess ? DET_GEMM_OK : DET_GEMM_EHIP;
     }
@@ -656,8 +664,9 @@ __global__ __launch_bounds__(256) void shard_reduce_kernel(Parts parts, int64_t 
     for (int k = 0; k < NP; ++k) {
         const uint16_t *src = parts.p[k] + r * ldp + c0;
         if (vec && n == 8) {
-            const uint4 w = *reinterpret_cast<const uint4 *>(src);
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+            // each part and the output are touched once: non-temporal
+            const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src));
+            const uint32_t ww[4] = {w[0], w[1], w[2], w[3]};
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 vals[k][e] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
@@ -677,9 +686,9 @@ __global__ __launch_bounds__(256) void shard_reduce_kernel(Parts parts, int64_t 
     }
     uint16_t *dst = out + r * ldo + c0;
     if (vec && n == 8) {
-        *reinterpret_cast<uint4 *>(dst) =
-            make_uint4(res[0] | ((uint32_t)res[1] << 16), res[2] | ((uint32_t)res[3] << 16),
-                       res[4] | ((uint32_t)res[5] << 16), res[6] | ((uint32_t)res[7] << 16));
+        const u32x4 o = {res[0] | ((uint32_t)res[1] << 16), res[2] | ((uint32_t)res[3] << 16),
+                         res[4] | ((uint32_t)res[5] << 16), res[6] | ((uint32_t)res[7] << 16)};
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(dst));
     } else {
         for (int e = 0; e < n; ++e)
             dst[e] = res[e];

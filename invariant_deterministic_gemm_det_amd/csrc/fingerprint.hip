@@ -26,6 +26,20 @@ constexpr int kUnroll = 4;  // 16-byte chunks in flight per thread (comparator, 
 constexpr int kUnrollDigest = 8;
 constexpr int64_t kMaxBlocks = 4096;
 
+// A 16-byte chunk of a buffer read once.  NT: a non-temporal load (measured:
+// the whole-buffer digest and the comparator gain 7 and 9 %; the row digests,
+// one wave per row, do not, and keep plain loads).
+typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
+template <bool NT = true>
+__device__ __forceinline__ uint4 load_once(const uint4 *q) {
+    if constexpr (NT) {
+        const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4 *>(q));
+        return make_uint4(v[0], v[1], v[2], v[3]);
+    } else {
+        return *q;
+    }
+}
+
 __device__ __forceinline__ uint64_t mix64(uint64_t z) {
     z ^= z >> 30;
     z *= 0xBF58476D1CE4E5B9ull;
@@ -73,7 +87,7 @@ __device__ __forceinline__ unsigned long long wave_min(unsigned long long s) {
 // (two words each) when the bytes are 16-byte aligned (VEC), then the words
 // past the last whole chunk (or all words) from single bytes.  The position
 // term advances by a constant from one chunk of the thread to the next.
-template <bool VEC, int U>
+template <bool VEC, int U, bool NT>
 __device__ __forceinline__ uint64_t partial_sum(const uint8_t *p, int64_t n, int64_t first,
                                                 int64_t stride) {
     const int64_t W = (n + 7) / 8;
@@ -89,7 +103,7 @@ __device__ __forceinline__ uint64_t partial_sum(const uint8_t *p, int64_t n, int
             uint4 v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                v[u] = q[c + u * stride];
+                v[u] = load_once<NT>(q + c + u * stride);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 s += chunk_terms(v[u], g);
@@ -97,7 +111,7 @@ __device__ __forceinline__ uint64_t partial_sum(const uint8_t *p, int64_t n, int
             }
         }
         for (; c < C; c += stride) {
-            s += chunk_terms(q[c], g);
+            s += chunk_terms(load_once<NT>(q + c), g);
             g += step;
         }
         wdone = 2 * C;
@@ -114,8 +128,8 @@ __global__ __launch_bounds__(kThreads) void digest_sum_kernel(const uint8_t *p, 
                                                               unsigned long long *acc) {
     __shared__ uint64_t part[kThreads / 64];
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    uint64_t s = partial_sum<VEC, kUnrollDigest>(p, n, (int64_t)blockIdx.x * kThreads + threadIdx.x,
-                                                  stride);
+    uint64_t s = partial_sum<VEC, kUnrollDigest, true>(p, n, (int64_t)blockIdx.x * kThreads + threadIdx.x,
+                                                        stride);
     s = wave_sum(s);
     if ((threadIdx.x & 63) == 0)
         part[threadIdx.x >> 6] = s;
@@ -141,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void digest_rows_kernel(const uint8_t *p,
     if (r >= rows)
         return;
     const uint64_t s =
-        wave_sum(partial_sum<VEC, kUnroll>(p + r * ld, row_bytes, threadIdx.x & 63, 64));
+        wave_sum(partial_sum<VEC, kUnroll, false>(p + r * ld, row_bytes, threadIdx.x & 63, 64));
     if ((threadIdx.x & 63) == 0)
         out[r] = mix64(s + (uint64_t)row_bytes);
 }
@@ -174,8 +188,8 @@ __global__ __launch_bounds__(kThreads) void mismatch_kernel(const uint8_t *a, co
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int64_t cu = c + u * stride;
-                va[u] = cu < C ? qa[cu] : uint4{0u, 0u, 0u, 0u};
-                vb[u] = cu < C ? qb[cu] : uint4{0u, 0u, 0u, 0u};
+                va[u] = cu < C ? load_once(qa + cu) : uint4{0u, 0u, 0u, 0u};
+                vb[u] = cu < C ? load_once(qb + cu) : uint4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {

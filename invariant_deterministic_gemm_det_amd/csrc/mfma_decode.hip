@@ -107,13 +107,22 @@ __device__ __forceinline__ u32x4 rsrc_at(const void *base) {
 
 // One 1 KB (or, with fewer active lanes, smaller) LDS DMA.  Waits for the
 // wave's outstanding LDS reads first: the slot being refilled was read by the
-// previous unit.  One wait state separates the M0 write from the load.
+// previous unit.  One wait state separates the M0 write from the load.  NT:
+// a non-temporal load (weights that do not stay in the caches).
+template <bool NT = false>
 __device__ __forceinline__ void dma16(uint32_t lds, int voff, u32x4 rs) {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\t"
-                 "buffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds), "v"(voff), "s"(rs)
-                 : "memory", "m0");
+    if constexpr (NT)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\t"
+                     "buffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                     :
+                     : "s"(lds), "v"(voff), "s"(rs)
+                     : "memory", "m0");
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\t"
+                     "buffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :
+                     : "s"(lds), "v"(voff), "s"(rs)
+                     : "memory", "m0");
 }
 
 // The pending left siblings of one 16 x 16 block of a wave: one 16-dword
@@ -344,6 +353,13 @@ void mfma_decode_kernel(MfmaParams p) {
     const uint32_t ring_lds =
         (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char *)ring);
 
+    const bool ynt = __builtin_amdgcn_readfirstlane(p.ynt) != 0;
+    auto ycopy = [&](uint32_t lds, int voff, u32x4 rs) {
+        if (ynt)
+            dma16<true>(lds, voff, rs);
+        else
+            dma16<false>(lds, voff, rs);
+    };
     auto issue = [&](int u) {  // local unit u into slot u % NB
         const int unit = ulo + u;
         const uint32_t slot = ring_lds + (uint32_t)((u % S::NB) * S::SLOT);
@@ -352,7 +368,7 @@ void mfma_decode_kernel(MfmaParams p) {
         if (UL == 2) {
 #pragma unroll
             for (int e = 0; e < 2 * CB; ++e)
-                dma16(slot + e * 1024, yoff[e], rs);
+                ycopy(slot + e * 1024, yoff[e], rs);
             if (MP == 1) {
                 if (lane < 8)
                     dma16(slot + S::Y_BYTES, xoff2[0][0], xs);
@@ -366,7 +382,7 @@ void mfma_decode_kernel(MfmaParams p) {
         } else {
 #pragma unroll
             for (int q = 0; q < CB; ++q)
-                dma16(slot + q * 1024, yoff[q], rs);
+                ycopy(slot + q * 1024, yoff[q], rs);
             if (MP == 1) {
                 if (lane < 4)
                     dma16(slot + S::Y_BYTES, xoff[0], xs);

@@ -63,6 +63,7 @@ struct MfmaParams {
     int32_t xvec, yvec;  // 16-byte aligned rows/columns: vector loads allowed
     int32_t cvec;        // 16-byte aligned output rows: vector stores allowed
     int32_t levels;      // TREE_BLOCK: levels above the blocks; TREE_STACK: stack depth
+    int32_t ynt;         // decode kernel: copy Y with non-temporal loads
 };
 
 // 16-byte chunk swizzle of the [row][64] stage tiles: measured on gfx950 at the
