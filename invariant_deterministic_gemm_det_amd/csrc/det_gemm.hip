@@ -277,7 +277,15 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
             if (pr.I > 64 && t128 <= 256 && wide_ok(pr, t, kTileCfgs[13], up))
                 return 13;
         }
-        if ((pr.I > 16 && t32 * blocks > 1400) || (pr.I > 64 && t32 * blocks > 600)) {
+        const bool line_units = pr.yk && (pr.R / 32) % 2 == 0;  // two-leaf copies read whole lines
+        // A K-major weight read in whole lines keeps up to 32 rows on the
+        // decode kernel at any width (its copies of a weight larger than the
+        // Infinity Cache are non-temporal): N = 151936, M = 32: 279 us
+        // instead of 306 on the wide kernel; N = 40960, M = 17: 73 instead
+        // of 109; N = 28672: equal.
+        const bool decode_lines = line_units && pr.I <= 32;
+        if (!decode_lines &&
+            ((pr.I > 16 && t32 * blocks > 1400) || (pr.I > 64 && t32 * blocks > 600))) {
             const int first = (pr.J + 127) / 128 > 128 ? 8 : 6;
             for (int c : {first, first == 8 ? 6 : 8})
                 if (wide_ok(pr, t, kTileCfgs[c], up))
@@ -285,7 +293,6 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
         }
         if (pr.I > 64)
             return 10;  // eight row blocks: 16-column tiles only
-        const bool line_units = pr.yk && (pr.R / 32) % 2 == 0;  // two-leaf copies read whole lines
         if (!line_units && pr.I <= 16 && (pr.J + 63) / 64 > 128)
             return 11;
         return t32 > 128 ? 12 : 10;

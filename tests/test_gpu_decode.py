@@ -146,6 +146,21 @@ def test_decode_lm_head_row(dev):
             assert np.array_equal(bits(_forced(cfg, lambda: dg.det_gemm_fwd(A[:m], B))), ref), (m, cfg)
 
 
+def test_lm_head_transposed_weight_rows_across_kernels(dev):
+    """LM head in the nn.Linear layout (W [N][K], 1.2 GB: the decode kernel's
+    weight copies are non-temporal): 1, 16, 17 and 32 rows run on the decode
+    kernel, 33 and 256 rows on the wide kernel; every row equals the same row
+    of the 256-row call, and the 32-row call equals the general kernel."""
+    say("LM head W [N][K] rows across the decode and wide kernels")
+    A = W.randn_bf16((256, 4096), 1.0, 1310).to(dev)
+    Bt = W.randn_bf16((151936, 4096), 0.02, 1311, device=dev)
+    full = bits(dg.det_gemm_fwd_rhs_transposed(A, Bt))
+    for m in (1, 16, 17, 32, 33):
+        assert np.array_equal(bits(dg.det_gemm_fwd_rhs_transposed(A[:m], Bt)), full[:m]), m
+    ref = bits(_forced(GENERAL_CFG, lambda: dg.det_gemm_fwd_rhs_transposed(A[:32], Bt)))
+    assert np.array_equal(full[:32], ref)
+
+
 @pytest.mark.parametrize("case", ["rows129", "leaves7", "ragged_k", "unaligned", "n_not_8"])
 def test_decode_rejects_unsupported(dev, case):
     """Forcing configuration 10, 11 or 12 on a problem it does not take is EINVAL;

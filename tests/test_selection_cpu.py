@@ -73,6 +73,17 @@ def test_small_m_leaf_count_the_wide_kernel_refuses():
     assert cfg(dg.OP_FWD, 40, 28672, 1536) == 12
 
 
+@pytest.mark.parametrize("M,N,want_t", [
+    (17, 151936, 12),   # a K-major weight read in whole lines: the decode kernel up to 32 rows
+    (32, 151936, 12),
+    (32, 40960, 12),
+    (33, 151936, 8),    # more rows: the wide kernel
+])
+def test_small_m_transposed_weight_stays_on_decode_up_to_32_rows(M, N, want_t):
+    assert cfg(dg.OP_FWD_RHS_TRANSPOSED, M, N, 4096) == want_t
+    assert cfg(dg.OP_FWD, M, N, 4096) == 8          # a [K][N] weight: the wide kernel
+
+
 def test_small_m_transposed_weight():
     # W [N][K] with an even leaf count is read in two-leaf lines at any width:
     # 32 columns even for the LM head; an odd leaf count takes 64 columns
