@@ -16,9 +16,10 @@
  *              from position 0, whatever the batch, the lengths of the other
  *              sequences or Smax;
  *   per split  scores s_j = (sum over d of q_d k_jd) * scale * log2(e), the
- *              dot product in four 32-wide parts, each a chain of 16 bf16-pair
- *              dot instructions in ascending d, the parts joined as
- *              (0 + 1) + (2 + 3); m = max s_j;
+ *              dot product in sixteen 8-wide parts c = 0..15, each a chain
+ *              of 4 bf16-pair dot instructions in ascending d, the parts
+ *              joined in a balanced tree that pairs c with c + 8, then with
+ *              c + 4, c + 2, c + 1; m = max s_j;
  *              p_j = 2^(s_j - m); l = pairwise sum of p_j over the split's
  *              256 slots (empty slots 0); acc_d = sum of p_j v_jd in
  *              ascending j;

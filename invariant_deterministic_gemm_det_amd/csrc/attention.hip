@@ -85,7 +85,7 @@ struct PrefillTiles {
 // has its own length, and the arithmetic of each one is that of a decode
 // query with that length.
 template <int GM, bool PF>
-__global__ __launch_bounds__(kThreads) void attn_split_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) void attn_split_kernel(
     const uint16_t *Q, const uint16_t *K, const uint16_t *V, const int32_t *lens, int Hq, int Hkv,
     int Smax, int G, int NS, float scale_log2, float *work, PrefillTiles pt) {
     __shared__ __attribute__((aligned(16))) float sc[GM][kSplit];
@@ -129,64 +129,70 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
     const int64_t head = ((int64_t)seq * Hkv + kvh) * Smax;
     const uint16_t *Kh = K + (head + j0) * kD, *Vh = V + (head + j0) * kD;
 
-    // ---- scores: thread t takes position r = t / 4 of a tile and the 32-wide
-    // part pp = t % 4 of the dot products (its q part in registers as bf16
-    // pairs, v_dot2 over the 16 pairs in ascending order); the four parts
-    // meet as (0 + 1) + (2 + 3)
-    const int r = t >> 2, pp = t & 3;
-    uint32_t qp[GM][16];
+    // ---- scores.  Lane l of wave w holds the 16-byte chunk cc = l % 16 of
+    // four key rows of a tile, rows w * 16 + 4c + l / 16 for c = 0..3, so each
+    // of its four loads reads 1 KB of whole rows; its q chunk cc of every
+    // head stays in four registers.  The score of a row is the sum over the
+    // 16 chunks of each chunk's 4-pair v_dot2 chain (pairs in ascending
+    // order), the chunks meeting in a balanced tree: cc with cc ^ 8 first,
+    // then ^ 4, ^ 2, ^ 1.  The first two levels spread the four rows over the
+    // lanes (bit 3 of the lane picks rows 2,3 over rows 0,1, bit 2 the odd
+    // row), so each lane ends with one row's score.
+    const int cc = lane & 15, rq = lane >> 4;
+    const int h3 = (lane >> 3) & 1, h2 = (lane >> 2) & 1;
+    const int myrow = wave * 16 + (2 * h3 + h2) * 4 + rq;  // the row whose score this lane ends with
+    uint32_t qc[GM][4];
 #pragma unroll
-    for (int g = 0; g < GM; ++g)
+    for (int g = 0; g < GM; ++g) {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (g < VG)
+            v = *reinterpret_cast<const uint4 *>(
+                Q + ((int64_t)(row0 + g / G) * Hq + kvh * G + g % G) * kD + cc * 8);
+        qc[g][0] = v.x;
+        qc[g][1] = v.y;
+        qc[g][2] = v.z;
+        qc[g][3] = v.w;
+    }
+    const int ntiles = (n + kTile - 1) / kTile;
+    auto key_chunks = [&](uint4 (&kv)[4], int sub) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (g < VG)
-                v = *reinterpret_cast<const uint4 *>(
-                    Q + ((int64_t)(row0 + g / G) * Hq + kvh * G + g % G) * kD + pp * 32 + c * 8);
-            qp[g][4 * c] = v.x;
-            qp[g][4 * c + 1] = v.y;
-            qp[g][4 * c + 2] = v.z;
-            qp[g][4 * c + 3] = v.w;
-        }
-    // The key slice of thread (r, pp) -- 64 contiguous bytes of row r -- is read
-    // straight from global memory (a wave reads 16 whole rows, 4 KB
-    // contiguous) one tile ahead; keys need no LDS.
-    const int ntiles = (n + kTile - 1) / kTile;
-    auto key_slice = [&](uint4 (&kv)[4], int sub) {
-        const int row = sub * kTile + r;
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            kv[c] = row < n ? *reinterpret_cast<const uint4 *>(Kh + (int64_t)row * kD + pp * 32 + c * 8)
+            const int row = sub * kTile + wave * 16 + c * 4 + rq;
+            kv[c] = row < n ? *reinterpret_cast<const uint4 *>(Kh + (int64_t)row * kD + cc * 8)
                             : make_uint4(0u, 0u, 0u, 0u);
+        }
     };
     uint4 kcur[4], knext[4];
-    key_slice(knext, 0);
+    key_chunks(knext, 0);
     for (int sub = 0; sub < ntiles; ++sub) {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
             kcur[c] = knext[c];
         if (sub + 1 < ntiles)
-            key_slice(knext, sub + 1);
-        uint32_t kw[16];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            kw[4 * c] = kcur[c].x;
-            kw[4 * c + 1] = kcur[c].y;
-            kw[4 * c + 2] = kcur[c].z;
-            kw[4 * c + 3] = kcur[c].w;
-        }
-        const int j = sub * kTile + r;
+            key_chunks(knext, sub + 1);
+        const int j = sub * kTile + myrow;
 #pragma unroll
         for (int g = 0; g < GM; ++g) {
             if (g < VG) {
-                float part = 0.0f;
+                float part[4];
 #pragma unroll
-                for (int c = 0; c < 16; ++c)
-                    part = __builtin_amdgcn_fdot2_f32_bf16(as_pair(qp[g][c]), as_pair(kw[c]), part,
-                                                           false);
-                float v = part + __shfl_xor(part, 1, 64);
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t kw[4] = {kcur[c].x, kcur[c].y, kcur[c].z, kcur[c].w};
+                    float x = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        x = __builtin_amdgcn_fdot2_f32_bf16(as_pair(qc[g][e]), as_pair(kw[e]), x, false);
+                    part[c] = x;
+                }
+                // level cc ^ 8: keep rows 2 h3, 2 h3 + 1, hand the other two over
+                const float s0 = h3 ? part[0] : part[2], s1 = h3 ? part[1] : part[3];
+                const float k0 = h3 ? part[2] : part[0], k1 = h3 ? part[3] : part[1];
+                const float a0 = k0 + __shfl_xor(s0, 8, 64), a1 = k1 + __shfl_xor(s1, 8, 64);
+                // level cc ^ 4: keep row 2 h3 + h2
+                float v = (h2 ? a1 : a0) + __shfl_xor(h2 ? a0 : a1, 4, 64);
                 v = v + __shfl_xor(v, 2, 64);
-                if (pp == 0)
+                v = v + __shfl_xor(v, 1, 64);
+                if ((lane & 3) == 0)
                     sc[g][j] = j < nv[g] ? v * scale_log2 : -__builtin_inff();
             }
         }
@@ -259,6 +265,7 @@ __global__ __launch_bounds__(kThreads) void attn_split_kernel(
             if (o < npairs) {
                 const int g = o >> 6, dp = o & 63;
                 const float *pw = &sc[g][sub * kTile];
+#pragma unroll 4
                 for (int rr = 0; rr < kTile; rr += 4) {
                     const float4 w4 = *reinterpret_cast<const float4 *>(pw + rr);
                     const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
