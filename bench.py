@@ -229,6 +229,7 @@ def moe_leg(dev, steps, warmup, with_cpu, context=True):
 
 
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+COLD_COPIES = 13            # 13 x 50 MB QKV weights: 650 MB, beyond the 256 MB Infinity Cache
 FP_BYTES = 1 << 30
 FP_ROWS, FP_ROW_BYTES = 16384, 32768
 
@@ -296,18 +297,20 @@ def fingerprint_leg(dev, steps, warmup, with_cpu):
 NORM_R, NORM_H = 8192, 4096
 
 
-def graph_time(fn, out, steps):
+def graph_time(fn, out, steps, rotate=None):
     """Per-call time of `fn` (which writes `out`) from `steps` calls replayed
     back to back out of a captured graph: the GPU time of calls shorter than
-    the host's launch path.  Every replay must reproduce the eager bits."""
+    the host's launch path.  Every replay must reproduce the eager bits.
+    `rotate`: calls equal to `fn` on copies of its operands, taken in turn."""
     import torch
     fn()
     torch.cuda.synchronize()
     ref = out.clone()
+    calls = rotate or [fn]
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        for _ in range(steps):
-            fn()
+        for i in range(steps):
+            calls[i % len(calls)]()
     graph.replay()
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.uint8), ref.view(torch.uint8)), "graph replay differs"
@@ -511,6 +514,7 @@ def small_m_leg(dev, steps, warmup, decode_only=False):
         # wide kernel)
         cases = [c for c in cases if c[2] <= 16 or (c[0] == "qkv" and c[2] <= 128)]
     rows = []
+    cold_copies = {}
     for name, layout, m in cases:
         if name == "qkv":
             x, k, n = Xq[:m], Wk.QKV_K, Wk.QKV_N
@@ -529,6 +533,20 @@ def small_m_leg(dev, steps, warmup, decode_only=False):
               (lambda: dg.det_gemm_fwd_rhs_transposed(x, Wqt, out=out)) if name == "qkv" else \
               (lambda: dg.det_gemm_fwd(x, Wl, out=out))
         t = graph_time(run, out, steps)
+        # The same calls, each on another copy of the weight, the copies
+        # together well beyond the 256 MB Infinity Cache: what a model's
+        # decode step sees, each layer's weight read once per token.  The LM
+        # head's weight alone exceeds the cache.
+        if name == "qkv":
+            if layout not in cold_copies:
+                base = Wq if layout == "W[K][N]" else Wqt
+                cold_copies[layout] = [base] + [base.clone() for _ in range(COLD_COPIES - 1)]
+            copies = cold_copies[layout]
+            rot = [(lambda w=w: dg.det_gemm_fwd(x, w, out=out)) if layout == "W[K][N]" else
+                   (lambda w=w: dg.det_gemm_fwd_rhs_transposed(x, w, out=out)) for w in copies]
+            t_cold = graph_time(run, out, steps, rotate=rot)
+        else:
+            t_cold = t
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(steps):
@@ -546,15 +564,22 @@ def small_m_leg(dev, steps, warmup, decode_only=False):
                   else "mfma_wide_kernel" if cfg >= 5 else "mfma_kernel")
         nbytes = (m * k + k * n + m * n) * 2
         gbs = nbytes / (t * 1e-3) / 1e9
+        gbs_cold = nbytes / (t_cold * 1e-3) / 1e9
         rows.append({"op": name, "weight": layout, "M": m, "K": k, "N": n, "us": round(t * 1e3, 2),
                      "us_eager_calls": round(t_eager * 1e3, 2),
                      "GB/s": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                     "us_cold_weight": round(t_cold * 1e3, 2),
+                     "frac_of_hbm_cold_weight": round(gbs_cold / PEAK_HBM_GBS, 4),
                      "kernel": kernel, "config": cfg})
     return {"workload": "forward products with 1..256 rows: the weight read once per call "
                         "(the decode kernel; from 33 to 128 rows, narrow wide tiles whose tree is "
                         "split over two or four wave groups; the wide kernel when wide in N)",
-            "timing": "us: per call, calls replayed from a captured graph; us_eager_calls: "
-                      "back-to-back calls through the binding (host launch path included)",
+            "timing": "us: per call, calls replayed from a captured graph (the QKV weight, "
+                      "50 MB, stays in the 256 MB Infinity Cache from call to call); "
+                      "us_cold_weight: the same, each call on another of "
+                      f"{COLD_COPIES} copies of the weight (as a model's layers: the weight "
+                      "comes from HBM); us_eager_calls: back-to-back calls through the "
+                      "binding (host launch path included)",
             "roofline": "hbm, 8000 GB/s", "rows": rows}
 
 

@@ -238,7 +238,15 @@ bool decode_ok(const Problem &pr) {
 // kernel stays faster), and 65 to 128 rows of a
 // [K][N] weight with 129 to 256 column tiles take 64x64 tiles on four wave
 // groups, whose weight copies are whole lines (M = 128, N = 6144: 22.8 us
-// instead of 24.1 on 128x32; N = 8192: 23.0 instead of 25.8).  Otherwise the
+// instead of 24.1 on 128x32; N = 8192: 23.0 instead of 25.8).  First of all,
+// 17 to 64 rows (33 to 64 of a K-major Y) with 129 to 256 column tiles of 64
+// take 64x64 tiles on four wave groups (K = 4096, N = 9216 .. 16384: 23 to
+// 27 us instead of 30 to 40; more tiles than one round lost with the weight
+// in HBM).  A [K][N] Y on 32-column split tiles reads half lines, whose other
+// halves the split kernel's XCD pairing turns into L2 hits, so it takes the
+// 64x32 tiles at 129 to 256 column tiles too (M = 48, N = 8192: 17.7 us
+// instead of 22.5 on the decode kernel), and above 192 of them from 17 rows
+// on four wave groups (M = 32: 16.5 instead of 17.0).  Otherwise the
 // wide kernel
 // (N = 28672: 54 us instead of 65 at M = 32, 54 instead of 83 at M = 64),
 // on 128x128 tiles above 128 column tiles (N = 18432, M = 64: 51 us, 55 on
@@ -252,6 +260,13 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     int up = 0;
     if (decode_ok(pr)) {
         const int64_t t32 = (pr.J + 31) / 32, blocks = (pr.I + 15) / 16;
+        // 17 to 64 rows (33 to 64 of a K-major Y) with 129 to 256 tiles of
+        // 64x64: those tiles on four wave groups, one round over the compute
+        // units
+        const int64_t t64x64 = (pr.J + 63) / 64;
+        if (pr.I > (pr.yk ? 32 : 16) && pr.I <= 64 && t64x64 > 128 && t64x64 <= 256 &&
+            wide_ok(pr, t, kTileCfgs[16], up))
+            return 16;
         // 33 to 128 rows: the narrow wide tiles that split the tree over
         // wave groups, while their tiles make at most one round over the
         // compute units (and, up to 64 rows of a [K][N] weight, while the
@@ -259,15 +274,14 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
         // 17 to 32 rows of a K-major Y with 129 to 256 column tiles: the
         // 64x32 tiles on four wave groups (the decode kernel's two row blocks
         // wait on longer chains)
-        if (pr.I > 16 && pr.I <= 32 && pr.yk && t32 > 128 && t32 <= 256 &&
+        if (pr.I > 16 && pr.I <= 32 && t32 > (pr.yk ? 128 : 192) && t32 <= 256 &&
             wide_ok(pr, t, kTileCfgs[15], up))
             return 15;
         if (pr.I > 32) {
             const int64_t t64 = (pr.I + 63) / 64 * t32, t128 = (pr.I + 127) / 128 * t32;
             if (pr.yk && t64 <= 256 && wide_ok(pr, t, kTileCfgs[15], up))
                 return 15;
-            if (t64 <= 256 && (pr.I > 64 || (t32 > 128 && t32 <= 192)) &&
-                wide_ok(pr, t, kTileCfgs[14], up))
+            if (t64 <= 256 && (pr.I > 64 || t32 > 128) && wide_ok(pr, t, kTileCfgs[14], up))
                 return 14;
             // 65 to 128 rows of a [K][N] weight with 129 to 256 column tiles:
             // 64x64 tiles on four wave groups read whole 128-byte weight lines

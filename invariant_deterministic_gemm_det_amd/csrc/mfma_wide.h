@@ -1249,8 +1249,18 @@ __device__ __attribute__((noinline)) void split_valu_tile(MfmaParams q, int tile
 template <bool YK, int OUT, int FM, int FN, int WM, int WN, int NBUF, int GL, int RU, int KS, int OCC>
 __global__ __launch_bounds__(64 * KS * WM * WN) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void mfma_wide_split_kernel(MfmaParams p) {
-    if (split_tile<WideMatrixAdd, YK, OUT, FM, FN, WM, WN, NBUF, GL, RU, KS>(p, blockIdx.x))
-        split_valu_tile<YK, OUT, FM, FN, WM, WN, NBUF, GL, RU, KS>(p, blockIdx.x);
+    // An MN-major Y ([R][J]) of 32-column tiles gives each tile half of every
+    // 128-byte line of its panel: tiles 2u and 2u + 1 go to workgroups b and
+    // b + 8 of a run of 16, which land on the same XCD (workgroup b runs on
+    // XCD b mod 8), so the second half of each line is an L2 hit.  Workgroups
+    // past the last whole run keep their own index.
+    int tile = blockIdx.x;
+    if (!YK && blockIdx.x < (gridDim.x & ~15u)) {
+        const int b = blockIdx.x;
+        tile = (b & ~15) + 2 * (b & 7) + ((b >> 3) & 1);
+    }
+    if (split_tile<WideMatrixAdd, YK, OUT, FM, FN, WM, WN, NBUF, GL, RU, KS>(p, tile))
+        split_valu_tile<YK, OUT, FM, FN, WM, WN, NBUF, GL, RU, KS>(p, tile);
 }
 
 // ---- grouped launch (MoE grouped GEMM): the row-major X is cut into

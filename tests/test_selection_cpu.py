@@ -56,8 +56,11 @@ def test_step_products_run_on_the_wide_kernel():
     (1, 11008, 11),    # 172 tiles of 64 columns
     (16, 151936, 11),  # LM head
     (32, 6144, 12),    # two row blocks, 384 (tiles x blocks)
-    (64, 11008, 12),   # 344 x 4 = 1376: decode
-    (64, 14336, 6),    # 448 x 4 = 1792: wide, 112 tiles of 128 columns
+    (64, 11008, 16),   # 172 tiles of 64x64 on four wave groups
+    (17, 14336, 16),   # 224 tiles of 64x64
+    (17, 16384, 16),   # 256 tiles of 64x64: still one round
+    (17, 18432, 12),   # 288 tiles of 64x64: more than one round; decode
+    (64, 18432, 8),    # 576 x 4 = 2304: wide, 144 tiles of 128 columns
     (17, 28672, 8),    # 896 x 2: wide, 224 tiles of 128 columns
     (48, 151936, 8),
 ])
@@ -132,7 +135,9 @@ def test_argument_errors():
     (128, 2048, 14, 15),   # 2 x 64 tiles of 64x32
     (128, 4096, 14, 15),   # 2 x 128 = 256 tiles: one round over the compute units
     (64, 2048, 10, 15),    # at most 128 column tiles: the decode kernel for W [K][N]
-    (48, 8192, 12, 15),    # 256 column tiles: the decode kernel for W [K][N]
+    (48, 8192, 14, 15),    # 256 column tiles of 64x32 ([K][N]: tiles 2u, 2u + 1 on one XCD)
+    (48, 10240, 16, 16),   # 160 tiles of 64x64 on four wave groups
+    (48, 18432, 8, 8),     # 288 tiles of 64x64: the wide kernel
     (128, 14336, 6, 6),    # 448 tiles of 128x32: the 128x64 wide kernel
 ])
 def test_narrow_split_tiles(M, N, want, want_t):
@@ -151,7 +156,19 @@ def test_narrow_split_tiles(M, N, want, want_t):
 ])
 def test_split_tiles_for_17_to_32_rows_of_a_k_major_weight(M, N, want_t):
     assert cfg(dg.OP_FWD_RHS_TRANSPOSED, M, N, 4096) == want_t
-    assert cfg(dg.OP_FWD, M, N, 4096) in (10, 11, 12)   # a [K][N] weight keeps the decode kernel
+
+
+@pytest.mark.parametrize("M,N,want", [
+    (17, 6144, 12),    # 192 column tiles of 32: the decode kernel
+    (32, 6144, 12),
+    (24, 8192, 15),    # 193 to 256 column tiles: 64x32 on four wave groups
+    (32, 8192, 15),
+    (32, 4096, 10),    # at most 128 column tiles: the decode kernel
+    (32, 10240, 16),   # 160 tiles of 64x64 on four wave groups
+    (16, 10240, 11),   # at most 16 rows: the decode kernel
+])
+def test_split_tiles_for_17_to_32_rows_of_a_row_major_weight(M, N, want):
+    assert cfg(dg.OP_FWD, M, N, 4096) == want
 
 
 def test_narrow_split_tiles_need_a_power_of_two_leaf_count():
