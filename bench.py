@@ -108,6 +108,8 @@ def parse():
     ap.add_argument("--no-attention", action="store_true", help="skip the decode attention leg")
     ap.add_argument("--no-shard", action="store_true", help="skip the K-shard combination leg")
     ap.add_argument("--no-small-m", action="store_true", help="skip the decode-shaped products")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other transformer-shaped products (MLP, backward, LM head, depth cap)")
     ap.add_argument("--profile-only", action="store_true",
                     help="run only the GPU steps (for rocprofv3 runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -583,6 +585,91 @@ def small_m_leg(dev, steps, warmup, decode_only=False):
             "roofline": "hbm, 8000 GB/s", "rows": rows}
 
 
+def configs_leg(dev, reps=5):
+    """TFLOP/s of the other transformer-shaped products, one launch each per
+    rep (median of `reps` after one warm-up call): the MLP of an 8B-class
+    model at 8192 rows (gate+up K = 4096, N = 24576; down K = 12288, N = 4096,
+    384 leaves), the backward at M = 8192, K = N = 4096 (dA; dB and its
+    [N,K] form, reduction depth 8192), the LM head at 4096 rows (N = 151936,
+    bf16 and fp32 out) and the depth cap (K = 32768, N = 4096, 2048 rows)."""
+    import torch
+    import det_workloads as Wk
+    import invariant_deterministic_gemm_det_amd as dg
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts), min(ts), max(ts)
+
+    rows = []
+
+    def add(name, shape, flop, fn, cfg):
+        med, lo, hi = timed(fn)
+        tf = flop / (med * 1e-3) / 1e12
+        rows.append({"product": name, "M,N,K": shape, "median_ms": round(med, 4),
+                     "min_ms": round(lo, 4), "max_ms": round(hi, 4), "tflops": round(tf, 1),
+                     "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2), "config": cfg})
+
+    def cfg_of(op, a, lda, b, ldb, c, ldc, M, N, K):
+        return dg.det_gemm_debug_config(op, a.data_ptr(), lda, b.data_ptr(), ldb, c.data_ptr(), ldc,
+                                        M, N, K)
+
+    X, Wgu, H, Wd = Wk.mlp_inputs(dev)
+    M, K, N = X.shape[0], X.shape[1], Wgu.shape[1]
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    add("MLP gate+up fwd", [M, N, K], 2.0 * M * N * K, lambda: dg.det_gemm_fwd(X, Wgu, out=out),
+        cfg_of(dg.OP_FWD, X, K, Wgu, N, out, N, M, N, K))
+    M, K, N = H.shape[0], H.shape[1], Wd.shape[1]
+    out2 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    add("MLP down fwd (L = 384)", [M, N, K], 2.0 * M * N * K,
+        lambda: dg.det_gemm_fwd(H, Wd, out=out2), cfg_of(dg.OP_FWD, H, K, Wd, N, out2, N, M, N, K))
+    del X, Wgu, H, Wd, out, out2
+
+    A, B, dC = Wk.backward_inputs(dev)
+    M, K, N = A.shape[0], A.shape[1], B.shape[1]
+    dA = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dB = torch.empty((K, N), dtype=torch.bfloat16, device=dev)
+    dBt = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    add("backward da (R = 4096)", [M, N, K], 2.0 * M * N * K, lambda: dg.det_gemm_da(dC, B, out=dA),
+        cfg_of(dg.OP_DA, dC, N, B, N, dA, K, M, N, K))
+    add("backward db (R = 8192)", [M, N, K], 2.0 * M * N * K, lambda: dg.det_gemm_db(A, dC, out=dB),
+        cfg_of(dg.OP_DB, A, K, dC, N, dB, N, M, N, K))
+    add("backward db_transposed (R = 8192)", [M, N, K], 2.0 * M * N * K,
+        lambda: dg.det_gemm_db_transposed(A, dC, out=dBt), cfg_of(dg.OP_DB_TRANSPOSED, A, K, dC, N, dBt, K, M, N, K))
+    del A, B, dC, dA, dB, dBt
+
+    Xl, Wl = Wk.lm_head_inputs(dev, M=4096)
+    M, K, N = Xl.shape[0], Xl.shape[1], Wl.shape[1]
+    ol = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    add("LM head fwd, bf16 out", [M, N, K], 2.0 * M * N * K, lambda: dg.det_gemm_fwd(Xl, Wl, out=ol),
+        cfg_of(dg.OP_FWD, Xl, K, Wl, N, ol, N, M, N, K))
+    del ol
+    of = torch.empty((M, N), dtype=torch.float32, device=dev)
+    add("LM head fwd, fp32 out", [M, N, K], 2.0 * M * N * K, lambda: dg.det_gemm_fwd_fp32(Xl, Wl, out=of),
+        cfg_of(dg.OP_FWD_FP32, Xl, K, Wl, N, of, N, M, N, K))
+    del Xl, Wl, of
+
+    Ad, Bd = Wk.deep_inputs(dev)
+    M, K, N = Ad.shape[0], Ad.shape[1], Bd.shape[1]
+    od = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    add("depth cap fwd (K = 32768, L = 1024)", [M, N, K], 2.0 * M * N * K,
+        lambda: dg.det_gemm_fwd(Ad, Bd, out=od), cfg_of(dg.OP_FWD, Ad, K, Bd, N, od, N, M, N, K))
+    del Ad, Bd, od
+    torch.cuda.empty_cache()
+    return {"workload": "the other transformer-shaped products, inputs seeded as the parity "
+                        "tests' (MLP 3001-3004, backward 4001-4003, LM head 5001-5002, depth cap "
+                        "5003-5004), resident in HBM",
+            "timing": f"median of {reps} launches after one warm-up, HIP events", "rows": rows}
+
+
 def issue_probe_leg(iters=4000):
     """The instruction mix of one pipeline stage of the 128x128 wide kernel
     (per wave: 32 MFMAs, 64 bf16 conversions, each conversion feeding the next
@@ -755,6 +842,7 @@ def main():
                                                         not args.no_cpu)
     shard = None if args.no_shard else shard_leg(dev, args.steps, args.warmup)
     small = None if args.no_small_m else small_m_leg(dev, args.steps, args.warmup)
+    others = None if args.no_configs else configs_leg(dev)
     strict = strict_leg(X, W, 256)
 
     wall, ops = timed_step_loop()
@@ -861,6 +949,7 @@ def main():
         "attention_decode": attn,
         "shard_reduce": shard,
         "small_m": small,
+        "other_configs": others,
     }
     print(json.dumps(line))
 
