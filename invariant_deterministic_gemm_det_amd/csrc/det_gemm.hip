@@ -250,10 +250,14 @@ bool decode_ok(const Problem &pr) {
 // wide kernel
 // (N = 28672: 54 us instead of 65 at M = 32, 54 instead of 83 at M = 64),
 // on 128x128 tiles above 128 column tiles (N = 18432, M = 64: 51 us, 55 on
-// 128x64).  Otherwise 128x128 wide tiles when they make at least four waves
-// of workgroups over the 256 compute units, else the 128x64 wide kernel, two
+// 128x64).  Otherwise 128x128 wide tiles when they make at least two waves
+// of workgroups over the 256 compute units (M = 2048, N = 4096, K = 4096:
+// 539 TFLOP/s instead of 473 on 128x64), else the 128x64 wide kernel, two
 // workgroups per compute unit, which keeps more units busy on small and
-// mid-size products (M = 1024 at K = 4096, N = 6144: 94 us instead of 111 us).
+// mid-size products (M = 1024 at K = 4096, N = 6144: 94 us instead of 111 us)
+// -- but from 256 leaves its parked tree levels leave LDS for one workgroup
+// per unit, and beyond one round of its tiles the 128x128 tiles win (K = 8192,
+// M = 1024, N = 4096: 553 TFLOP/s instead of 388).
 int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     if (g_force_config >= 0)
         return g_force_config;
@@ -312,15 +316,21 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
         return t32 > 128 ? 12 : 10;
     }
     const int64_t t128 = ((pr.I + 127) / 128) * ((pr.J + 127) / 128);
-    if (t128 >= 4 * 256)
+    if (t128 >= 2 * 256)
         for (int c : {8, 5, 9, 7})  // three stage buffers with early copies if the LDS holds them
             if (wide_ok(pr, t, kTileCfgs[c], up))
                 return c;
-    if (wide_ok(pr, t, kTileCfgs[6], up))
+    // 128x64 tiles while they fit one round, or two workgroups per compute
+    // unit: from 256 leaves their parked tree levels leave LDS for one, and
+    // four waves per unit ran 30 % below the 128x128 tiles
+    if (wide_ok(pr, t, kTileCfgs[6], up) &&
+        (2 * t128 <= 256 || 2 * kTileCfgs[6].lds_bytes(up) <= kLdsMax))
         return 6;
     for (int c : {8, 5, 9, 7})
         if (wide_ok(pr, t, kTileCfgs[c], up))
             return c;
+    if (wide_ok(pr, t, kTileCfgs[6], up))  // deeper trees than the 128x128 tiles' LDS holds
+        return 6;
     if (pr.I <= 16)
         return 1;
     // 8-wave 128x64 tiles for blocks of 8 leaves; the 4-wave 64x64 tile (twice

@@ -176,3 +176,16 @@ def test_narrow_split_tiles_need_a_power_of_two_leaf_count():
     assert cfg(dg.OP_FWD, 128, 6144, 4128) == 10
     # da at 128 rows reduces over N = 4096 (128 leaves) into 6144 columns
     assert cfg(dg.OP_DA, 128, 4096, 6144) == 13
+
+
+@pytest.mark.parametrize("M,N,K,want", [
+    (512, 4096, 4096, 6),      # 128 tiles of 128x128: 128x64 tiles, one round
+    (1024, 6144, 4096, 6),     # 384 tiles: 128x64, two workgroups per compute unit
+    (2048, 4096, 4096, 8),     # 512 tiles: two rounds of 128x128
+    (512, 4096, 8192, 6),      # 256 leaves, 128x64 tiles still one round
+    (1024, 4096, 8192, 8),     # 256 leaves: 128x64 would hold one workgroup per unit
+    (2048, 4096, 16384, 5),    # 512 leaves: two stage buffers (three do not fit the LDS)
+    (2048, 4096, 32768, 6),    # 1024 leaves: the 128x128 tiles' LDS cannot hold the tree
+])
+def test_mid_size_products_by_leaves_and_tiles(M, N, K, want):
+    assert cfg(dg.OP_FWD, M, N, K) == want
