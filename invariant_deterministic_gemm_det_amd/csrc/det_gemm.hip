@@ -317,7 +317,7 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     }
     const int64_t t128 = ((pr.I + 127) / 128) * ((pr.J + 127) / 128);
     if (t128 >= 2 * 256)
-        for (int c : {8, 5, 9, 7})  // three stage buffers with early copies if the LDS holds them
+        for (int c : {8, 5, 9, 7, 17})  // three stage buffers with early copies if the LDS holds them
             if (wide_ok(pr, t, kTileCfgs[c], up))
                 return c;
     // 128x64 tiles while they fit one round, or two workgroups per compute
@@ -326,10 +326,13 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     if (wide_ok(pr, t, kTileCfgs[6], up) &&
         (2 * t128 <= 256 || 2 * kTileCfgs[6].lds_bytes(up) <= kLdsMax))
         return 6;
-    for (int c : {8, 5, 9, 7})
+    // deeper trees than configurations 5 and 8 hold: 128x128 tiles with a
+    // second register level (K = 32768, M = 2048, N = 4096: 420 TFLOP/s
+    // instead of 355 on 128x64; at 512 leaves and fewer it loses to them)
+    for (int c : {8, 5, 9, 7, 17})
         if (wide_ok(pr, t, kTileCfgs[c], up))
             return c;
-    if (wide_ok(pr, t, kTileCfgs[6], up))  // deeper trees than the 128x128 tiles' LDS holds
+    if (wide_ok(pr, t, kTileCfgs[6], up))
         return 6;
     if (pr.I <= 16)
         return 1;

@@ -64,8 +64,8 @@ constexpr TileCfg kTileCfgs[] = {
     {1, 1, 1, 1, KIND_DECODE, 0, 0, 0, 1},  {1, 4, 1, 1, KIND_DECODE, 0, 0, 0, 1},
     {1, 2, 1, 1, KIND_DECODE, 0, 0, 0, 1},  {2, 2, 4, 1, KIND_WIDE, 4, 3, 2, 1, 2},
     {2, 1, 2, 2, KIND_WIDE, 6, 3, 2, 1, 2},  {2, 1, 2, 2, KIND_WIDE, 3, 3, 2, 1, 4},
-    {2, 2, 2, 2, KIND_WIDE, 2, 3, 2, 1, 4}};
-constexpr int kNumTileCfgs = 17;
+    {2, 2, 2, 2, KIND_WIDE, 2, 3, 2, 1, 4}, {4, 2, 2, 4, KIND_WIDE, 2, 4, 2, 1}};
+constexpr int kNumTileCfgs = 18;
 
 struct TreeSel {
     int mode;  // TREE_BLOCK or TREE_STACK
@@ -255,6 +255,10 @@ hipError_t launch_layout(int cfg, const TreeSel &t, const MfmaParams &p, int64_t
         return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 1, 4, 1, 2>(p, tiles, st);
     case 9:
         return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 3, 2, 1, 2>(p, tiles, st);
+    // 128x128 for trees deeper than configurations 5 and 8 park in the LDS
+    // (1024 leaves): a second level of pending nodes in registers
+    case 17:
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 2, 1, 4, 2, 2>(p, tiles, st);
     // Narrow tiles for 33 to 128 rows (X K-major, row-major output), the tree
     // split over wave groups (the stages per tile divided by their number):
     // 128x32 on 2 x 4 waves of 2 x 2 blocks with four stage buffers per group,

@@ -8,7 +8,8 @@ alignment and leaf count without touching memory.  Configurations: 5 to 9
 wide kernels (6: 128x64 tiles; 8: 128x128 two-leaf units; 9: three-leaf
 units), 10 to 12 decode kernels with 16, 64 and 32 columns per workgroup, 13
 and 14 the 128x32 and 64x32 wide tiles whose tree is split at its root over
-two wave groups, 15 and 16 the 64x32 and 64x64 tiles on four wave groups.
+two wave groups, 15 and 16 the 64x32 and 64x64 tiles on four wave groups,
+17 the 128x128 tiles with two register levels for the deepest trees.
 """
 import pytest
 
@@ -185,7 +186,8 @@ def test_narrow_split_tiles_need_a_power_of_two_leaf_count():
     (512, 4096, 8192, 6),      # 256 leaves, 128x64 tiles still one round
     (1024, 4096, 8192, 8),     # 256 leaves: 128x64 would hold one workgroup per unit
     (2048, 4096, 16384, 5),    # 512 leaves: two stage buffers (three do not fit the LDS)
-    (2048, 4096, 32768, 6),    # 1024 leaves: the 128x128 tiles' LDS cannot hold the tree
+    (2048, 4096, 32768, 17),   # 1024 leaves: 128x128 with a second register level
+    (512, 4096, 32768, 6),     # ... unless 128x64 tiles fit one round
 ])
 def test_mid_size_products_by_leaves_and_tiles(M, N, K, want):
     assert cfg(dg.OP_FWD, M, N, K) == want
