@@ -165,14 +165,16 @@ bool aligned16(const void *p, int64_t ld) {
 
 // The direct-to-LDS kernels take whole 64-index stages, 16-byte aligned rows
 // and, for an operand whose row index is contiguous, whole 8-row chunks.
-bool fast_ok(const Problem &pr, const TreeSel &t) {
-    return pr.out != OUT_LEAVES && t.mode == TREE_BLOCK && pr.R % 64 == 0 &&
-           aligned16(pr.x, pr.ldx) && aligned16(pr.y, pr.ldy) && (pr.xk || pr.I % 8 == 0) &&
-           (pr.yk || pr.J % 8 == 0);
+bool staged_ok(const Problem &pr) {
+    return pr.out != OUT_LEAVES && pr.R % 64 == 0 && aligned16(pr.x, pr.ldx) &&
+           aligned16(pr.y, pr.ldy) && (pr.xk || pr.I % 8 == 0) && (pr.yk || pr.J % 8 == 0);
 }
 
+bool fast_ok(const Problem &pr, const TreeSel &t) { return t.mode == TREE_BLOCK && staged_ok(pr); }
+
 // The wide kernel: the fast kernel's operand conditions and a leaf count
-// L = 2 * tb * 2^k with at least one group of 2^gl nodes of 2 * tb leaves
+// L = 2 * tb * 2^k (tb = 1, 3 or 5: the mid-split tree is the perfect tree
+// over units of tb leaves) with at least one group of 2^gl nodes of 2 * tb leaves
 // (with exactly one group, the group root is the root); a tree split at its
 // root over two or four wave groups needs units of one leaf, a K-major X, a
 // row-major output and a group of stages in each part.  `up` receives the
@@ -180,7 +182,7 @@ bool fast_ok(const Problem &pr, const TreeSel &t) {
 bool wide_ok(const Problem &pr, const TreeSel &t, const TileCfg &c, int &up) {
     const int64_t L = (pr.R + 31) / 32;
     const bool split = c.ks > 1;
-    if (!fast_ok(pr, t) || L % (2 * c.tb) != 0 ||
+    if (!staged_ok(pr) || L % (2 * c.tb) != 0 ||
         (split && (!pr.xk || c.tb != 1 || pr.out == OUT_BF16_T)))
         return false;
     const int64_t S = L / (2 * c.tb), G = int64_t(1) << c.gl;  // nodes of 2 * tb leaves
@@ -317,7 +319,7 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     }
     const int64_t t128 = ((pr.I + 127) / 128) * ((pr.J + 127) / 128);
     if (t128 >= 2 * 256)
-        for (int c : {8, 5, 9, 7, 17})  // three stage buffers with early copies if the LDS holds them
+        for (int c : {8, 5, 9, 7, 17, 18})  // three stage buffers with early copies if the LDS holds them
             if (wide_ok(pr, t, kTileCfgs[c], up))
                 return c;
     // 128x64 tiles while they fit one round, or two workgroups per compute
@@ -329,7 +331,7 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     // deeper trees than configurations 5 and 8 hold: 128x128 tiles with a
     // second register level (K = 32768, M = 2048, N = 4096: 420 TFLOP/s
     // instead of 355 on 128x64; at 512 leaves and fewer it loses to them)
-    for (int c : {8, 5, 9, 7, 17})
+    for (int c : {8, 5, 9, 7, 17, 18})
         if (wide_ok(pr, t, kTileCfgs[c], up))
             return c;
     if (wide_ok(pr, t, kTileCfgs[6], up))

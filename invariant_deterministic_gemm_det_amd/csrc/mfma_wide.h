@@ -702,7 +702,7 @@ struct WideEngine {
 template <class E, class Arith, int TB, int GL, int RU, bool EPI = false>
 struct WideTree {
     static constexpr int G = 1 << GL;
-    static_assert(TB == 1 || TB == 3, "units of one or three leaves");
+    static_assert(TB == 1 || TB == 3 || TB == 5, "units of one, three or five leaves");
     static_assert(GL >= 1, "groups of at least two stages");
     // RU >= 1: the zero-leaf step of group 0 writes the first upper slot,
     // which must then be a register (with no upper levels, no LDS slot exists).
@@ -992,6 +992,96 @@ struct WideTree {
         return finish_root(final_chain(wpack(add(c.u0, u1))));
     }
 
+    // ---- L = 5 * 2^a.  Units of five leaves, u = (x0 (+) x1) (+) (x2 (+) (x3
+    // (+) x4)); five stages (a0 a1 | b0 b1 | c0 c1 | d0 d1 | e0 e1) hold two
+    // units, (a0 (+) a1) (+) (b0 (+) (b1 (+) c0)) and (c1 (+) d0) (+) (d1 (+)
+    // (e0 (+) e1)).  With matrix-core adds the leaves one level above the
+    // deepest (a0 a1 b0, c1 d0 d1) are computed with swapped operands, so both
+    // children of every add share a layout.  The tree work of the previous
+    // super-stage and of this one's first unit is spread over the stages:
+    //   A: u1 = pcd (+) (d1 (+) (e0 (+) e1)), then leaves a0, a1;
+    //   B: the ten-leaf node u0 (+) u1 climbs, then leaves b0, b1;
+    //   C: p01 = a0 (+) a1, then leaves c0, c1;
+    //   D: u0 = p01 (+) (b0 (+) (b1 (+) c0)), then leaves d0, d1;
+    //   E: pcd = c1 (+) d0, then leaves e0, e1.
+    struct Carry5 {
+        P a0, a1, b0, b1, c0, c1, d0, d1, e0, e1, p01, u0, u1, pcd;
+    };
+
+    template <int U>
+    __device__ __forceinline__ void stage5(int t, Carry5 &c) {
+        constexpr bool T = Arith::kTransposes;
+        const int s = 5 * (t * G + U);
+        e.template begin<U & 1>(s);
+        c.u1 = wpack(add(c.pcd, wpack(add(c.d1, wpack(add(c.e0, c.e1))))));
+        e.template read<1>();
+        c.a0 = e.template leaf<0, T>();
+        c.a1 = e.template leaf<1, T>();
+        pin_p(c.u1);
+        pin_p(c.a0);
+        pin_p(c.a1);
+        e.template begin<(U + 1) & 1>(s + 1);
+        if constexpr (U == 0)
+            climb_low<G - 1, 0>(wpack(add(c.u0, c.u1)), t > 0 ? t - 1 : 0);
+        else
+            climb_low<U - 1, 0>(wpack(add(c.u0, c.u1)), t);
+        e.template read<1>();
+        c.b0 = e.template leaf<0, T>();
+        c.b1 = e.template leaf<1, false>();
+        pin_p(c.b0);
+        pin_p(c.b1);
+        e.template begin<U & 1>(s + 2);
+        c.p01 = wpack(add(c.a0, c.a1));
+        e.template read<1>();
+        c.c0 = e.template leaf<0, false>();
+        c.c1 = e.template leaf<1, T>();
+        pin_p(c.p01);
+        pin_p(c.c0);
+        pin_p(c.c1);
+        e.template begin<(U + 1) & 1>(s + 3);
+        c.u0 = wpack(add(c.p01, wpack(add(c.b0, wpack(add(c.b1, c.c0))))));
+        e.template read<1>();
+        c.d0 = e.template leaf<0, T>();
+        c.d1 = e.template leaf<1, T>();
+        pin_p(c.u0);
+        pin_p(c.d0);
+        pin_p(c.d1);
+        e.template begin<U & 1>(s + 4);
+        c.pcd = wpack(add(c.c1, c.d0));
+        e.template read<1>();
+        c.e0 = e.template leaf<0, false>();
+        c.e1 = e.template leaf<1, false>();
+        pin_p(c.pcd);
+        pin_p(c.e0);
+        pin_p(c.e1);
+        if constexpr (U + 1 < G)
+            stage5<U + 1>(t, c);
+    }
+
+    __device__ __forceinline__ bool run5() {
+        const int T = e.S / (5 * G);
+        e.prologue();
+        Carry5 c;
+        zero_p(c.a0, c.a1, c.b0, c.b1, c.c0, c.c1, c.d0);
+        zero_p(c.d1, c.e0, c.e1, c.p01, c.u0, c.u1, c.pcd);
+        for (int t = 0; t < T; ++t)
+            stage5<0>(t, c);
+        const P u1 = wpack(add(c.pcd, wpack(add(c.d1, wpack(add(c.e0, c.e1))))));
+        return finish_root(final_chain(wpack(add(c.u0, u1))));
+    }
+
+    template <class... Ps>
+    __device__ __forceinline__ static void zero_p(Ps &...xs) {
+        (zero_one(xs), ...);
+    }
+    __device__ __forceinline__ static void zero_one(P &x) {
+#pragma unroll
+        for (int a = 0; a < E::kFM; ++a)
+#pragma unroll
+            for (int b = 0; b < E::kFN; ++b)
+                x.w[a][b] = u32x2{0u, 0u};
+    }
+
     // Requires S = e.S = G * 2^nup (units of one leaf).  Computes the root
     // (unrounded fp32, in the layout of its parity) without storing it.
     __device__ __forceinline__ F run_root() {
@@ -1017,6 +1107,8 @@ struct WideTree {
     __device__ __forceinline__ bool run() {
         if constexpr (TB == 3)
             return run3();
+        else if constexpr (TB == 5)
+            return run5();
         else
             return finish_root(run_root());
     }

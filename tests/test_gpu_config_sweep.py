@@ -27,10 +27,10 @@ GENERAL_CFG = 2
 # Row counts around the decode limits (16, 32, 64, 128 rows) and the tile
 # heights; column counts around the 16-, 32-, 64- and 128-column tiles,
 # ragged ones included; reduction lengths with 1 to 192 leaves, powers of two,
-# 3 * 2^a and others, and two that are not whole leaves.
+# 3, 5 and 7 times 2^a and others, and two that are not whole leaves.
 ROWS = [1, 2, 3, 15, 16, 17, 31, 32, 33, 48, 63, 64, 65, 96, 100, 127, 128, 129, 200, 256, 300]
 COLS = [8, 16, 24, 40, 64, 100, 128, 136, 256, 392, 512, 1000, 1024, 2048, 2056, 6144]
-REDS = [32, 64, 96, 160, 224, 256, 288, 512, 1024, 1536, 2048, 4096, 4128, 6144]
+REDS = [32, 64, 96, 160, 224, 256, 288, 512, 1024, 1536, 2048, 4096, 4128, 5120, 6144, 7168]
 OPS = ["fwd", "fwd_rhs_transposed", "fwd_fp32", "da", "db", "db_transposed"]
 PROBLEMS = 240
 
