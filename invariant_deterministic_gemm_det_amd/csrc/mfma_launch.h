@@ -37,7 +37,7 @@ struct TileCfg {
     int fm, fn, wm, wn;
     int kind;
     int nbuf, gl, ru;  // wide kernel: stage buffers, static group levels, register levels
-    int tb;            // wide kernel: leaves per unit (1, 3 or 5)
+    int tb;            // wide kernel: leaves per unit (1, 3, 5 or 7)
     int ks;            // wide kernel: wave groups splitting the tree at its root (0 or 1: none, 2)
     int bm() const { return 16 * fm * wm; }
     int bn() const { return 16 * fn * wn; }
@@ -65,8 +65,9 @@ constexpr TileCfg kTileCfgs[] = {
     {1, 2, 1, 1, KIND_DECODE, 0, 0, 0, 1},  {2, 2, 4, 1, KIND_WIDE, 4, 3, 2, 1, 2},
     {2, 1, 2, 2, KIND_WIDE, 6, 3, 2, 1, 2},  {2, 1, 2, 2, KIND_WIDE, 3, 3, 2, 1, 4},
     {2, 2, 2, 2, KIND_WIDE, 2, 3, 2, 1, 4}, {4, 2, 2, 4, KIND_WIDE, 2, 4, 2, 1},
-    {4, 2, 2, 4, KIND_WIDE, 3, 3, 1, 5}};
-constexpr int kNumTileCfgs = 19;
+    {4, 2, 2, 4, KIND_WIDE, 3, 3, 1, 5},    {4, 2, 2, 4, KIND_WIDE, 3, 2, 1, 7},
+    {4, 2, 2, 4, KIND_WIDE, 2, 2, 1, 7}};
+constexpr int kNumTileCfgs = 21;
 
 struct TreeSel {
     int mode;  // TREE_BLOCK or TREE_STACK
@@ -264,6 +265,13 @@ hipError_t launch_layout(int cfg, const TreeSel &t, const MfmaParams &p, int64_t
     // per pair of units
     case 18:
         return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 5, 3, 1, 2>(p, tiles, st);
+    // L = 7 * 2^a (K = 7168, 14336, 28672): units of seven leaves, seven
+    // stages per pair of units; two stage buffers where the parked levels of
+    // the deepest trees (L = 896) leave no room for three
+    case 19:
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 7, 2, 1, 2>(p, tiles, st);
+    case 20:
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 2, 7, 2, 1, 2>(p, tiles, st);
     // Narrow tiles for 33 to 128 rows (X K-major, row-major output), the tree
     // split over wave groups (the stages per tile divided by their number):
     // 128x32 on 2 x 4 waves of 2 x 2 blocks with four stage buffers per group,

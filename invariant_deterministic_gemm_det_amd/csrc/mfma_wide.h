@@ -702,7 +702,8 @@ struct WideEngine {
 template <class E, class Arith, int TB, int GL, int RU, bool EPI = false>
 struct WideTree {
     static constexpr int G = 1 << GL;
-    static_assert(TB == 1 || TB == 3 || TB == 5, "units of one, three or five leaves");
+    static_assert(TB == 1 || TB == 3 || TB == 5 || TB == 7, "units of one, three, five or seven leaves");
+    static_assert(TB != 7 || GL <= 2, "seven-leaf groups of at most four pairs of units");
     static_assert(GL >= 1, "groups of at least two stages");
     // RU >= 1: the zero-leaf step of group 0 writes the first upper slot,
     // which must then be a register (with no upper levels, no LDS slot exists).
@@ -1070,6 +1071,102 @@ struct WideTree {
         return finish_root(final_chain(wpack(add(c.u0, u1))));
     }
 
+    // ---- L = 7 * 2^a.  Units of seven leaves, u = (x0 (+) (x1 (+) x2)) (+)
+    // ((x3 (+) x4) (+) (x5 (+) x6)); seven stages (a0 a1 | ... | g0 g1) hold
+    // two units, (a0 (+) (a1 (+) b0)) (+) ((b1 (+) c0) (+) (c1 (+) d0)) and
+    // (d1 (+) (e0 (+) e1)) (+) ((f0 (+) f1) (+) (g0 (+) g1)); with matrix-core
+    // adds a0 and d1 (one level above the deepest) use swapped operands.
+    //   A: u1 = n (+) (o (+) (g0 (+) g1)), then leaves a0, a1;
+    //   B: the fourteen-leaf node u0 (+) u1 climbs, then leaves b0, b1;
+    //   C: y = a0 (+) (a1 (+) b0), then leaves c0, c1;
+    //   D: z = b1 (+) c0, then leaves d0, d1;
+    //   E: u0 = y (+) (z (+) (c1 (+) d0)), then leaves e0, e1;
+    //   F: n = d1 (+) (e0 (+) e1), then leaves f0, f1;
+    //   G: o = f0 (+) f1, then leaves g0, g1.
+    // A group is four pairs of units at most (GL <= 2): the recomputation with
+    // element-wise adds is a called function, and at eight pairs its code
+    // outgrew the range of a short branch; the compiler's long branches then
+    // reused the registers of the return address, and the call never returned.
+    struct Carry7 {
+        P a0, a1, b0, b1, c0, c1, d0, d1, e0, e1, f0, f1, g0, g1, y, z, u0, u1, n, o;
+    };
+    template <int U>
+    __device__ __forceinline__ void stage7(int t, Carry7 &c) {
+        constexpr bool T = Arith::kTransposes;
+        const int s = 7 * (t * G + U);
+        e.template begin<U & 1>(s);
+        c.u1 = wpack(add(c.n, wpack(add(c.o, wpack(add(c.g0, c.g1))))));
+        e.template read<1>();
+        c.a0 = e.template leaf<0, T>();
+        c.a1 = e.template leaf<1, false>();
+        pin_p(c.u1);
+        pin_p(c.a0);
+        pin_p(c.a1);
+        e.template begin<(U + 1) & 1>(s + 1);
+        if constexpr (U == 0)
+            climb_low<G - 1, 0>(wpack(add(c.u0, c.u1)), t > 0 ? t - 1 : 0);
+        else
+            climb_low<U - 1, 0>(wpack(add(c.u0, c.u1)), t);
+        e.template read<1>();
+        c.b0 = e.template leaf<0, false>();
+        c.b1 = e.template leaf<1, false>();
+        pin_p(c.b0);
+        pin_p(c.b1);
+        e.template begin<U & 1>(s + 2);
+        c.y = wpack(add(c.a0, wpack(add(c.a1, c.b0))));
+        e.template read<1>();
+        c.c0 = e.template leaf<0, false>();
+        c.c1 = e.template leaf<1, false>();
+        pin_p(c.y);
+        pin_p(c.c0);
+        pin_p(c.c1);
+        e.template begin<(U + 1) & 1>(s + 3);
+        c.z = wpack(add(c.b1, c.c0));
+        e.template read<1>();
+        c.d0 = e.template leaf<0, false>();
+        c.d1 = e.template leaf<1, T>();
+        pin_p(c.z);
+        pin_p(c.d0);
+        pin_p(c.d1);
+        e.template begin<U & 1>(s + 4);
+        c.u0 = wpack(add(c.y, wpack(add(c.z, wpack(add(c.c1, c.d0))))));
+        e.template read<1>();
+        c.e0 = e.template leaf<0, false>();
+        c.e1 = e.template leaf<1, false>();
+        pin_p(c.u0);
+        pin_p(c.e0);
+        pin_p(c.e1);
+        e.template begin<(U + 1) & 1>(s + 5);
+        c.n = wpack(add(c.d1, wpack(add(c.e0, c.e1))));
+        e.template read<1>();
+        c.f0 = e.template leaf<0, false>();
+        c.f1 = e.template leaf<1, false>();
+        pin_p(c.n);
+        pin_p(c.f0);
+        pin_p(c.f1);
+        e.template begin<U & 1>(s + 6);
+        c.o = wpack(add(c.f0, c.f1));
+        e.template read<1>();
+        c.g0 = e.template leaf<0, false>();
+        c.g1 = e.template leaf<1, false>();
+        pin_p(c.o);
+        pin_p(c.g0);
+        pin_p(c.g1);
+        if constexpr (U + 1 < G)
+            stage7<U + 1>(t, c);
+    }
+    __device__ __forceinline__ bool run7() {
+        const int T = e.S / (7 * G);
+        e.prologue();
+        Carry7 c;
+        zero_p(c.a0, c.a1, c.b0, c.b1, c.c0, c.c1, c.d0, c.d1, c.e0, c.e1);
+        zero_p(c.f0, c.f1, c.g0, c.g1, c.y, c.z, c.u0, c.u1, c.n, c.o);
+        for (int t = 0; t < T; ++t)
+            stage7<0>(t, c);
+        const P u1 = wpack(add(c.n, wpack(add(c.o, wpack(add(c.g0, c.g1))))));
+        return finish_root(final_chain(wpack(add(c.u0, u1))));
+    }
+
     template <class... Ps>
     __device__ __forceinline__ static void zero_p(Ps &...xs) {
         (zero_one(xs), ...);
@@ -1109,6 +1206,8 @@ struct WideTree {
             return run3();
         else if constexpr (TB == 5)
             return run5();
+        else if constexpr (TB == 7)
+            return run7();
         else
             return finish_root(run_root());
     }

@@ -390,7 +390,7 @@ def test_mfma_tile_configs_identical(dev, K):
 FAST_SHAPES = [(200, 192, 256), (256, 136, 768), (320, 256, 4096), (128, 64, 12288),
                (72, 64, 32768), (512, 512, 1024), (264, 392, 8192), (768, 384, 1536),
                (384, 768, 6144)]
-GENERAL_CFG, FAST_CFGS = 2, (3, 4, 5, 6, 7, 8, 9, 13, 14, 15, 16, 17, 18)
+GENERAL_CFG, FAST_CFGS = 2, (3, 4, 5, 6, 7, 8, 9, 13, 14, 15, 16, 17, 18, 19, 20)
 
 
 def _six_forced(cfg, A, B, dC):
@@ -512,24 +512,18 @@ def test_errors_leave_output_untouched(dev):
     assert np.array_equal(roots, bits(got))
 
 
-# Leaf counts L = 5 * 2^a (and 7 * 2^a, whose units are not in the library):
-# the mid-split tree is the perfect tree over units of five leaves, which the
-# wide kernel evaluates in configuration 18 (five stages per pair of units).  Each
+# Leaf counts L = 5 * 2^a and 7 * 2^a: the mid-split tree is the perfect tree
+# over units of five or seven leaves, which the wide kernel evaluates in
+# configurations 18, 19 and 20 (five or seven stages per pair of units).  Each
 # reduction (K for the forward family, N for da, M for db) with such a leaf
 # count, ragged tiles included, against the general kernel, bit for bit.
-SEVEN_LEAF_OFF = pytest.mark.skip(
-    reason="units of seven leaves (L = 7 * 2^a) are not in the library: with non-finite "
-           "inputs their run did not finish, cause not found; these products run on the "
-           "general kernel")
-
-
 @pytest.mark.parametrize("M,N,K", [
     (256, 384, 5120),     # L = 160 over K
-    pytest.param(200, 136, 7168, marks=SEVEN_LEAF_OFF),    # L = 224 over K, ragged
-    pytest.param(384, 256, 14336, marks=SEVEN_LEAF_OFF),   # L = 448
+    (200, 136, 7168),     # L = 224 over K, ragged rows and columns
+    (384, 256, 14336),    # L = 448
     (256, 256, 20480),    # L = 640: upper levels parked in LDS
-    pytest.param(128, 256, 28672, marks=SEVEN_LEAF_OFF),   # L = 896
-    pytest.param(256, 7168, 320, marks=SEVEN_LEAF_OFF),    # da: L = 224 over N
+    (128, 256, 28672),    # L = 896: two stage buffers (configuration 20)
+    (256, 7168, 320),     # da: L = 224 over N
     (5120, 256, 384),     # db: L = 160 over M
     (256, 10240, 320),    # da: L = 320 over N
 ])
@@ -538,7 +532,7 @@ def test_wide_kernel_five_and_seven_leaf_units(dev, M, N, K):
     A, B, dC = [t.to(dev) for t in _inputs(M, N, K, 970 + K + M, sigma=0.02)]
     ref = _six_forced(GENERAL_CFG, A, B, dC)
     ran = 0
-    for cfg in (18,):
+    for cfg in (18, 19, 20):
         got = _six_forced(cfg, A, B, dC)
         for op, g in got.items():
             if g is None:
@@ -555,7 +549,7 @@ def test_wide_kernel_five_and_seven_leaf_units(dev, M, N, K):
 # The wide kernels' tree adds run on the matrix core, where one non-finite node
 # spoils the other sums of its row; such tiles are recomputed with element-wise
 # adds.  Inf and NaN inputs must give the general kernel's bits.
-@pytest.mark.parametrize("K", [1024, 1536, 5120, pytest.param(7168, marks=SEVEN_LEAF_OFF)])
+@pytest.mark.parametrize("K", [1024, 1536, 5120, 7168])
 def test_wide_kernel_nonfinite_inputs(dev, K):
     say("wide kernels, non-finite inputs vs general kernel", K)
     M, N = 1024, 768
@@ -567,7 +561,7 @@ def test_wide_kernel_nonfinite_inputs(dev, K):
     Ad, Bd, dCd = A.to(dev), B.to(dev), dC.to(dev)
     ref = _six_forced(GENERAL_CFG, Ad, Bd, dCd)
     ran = 0
-    for cfg in (5, 6, 7, 8, 9, 13, 14, 15, 16, 17, 18):
+    for cfg in (5, 6, 7, 8, 9, 13, 14, 15, 16, 17, 18, 19, 20):
         got = _six_forced(cfg, Ad, Bd, dCd)
         for op, g in got.items():
             if g is None:
