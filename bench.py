@@ -591,7 +591,8 @@ def configs_leg(dev, reps=5):
     model at 8192 rows (gate+up K = 4096, N = 24576; down K = 12288, N = 4096,
     384 leaves), the backward at M = 8192, K = N = 4096 (dA; dB and its
     [N,K] form, reduction depth 8192), the LM head at 4096 rows (N = 151936,
-    bf16 and fp32 out) and the depth cap (K = 32768, N = 4096, 2048 rows)."""
+    bf16 and fp32 out), two MLP down projections with other leaf counts
+    (K = 14336 and 11008) and the depth cap (K = 32768, N = 4096, 2048 rows)."""
     import torch
     import det_workloads as Wk
     import invariant_deterministic_gemm_det_amd as dg
@@ -657,6 +658,19 @@ def configs_leg(dev, reps=5):
         cfg_of(dg.OP_FWD_FP32, Xl, K, Wl, N, of, N, M, N, K))
     del Xl, Wl, of
 
+    # MLP down projections whose leaf counts are not 2^a or 3 * 2^a: an
+    # 8B-class model's (K = 14336, L = 448 = 7 * 64: units of seven leaves) and
+    # a 7B-class one's (K = 11008, L = 344 = 43 * 8: no unit schedule, the
+    # general kernel)
+    for kd, name in ((14336, "MLP down, K = 14336 (L = 448, seven-leaf units)"),
+                     (11008, "MLP down, K = 11008 (L = 344, general kernel)")):
+        Hd = Wk.randn_bf16((8192, kd), 1.0, 3005, dev)
+        Wdd = Wk.randn_bf16((kd, 4096), 0.02, 3006, dev)
+        od = torch.empty((8192, 4096), dtype=torch.bfloat16, device=dev)
+        add(name, [8192, 4096, kd], 2.0 * 8192 * 4096 * kd,
+            lambda: dg.det_gemm_fwd(Hd, Wdd, out=od), cfg_of(dg.OP_FWD, Hd, kd, Wdd, 4096, od, 4096, 8192, 4096, kd))
+        del Hd, Wdd, od
+
     Ad, Bd = Wk.deep_inputs(dev)
     M, K, N = Ad.shape[0], Ad.shape[1], Bd.shape[1]
     od = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -666,7 +680,7 @@ def configs_leg(dev, reps=5):
     torch.cuda.empty_cache()
     return {"workload": "the other transformer-shaped products, inputs seeded as the parity "
                         "tests' (MLP 3001-3004, backward 4001-4003, LM head 5001-5002, depth cap "
-                        "5003-5004), resident in HBM",
+                        "5003-5004; the two other MLP down projections 3005-3006), resident in HBM",
             "timing": f"median of {reps} launches after one warm-up, HIP events", "rows": rows}
 
 
