@@ -37,7 +37,7 @@ struct TileCfg {
     int fm, fn, wm, wn;
     int kind;
     int nbuf, gl, ru;  // wide kernel: stage buffers, static group levels, register levels
-    int tb;            // wide kernel: leaves per unit (1, 3, 5 or 7)
+    int tb;            // wide kernel: leaves per unit (1 or odd)
     int ks;            // wide kernel: wave groups splitting the tree at its root (0 or 1: none, 2)
     int bm() const { return 16 * fm * wm; }
     int bn() const { return 16 * fn * wn; }
@@ -66,8 +66,9 @@ constexpr TileCfg kTileCfgs[] = {
     {2, 1, 2, 2, KIND_WIDE, 6, 3, 2, 1, 2},  {2, 1, 2, 2, KIND_WIDE, 3, 3, 2, 1, 4},
     {2, 2, 2, 2, KIND_WIDE, 2, 3, 2, 1, 4}, {4, 2, 2, 4, KIND_WIDE, 2, 4, 2, 1},
     {4, 2, 2, 4, KIND_WIDE, 3, 3, 1, 5},    {4, 2, 2, 4, KIND_WIDE, 3, 2, 1, 7},
-    {4, 2, 2, 4, KIND_WIDE, 2, 2, 1, 7}};
-constexpr int kNumTileCfgs = 21;
+    {4, 2, 2, 4, KIND_WIDE, 2, 2, 1, 7},    {4, 2, 2, 4, KIND_WIDE, 3, 0, 1, 43},
+    {4, 2, 2, 4, KIND_WIDE, 3, 0, 1, 27}};
+constexpr int kNumTileCfgs = 23;
 
 struct TreeSel {
     int mode;  // TREE_BLOCK or TREE_STACK
@@ -272,6 +273,12 @@ hipError_t launch_layout(int cfg, const TreeSel &t, const MfmaParams &p, int64_t
         return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 7, 2, 1, 2>(p, tiles, st);
     case 20:
         return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 2, 7, 2, 1, 2>(p, tiles, st);
+    // L = 43 * 2^a (K = 11008, 22016) and 27 * 2^a (K = 13824, 27648): the
+    // unit trees walked with a stack of static register slots
+    case 21:
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 43, 0, 1, 2>(p, tiles, st);
+    case 22:
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 27, 0, 1, 2>(p, tiles, st);
     // Narrow tiles for 33 to 128 rows (X K-major, row-major output), the tree
     // split over wave groups (the stages per tile divided by their number):
     // 128x32 on 2 x 4 waves of 2 x 2 blocks with four stage buffers per group,

@@ -702,9 +702,10 @@ struct WideEngine {
 template <class E, class Arith, int TB, int GL, int RU, bool EPI = false>
 struct WideTree {
     static constexpr int G = 1 << GL;
-    static_assert(TB == 1 || TB == 3 || TB == 5 || TB == 7, "units of one, three, five or seven leaves");
+    static_assert(TB == 1 || (TB % 2 == 1 && TB <= 255), "units of one leaf or of an odd count");
     static_assert(TB != 7 || GL <= 2, "seven-leaf groups of at most four pairs of units");
-    static_assert(GL >= 1, "groups of at least two stages");
+    static_assert(TB <= 7 || GL == 0, "generic units: one pair of units per group");
+    static_assert(GL >= 1 || TB > 7, "groups of at least two stages");
     // RU >= 1: the zero-leaf step of group 0 writes the first upper slot,
     // which must then be a register (with no upper levels, no LDS slot exists).
     static_assert(RU >= 1, "the first upper level is held in registers");
@@ -1167,6 +1168,144 @@ struct WideTree {
         return finish_root(final_chain(wpack(add(c.u0, u1))));
     }
 
+    // ---- L = m * 2^a for another odd m (TB = m; 43 for K = 11008, 27 for
+    // K = 13824), one pair of units per group (GL = 0: the recomputation with
+    // element-wise adds is a called function, whose code must stay within
+    // the range of a short branch).  The mid-split tree over the m leaves of a unit is walked in
+    // post-order with its pending left siblings on a stack of static register
+    // slots: the tree is fixed by m, so where each leaf stands (its depth,
+    // the adds that follow it, the stack height before it) is computed at
+    // compile time.  m stages hold two units (leaves j = 0 .. 2m - 1 of the
+    // pair: unit j / m, leaf j % m).  A leaf at depth d of a unit of height h
+    // is computed with swapped operands when h - d is odd (matrix-core adds),
+    // so both children of every add share a layout.  Stage k of a pair opens
+    // with the tree work of the previous stage's two leaves (for k = 0: the
+    // previous pair's last two, which close its second unit, whose node with
+    // the first climbs), then computes its own two leaves.
+    static constexpr int unit_depth(int t) {
+        int lo = 0, hi = TB, d = 0;
+        while (hi - lo > 1) {
+            const int mid = lo + (hi - lo) / 2;
+            if (t < mid)
+                hi = mid;
+            else
+                lo = mid;
+            ++d;
+        }
+        return d;
+    }
+    static constexpr int unit_merges(int t) {   // inner nodes whose range ends at t + 1
+        int lo = 0, hi = TB, m = 0;
+        while (hi - lo > 1) {
+            if (hi == t + 1)
+                ++m;
+            const int mid = lo + (hi - lo) / 2;
+            if (t < mid)
+                hi = mid;
+            else
+                lo = mid;
+        }
+        return m;
+    }
+    static constexpr int unit_height() {
+        int h = 0;
+        for (int t = 0; t < TB; ++t)
+            h = unit_depth(t) > h ? unit_depth(t) : h;
+        return h;
+    }
+    static constexpr int unit_sp(int t) {   // pending nodes before leaf t
+        int sp = 0;
+        for (int q = 0; q < t; ++q)
+            sp += 1 - unit_merges(q);
+        return sp;
+    }
+    static constexpr bool unit_swap(int t) {
+        return Arith::kTransposes && ((unit_height() - unit_depth(t)) & 1) != 0;
+    }
+    struct CarryU {
+        P cur0, cur1, r0, st0, st1, st2, st3, st4, st5, st6, st7;
+    };
+    template <int D>
+    __device__ __forceinline__ static P &slot(CarryU &c) {
+        static_assert(D >= 0 && D < 8, "unit stacks of at most eight pending nodes");
+        if constexpr (D == 0) return c.st0;
+        else if constexpr (D == 1) return c.st1;
+        else if constexpr (D == 2) return c.st2;
+        else if constexpr (D == 3) return c.st3;
+        else if constexpr (D == 4) return c.st4;
+        else if constexpr (D == 5) return c.st5;
+        else if constexpr (D == 6) return c.st6;
+        else return c.st7;
+    }
+    // The adds that follow leaf t: the I-th pops the pending node at height
+    // SP - 1 - I (its left sibling at that moment).
+    template <int SP, int I, int NM>
+    __device__ __forceinline__ P unit_pops(CarryU &c, const P &x) {
+        if constexpr (I == NM)
+            return x;
+        else
+            return unit_pops<SP, I + 1, NM>(c, wpack(add(slot<SP - 1 - I>(c), x)));
+    }
+    // Leaf j of a pair (packed, in its layout): its adds, then it waits on the
+    // stack, or it is a unit's root (the first unit's in r0, the second's left
+    // in x).
+    template <int J>
+    __device__ __forceinline__ void unit_leaf(CarryU &c, P &x) {
+        constexpr int t = J % TB;
+        constexpr int sp = unit_sp(t), nm = unit_merges(t);
+        const P y = unit_pops<sp, 0, nm>(c, x);
+        if constexpr (t + 1 < TB) {
+            slot<sp - nm>(c) = y;
+            pin_p(slot<sp - nm>(c));
+        } else if constexpr (J < TB) {
+            c.r0 = y;
+            pin_p(c.r0);
+        } else {
+            x = y;
+        }
+    }
+    template <int U, int K>
+    __device__ __forceinline__ void stageU(int t, CarryU &c) {
+        const int s = TB * (t * G + U) + K;
+        e.template begin<K & 1>(s);
+        if constexpr (K == 0) {
+            unit_leaf<2 * TB - 2>(c, c.cur0);
+            P r1 = c.cur1;
+            unit_leaf<2 * TB - 1>(c, r1);
+            if constexpr (U == 0)
+                climb_low<G - 1, 0>(wpack(add(c.r0, r1)), t > 0 ? t - 1 : 0);
+            else
+                climb_low<U - 1, 0>(wpack(add(c.r0, r1)), t);
+        } else {
+            unit_leaf<2 * K - 2>(c, c.cur0);
+            unit_leaf<2 * K - 1>(c, c.cur1);
+        }
+        e.template read<1>();
+        c.cur0 = e.template leaf<0, unit_swap((2 * K) % TB)>();
+        c.cur1 = e.template leaf<1, unit_swap((2 * K + 1) % TB)>();
+        pin_p(c.cur0);
+        pin_p(c.cur1);
+        if constexpr (K + 1 < TB)
+            stageU<U, K + 1>(t, c);
+        else if constexpr (U + 1 < G)
+            stageU<U + 1, 0>(t, c);
+    }
+    __device__ __forceinline__ bool runU() {
+        const int T = e.S / (TB * G);
+        e.prologue();
+        CarryU c;
+        zero_p(c.cur0, c.cur1, c.r0, c.st0, c.st1, c.st2, c.st3, c.st4, c.st5, c.st6, c.st7);
+        for (int t = 0; t < T; ++t)
+            stageU<0, 0>(t, c);
+        unit_leaf<2 * TB - 2>(c, c.cur0);
+        P r1 = c.cur1;
+        unit_leaf<2 * TB - 1>(c, r1);
+        // one pair per group: the pair's node is the group root, which climbs
+        // as a right child up to the root
+        const F y = add(c.r0, r1);
+        return finish_root(nup > 0 ? final_up<0>(wpack(y), y) : y);
+    }
+
     template <class... Ps>
     __device__ __forceinline__ static void zero_p(Ps &...xs) {
         (zero_one(xs), ...);
@@ -1208,6 +1347,8 @@ struct WideTree {
             return run5();
         else if constexpr (TB == 7)
             return run7();
+        else if constexpr (TB > 7)
+            return runU();
         else
             return finish_root(run_root());
     }

@@ -390,7 +390,7 @@ def test_mfma_tile_configs_identical(dev, K):
 FAST_SHAPES = [(200, 192, 256), (256, 136, 768), (320, 256, 4096), (128, 64, 12288),
                (72, 64, 32768), (512, 512, 1024), (264, 392, 8192), (768, 384, 1536),
                (384, 768, 6144)]
-GENERAL_CFG, FAST_CFGS = 2, (3, 4, 5, 6, 7, 8, 9, 13, 14, 15, 16, 17, 18, 19, 20)
+GENERAL_CFG, FAST_CFGS = 2, (3, 4, 5, 6, 7, 8, 9, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22)
 
 
 def _six_forced(cfg, A, B, dC):
@@ -512,9 +512,10 @@ def test_errors_leave_output_untouched(dev):
     assert np.array_equal(roots, bits(got))
 
 
-# Leaf counts L = 5 * 2^a and 7 * 2^a: the mid-split tree is the perfect tree
-# over units of five or seven leaves, which the wide kernel evaluates in
-# configurations 18, 19 and 20 (five or seven stages per pair of units).  Each
+# Leaf counts L = m * 2^a for m = 5, 7, 27, 43: the mid-split tree is the
+# perfect tree over units of m leaves, which the wide kernel evaluates in
+# configurations 18 to 22 (m stages per pair of units; 27 and 43 walk each
+# unit's tree with a stack of static register slots).  Each
 # reduction (K for the forward family, N for da, M for db) with such a leaf
 # count, ragged tiles included, against the general kernel, bit for bit.
 @pytest.mark.parametrize("M,N,K", [
@@ -526,13 +527,18 @@ def test_errors_leave_output_untouched(dev):
     (256, 7168, 320),     # da: L = 224 over N
     (5120, 256, 384),     # db: L = 160 over M
     (256, 10240, 320),    # da: L = 320 over N
+    (256, 384, 11008),    # L = 344 = 43 * 8: units of 43 leaves (configuration 21)
+    (200, 136, 13824),    # L = 432 = 27 * 16: units of 27 leaves (configuration 22)
+    (256, 256, 22016),    # L = 688 = 43 * 16: upper levels parked in LDS
+    (256, 11008, 320),    # da: L = 344 over N
+    (11008, 256, 384),    # db: L = 344 over M
 ])
 def test_wide_kernel_five_and_seven_leaf_units(dev, M, N, K):
     say("wide kernel, units of five and seven leaves vs general kernel", M, N, K)
     A, B, dC = [t.to(dev) for t in _inputs(M, N, K, 970 + K + M, sigma=0.02)]
     ref = _six_forced(GENERAL_CFG, A, B, dC)
     ran = 0
-    for cfg in (18, 19, 20):
+    for cfg in (18, 19, 20, 21, 22):
         got = _six_forced(cfg, A, B, dC)
         for op, g in got.items():
             if g is None:
@@ -549,7 +555,7 @@ def test_wide_kernel_five_and_seven_leaf_units(dev, M, N, K):
 # The wide kernels' tree adds run on the matrix core, where one non-finite node
 # spoils the other sums of its row; such tiles are recomputed with element-wise
 # adds.  Inf and NaN inputs must give the general kernel's bits.
-@pytest.mark.parametrize("K", [1024, 1536, 5120, 7168])
+@pytest.mark.parametrize("K", [1024, 1536, 5120, 7168, 11008, 13824])
 def test_wide_kernel_nonfinite_inputs(dev, K):
     say("wide kernels, non-finite inputs vs general kernel", K)
     M, N = 1024, 768
@@ -561,7 +567,7 @@ def test_wide_kernel_nonfinite_inputs(dev, K):
     Ad, Bd, dCd = A.to(dev), B.to(dev), dC.to(dev)
     ref = _six_forced(GENERAL_CFG, Ad, Bd, dCd)
     ran = 0
-    for cfg in (5, 6, 7, 8, 9, 13, 14, 15, 16, 17, 18, 19, 20):
+    for cfg in (5, 6, 7, 8, 9, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22):
         got = _six_forced(cfg, Ad, Bd, dCd)
         for op, g in got.items():
             if g is None:
