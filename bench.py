@@ -660,10 +660,9 @@ def configs_leg(dev, reps=5):
 
     # MLP down projections whose leaf counts are not 2^a or 3 * 2^a: an
     # 8B-class model's (K = 14336, L = 448 = 7 * 64: units of seven leaves) and
-    # a 7B-class one's (K = 11008, L = 344 = 43 * 8: no unit schedule, the
-    # general kernel)
+    # a 7B-class one's (K = 11008, L = 344 = 43 * 8: units of 43 leaves)
     for kd, name in ((14336, "MLP down, K = 14336 (L = 448, seven-leaf units)"),
-                     (11008, "MLP down, K = 11008 (L = 344, general kernel)")):
+                     (11008, "MLP down, K = 11008 (L = 344, 43-leaf units)")):
         Hd = Wk.randn_bf16((8192, kd), 1.0, 3005, dev)
         Wdd = Wk.randn_bf16((kd, 4096), 0.02, 3006, dev)
         od = torch.empty((8192, 4096), dtype=torch.bfloat16, device=dev)
