@@ -9,7 +9,8 @@ wide kernels (6: 128x64 tiles; 8: 128x128 two-leaf units; 9: three-leaf
 units), 10 to 12 decode kernels with 16, 64 and 32 columns per workgroup, 13
 and 14 the 128x32 and 64x32 wide tiles whose tree is split at its root over
 two wave groups, 15 and 16 the 64x32 and 64x64 tiles on four wave groups,
-17 the 128x128 tiles with two register levels for the deepest trees.
+17 the 128x128 tiles with two register levels for the deepest trees, 18 to
+22 the 128x128 tiles over units of 5, 7, 43 and 27 leaves.
 """
 import pytest
 
@@ -191,3 +192,19 @@ def test_narrow_split_tiles_need_a_power_of_two_leaf_count():
 ])
 def test_mid_size_products_by_leaves_and_tiles(M, N, K, want):
     assert cfg(dg.OP_FWD, M, N, K) == want
+
+
+@pytest.mark.parametrize("K,want", [
+    (5120, 18),     # L = 160 = 5 * 32: five-leaf units
+    (10240, 18),
+    (7168, 19),     # L = 224 = 7 * 32: seven-leaf units
+    (14336, 19),
+    (28672, 20),    # L = 896: seven-leaf units on two stage buffers
+    (11008, 21),    # L = 344 = 43 * 8: 43-leaf units
+    (22016, 21),
+    (13824, 22),    # L = 432 = 27 * 16: 27-leaf units
+    (27648, 2),     # L = 864 = 27 * 32: its parked levels exceed the LDS; general kernel
+    (4128, 2),      # L = 129: no unit schedule
+])
+def test_unit_schedules_by_leaf_count(K, want):
+    assert cfg(dg.OP_FWD, 4096, 4096, K) == want
