@@ -67,8 +67,9 @@ constexpr TileCfg kTileCfgs[] = {
     {2, 2, 2, 2, KIND_WIDE, 2, 3, 2, 1, 4}, {4, 2, 2, 4, KIND_WIDE, 2, 4, 2, 1},
     {4, 2, 2, 4, KIND_WIDE, 3, 3, 1, 5},    {4, 2, 2, 4, KIND_WIDE, 3, 2, 1, 7},
     {4, 2, 2, 4, KIND_WIDE, 2, 2, 1, 7},    {4, 2, 2, 4, KIND_WIDE, 3, 0, 1, 43},
-    {4, 2, 2, 4, KIND_WIDE, 3, 0, 1, 27}};
-constexpr int kNumTileCfgs = 23;
+    {4, 2, 2, 4, KIND_WIDE, 3, 0, 1, 27},   {4, 2, 2, 4, KIND_WIDE, 2, 0, 1, 27},
+    {4, 2, 2, 4, KIND_WIDE, 3, 0, 1, 37}};
+constexpr int kNumTileCfgs = 25;
 
 struct TreeSel {
     int mode;  // TREE_BLOCK or TREE_STACK
@@ -279,6 +280,12 @@ hipError_t launch_layout(int cfg, const TreeSel &t, const MfmaParams &p, int64_t
         return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 43, 0, 1, 2>(p, tiles, st);
     case 22:
         return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 27, 0, 1, 2>(p, tiles, st);
+    // 27-leaf units on two stage buffers, for the parked levels of L = 864
+    // (K = 27648); 37-leaf units (K = 18944, L = 592)
+    case 23:
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 2, 27, 0, 1, 2>(p, tiles, st);
+    case 24:
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 37, 0, 1, 2>(p, tiles, st);
     // Narrow tiles for 33 to 128 rows (X K-major, row-major output), the tree
     // split over wave groups (the stages per tile divided by their number):
     // 128x32 on 2 x 4 waves of 2 x 2 blocks with four stage buffers per group,
