@@ -319,3 +319,44 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_no_long_branch_through_a_return_address(tmp_path):
+    """The library's device code (built here from its sources) has no long
+    branch that goes through s[30:31]: in a called function those registers
+    hold the return address, and a long branch that reuses them makes the
+    function jump back into its own body when it returns (a recomputation
+    of non-finite tiles whose unrolled code outgrew the range of a short
+    branch never returned).  Each translation unit's offload bundle is
+    unbundled and disassembled with the ROCm LLVM tools."""
+    import re
+    import shutil
+    import subprocess
+    llvm = "/opt/rocm/llvm/bin"
+    tools = [os.path.join(llvm, t) for t in ("llvm-objcopy", "clang-offload-bundler", "llvm-objdump")]
+    if not all(os.path.exists(t) for t in tools) or not os.path.exists(dg.LIB_PATH):
+        pytest.skip("ROCm LLVM tools or the built library not present")
+    objcopy, bundler, objdump = tools
+    fatbin = tmp_path / "fatbin.bin"
+    subprocess.run([objcopy, "--dump-section", f".hip_fatbin={fatbin}", dg.LIB_PATH,
+                    str(tmp_path / "lib_copy.so")], check=True, capture_output=True)
+    data = fatbin.read_bytes()
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    starts = [m.start() for m in re.finditer(re.escape(magic), data)]
+    assert starts, "no offload bundles in the library"
+    scanned = 0
+    for i, o in enumerate(starts):
+        chunk = tmp_path / f"b{i}.bin"
+        chunk.write_bytes(data[o:starts[i + 1] if i + 1 < len(starts) else len(data)])
+        co = tmp_path / f"b{i}.co"
+        subprocess.run([bundler, "--type=o", "--targets=hipv4-amdgcn-amd-amdhsa--gfx950",
+                        f"--input={chunk}", f"--output={co}", "--unbundle"],
+                       check=True, capture_output=True)
+        if co.stat().st_size == 0:
+            continue
+        dis = subprocess.run([objdump, "-d", "--mcpu=gfx950", str(co)], check=True,
+                             capture_output=True, text=True).stdout
+        scanned += 1
+        assert not re.search(r"s_getpc_b64 s\[30:31\]", dis), f"translation unit {i}"
+    assert scanned >= 8
+    shutil.rmtree(tmp_path, ignore_errors=True)
