@@ -73,7 +73,7 @@ constexpr int kNumTileCfgs = 25;
 
 struct TreeSel {
     int mode;  // TREE_BLOCK or TREE_STACK
-    int tb;    // block base size b (1 or 3)
+    int tb;    // block base size b of the fast and general kernels (1 or 3)
     int tk;    // block = b * 2^tk leaves: 8 for b = 1, 12 for b = 3
 };
 

@@ -1,11 +1,14 @@
-// Wide-wave MFMA det_gemm kernel for gfx950, for power-of-two leaf counts.
+// Wide-wave MFMA det_gemm kernel for gfx950, for leaf counts L = m * 2^a with
+// m = 1, 3, 5, 7 or an odd m whose unit schedule is instantiated (27, 37, 43).
 //
 // Same leaves and same tree as mfma_kernel.h and mfma_fast.h, hence the same
 // bits (RL-Kernel operator page "Batch-Invariant Deterministic GEMM (det_gemm)",
 // sections "Guarantees" and "Ascend NPU backend": 32-element leaves rounded once
 // to bf16, mid-split tree of bf16 adds).  With L = 2^a the mid-split tree is the
 // perfect binary tree, and its lowest inner nodes are the pairs (2s, 2s + 1),
-// i.e. the two leaves of pipeline stage s.  What differs is the work layout:
+// i.e. the two leaves of pipeline stage s; with L = m * 2^a it is the perfect
+// tree over units of m leaves (WideTree below).  What differs is the work
+// layout:
 //   * each wave owns FM x FN blocks of 16x16 outputs (4 x 2: 64 x 32), so every
 //     step of the tree is FM * FN independent matrix-core instructions and a
 //     dependent step never waits on the latency of the previous one;
