@@ -173,7 +173,7 @@ bool staged_ok(const Problem &pr) {
 bool fast_ok(const Problem &pr, const TreeSel &t) { return t.mode == TREE_BLOCK && staged_ok(pr); }
 
 // The wide kernel: the fast kernel's operand conditions and a leaf count
-// L = 2 * tb * 2^k (tb = 1, 3, 5, 7, 27, 37 or 43: the mid-split tree is the perfect tree
+// L = 2 * tb * 2^k (tb = 1, 3, 5, 7, 11, 17, 19, 25, 27, 35, 37 or 43: the mid-split tree is the perfect tree
 // over units of tb leaves) with at least one group of 2^gl nodes of 2 * tb leaves
 // (with exactly one group, the group root is the root); a tree split at its
 // root over two or four wave groups needs units of one leaf, a K-major X, a
@@ -319,7 +319,7 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     }
     const int64_t t128 = ((pr.I + 127) / 128) * ((pr.J + 127) / 128);
     if (t128 >= 2 * 256)
-        for (int c : {8, 5, 9, 7, 17, 18, 19, 20, 21, 22, 23, 24})  // three stage buffers with early copies if the LDS holds them
+        for (int c : {8, 5, 9, 7, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29})  // three stage buffers with early copies if the LDS holds them
             if (wide_ok(pr, t, kTileCfgs[c], up))
                 return c;
     // 128x64 tiles while they fit one round, or two workgroups per compute
@@ -331,7 +331,7 @@ int pick_config(const Problem &pr, const TreeSel &t, int levels) {
     // deeper trees than configurations 5 and 8 hold: 128x128 tiles with a
     // second register level (K = 32768, M = 2048, N = 4096: 420 TFLOP/s
     // instead of 355 on 128x64; at 512 leaves and fewer it loses to them)
-    for (int c : {8, 5, 9, 7, 17, 18, 19, 20, 21, 22, 23, 24})
+    for (int c : {8, 5, 9, 7, 17, 18, 19, 20, 21, 22, 23, 24, 25, 26, 27, 28, 29})
         if (wide_ok(pr, t, kTileCfgs[c], up))
             return c;
     if (wide_ok(pr, t, kTileCfgs[6], up))

@@ -68,8 +68,10 @@ constexpr TileCfg kTileCfgs[] = {
     {4, 2, 2, 4, KIND_WIDE, 3, 3, 1, 5},    {4, 2, 2, 4, KIND_WIDE, 3, 2, 1, 7},
     {4, 2, 2, 4, KIND_WIDE, 2, 2, 1, 7},    {4, 2, 2, 4, KIND_WIDE, 3, 0, 1, 43},
     {4, 2, 2, 4, KIND_WIDE, 3, 0, 1, 27},   {4, 2, 2, 4, KIND_WIDE, 2, 0, 1, 27},
-    {4, 2, 2, 4, KIND_WIDE, 3, 0, 1, 37}};
-constexpr int kNumTileCfgs = 25;
+    {4, 2, 2, 4, KIND_WIDE, 3, 0, 1, 37},   {4, 2, 2, 4, KIND_WIDE, 3, 0, 1, 11},
+    {4, 2, 2, 4, KIND_WIDE, 2, 0, 1, 17},   {4, 2, 2, 4, KIND_WIDE, 3, 0, 1, 19},
+    {4, 2, 2, 4, KIND_WIDE, 2, 0, 1, 25},   {4, 2, 2, 4, KIND_WIDE, 3, 0, 1, 35}};
+constexpr int kNumTileCfgs = 30;
 
 struct TreeSel {
     int mode;  // TREE_BLOCK or TREE_STACK
@@ -286,6 +288,19 @@ hipError_t launch_layout(int cfg, const TreeSel &t, const MfmaParams &p, int64_t
         return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 2, 27, 0, 1, 2>(p, tiles, st);
     case 24:
         return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 37, 0, 1, 2>(p, tiles, st);
+    // more odd unit sizes of common reduction lengths: 11 (K = 2816, 5632),
+    // 17 (17408), 19 (4864, 9728), 25 (25600), 35 (8960); 17 and 25 on two
+    // stage buffers, whose LDS holds the parked levels of L = 544 and 800
+    case 25:
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 11, 0, 1, 2>(p, tiles, st);
+    case 26:
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 2, 17, 0, 1, 2>(p, tiles, st);
+    case 27:
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 19, 0, 1, 2>(p, tiles, st);
+    case 28:
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 2, 25, 0, 1, 2>(p, tiles, st);
+    case 29:
+        return launch_wide<XK, YK, OUT, 4, 2, 2, 4, 3, 35, 0, 1, 2>(p, tiles, st);
     // Narrow tiles for 33 to 128 rows (X K-major, row-major output), the tree
     // split over wave groups (the stages per tile divided by their number):
     // 128x32 on 2 x 4 waves of 2 x 2 blocks with four stage buffers per group,

@@ -1,5 +1,6 @@
 // Wide-wave MFMA det_gemm kernel for gfx950, for leaf counts L = m * 2^a with
-// m = 1, 3, 5, 7 or an odd m whose unit schedule is instantiated (27, 37, 43).
+// m = 1, 3, 5, 7 or an odd m whose unit schedule is instantiated (11, 17, 19,
+// 25, 27, 35, 37, 43).
 //
 // Same leaves and same tree as mfma_kernel.h and mfma_fast.h, hence the same
 // bits (RL-Kernel operator page "Batch-Invariant Deterministic GEMM (det_gemm)",

@@ -390,7 +390,7 @@ def test_mfma_tile_configs_identical(dev, K):
 FAST_SHAPES = [(200, 192, 256), (256, 136, 768), (320, 256, 4096), (128, 64, 12288),
                (72, 64, 32768), (512, 512, 1024), (264, 392, 8192), (768, 384, 1536),
                (384, 768, 6144)]
-GENERAL_CFG, FAST_CFGS = 2, (3, 4, 5, 6, 7, 8, 9, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23, 24)
+GENERAL_CFG, FAST_CFGS = 2, (3, 4, 5, 6, 7, 8, 9, 13, 14, 15, 16, 17) + tuple(range(18, 30))
 
 
 def _six_forced(cfg, A, B, dC):
@@ -512,10 +512,10 @@ def test_errors_leave_output_untouched(dev):
     assert np.array_equal(roots, bits(got))
 
 
-# Leaf counts L = m * 2^a for m = 5, 7, 27, 37, 43: the mid-split tree is the
-# perfect tree over units of m leaves, which the wide kernel evaluates in
-# configurations 18 to 24 (m stages per pair of units; 27, 37 and 43 walk each
-# unit's tree with a stack of static register slots).  Each
+# Leaf counts L = m * 2^a for m = 5, 7, 11, 17, 19, 25, 27, 35, 37, 43: the
+# mid-split tree is the perfect tree over units of m leaves, which the wide
+# kernel evaluates in configurations 18 to 29 (m stages per pair of units; from
+# m = 11 on, each unit's tree walked with a stack of static register slots).  Each
 # reduction (K for the forward family, N for da, M for db) with such a leaf
 # count, ragged tiles included, against the general kernel, bit for bit.
 @pytest.mark.parametrize("M,N,K", [
@@ -534,13 +534,18 @@ def test_errors_leave_output_untouched(dev):
     (11008, 256, 384),    # db: L = 344 over M
     (128, 256, 27648),    # L = 864 = 27 * 32: two stage buffers (configuration 23)
     (256, 200, 18944),    # L = 592 = 37 * 16: units of 37 leaves (configuration 24)
+    (256, 136, 5632),     # L = 176 = 11 * 16 (configuration 25)
+    (128, 256, 17408),    # L = 544 = 17 * 32, two stage buffers (26)
+    (200, 256, 9728),     # L = 304 = 19 * 16 (27)
+    (128, 128, 25600),    # L = 800 = 25 * 32, two stage buffers (28)
+    (256, 256, 8960),     # L = 280 = 35 * 8 (29)
 ])
 def test_wide_kernel_five_and_seven_leaf_units(dev, M, N, K):
     say("wide kernel, units of five and seven leaves vs general kernel", M, N, K)
     A, B, dC = [t.to(dev) for t in _inputs(M, N, K, 970 + K + M, sigma=0.02)]
     ref = _six_forced(GENERAL_CFG, A, B, dC)
     ran = 0
-    for cfg in (18, 19, 20, 21, 22, 23, 24):
+    for cfg in range(18, 30):
         got = _six_forced(cfg, A, B, dC)
         for op, g in got.items():
             if g is None:
@@ -557,7 +562,7 @@ def test_wide_kernel_five_and_seven_leaf_units(dev, M, N, K):
 # The wide kernels' tree adds run on the matrix core, where one non-finite node
 # spoils the other sums of its row; such tiles are recomputed with element-wise
 # adds.  Inf and NaN inputs must give the general kernel's bits.
-@pytest.mark.parametrize("K", [1024, 1536, 5120, 7168, 11008, 13824, 18944])
+@pytest.mark.parametrize("K", [1024, 1536, 5120, 7168, 11008, 13824, 18944, 5632, 8960])
 def test_wide_kernel_nonfinite_inputs(dev, K):
     say("wide kernels, non-finite inputs vs general kernel", K)
     M, N = 1024, 768
@@ -569,7 +574,7 @@ def test_wide_kernel_nonfinite_inputs(dev, K):
     Ad, Bd, dCd = A.to(dev), B.to(dev), dC.to(dev)
     ref = _six_forced(GENERAL_CFG, Ad, Bd, dCd)
     ran = 0
-    for cfg in (5, 6, 7, 8, 9, 13, 14, 15, 16, 17, 18, 19, 20, 21, 22, 23, 24):
+    for cfg in (5, 6, 7, 8, 9, 13, 14, 15, 16, 17) + tuple(range(18, 30)):
         got = _six_forced(cfg, Ad, Bd, dCd)
         for op, g in got.items():
             if g is None:

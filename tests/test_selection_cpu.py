@@ -10,7 +10,8 @@ units), 10 to 12 decode kernels with 16, 64 and 32 columns per workgroup, 13
 and 14 the 128x32 and 64x32 wide tiles whose tree is split at its root over
 two wave groups, 15 and 16 the 64x32 and 64x64 tiles on four wave groups,
 17 the 128x128 tiles with two register levels for the deepest trees, 18 to
-24 the 128x128 tiles over units of 5, 7, 43, 27 and 37 leaves.
+29 the 128x128 tiles over units of 5, 7, 43, 27, 37, 11, 17, 19, 25 and 35
+leaves.
 """
 import pytest
 
@@ -205,6 +206,11 @@ def test_mid_size_products_by_leaves_and_tiles(M, N, K, want):
     (13824, 22),    # L = 432 = 27 * 16: 27-leaf units
     (27648, 23),    # L = 864 = 27 * 32: 27-leaf units on two stage buffers
     (18944, 24),    # L = 592 = 37 * 16: 37-leaf units
+    (5632, 25),     # L = 176 = 11 * 16
+    (17408, 26),    # L = 544 = 17 * 32, two stage buffers
+    (9728, 27),     # L = 304 = 19 * 16
+    (25600, 28),    # L = 800 = 25 * 32, two stage buffers
+    (8960, 29),     # L = 280 = 35 * 8
     (4128, 2),      # L = 129: no unit schedule
 ])
 def test_unit_schedules_by_leaf_count(K, want):
