@@ -582,3 +582,23 @@ def test_wide_kernel_nonfinite_inputs(dev, K):
             ran += 1
             assert np.array_equal(g, ref[op]), (cfg, op)
     assert ran >= 6
+
+
+# The batch-invariance guarantee across the kernels that the automatic choice
+# picks for one weight as M grows (decode kernel, split tiles, the wide
+# kernel's unit schedules): a row's bits do not depend on how many rows are
+# computed with it.
+@pytest.mark.parametrize("K", [5120, 7168, 11008, 13824])
+def test_rows_invariant_across_batch_sizes_with_unit_schedules(dev, K):
+    say("rows across batch sizes, unit schedules", K)
+    N = 384
+    X = W.randn_bf16((1024, K), 1.0, 990 + K).to(dev)
+    Wt = W.randn_bf16((K, N), 0.02, 991 + K).to(dev)
+    full = dg.det_gemm_fwd(X, Wt).view(torch.int16)
+    full_t = dg.det_gemm_fwd_rhs_transposed(X, Wt.t().contiguous()).view(torch.int16)
+    assert torch.equal(full, full_t)
+    for m in (1, 16, 40, 100, 300):
+        part = dg.det_gemm_fwd(X[:m].contiguous(), Wt).view(torch.int16)
+        assert torch.equal(part, full[:m]), m
+    off = dg.det_gemm_fwd(X[517:517 + 200].contiguous(), Wt).view(torch.int16)
+    assert torch.equal(off, full[517:717])
